@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of hierarchical block-then-token sparse attention on one GPU.
+
+One step = one hsa_forward call over the workload's whole batch: block
+summaries of every block, block top-m, token top-k and sparse attention,
+with inputs already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Per-step stage times come from HIP events that hsa_forward records on its
+stream inside the timed region (hsa_sparse_set_stage_events).  The roofline
+entry uses the dominant stage's algorithmic bytes (or flops) per launch,
+computed in closed form below, divided by its measured average duration.
+The CPU baseline times the plain CPU oracle on a stratified sample of the
+same workload's queries, before the GPU is touched.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from hierarchical_index_sparse_amd import datagen  # noqa: E402
+from hierarchical_index_sparse_amd.workloads import WORKLOADS, Workload  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+STAGES = ("block_summary", "block_topm", "token_topk", "sparse_attn")
+
+
+# --------------------------------------------------------------- work model
+
+
+def per_query_counts(w: Workload):
+    """Closed-form per-query sizes: scored blocks, candidate tokens, kept tokens."""
+    t = w.seq_len - w.n_q + np.arange(w.n_q, dtype=np.int64)
+    c = t // w.block
+    scored_blocks = np.where(c + 1 <= w.top_m, 0, c - 1)
+    n_sel = np.minimum(c + 1, w.top_m)
+    n_valid = (n_sel - 1) * w.block + (t - c * w.block + 1)
+    scored_tokens = np.where(n_valid <= w.top_k, 0, n_valid)
+    kept = np.minimum(n_valid, w.top_k)
+    return scored_blocks, scored_tokens, kept
+
+
+def algorithmic_work(w: Workload) -> dict:
+    """Bytes each step must move (and flops it must do), per stage."""
+    sb, st, kept = per_query_counts(w)
+    b, nq = w.batch, w.n_q
+    dI, nL, d = w.d_index, w.n_landmarks, w.head_dim
+    start = (w.seq_len - nq) // w.block
+    summ_rows = min(w.seq_len, w.n_blocks * w.block) - start * w.block
+    summ_bytes = b * summ_rows * dI * 2 + b * (w.n_blocks - start) * nL * dI * 2
+    topm_flops = 2.0 * dI * nL * b * sb.sum()
+    topm_bytes = b * (nq * dI * 2 + sb.sum() * nL * dI * 2 + nq * w.top_m * 4)
+    topk_bytes = b * (st.sum() * dI * 2 + nq * w.top_k * 4 + nq * w.top_m * 4)
+    attn_bytes = b * (kept.sum() * w.n_heads_kv * d * 2 * 2 + nq * w.n_heads_q * d * (2 + 4)
+                      + nq * w.top_k * 4)
+    attn_flops = 4.0 * d * w.n_heads_q * b * kept.sum()
+    return {
+        "block_summary": {"bytes": float(summ_bytes), "flops": 0.0},
+        "block_topm": {"bytes": float(topm_bytes), "flops": float(topm_flops)},
+        "token_topk": {"bytes": float(topk_bytes), "flops": float(2.0 * dI * b * st.sum())},
+        "sparse_attn": {"bytes": float(attn_bytes), "flops": float(attn_flops)},
+    }
+
+
+# -------------------------------------------------------------- CPU oracle
+
+
+_ORC_STATE = {}
+
+
+def _oracle_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_one(args):
+    from oracle import hisa_oracle as orc
+    b, i = args
+    w, inp, S = _ORC_STATE["w"], _ORC_STATE["inp"], _ORC_STATE["S"]
+    orc.forward_query(inp, b, i, w.query_pos(i), w.block, w.top_m, w.top_k, w.scale, S_bits=S[b])
+    return 1
+
+
+def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
+    """Time the CPU oracle on an evenly spaced sample of the workload's queries."""
+    import multiprocessing as mp
+
+    from oracle import hisa_oracle as orc
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cores = max(1, min(cores, 16))
+    t0 = time.perf_counter()
+    S = [orc.block_summary(inp["kI"][b], w.block, inp.get("W")) for b in range(w.batch)]
+    t_summary = time.perf_counter() - t0
+    total = w.batch * w.n_q
+    n = min(sample, total)
+    flat = np.unique(np.linspace(0, total - 1, n).round().astype(np.int64))
+    queries = [(int(x // w.n_q), int(x % w.n_q)) for x in flat]
+    _ORC_STATE.update(w=w, inp=inp, S=S)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores, initializer=_oracle_worker_init) as pool:
+        done = sum(pool.map(_oracle_one, queries, chunksize=max(1, len(queries) // (4 * cores))))
+    wall = time.perf_counter() - t0
+    _ORC_STATE.clear()
+    # the summaries are built once per sequence: charge them in full
+    return {
+        "value": done / (wall + t_summary),
+        "unit": "queries/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{done} of {total} queries, evenly spaced over the batch and positions; "
+                  f"block summaries of all {w.batch} sequence(s) built once ({t_summary:.2f} s); "
+                  f"{wall:.1f} s wall on {cores} worker processes",
+    }
+
+
+# ------------------------------------------------------------- HIP events
+
+
+class HipEvents:
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(b) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+# ------------------------------------------------------------------- main
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_64k", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="queries the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sequences or queries would shard with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    inp = datagen.make_inputs(w)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_sample)
+
+    import torch
+
+    from hierarchical_index_sparse_amd import _lib, pipeline
+    dev = pipeline.to_device(inp)
+    out = pipeline.alloc_outputs(w)
+    shape = _lib.shape_of(w)
+    ws = torch.empty(_lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_FORWARD), dtype=torch.uint8,
+                     device="cuda")
+
+    # summaries of blocks before the new queries are state (built once at
+    # ingest); each step re-summarises the blocks the queries' tokens touch
+    start_block = (w.seq_len - w.n_q) // w.block
+    _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), 0, out["S"])
+
+    def step():
+        _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), start_block, out["S"], dev["Q"], dev["K"],
+                         dev["V"], None, None, out["O"], out["lse"], ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    events = [[hip.create() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        _lib.hsa_sparse_set_stage_events(events[s])
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.hsa_sparse_set_stage_events(None)
+
+    stage_ms = {name: float(np.mean([hip.elapsed_ms(ev[i], ev[i + 1]) for ev in events]))
+                for i, name in enumerate(STAGES)}
+    gpu_step_ms = float(np.mean([hip.elapsed_ms(ev[0], ev[4]) for ev in events]))
+    for ev in events:
+        for e in ev:
+            hip.destroy(e)
+
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    queries = w.batch * w.n_q
+    value = queries / (ms_per_step / 1000.0)
+
+    work = algorithmic_work(w)
+    dom = max(STAGES, key=lambda n: stage_ms[n])
+    dom_s = stage_ms[dom] / 1000.0
+    if dom == "block_topm":
+        achieved = work[dom]["flops"] / dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    else:
+        achieved = work[dom]["bytes"] / dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    roof["stage"] = dom
+    roof["algorithmic_per_launch"] = work[dom]["flops"] if dom == "block_topm" else work[dom]["bytes"]
+
+    res = {
+        "metric": "queries/sec end-to-end (index+attn)",
+        "value": value,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp32 accumulate",
+        "data": "synthetic (seeded; integer-valued bf16 indexer vectors, N(0,1) bf16 Q/K/V)",
+        "config": {"workload": w.name, "summary_start_block": start_block, "batch": w.batch, "seq_len": w.seq_len, "n_q": w.n_q,
+                   "d_index": w.d_index, "block": w.block, "top_m": w.top_m, "top_k": w.top_k,
+                   "heads_q": w.n_heads_q, "heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
+                   "n_landmarks": w.n_landmarks, "parallelism": "single GPU"},
+        "stage_ms": stage_ms,
+        "gpu_step_ms": gpu_step_ms,
+        "stage_hbm_frac": {n: work[n]["bytes"] / (stage_ms[n] / 1000.0) / 1e9 / HBM_PEAK_GBS for n in STAGES},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+"""ctypes binding of libhsa_sparse.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU (torch is used for device memory and
+streams only).  bf16 tensors may be ``torch.bfloat16`` or 16-bit integer
+views of the same bits.  There is no fallback: if the shared library is
+missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhsa_sparse.so")
+
+HSA_SPARSE_OP_BLOCK_SUMMARY = 0
+HSA_SPARSE_OP_BLOCK_TOPM = 1
+HSA_SPARSE_OP_TOKEN_TOPK = 2
+HSA_SPARSE_OP_SPARSE_ATTN = 3
+HSA_SPARSE_OP_FORWARD = 4
+
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "HIP_ERROR"}
+
+EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_error",
+           "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
+           "hsa_sparse_set_stage_events")
+
+
+class HsaSparseShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seq_len", "n_q", "d_index", "block", "n_landmarks", "top_m", "top_k",
+        "n_heads_q", "n_heads_kv", "head_dim")] + [("scale", ctypes.c_float)]
+
+
+class HsaSparseError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: {self.status_name}: {detail}")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m hierarchical_index_sparse_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    P, S, I32, SZ = ctypes.c_void_p, ctypes.POINTER(HsaSparseShape), ctypes.c_int32, ctypes.c_size_t
+    lib.hsa_sparse_workspace_size.argtypes = [S, ctypes.c_int]
+    lib.hsa_sparse_workspace_size.restype = SZ
+    lib.hsa_sparse_strerror.argtypes = [ctypes.c_int]
+    lib.hsa_sparse_strerror.restype = ctypes.c_char_p
+    lib.hsa_sparse_last_error.argtypes = []
+    lib.hsa_sparse_last_error.restype = ctypes.c_char_p
+    lib.hsa_block_summary.argtypes = [S, P, P, I32, P, P]
+    lib.hsa_block_topm.argtypes = [S, P, P, P, P, SZ, P]
+    lib.hsa_token_topk.argtypes = [S, P, P, P, P, P, SZ, P]
+    lib.hsa_sparse_attn.argtypes = [S, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward.argtypes = [S, P, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_sparse_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
+                 "hsa_sparse_set_stage_events"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_shape(batch, seq_len, n_q, d_index, block, top_m, top_k, n_heads_q=1, n_heads_kv=1,
+               head_dim=128, n_landmarks=1, scale=None) -> HsaSparseShape:
+    if scale is None:
+        scale = head_dim ** -0.5
+    return HsaSparseShape(batch, seq_len, n_q, d_index, block, n_landmarks, top_m, top_k,
+                          n_heads_q, n_heads_kv, head_dim, scale)
+
+
+def shape_of(w) -> HsaSparseShape:
+    """Shape struct of a workloads.Workload."""
+    return make_shape(w.batch, w.seq_len, w.n_q, w.d_index, w.block, w.top_m, w.top_k,
+                      w.n_heads_q, w.n_heads_kv, w.head_dim, w.n_landmarks, w.scale)
+
+
+def _ptr(t, name, dtypes, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_I8 = (torch.int8,)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        lib = load()
+        raise HsaSparseError(status, where, lib.hsa_sparse_last_error().decode())
+
+
+def hsa_sparse_workspace_size(shape: HsaSparseShape, op: int) -> int:
+    return int(load().hsa_sparse_workspace_size(ctypes.byref(shape), op))
+
+
+def _workspace(shape, op, ws, device):
+    need = hsa_sparse_workspace_size(shape, op)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def hsa_block_summary(shape, kI, W, start_block, S, stream=None):
+    st = load().hsa_block_summary(ctypes.byref(shape), _ptr(kI, "kI", _BF16), _ptr(W, "W", _I8, True),
+                                  int(start_block), _ptr(S, "S", _BF16), _stream(stream))
+    _check(st, "hsa_block_summary")
+
+
+def hsa_block_topm(shape, qI, S, blk, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_BLOCK_TOPM, workspace, qI.device)
+    st = load().hsa_block_topm(ctypes.byref(shape), _ptr(qI, "qI", _BF16), _ptr(S, "S", _BF16),
+                               _ptr(blk, "blk", _I32), ws.data_ptr(), nbytes, _stream(stream))
+    _check(st, "hsa_block_topm")
+
+
+def hsa_token_topk(shape, qI, kI, blk, tok, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_TOKEN_TOPK, workspace, qI.device)
+    st = load().hsa_token_topk(ctypes.byref(shape), _ptr(qI, "qI", _BF16), _ptr(kI, "kI", _BF16),
+                               _ptr(blk, "blk", _I32), _ptr(tok, "tok", _I32), ws.data_ptr(), nbytes,
+                               _stream(stream))
+    _check(st, "hsa_token_topk")
+
+
+def hsa_sparse_attn(shape, Q, K, V, tok, O, lse=None, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_SPARSE_ATTN, workspace, Q.device)
+    st = load().hsa_sparse_attn(ctypes.byref(shape), _ptr(Q, "Q", _BF16), _ptr(K, "K", _BF16),
+                                _ptr(V, "V", _BF16), _ptr(tok, "tok", _I32), _ptr(O, "O", _F32),
+                                _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes, _stream(stream))
+    _check(st, "hsa_sparse_attn")
+
+
+def hsa_forward(shape, qI, kI, W, summary_start_block, S, Q, K, V, blk_out, tok_out, O, lse=None,
+                workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_FORWARD, workspace, Q.device)
+    st = load().hsa_forward(ctypes.byref(shape), _ptr(qI, "qI", _BF16), _ptr(kI, "kI", _BF16),
+                            _ptr(W, "W", _I8, True), int(summary_start_block), _ptr(S, "S", _BF16),
+                            _ptr(Q, "Q", _BF16), _ptr(K, "K", _BF16), _ptr(V, "V", _BF16),
+                            _ptr(blk_out, "blk_out", _I32, True), _ptr(tok_out, "tok_out", _I32, True),
+                            _ptr(O, "O", _F32), _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes,
+                            _stream(stream))
+    _check(st, "hsa_forward")
+
+
+def hsa_sparse_set_stage_events(events):
+    """events: 5 raw hipEvent_t handles (ints), or None to stop recording."""
+    lib = load()
+    if events is None:
+        _check(lib.hsa_sparse_set_stage_events(None, 0), "hsa_sparse_set_stage_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check(lib.hsa_sparse_set_stage_events(arr, len(events)), "hsa_sparse_set_stage_events")

@@ -1,0 +1,259 @@
+// C ABI of the library: argument validation, workspace layout and the
+// launch sequence of each entry point.  Nothing here allocates device memory
+// or synchronises the host; every check runs before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "hsa_sparse.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hsa_sparse_event_t g_stage_events[5];
+thread_local bool g_record_stages = false;
+
+hsa_sparse_status_t fail(hsa_sparse_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+hsa_sparse_status_t hip_fail(hipError_t e, const char* where) {
+  return fail(HSA_SPARSE_HIP_ERROR, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+enum : unsigned { kSummary = 1u, kSelect = 2u, kAttn = 4u };
+
+// Checks shared by every entry point; `parts` names the fields the entry
+// point reads.  Fills `d` on success.
+hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsigned parts) {
+  const bool need_index = parts & (kSummary | kSelect);
+  const bool need_attn = parts & kAttn;
+  if (!s) return fail(HSA_SPARSE_INVALID_ARG, "shape is NULL");
+  if (s->batch < 0 || s->seq_len < 0 || s->n_q < 0)
+    return fail(HSA_SPARSE_INVALID_ARG, "negative batch / seq_len / n_q");
+  if (s->n_q > s->seq_len) return fail(HSA_SPARSE_INVALID_ARG, "n_q (%d) > seq_len (%d)", s->n_q, s->seq_len);
+  if (parts & kSelect) {
+    if (s->top_m < 2) return fail(HSA_SPARSE_INVALID_ARG, "top_m must be >= 2 (first and last block are kept)");
+    if (s->top_k < 1) return fail(HSA_SPARSE_INVALID_ARG, "top_k must be >= 1");
+  }
+  if (need_index) {
+    if (s->d_index != 64 && s->d_index != 128)
+      return fail(HSA_SPARSE_UNSUPPORTED, "d_index must be 64 or 128 (got %d)", s->d_index);
+    if (!is_pow2(s->block) || s->block < 8 || s->block > 128)
+      return fail(HSA_SPARSE_UNSUPPORTED, "block must be a power of two in [8, 128] (got %d)", s->block);
+    if (s->n_landmarks != 1 && s->n_landmarks != 2 && s->n_landmarks != 4)
+      return fail(HSA_SPARSE_UNSUPPORTED, "n_landmarks must be 1, 2 or 4 (got %d)", s->n_landmarks);
+    const long long nb = ((long long)s->seq_len + s->block - 1) / s->block;
+    if (nb - 2 > 32768) return fail(HSA_SPARSE_UNSUPPORTED, "too many blocks (%lld > 32770)", nb);
+    if ((parts & kSelect) && (long long)s->top_m * s->block > 32768 &&
+        (long long)s->top_k < (long long)s->top_m * s->block)
+      return fail(HSA_SPARSE_UNSUPPORTED, "top_m * block > 32768 candidates with top_k < top_m * block");
+  }
+  if (!(parts & kSelect) && need_attn && s->top_k < 1) return fail(HSA_SPARSE_INVALID_ARG, "top_k must be >= 1");
+  if (need_attn) {
+    if (s->head_dim != 128) return fail(HSA_SPARSE_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
+    if (s->n_heads_q < 1 || s->n_heads_kv < 1 || s->n_heads_q % s->n_heads_kv != 0)
+      return fail(HSA_SPARSE_INVALID_ARG, "n_heads_kv must divide n_heads_q");
+    if (s->n_heads_q / s->n_heads_kv > 16)
+      return fail(HSA_SPARSE_UNSUPPORTED, "at most 16 query heads per kv head");
+    if (!(s->scale == s->scale)) return fail(HSA_SPARSE_INVALID_ARG, "scale is NaN");
+  }
+  const long long nq_total = (long long)s->batch * s->n_q;
+  if (nq_total > (1ll << 30)) return fail(HSA_SPARSE_UNSUPPORTED, "batch * n_q too large");
+  d.b = s->batch;
+  d.L = s->seq_len;
+  d.nq = s->n_q;
+  d.dI = s->d_index;
+  d.B = s->block > 0 ? s->block : 1;
+  d.nL = s->n_landmarks;
+  d.m = s->top_m;
+  d.k = s->top_k;
+  d.Hq = s->n_heads_q;
+  d.Hkv = s->n_heads_kv;
+  d.d = s->head_dim;
+  d.scale = s->scale;
+  d.nb = (int)(((long long)s->seq_len + d.B - 1) / d.B);
+  g_last_error.clear();
+  return HSA_SPARSE_OK;
+}
+
+bool empty(const hsa::Dims& d) { return d.b == 0 || d.nq == 0; }
+
+struct ForwardLayout {
+  size_t blk_off, tok_off, stage_off, total;
+};
+
+ForwardLayout forward_layout(const hsa::Dims& d) {
+  using hsa::align_up;
+  ForwardLayout f;
+  const size_t nqt = (size_t)d.b * d.nq;
+  f.blk_off = 0;
+  f.tok_off = align_up(nqt * d.m * sizeof(int32_t));
+  f.stage_off = f.tok_off + align_up(nqt * d.k * sizeof(int32_t));
+  size_t stage = hsa::block_topm_ws_bytes(d);
+  stage = std::max(stage, hsa::token_topk_ws_bytes(d));
+  stage = std::max(stage, hsa::sparse_attn_ws_bytes(d));
+  f.total = f.stage_off + stage;
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hsa_sparse_strerror(hsa_sparse_status_t status) {
+  switch (status) {
+    case HSA_SPARSE_OK: return "success";
+    case HSA_SPARSE_INVALID_ARG: return "invalid argument";
+    case HSA_SPARSE_UNSUPPORTED: return "unsupported shape";
+    case HSA_SPARSE_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case HSA_SPARSE_HIP_ERROR: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* hsa_sparse_last_error(void) { return g_last_error.c_str(); }
+
+hsa_sparse_status_t hsa_sparse_set_stage_events(hsa_sparse_event_t const* events, int n_events) {
+  if (n_events == 0 && !events) {
+    g_record_stages = false;
+    return HSA_SPARSE_OK;
+  }
+  if (n_events != 5 || !events) return fail(HSA_SPARSE_INVALID_ARG, "need 5 events (or 0 and NULL)");
+  for (int i = 0; i < 5; ++i) {
+    if (!events[i]) return fail(HSA_SPARSE_INVALID_ARG, "event %d is NULL", i);
+    g_stage_events[i] = events[i];
+  }
+  g_record_stages = true;
+  return HSA_SPARSE_OK;
+}
+
+size_t hsa_sparse_workspace_size(const hsa_sparse_shape_t* shape, int op) {
+  hsa::Dims d;
+  switch (op) {
+    case HSA_SPARSE_OP_BLOCK_SUMMARY: return 0;  // streams kI once, no scratch
+    case HSA_SPARSE_OP_BLOCK_TOPM:
+      return check_shape(shape, d, kSelect | kSummary) == HSA_SPARSE_OK ? hsa::block_topm_ws_bytes(d) : 0;
+    case HSA_SPARSE_OP_TOKEN_TOPK:
+      return check_shape(shape, d, kSelect | kSummary) == HSA_SPARSE_OK ? hsa::token_topk_ws_bytes(d) : 0;
+    case HSA_SPARSE_OP_SPARSE_ATTN:
+      return check_shape(shape, d, kAttn) == HSA_SPARSE_OK ? hsa::sparse_attn_ws_bytes(d) : 0;
+    case HSA_SPARSE_OP_FORWARD:
+      return check_shape(shape, d, kSummary | kSelect | kAttn) == HSA_SPARSE_OK ? forward_layout(d).total : 0;
+    default: return 0;
+  }
+}
+
+hsa_sparse_status_t hsa_block_summary(const hsa_sparse_shape_t* shape, const uint16_t* kI, const int8_t* landmark_W,
+                                      int32_t start_block, uint16_t* S, hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSummary);
+  if (st != HSA_SPARSE_OK) return st;
+  if (start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "start_block < 0");
+  if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
+  if (d.b == 0 || d.L == 0 || start_block >= d.nb) return HSA_SPARSE_OK;
+  if (!kI || !S) return fail(HSA_SPARSE_INVALID_ARG, "kI or S is NULL");
+  hipError_t e = hsa::launch_block_summary(d, kI, landmark_W, start_block, S, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_block_summary");
+}
+
+hsa_sparse_status_t hsa_block_topm(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* S,
+                                   int32_t* blk, void* workspace, size_t workspace_bytes,
+                                   hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSelect | kSummary);
+  if (st != HSA_SPARSE_OK) return st;
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!qI || !S || !blk) return fail(HSA_SPARSE_INVALID_ARG, "qI, S or blk is NULL");
+  const size_t need = hsa::block_topm_ws_bytes(d);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "block_topm needs %zu workspace bytes", need);
+  hipError_t e = hsa::launch_block_topm(d, qI, S, blk, workspace, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_block_topm");
+}
+
+hsa_sparse_status_t hsa_token_topk(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,
+                                   const int32_t* blk, int32_t* tok, void* workspace, size_t workspace_bytes,
+                                   hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSelect | kSummary);
+  if (st != HSA_SPARSE_OK) return st;
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!qI || !kI || !blk || !tok) return fail(HSA_SPARSE_INVALID_ARG, "qI, kI, blk or tok is NULL");
+  const size_t need = hsa::token_topk_ws_bytes(d);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "token_topk needs %zu workspace bytes", need);
+  hipError_t e = hsa::launch_token_topk(d, qI, kI, blk, tok, workspace, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_token_topk");
+}
+
+hsa_sparse_status_t hsa_sparse_attn(const hsa_sparse_shape_t* shape, const uint16_t* Q, const uint16_t* K,
+                                    const uint16_t* V, const int32_t* tok, float* O, float* lse, void* workspace,
+                                    size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kAttn);
+  if (st != HSA_SPARSE_OK) return st;
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!Q || !K || !V || !tok || !O) return fail(HSA_SPARSE_INVALID_ARG, "Q, K, V, tok or O is NULL");
+  const size_t need = hsa::sparse_attn_ws_bytes(d);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "sparse_attn needs %zu workspace bytes", need);
+  hipError_t e = hsa::launch_sparse_attn(d, Q, K, V, tok, O, lse, workspace, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_sparse_attn");
+}
+
+hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,
+                                const int8_t* landmark_W, int32_t summary_start_block, uint16_t* S,
+                                const uint16_t* Q, const uint16_t* K, const uint16_t* V, int32_t* blk_out,
+                                int32_t* tok_out, float* O, float* lse, void* workspace, size_t workspace_bytes,
+                                hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSummary | kSelect | kAttn);
+  if (st != HSA_SPARSE_OK) return st;
+  if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
+  if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!qI || !kI || !S || !Q || !K || !V || !O)
+    return fail(HSA_SPARSE_INVALID_ARG, "qI, kI, S, Q, K, V or O is NULL");
+  const ForwardLayout f = forward_layout(d);
+  if (workspace_bytes < f.total || !workspace)
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "forward needs %zu workspace bytes", f.total);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* blk = blk_out ? blk_out : reinterpret_cast<int32_t*>(ws + f.blk_off);
+  int32_t* tok = tok_out ? tok_out : reinterpret_cast<int32_t*>(ws + f.tok_off);
+  void* stage = ws + f.stage_off;
+  const bool rec = g_record_stages;
+#define HSA_MARK(i)                                                              \
+  if (rec) {                                                                     \
+    hipError_t er = hipEventRecord((hipEvent_t)g_stage_events[i], stream);       \
+    if (er != hipSuccess) return hip_fail(er, "hsa_forward (stage event)");      \
+  }
+  HSA_MARK(0)
+  hipError_t e = hsa::launch_block_summary(d, kI, landmark_W, summary_start_block, S, stream);
+  if (e != hipSuccess) return hip_fail(e, "hsa_forward (block summary)");
+  HSA_MARK(1)
+  e = hsa::launch_block_topm(d, qI, S, blk, stage, stream);
+  if (e != hipSuccess) return hip_fail(e, "hsa_forward (block top-m)");
+  HSA_MARK(2)
+  e = hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
+  if (e != hipSuccess) return hip_fail(e, "hsa_forward (token top-k)");
+  HSA_MARK(3)
+  e = hsa::launch_sparse_attn(d, Q, K, V, tok, O, lse, stage, stream);
+  if (e != hipSuccess) return hip_fail(e, "hsa_forward (sparse attention)");
+  HSA_MARK(4)
+#undef HSA_MARK
+  return HSA_SPARSE_OK;
+}
+
+}  // extern "C"

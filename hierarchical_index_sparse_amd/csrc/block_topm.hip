@@ -1,0 +1,156 @@
+// Step 2: block scores and the top-m block selection.
+//
+// HISA page (two-step method, step one): the block summaries are scored with
+// the indexer's own rule (dot product with the query's indexer vector) and
+// the best m blocks are kept; the first block and the last block (the one
+// holding the query) are always kept.  HiLS page (section 2.2): a chunk's
+// coarse score comes from its landmark vectors; here the maximum over them.
+//
+// Kernel 1 (k_block_scores): score_j = max_l qI . S[j, l] for the causal
+// blocks 1..c-1 of every query that needs scoring (c + 1 > m), written as
+// fp32 to the workspace.  Each wave streams summary rows with 16-byte loads
+// (d_index/8 lanes per row), multiplies by the query chunk it holds in
+// registers and reduces across the row's lanes with xor shuffles.
+// Kernel 2 (k_block_select): one workgroup per query runs the exact
+// register-resident select of select.hpp over those scores.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "select.hpp"
+
+namespace hsa {
+
+constexpr int kScoreBlocksPerWG = 64;
+
+template <int DI, int NL>
+__global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict__ qI,
+                                                      const uint16_t* __restrict__ S, float* __restrict__ scores,
+                                                      int L, int nq, int B, int nb, int m) {
+  constexpr int LPR = DI / 8;     // lanes per summary row
+  constexpr int RPL = kWave / LPR;  // rows per wave load
+  static_assert(RPL % NL == 0, "a block's landmarks must share one wave load");
+
+  const int q = blockIdx.y;  // b * nq + i
+  const int b = q / nq, i = q % nq;
+  const int t = query_pos(L, nq, i);
+  const int c = t / B;
+  if (c + 1 <= m) return;
+  const int j0 = max(1, blockIdx.x * kScoreBlocksPerWG);
+  const int j1 = min(c, (int)(blockIdx.x + 1) * kScoreBlocksPerWG);  // exclusive
+  if (j0 >= j1) return;
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int col8 = lane % LPR;
+  float qv[8];
+  {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(qI + (size_t)q * DI + col8 * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_lo(v[e]);
+      qv[2 * e + 1] = bf16_hi(v[e]);
+    }
+  }
+  const uint16_t* Sb = S + (size_t)b * nb * NL * DI;
+  const int row_end = j1 * NL;
+  for (int row0 = j0 * NL + wave * RPL; row0 < row_end; row0 += 4 * RPL) {
+    const int row = row0 + lane / LPR;
+    float dot = 0.f;
+    if (row < row_end) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + col8 * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot += qv[2 * e] * bf16_lo(v[e]);
+        dot += qv[2 * e + 1] * bf16_hi(v[e]);
+      }
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) dot += shfl_xor(dot, o);
+#pragma unroll
+    for (int o = LPR; o < LPR * NL; o <<= 1) dot = fmaxf(dot, shfl_xor(dot, o));
+    if (row < row_end && (lane % (LPR * NL)) == 0) scores[(size_t)q * nb + row / NL] = dot;
+  }
+}
+
+template <int NW, int R>
+__global__ __launch_bounds__(NW * 64) void k_block_select(const float* __restrict__ scores, int32_t* __restrict__ blk,
+                                                          int L, int nq, int B, int nb, int m) {
+  __shared__ int lds[select_lds_words<NW>()];
+  const int q = blockIdx.x;
+  const int i = q % nq;
+  const int t = query_pos(L, nq, i);
+  const int c = t / B;
+  int32_t* out = blk + (size_t)q * m;
+  if (c + 1 <= m) {
+    for (int j = threadIdx.x; j < m; j += NW * 64) out[j] = j <= c ? j : -1;
+    return;
+  }
+  const int want = m - 2;
+  const int n = c - 1;  // candidates: blocks 1 .. c-1 (index = block - 1)
+  if (threadIdx.x == 0) {
+    out[0] = 0;
+    out[m - 1] = c;
+  }
+  if (want == 0) return;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const float* sc = scores + (size_t)q * nb + 1;
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = wave * kWave * R + r * kWave + lane;
+    key[r] = idx < n ? score_key(sc[idx]) : 0u;
+  }
+  select_top<NW, R>(key, want, lds, [&](int pos, int idx) { out[1 + pos] = 1 + idx; });
+}
+
+template <int NW>
+static hipError_t launch_select(int R, int nq_total, const float* scores, int32_t* blk, const Dims& s,
+                                hipStream_t st) {
+  dim3 grid(nq_total), block(NW * 64);
+#define HSA_SEL(RR)                                                                                  \
+  case RR:                                                                                          \
+    hipLaunchKernelGGL((k_block_select<NW, RR>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m); \
+    break;
+  switch (R) {
+    HSA_SEL(1) HSA_SEL(2) HSA_SEL(4) HSA_SEL(8) HSA_SEL(16) HSA_SEL(32)
+    default: return hipErrorInvalidValue;
+  }
+#undef HSA_SEL
+  return hipGetLastError();
+}
+
+size_t block_topm_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq * s.nb * sizeof(float)); }
+
+static int pick_r(int n, int nw) {
+  int r = 1;
+  while (r * 64 * nw < n) r <<= 1;
+  return r;
+}
+
+hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk, void* ws,
+                             hipStream_t st) {
+  const int nq_total = s.b * s.nq;
+  if (nq_total == 0) return hipSuccess;
+  float* scores = static_cast<float*>(ws);
+  // the last query has the most causal blocks
+  const int c_max = (s.L - 1) / s.B;
+  const int n_max = c_max - 1;
+  if (c_max + 1 > s.m) {
+    dim3 grid((c_max + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG, nq_total);
+    hipError_t e = hipSuccess;
+#define HSA_SC(DI, NL) hipLaunchKernelGGL((k_block_scores<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, s.nb, s.m)
+    if (s.dI == 64) {
+      if (s.nL == 1) HSA_SC(64, 1); else if (s.nL == 2) HSA_SC(64, 2); else HSA_SC(64, 4);
+    } else {
+      if (s.nL == 1) HSA_SC(128, 1); else if (s.nL == 2) HSA_SC(128, 2); else HSA_SC(128, 4);
+    }
+#undef HSA_SC
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // many queries: a 4-wave workgroup per query; few queries: 16 waves
+  if (nq_total >= 512 && n_max <= 4 * 64 * 32) return launch_select<4>(pick_r(n_max, 4), nq_total, scores, blk, s, st);
+  return launch_select<16>(pick_r(n_max, 16), nq_total, scores, blk, s, st);
+}
+
+}  // namespace hsa

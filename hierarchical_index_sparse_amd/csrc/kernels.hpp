@@ -1,0 +1,40 @@
+// Host-side launchers of the library's kernels.  Each takes validated
+// arguments (see api.cpp) and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hsa_sparse.h"
+
+namespace hsa {
+
+struct Dims {
+  int b, L, nq, dI, B, nL, m, k, Hq, Hkv, d;
+  float scale;
+  int nb;  // ceil(L / B)
+};
+
+// step 1
+hipError_t launch_block_summary(const Dims& s, const uint16_t* kI, const int8_t* W, int start_block,
+                                uint16_t* S, hipStream_t st);
+
+// step 2: scores into `scores` [b*nq, nb] fp32, then the top-m select
+size_t block_topm_ws_bytes(const Dims& s);
+hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk,
+                             void* ws, hipStream_t st);
+
+// step 3: scores into [b*nq, m*B] fp32, then the top-k select
+size_t token_topk_ws_bytes(const Dims& s);
+hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
+                             int32_t* tok, void* ws, hipStream_t st);
+
+// step 4
+size_t sparse_attn_ws_bytes(const Dims& s);
+hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                              const int32_t* tok, float* O, float* lse, void* ws, hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+}  // namespace hsa

@@ -1,0 +1,276 @@
+// Step 4: exact softmax attention of each query over its kept K/V rows.
+//
+// HISA page: the indexer's output feeds the unchanged token-level sparse
+// attention.  HiLS pseudocode, step 4: softmax(q K_sel^T * scale) V_sel over
+// the concatenated rows of the kept chunks.
+//
+// One wave per (query, kv head, split of the token list).  The G = Hq/Hkv
+// query heads that share a kv head form the 16-wide N side of
+// v_mfma_f32_16x16x32_bf16 (zero-padded when G < 16), so every gathered K/V
+// row (256 bytes) is read once for all G heads.  Per tile of 32 list
+// entries:
+//   * S^T = K_tile Q^T (2 x 4 MFMAs): A = 16 gathered K rows (16-byte loads
+//     of 8 head dims each), B = the query heads, held in registers.  The
+//     accumulator layout gives each lane one head and 8 tokens, which is the
+//     A-operand layout P needs for P V, so no shuffle of P is required.
+//   * online softmax in the exp2 domain (running max and sum per head).
+//   * O += P V (8 output tiles of 16 dims): each lane gathers, for its 8
+//     tokens, the 32-bit pair (dim 2j, dim 2j+1) of 4 column groups and
+//     splits the pairs into the even-dim and odd-dim B operands, so V needs
+//     no LDS transpose.  P is split into bf16 hi + lo parts (two MFMAs),
+//     which keeps P's rounding error near 2^-17 instead of bf16's 2^-9.
+// Splits (decode) write unnormalised partial results with their running max
+// and sum; k_attn_merge combines them (log-sum-exp merge).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hsa {
+
+constexpr int kPartStride = 130;  // 128 dims + running max + running sum
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+template <bool SPLIT>
+__global__ __launch_bounds__(256) void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                     const uint16_t* __restrict__ V, const int32_t* __restrict__ tok,
+                                                     float* __restrict__ O, float* __restrict__ lse,
+                                                     float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
+                                                     int chunk, int nsplit, float scale_log2, int n_items) {
+  const int wave = threadIdx.x / kWave;
+  const int item = blockIdx.x * 4 + wave;
+  if (item >= n_items) return;
+  const int split = item % nsplit;
+  const int qg = item / nsplit;
+  const int g = qg % Hkv;
+  const int q = qg / Hkv;
+  const int b = q / nq;
+  const int G = Hq / Hkv;
+  const int lane = lane_id();
+  const int jl = lane & 15;
+  const int gq = lane >> 4;
+
+  // B operand of S^T = K Q^T: head jl, dims 8 gq + 32 ks .. + 7
+  bf16x8 qf[4];
+  {
+    const uint16_t* qrow = Q + ((size_t)q * Hq + (size_t)g * G + jl) * 128 + 8 * gq;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (jl < G) v = *reinterpret_cast<const u32x4*>(qrow + 32 * ks);
+      qf[ks] = as_bf16x8(v);
+    }
+  }
+
+  const int start = split * chunk;
+  const int end = min(k, start + chunk);
+  const int32_t* tl = tok + (size_t)q * k;
+  const size_t kv_row0 = (size_t)b * L;
+  const uint16_t* Kg = K + (size_t)g * 128;
+  const uint16_t* Vg = V + (size_t)g * 128;
+  const size_t row_stride = (size_t)Hkv * 128;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int p0 = start; p0 < end; p0 += 32) {
+    const int pos = p0 + (lane & 31);
+    int my = pos < end ? tl[pos] : -1;
+    if (my >= L) my = -1;
+    const uint32_t vmask = (uint32_t)ballot(my >= 0);
+    if (vmask == 0u) continue;
+    const int mine = my < 0 ? 0 : my;
+
+    // ---- S^T = K Q^T over two 16-token tiles
+    const int t0 = __shfl(mine, jl, kWave);
+    const int t1 = __shfl(mine, 16 + jl, kWave);
+    const uint16_t* k0 = Kg + (kv_row0 + t0) * row_stride + 8 * gq;
+    const uint16_t* k1 = Kg + (kv_row0 + t1) * row_stride + 8 * gq;
+    u32x4 ka[4], kb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      ka[ks] = *reinterpret_cast<const u32x4*>(k0 + 32 * ks);
+      kb[ks] = *reinterpret_cast<const u32x4*>(k1 + 32 * ks);
+    }
+    // V tokens of this lane's 8 P slots: 4 gq + e and 16 + 4 gq + e
+    int vt[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vt[e] = __shfl(mine, 4 * gq + e, kWave);
+      vt[4 + e] = __shfl(mine, 16 + 4 * gq + e, kWave);
+    }
+    uint32_t w[4][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t* vrow = reinterpret_cast<const uint32_t*>(Vg + (kv_row0 + vt[e]) * row_stride) + jl;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr) w[pr][e] = vrow[16 * pr];
+    }
+
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), qf[ks], s1, 0, 0, 0);
+    }
+
+    // ---- online softmax (lane: head jl, tokens 4gq+e and 16+4gq+e)
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = ((vmask >> (4 * gq + e)) & 1u) ? s0[e] * scale_log2 : -INFINITY;
+      sv[4 + e] = ((vmask >> (16 + 4 * gq + e)) & 1u) ? s1[e] * scale_log2 : -INFINITY;
+    }
+    float mx = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float pa = exp2f(sv[e] - m_new);
+      const float pb = exp2f(sv[e + 1] - m_new);
+      psum += pa + pb;
+      const uint32_t ha = f32_to_bf16_rne(pa), hb = f32_to_bf16_rne(pb);
+      const uint32_t la = f32_to_bf16_rne(pa - __uint_as_float(ha << 16));
+      const uint32_t lb = f32_to_bf16_rne(pb - __uint_as_float(hb << 16));
+      ph[e / 2] = ha | (hb << 16);
+      pl[e / 2] = la | (lb << 16);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const bf16x8 p_hi = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 p_lo = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
+
+    // ---- rescale O (rows = heads 4gq+i) and accumulate P V
+    float a_i[4];
+#pragma unroll
+    for (int i2 = 0; i2 < 4; ++i2) a_i[i2] = __shfl(alpha, 4 * gq + i2, kWave);
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr) {
+      u32x4 ev, od;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t x0 = w[pr][2 * e2], x1 = w[pr][2 * e2 + 1];
+        ev[e2] = (x0 & 0xFFFFu) | (x1 << 16);
+        od[e2] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x4 acc = o[2 * pr + hh];
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) acc[i2] *= a_i[i2];
+        const bf16x8 vb = as_bf16x8(hh ? od : ev);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc, 0, 0, 0);
+        o[2 * pr + hh] = acc;
+      }
+    }
+  }
+
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  // outputs: lane holds heads 4gq+i, dims 32 pr + 2 jl + hh
+#pragma unroll
+  for (int i2 = 0; i2 < 4; ++i2) {
+    const int head = 4 * gq + i2;
+    const float l_h = __shfl(l_run, head, kWave);
+    if (head >= G) continue;
+    if constexpr (SPLIT) {
+      float* dst = part + ((size_t)item * 16 + head) * kPartStride;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr)
+        *reinterpret_cast<float2*>(dst + 32 * pr + 2 * jl) = make_float2(o[2 * pr][i2], o[2 * pr + 1][i2]);
+    } else {
+      const float inv = l_h > 0.f ? 1.f / l_h : 0.f;
+      float* dst = O + ((size_t)q * Hq + (size_t)g * G + head) * 128;
+#pragma unroll
+      for (int pr = 0; pr < 4; ++pr)
+        *reinterpret_cast<float2*>(dst + 32 * pr + 2 * jl) =
+            make_float2(o[2 * pr][i2] * inv, o[2 * pr + 1][i2] * inv);
+    }
+  }
+  if (gq == 0 && jl < G) {
+    if constexpr (SPLIT) {
+      float* dst = part + ((size_t)item * 16 + jl) * kPartStride;
+      dst[128] = m_run;
+      dst[129] = l_run;
+    } else if (lse) {
+      lse[(size_t)q * Hq + (size_t)g * G + jl] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    }
+  }
+}
+
+__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, float* __restrict__ O,
+                                                    float* __restrict__ lse, int Hq, int Hkv, int nsplit) {
+  const int qh = blockIdx.x;
+  const int q = qh / Hq, h = qh % Hq;
+  const int G = Hq / Hkv;
+  const int g = h / G, head = h % G;
+  const int dim = threadIdx.x;
+  const float* base = part + ((size_t)(q * Hkv + g) * nsplit * 16 + head) * kPartStride;
+  const size_t sstride = (size_t)16 * kPartStride;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * sstride + 128]);
+  float acc = 0.f, Lt = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float* p = base + s * sstride;
+      const float wgt = exp2f(p[128] - M);
+      acc += wgt * p[dim];
+      Lt += wgt * p[129];
+    }
+  }
+  O[(size_t)qh * 128 + dim] = Lt > 0.f ? acc / Lt : 0.f;
+  if (lse && dim == 0) lse[qh] = Lt > 0.f ? (M + log2f(Lt)) * 0.69314718055994531f : -INFINITY;
+}
+
+// Split plan: enough waves to fill the chip when there are few queries.
+static void split_plan(const Dims& s, int& nsplit, int& chunk) {
+  const long long items = (long long)s.b * s.nq * s.Hkv;
+  const int tiles = (s.k + 31) / 32;
+  long long want = (items <= 0 || items >= 2048) ? 1 : (2048 + items - 1) / items;
+  if (want > (tiles + 1) / 2) want = (tiles + 1) / 2;  // at least 2 tiles per split
+  if (want < 1) want = 1;
+  const int tiles_per = (int)((tiles + want - 1) / want);
+  chunk = tiles_per * 32;
+  nsplit = (s.k + chunk - 1) / chunk;
+}
+
+size_t sparse_attn_ws_bytes(const Dims& s) {
+  int nsplit, chunk;
+  split_plan(s, nsplit, chunk);
+  if (nsplit <= 1) return 0;
+  return align_up((size_t)s.b * s.nq * s.Hkv * nsplit * 16 * kPartStride * sizeof(float));
+}
+
+hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                              const int32_t* tok, float* O, float* lse, void* ws, hipStream_t st) {
+  const long long nq_total = (long long)s.b * s.nq;
+  if (nq_total == 0) return hipSuccess;
+  int nsplit, chunk;
+  split_plan(s, nsplit, chunk);
+  const int n_items = (int)(nq_total * s.Hkv * nsplit);
+  const float scale_log2 = s.scale * 1.4426950408889634f;
+  dim3 grid((n_items + 3) / 4), block(256);
+  if (nsplit == 1) {
+    hipLaunchKernelGGL((k_sparse_attn<false>), grid, block, 0, st, Q, K, V, tok, O, lse, nullptr, s.L, s.nq, s.Hq,
+                       s.Hkv, s.k, chunk, nsplit, scale_log2, n_items);
+    return hipGetLastError();
+  }
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL((k_sparse_attn<true>), grid, block, 0, st, Q, K, V, tok, O, lse, part, s.L, s.nq, s.Hq, s.Hkv,
+                     s.k, chunk, nsplit, scale_log2, n_items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(nq_total * s.Hq)), dim3(128), 0, st, part, O, lse, s.Hq, s.Hkv,
+                     nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace hsa

@@ -1,0 +1,203 @@
+/*
+ * hsa_sparse.h - hierarchical block-then-token sparse attention on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (HISA page, "北大团队改造DeepSeek注意力，速度快四倍还不丢精度",
+ * two-step method; HiLS page, "把稀疏注意力做对 HiLS-Attention …", sections
+ * 2.1-2.2 and its hils_attention pseudocode) replaces a flat top-k indexer
+ * that scores every earlier token by four steps:
+ *   1. summarise every block of B indexer keys into one vector (the mean) or
+ *      into n_landmarks landmark vectors (fixed 0/1 projection of the block);
+ *   2. score the causal blocks with the indexer rule (dot product with the
+ *      query's indexer vector; max over landmarks) and keep m blocks, the
+ *      first block and the query's own block always among them;
+ *   3. score only the tokens of the kept blocks and keep k of them;
+ *   4. run exact softmax attention over the k kept K/V rows (unchanged
+ *      downstream sparse attention).
+ *
+ * Conventions shared by every entry point:
+ *   - bf16 tensors are passed as raw bit patterns (uint16_t*).  Every tensor
+ *     is contiguous, row-major, and lives in device memory on the current
+ *     HIP device.
+ *   - Each of the `batch` sequences has `seq_len` tokens; its n_q queries
+ *     sit at the last n_q positions: query i has position t = seq_len-n_q+i.
+ *     A token s is a candidate for the query at t only when s <= t.
+ *   - Selection order is (score descending, index ascending): ties go to the
+ *     lower block / token index.  Index lists are ascending and padded with
+ *     -1.  When a query has at most m causal blocks (or at most k candidate
+ *     tokens) all of them are kept without scoring.
+ *   - m counts the two forced blocks (block 0 and block t / B).
+ *   - Calls are asynchronous on `stream` (NULL = the default stream) and
+ *     never synchronise the host; results are valid once the stream has
+ *     reached them.  The library allocates no device memory: scratch space
+ *     is the caller's `workspace`, sized by hsa_sparse_workspace_size().
+ *   - Arguments are validated before anything is launched.  On an error
+ *     nothing is written and nothing is enqueued.  hsa_sparse_last_error()
+ *     returns a message for the calling thread's last failure.
+ *
+ * Supported shapes: head_dim == 128; d_index in {64, 128}; block a power of
+ * two in [8, 128]; n_landmarks in {1, 2, 4}; n_heads_kv divides n_heads_q
+ * with at most 16 query heads per kv head; top_m >= 2; top_k >= 1;
+ * ceil(seq_len / block) - 2 <= 32768; top_m * block <= 32768 unless
+ * top_k >= top_m * block (then no token scoring is needed).
+ */
+#ifndef HSA_SPARSE_H
+#define HSA_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum hsa_sparse_status {
+  HSA_SPARSE_OK = 0,
+  HSA_SPARSE_INVALID_ARG = 1,          /* null pointer, inconsistent sizes */
+  HSA_SPARSE_UNSUPPORTED = 2,          /* valid but outside the supported shapes */
+  HSA_SPARSE_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < required size */
+  HSA_SPARSE_HIP_ERROR = 4             /* a HIP call or kernel launch failed */
+} hsa_sparse_status_t;
+
+typedef struct hsa_sparse_shape {
+  int32_t batch;        /* b: independent sequences */
+  int32_t seq_len;      /* L: tokens per sequence, queries included */
+  int32_t n_q;          /* queries per sequence (the last n_q positions) */
+  int32_t d_index;      /* indexer vector width d_I */
+  int32_t block;        /* B: tokens per key block */
+  int32_t n_landmarks;  /* summary vectors per block: 1 = mean */
+  int32_t top_m;        /* m: kept blocks per query, forced ones included */
+  int32_t top_k;        /* k: kept tokens per query */
+  int32_t n_heads_q;    /* Hq */
+  int32_t n_heads_kv;   /* Hkv; query head h reads kv head h / (Hq / Hkv) */
+  int32_t head_dim;     /* d */
+  float scale;          /* softmax scale applied to q . k */
+} hsa_sparse_shape_t;
+
+/* Same object as hipStream_t. */
+typedef struct ihipStream_t* hsa_sparse_stream_t;
+
+enum {
+  HSA_SPARSE_OP_BLOCK_SUMMARY = 0,
+  HSA_SPARSE_OP_BLOCK_TOPM = 1,
+  HSA_SPARSE_OP_TOKEN_TOPK = 2,
+  HSA_SPARSE_OP_SPARSE_ATTN = 3,
+  HSA_SPARSE_OP_FORWARD = 4
+};
+
+/* Bytes of device workspace the operation `op` needs for `shape`
+ * (0 for an invalid shape or op).  Host-only arithmetic. */
+size_t hsa_sparse_workspace_size(const hsa_sparse_shape_t* shape, int op);
+
+/* Static text of a status code. */
+const char* hsa_sparse_strerror(hsa_sparse_status_t status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* hsa_sparse_last_error(void);
+
+/*
+ * Step 1, block summaries (HISA page, step one: one summary vector per
+ * fixed-size block; HiLS page, section 2.1: landmark vectors per chunk).
+ *   kI          [batch, seq_len, d_index] bf16, integer-valued in the
+ *               workloads (then every sum below is exact in fp32).
+ *   landmark_W  NULL for mean mode (n_landmarks must be 1), else
+ *               [n_landmarks, block] int8 weights.
+ *   start_block summaries are written for blocks start_block .. nb-1 only
+ *               (nb = ceil(seq_len / block)); earlier ones are left as is.
+ *   S           [batch, nb, n_landmarks, d_index] bf16 output:
+ *               S[j, l] = bf16_rne(sum_r w[l, r] * kI[j*B + r] / B), with
+ *               w = 1 in mean mode and rows beyond seq_len counted as 0.
+ */
+hsa_sparse_status_t hsa_block_summary(const hsa_sparse_shape_t* shape,
+                                      const uint16_t* kI,
+                                      const int8_t* landmark_W,
+                                      int32_t start_block, uint16_t* S,
+                                      hsa_sparse_stream_t stream);
+
+/*
+ * Step 2, block scores and top-m (HISA page, step one scoring with the
+ * original indexer rule, and the always-kept first and last block; HiLS
+ * page, section 2.2 coarse layer).
+ *   qI   [batch, n_q, d_index] bf16 indexer queries.
+ *   S    [batch, nb, n_landmarks, d_index] bf16 summaries (step 1).
+ *   blk  [batch, n_q, top_m] int32 output: for the query at t with
+ *        c = t / block, all of 0..c if c + 1 <= top_m, else
+ *        {0, c} plus the best top_m - 2 blocks of 1..c-1 by
+ *        score_j = max_l qI . S[j, l]; ascending, -1 padded.
+ *   workspace  >= hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_BLOCK_TOPM).
+ */
+hsa_sparse_status_t hsa_block_topm(const hsa_sparse_shape_t* shape,
+                                   const uint16_t* qI, const uint16_t* S,
+                                   int32_t* blk, void* workspace,
+                                   size_t workspace_bytes,
+                                   hsa_sparse_stream_t stream);
+
+/*
+ * Step 3, token scores and top-k inside the kept blocks (HISA page, step
+ * two).
+ *   qI, kI  as above; blk [batch, n_q, top_m] from step 2.
+ *   tok     [batch, n_q, top_k] int32 output: candidates are the tokens
+ *           s <= t of the kept blocks; all of them if at most top_k, else
+ *           the best top_k by qI . kI[s]; ascending, -1 padded.
+ */
+hsa_sparse_status_t hsa_token_topk(const hsa_sparse_shape_t* shape,
+                                   const uint16_t* qI, const uint16_t* kI,
+                                   const int32_t* blk, int32_t* tok,
+                                   void* workspace, size_t workspace_bytes,
+                                   hsa_sparse_stream_t stream);
+
+/*
+ * Step 4, exact softmax attention over the kept tokens (HISA page: the
+ * downstream sparse attention is unchanged; HiLS pseudocode, step 4).
+ *   Q    [batch, n_q, n_heads_q, head_dim] bf16.
+ *   K, V [batch, seq_len, n_heads_kv, head_dim] bf16.
+ *   tok  [batch, n_q, top_k] int32 token lists (-1 entries are skipped;
+ *        every list must hold at least one valid entry in [0, seq_len)).
+ *   O    [batch, n_q, n_heads_q, head_dim] fp32 output:
+ *        softmax(scale * q_h . K[tok, g]) . V[tok, g] with g = h / (Hq/Hkv),
+ *        accumulated in fp32.
+ *   lse  NULL or [batch, n_q, n_heads_q] fp32: natural log of the softmax
+ *        denominator, log sum_s exp(scale * q_h . K[s, g]).
+ */
+hsa_sparse_status_t hsa_sparse_attn(const hsa_sparse_shape_t* shape,
+                                    const uint16_t* Q, const uint16_t* K,
+                                    const uint16_t* V, const int32_t* tok,
+                                    float* O, float* lse, void* workspace,
+                                    size_t workspace_bytes,
+                                    hsa_sparse_stream_t stream);
+
+/*
+ * Steps 1-4 in one call (the drop-in indexer plus the unchanged attention).
+ *   S        in-out summary state [batch, nb, n_landmarks, d_index]: blocks
+ *            from summary_start_block on are (re)computed from kI first;
+ *            pass 0 to build all of them, or the first block touched by new
+ *            tokens when the earlier summaries are already in S.
+ *   blk_out  NULL or [batch, n_q, top_m]: also return the block lists.
+ *   tok_out  NULL or [batch, n_q, top_k]: also return the token lists.
+ *   O, lse   as in hsa_sparse_attn.
+ */
+hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape,
+                                const uint16_t* qI, const uint16_t* kI,
+                                const int8_t* landmark_W,
+                                int32_t summary_start_block, uint16_t* S,
+                                const uint16_t* Q, const uint16_t* K,
+                                const uint16_t* V, int32_t* blk_out,
+                                int32_t* tok_out, float* O, float* lse,
+                                void* workspace, size_t workspace_bytes,
+                                hsa_sparse_stream_t stream);
+
+/*
+ * Per-step timing of hsa_forward (profiling aid).  After this call, every
+ * hsa_forward made by the calling thread records events[0] on its stream
+ * before step 1 and events[s] after step s (s = 1..4).  The events are the
+ * caller's hipEvent_t handles and must stay valid while such calls are
+ * made.  n_events must be 5, or 0 with events == NULL to stop recording.
+ */
+typedef struct ihipEvent_t* hsa_sparse_event_t;
+hsa_sparse_status_t hsa_sparse_set_stage_events(hsa_sparse_event_t const* events, int n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HSA_SPARSE_H */

@@ -1,0 +1,142 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, sizes workspaces, and rejects bad arguments before any HIP call (so
+these run without a GPU; no compute is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hierarchical_index_sparse_amd import _lib
+from hierarchical_index_sparse_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hsa_sparse.h")
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(hsa_[a-z_0-9]+)\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
+              "hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(_lib.EXPORTS)
+
+
+def test_strerror(lib):
+    assert lib.hsa_sparse_strerror(0) == b"success"
+    assert lib.hsa_sparse_strerror(3) == b"workspace too small"
+    assert lib.hsa_sparse_strerror(99) == b"unknown status"
+
+
+def shape(**kw):
+    base = dict(batch=1, seq_len=4096, n_q=4096, d_index=64, block=64, top_m=8, top_k=256,
+                n_heads_q=1, n_heads_kv=1, head_dim=128, n_landmarks=1)
+    base.update(kw)
+    return _lib.make_shape(**base)
+
+
+def call_attn(lib, s, ws_bytes=1 << 40, O=FAKE):
+    return lib.hsa_sparse_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, O, None, FAKE, ws_bytes, None)
+
+
+def call_forward(lib, s, ws_bytes=1 << 40, W=None, qI=FAKE):
+    return lib.hsa_forward(ctypes.byref(s), qI, FAKE, W, 0, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None,
+                           FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), 2),
+    (dict(n_heads_q=3, n_heads_kv=2), 1),
+    (dict(n_heads_q=64, n_heads_kv=2), 2),
+    (dict(top_k=0), 1),
+    (dict(n_q=5000), 1),
+])
+def test_attention_validation(lib, kw, status):
+    assert call_attn(lib, shape(**kw)) == status
+    assert lib.hsa_sparse_last_error() != b""
+
+
+def test_attention_null_output(lib):
+    assert call_attn(lib, shape(), O=None) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_m=1), 1),
+    (dict(top_k=0), 1),
+    (dict(d_index=96), 2),
+    (dict(block=48), 2),
+    (dict(block=256), 2),
+    (dict(block=4), 2),
+    (dict(n_landmarks=3), 2),
+    (dict(seq_len=128 * 40000, n_q=1, block=128), 2),
+    (dict(seq_len=1 << 20, n_q=1, block=128, top_m=512, top_k=4096), 2),
+    (dict(batch=-1), 1),
+])
+def test_forward_validation(lib, kw, status):
+    assert call_forward(lib, shape(**kw)) == status
+
+
+def test_forward_needs_landmark_weights(lib):
+    assert call_forward(lib, shape(n_landmarks=4)) == 1
+    assert call_forward(lib, shape(), qI=None) == 1
+
+
+def test_workspace_too_small(lib):
+    s = shape()
+    need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FORWARD)
+    assert need > 0
+    assert call_forward(lib, s, ws_bytes=need - 1) == 3
+    assert b"workspace" in lib.hsa_sparse_last_error()
+    st = lib.hsa_token_topk(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None)
+    assert st == 3
+
+
+def test_summary_validation(lib):
+    s = shape(top_m=0, top_k=0)  # selection fields are not read by the summary step
+    assert lib.hsa_block_summary(ctypes.byref(s), FAKE, None, -1, FAKE, None) == 1
+    assert lib.hsa_block_summary(ctypes.byref(shape(n_landmarks=2)), FAKE, None, 0, FAKE, None) == 1
+    assert lib.hsa_block_summary(ctypes.byref(shape(d_index=32)), FAKE, None, 0, FAKE, None) == 2
+
+
+def test_empty_inputs_are_no_ops(lib):
+    # nothing to do: returns OK without touching memory or the GPU
+    for kw in (dict(batch=0), dict(n_q=0)):
+        s = shape(**kw)
+        assert lib.hsa_block_topm(ctypes.byref(s), None, None, None, None, 0, None) == 0
+        assert lib.hsa_token_topk(ctypes.byref(s), None, None, None, None, None, 0, None) == 0
+        assert lib.hsa_sparse_attn(ctypes.byref(s), None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_workspace_sizes(lib):
+    for w in WORKLOADS.values():
+        s = _lib.shape_of(w)
+        nqt = w.batch * w.n_q
+        topm = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_BLOCK_TOPM)
+        assert topm >= nqt * w.n_blocks * 4
+        topk = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_TOKEN_TOPK)
+        if w.top_k >= w.top_m * w.block:
+            assert topk == 0
+        else:
+            assert topk >= nqt * w.top_m * w.block * 4
+        fwd = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FORWARD)
+        assert fwd >= nqt * (w.top_m + w.top_k) * 4 + max(topm, topk)
+        assert fwd % 256 == 0
+    assert lib.hsa_sparse_workspace_size(None, _lib.HSA_SPARSE_OP_FORWARD) == 0
+    assert lib.hsa_sparse_workspace_size(ctypes.byref(shape()), 42) == 0

@@ -1,0 +1,135 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Index sets (summaries, block lists, token lists) must match bit for bit;
+attention outputs and log-sum-exp within a max-abs error of 2e-3.
+Small cases compare every query; the named full-size workloads compare
+sampled queries against the oracle and check list invariants on every
+query.
+"""
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_index_sparse_amd import _lib, datagen, pipeline
+from hierarchical_index_sparse_amd.workloads import WORKLOADS, Workload
+from oracle import hisa_oracle as orc
+from parity import (check_list_invariants, check_queries, check_summaries, oracle_summaries,
+                    sample_queries)
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, **kw):
+    base = dict(batch=1, n_heads_q=1, n_heads_kv=1, n_landmarks=1)
+    base.update(kw)
+    return Workload(name=name, **base)
+
+
+# tie-heavy small cases: small integer ranges give many equal scores
+SMALL_CASES = [
+    (small("ragged_b8", seq_len=300, n_q=300, d_index=64, block=8, top_m=4, top_k=10), 2),
+    (small("gqa_lm2", seq_len=1000, n_q=77, d_index=128, block=16, top_m=5, top_k=37,
+           n_heads_q=4, n_heads_kv=2, n_landmarks=2), 2),
+    (small("lm4_g16", seq_len=2048, n_q=2048, d_index=128, block=32, top_m=6, top_k=100,
+           n_heads_q=16, n_heads_kv=1, n_landmarks=4), 3),
+    (small("m2_forced_only", batch=3, seq_len=517, n_q=5, d_index=64, block=16, top_m=2, top_k=20,
+           n_heads_q=8, n_heads_kv=8), 2),
+    (small("k1", batch=2, seq_len=4100, n_q=3, d_index=128, block=128, top_m=3, top_k=1,
+           n_heads_q=2, n_heads_kv=1), 8),
+    (small("keep_all", seq_len=64, n_q=64, d_index=64, block=8, top_m=100, top_k=1000), 2),
+    (small("decode_wide_select", batch=2, seq_len=40000, n_q=2, d_index=64, block=16, top_m=300,
+           top_k=1000, n_heads_q=16, n_heads_kv=1), 2),
+    (small("prefill_r64_select", seq_len=20000, n_q=512, d_index=128, block=128, top_m=100,
+           top_k=300, n_heads_q=2, n_heads_kv=1), 2),
+]
+
+
+def make_small(w, rng_range):
+    return datagen.make_inputs(w, q_range=rng_range, centre_range=max(1, rng_range // 2),
+                               noise_range=max(1, rng_range // 2))
+
+
+@pytest.mark.parametrize("w,vr", SMALL_CASES, ids=[c[0].name for c in SMALL_CASES])
+def test_small_case_all_queries(w, vr):
+    inp = make_small(w, vr)
+    dev = pipeline.to_device(inp)
+    gpu = pipeline.to_host(pipeline.run_stages(w, dev))
+    torch.cuda.synchronize()
+    S = oracle_summaries(inp, w)
+    check_summaries(gpu["S"], S)
+    check_list_invariants(gpu, w)
+    check_queries(gpu, inp, w, S, [(b, i) for b in range(w.batch) for i in range(w.n_q)])
+    # the fused entry point gives the same bits
+    fwd = pipeline.to_host(pipeline.run_forward(w, dev))
+    for key in ("S", "blk", "tok", "O", "lse"):
+        assert np.array_equal(fwd[key], gpu[key], equal_nan=True), key
+
+
+def test_dense_when_everything_is_kept():
+    # m covers every block and k every token: dense causal attention (torch, fp64, CPU)
+    w = small("dense", seq_len=96, n_q=96, d_index=64, block=8, top_m=12, top_k=96, n_heads_q=4, n_heads_kv=1)
+    inp = datagen.make_inputs(w)
+    gpu = pipeline.to_host(pipeline.run_forward(w, pipeline.to_device(inp)))
+    q = torch.tensor(orc.bf16_to_f64(inp["Q"][0])).permute(1, 0, 2)[None]
+    k = torch.tensor(orc.bf16_to_f64(inp["K"][0])).permute(1, 0, 2).repeat_interleave(4, 0)[None]
+    v = torch.tensor(orc.bf16_to_f64(inp["V"][0])).permute(1, 0, 2).repeat_interleave(4, 0)[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.scale)[0]
+    err = np.abs(gpu["O"][0] - ref.permute(1, 0, 2).numpy()).max()
+    assert err <= 2e-3
+
+
+def test_empty_calls_write_nothing():
+    w = small("empty", batch=0, seq_len=128, n_q=4, d_index=64, block=16, top_m=3, top_k=8)
+    dev = pipeline.to_device(datagen.make_inputs(w.with_(batch=1)))
+    out = pipeline.alloc_outputs(w.with_(batch=1))
+    pipeline.run_forward(w, dev, out)
+    torch.cuda.synchronize()
+    assert torch.all(out["blk"] == -7) and torch.all(out["tok"] == -7)
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w = WORKLOADS["tiny_prefill_4k"]
+    dev = pipeline.to_device(datagen.make_inputs(w))
+    a = pipeline.to_host(pipeline.run_forward(w, dev))
+    b = pipeline.to_host(pipeline.run_forward(w, dev))
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+_cache = {}
+
+
+def workload_inputs(name):
+    if name not in _cache:
+        _cache.clear()
+        w = WORKLOADS[name]
+        inp = datagen.make_inputs(w)
+        _cache[name] = (w, inp)
+    return _cache[name]
+
+
+def test_tiny_prefill_4k_all_queries():
+    w, inp = workload_inputs("tiny_prefill_4k")
+    gpu = pipeline.to_host(pipeline.run_forward(w, pipeline.to_device(inp)))
+    S = oracle_summaries(inp, w)
+    check_summaries(gpu["S"], S)
+    check_list_invariants(gpu, w)
+    check_queries(gpu, inp, w, S, [(0, i) for i in range(w.n_q)])
+
+
+@pytest.mark.parametrize("name", ["decode_128k", "decode_512k", "landmark_decode_1m",
+                                  "chunked_prefill_512k", "prefill_64k"])
+def test_full_size_workload(name):
+    w, inp = workload_inputs(name)
+    dev = pipeline.to_device(inp)
+    gpu = pipeline.to_host(pipeline.run_forward(w, dev))
+    del dev
+    torch.cuda.empty_cache()
+    S = oracle_summaries(inp, w)
+    check_summaries(gpu["S"], S)
+    check_list_invariants(gpu, w)
+    qs = sample_queries(w) if w.n_q > 1 else [(b, 0) for b in range(w.batch)]
+    check_queries(gpu, inp, w, S, qs)
+    if w.needles:
+        for b in range(w.batch):
+            assert set(inp["needles"][b].tolist()) <= set(gpu["blk"][b, 0].tolist())
