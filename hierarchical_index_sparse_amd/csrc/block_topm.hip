@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
 template <int NW, int R>
 __global__ __launch_bounds__(NW * 64) void k_block_select(const float* __restrict__ scores, int32_t* __restrict__ blk,
                                                           int L, int nq, int B, int nb, int m) {
-  __shared__ int lds[select_lds_words<NW>()];
+  __shared__ SelectSmem<NW> lds;
   const int q = blockIdx.x;
   const int i = q % nq;
   const int t = query_pos(L, nq, i);
@@ -98,7 +98,8 @@ __global__ __launch_bounds__(NW * 64) void k_block_select(const float* __restric
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int idx = wave * kWave * R + r * kWave + lane;
-    key[r] = idx < n ? score_key(sc[idx]) : 0u;
+    const float v = sc[idx < n ? idx : 0];  // branch-free: all loads in flight together
+    key[r] = idx < n ? score_key(v) : 0u;
   }
   select_top<NW, R>(key, want, lds, [&](int pos, int idx) { out[1 + pos] = 1 + idx; });
 }

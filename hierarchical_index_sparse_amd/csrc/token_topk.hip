@@ -22,6 +22,9 @@
 
 namespace hsa {
 
+// Largest m with m * B <= 32768 candidates at the smallest block size.
+constexpr int kMaxSelBlocks = 32768 / 8;
+
 __device__ __forceinline__ void candidate_count(int t, int B, int m, int& c, int& n_sel, int& n_valid) {
   c = t / B;
   n_sel = (c + 1 <= m) ? c + 1 : m;
@@ -75,23 +78,273 @@ __global__ __launch_bounds__(256) void k_token_scores(const uint16_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled scoring for prefill: one workgroup per tile of QT = 64 * QW
+// consecutive queries of one sequence.  The tile's kept blocks are merged
+// into a union (LDS bitmaps: one QT-bit mask of queries per block); every
+// union block is then read once and scored against just the queries whose
+// mask bit is set, 16 at a time, with v_mfma_f32_16x16x32_bf16
+// (A = 16 kI rows of the block, B = the 16 queries' indexer vectors, so the
+// accumulator holds 4 consecutive tokens of one query per lane and is
+// stored with one 16-byte write).  kI traffic per tile is the union size
+// times B rows instead of m blocks per query.
+// ---------------------------------------------------------------------------
+
+constexpr int kTiledWaves = 16;
+
+// Exclusive scan of two counters over the 1024 threads of the workgroup.
+__device__ __forceinline__ void wg_scan2(int a, int b, int* lds, int& a_ex, int& b_ex, int& a_tot, int& b_tot) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  int ai = a, bi = b;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int va = __shfl_up(ai, o, kWave), vb = __shfl_up(bi, o, kWave);
+    if (lane >= o) {
+      ai += va;
+      bi += vb;
+    }
+  }
+  if (lane == kWave - 1) {
+    lds[wave] = ai;
+    lds[kTiledWaves + wave] = bi;
+  }
+  __syncthreads();
+  int pa = 0, pb = 0, ta = 0, tb = 0;
+#pragma unroll
+  for (int w = 0; w < kTiledWaves; ++w) {
+    const int xa = lds[w], xb = lds[kTiledWaves + w];
+    if (w < wave) {
+      pa += xa;
+      pb += xb;
+    }
+    ta += xa;
+    tb += xb;
+  }
+  a_ex = pa + ai - a;
+  b_ex = pb + bi - b;
+  a_tot = ta;
+  b_tot = tb;
+  __syncthreads();
+}
+
+struct TiledLayout {
+  size_t bitmap, uidx, ulist, uoff, posbuf, qtile, scan, wscratch, total;
+};
+
+__host__ __device__ inline TiledLayout tiled_layout(int nJ, int QW, int m, int DI) {
+  TiledLayout t;
+  const int QT = 64 * QW;
+  size_t o = 0;
+  t.bitmap = o;
+  o += (size_t)nJ * QW * 8;
+  t.uidx = o;
+  o += (size_t)nJ * 4;
+  t.ulist = o;
+  o += (size_t)nJ * 4;
+  t.uoff = o;
+  o += (size_t)(nJ + 1) * 4;
+  t.posbuf = o;
+  o += ((size_t)QT * m * 2 + 15) / 16 * 16;
+  t.qtile = o;
+  o += (size_t)QT * DI * 2;
+  t.scan = o;
+  o += 2 * kTiledWaves * 4 + 16;
+  t.wscratch = o;  // per wave: query slot and list position of each mask rank
+  o += (size_t)kTiledWaves * QT * 4;
+  t.total = o;
+  return t;
+}
+
+template <int DI, int QW>
+__global__ __launch_bounds__(kTiledWaves * 64) void k_token_scores_tiled(
+    const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI, const int32_t* __restrict__ blk,
+    float* __restrict__ scores, int L, int nq, int B, int m, int k, int tiles_per_seq, int n_tiles, int nJ_max) {
+  constexpr int QT = 64 * QW;
+  constexpr int KS = DI / 32;
+  constexpr int NT = kTiledWaves * 64;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const TiledLayout lay = tiled_layout(nJ_max, QW, m, DI);
+  uint64_t* bitmap = reinterpret_cast<uint64_t*>(smem + lay.bitmap);
+  int* uidx = reinterpret_cast<int*>(smem + lay.uidx);
+  int* ulist = reinterpret_cast<int*>(smem + lay.ulist);
+  int* uoff = reinterpret_cast<int*>(smem + lay.uoff);
+  uint16_t* posbuf = reinterpret_cast<uint16_t*>(smem + lay.posbuf);
+  uint16_t* qtile = reinterpret_cast<uint16_t*>(smem + lay.qtile);
+  int* scan = reinterpret_cast<int*>(smem + lay.scan);
+
+  const int tile = n_tiles - 1 - (int)blockIdx.x;  // longest tiles first
+  const int b = tile / tiles_per_seq;
+  const int i0 = (tile % tiles_per_seq) * QT;
+  const int nqt = min(nq - i0, QT);
+  const int nJ = query_pos(L, nq, i0 + nqt - 1) / B + 1;
+  const int tid = threadIdx.x;
+  const size_t qrow0 = (size_t)b * nq + i0;
+
+  for (int x = tid; x < nJ * QW; x += NT) bitmap[x] = 0ull;
+  for (int x = tid; x < QT * (DI / 8); x += NT) {
+    const int qq = x / (DI / 8), c8 = x % (DI / 8);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (qq < nqt) v = *reinterpret_cast<const u32x4*>(qI + (qrow0 + qq) * DI + c8 * 8);
+    *reinterpret_cast<u32x4*>(qtile + qq * DI + c8 * 8) = v;
+  }
+  __syncthreads();
+
+  // 1. bitmaps of (block -> queries of the tile that kept it and need scoring)
+  for (int x = tid; x < nqt * m; x += NT) {
+    const int qq = x / m, p = x % m;
+    int c, n_sel, n_valid;
+    candidate_count(query_pos(L, nq, i0 + qq), B, m, c, n_sel, n_valid);
+    if (n_valid > k && p < n_sel) {
+      const int j = blk[(qrow0 + qq) * m + p];
+      atomicOr(reinterpret_cast<unsigned long long*>(&bitmap[j * QW + qq / 64]), 1ull << (qq % 64));
+    }
+  }
+  __syncthreads();
+
+  // 2. union list in ascending block order, with each entry's offset into posbuf
+  const int per = (nJ + NT - 1) / NT;
+  const int j_lo = min(nJ, tid * per), j_hi = min(nJ, j_lo + per);
+  int cu = 0, cp = 0;
+  for (int j = j_lo; j < j_hi; ++j) {
+    int pc = 0;
+#pragma unroll
+    for (int w = 0; w < QW; ++w) pc += __popcll(bitmap[j * QW + w]);
+    cu += pc > 0;
+    cp += pc;
+  }
+  int u_ex, p_ex, nU, n_pairs;
+  wg_scan2(cu, cp, scan, u_ex, p_ex, nU, n_pairs);
+  for (int j = j_lo; j < j_hi; ++j) {
+    int pc = 0;
+#pragma unroll
+    for (int w = 0; w < QW; ++w) pc += __popcll(bitmap[j * QW + w]);
+    if (pc > 0) {
+      ulist[u_ex] = j;
+      uoff[u_ex] = p_ex;
+      uidx[j] = u_ex;
+      ++u_ex;
+      p_ex += pc;
+    } else {
+      uidx[j] = -1;
+    }
+  }
+  __syncthreads();
+
+  // 3. list position of every (query, kept block) pair, in mask-rank order
+  for (int x = tid; x < nqt * m; x += NT) {
+    const int qq = x / m, p = x % m;
+    int c, n_sel, n_valid;
+    candidate_count(query_pos(L, nq, i0 + qq), B, m, c, n_sel, n_valid);
+    if (n_valid > k && p < n_sel) {
+      const int j = blk[(qrow0 + qq) * m + p];
+      int rank = 0;
+#pragma unroll
+      for (int w = 0; w < QW; ++w) {
+        const uint64_t word = bitmap[j * QW + w];
+        if (w < qq / 64) rank += __popcll(word);
+        else if (w == qq / 64) rank += __popcll(word & ((1ull << (qq % 64)) - 1ull));
+      }
+      posbuf[uoff[uidx[j]] + rank] = (uint16_t)p;
+    }
+  }
+  __syncthreads();
+
+  // 4. score every union block against the queries that kept it
+  const int wave = tid / kWave;
+  const int lane = lane_id();
+  const int slot = lane & 15;
+  const int kgrp = lane >> 4;
+  const size_t kseq = (size_t)b * L;
+  uint16_t* sq = reinterpret_cast<uint16_t*>(smem + lay.wscratch) + (size_t)wave * 2 * QT;
+  uint16_t* sp = sq + QT;
+  const int n_mt = B / 16;
+  for (int u = wave; u < nU; u += kTiledWaves) {
+    const int j = ulist[u];
+    const int off = uoff[u];
+    int pc = 0;
+#pragma unroll
+    for (int w = 0; w < QW; ++w) {
+      const uint64_t word = bitmap[j * QW + w];
+      if ((word >> lane) & 1ull) {
+        const int rank = pc + (int)lanes_below(word);
+        sq[rank] = (uint16_t)(w * 64 + lane);
+        sp[rank] = posbuf[off + rank];
+      }
+      pc += __popcll(word);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const uint16_t* blk_rows = kI + (kseq + (size_t)j * B) * DI + 8 * kgrp;
+    const int max_row = L - 1 - j * B;  // rows past the sequence end are clamped (their scores are unused)
+    u32x4 a_next[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a_next[ks] = *reinterpret_cast<const u32x4*>(blk_rows + (size_t)min(slot, max_row) * DI + 32 * ks);
+    for (int mt = 0; mt < n_mt; ++mt) {
+      bf16x8 a_cur[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a_cur[ks] = __builtin_bit_cast(bf16x8, a_next[ks]);
+      if (mt + 1 < n_mt) {
+        const int r = min(16 * (mt + 1) + slot, max_row);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          a_next[ks] = *reinterpret_cast<const u32x4*>(blk_rows + (size_t)r * DI + 32 * ks);
+      }
+      const int r0 = 16 * mt + 4 * kgrp;  // token offset inside the block of this lane's 4 scores
+      const int s0 = j * B + r0;
+      for (int g = 0; g * 16 < pc; ++g) {
+        const int rank = g * 16 + slot;
+        const bool valid = rank < pc;
+        const int qq = valid ? sq[rank] : 0;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (valid) v = *reinterpret_cast<const u32x4*>(qtile + qq * DI + 8 * kgrp + 32 * ks);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur[ks], __builtin_bit_cast(bf16x8, v), acc, 0, 0, 0);
+        }
+        if (valid) {
+          const int t = query_pos(L, nq, i0 + qq);
+          float* dst = scores + (qrow0 + qq) * (size_t)m * B + (size_t)sp[rank] * B + r0;
+          if (s0 + 3 <= t) {
+            *reinterpret_cast<f32x4*>(dst) = acc;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (s0 + e <= t) dst[e] = acc[e];
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 template <int NW, int R>
 __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ blk, int32_t* __restrict__ tok,
                                                           int L, int nq, int B, int m, int k) {
-  __shared__ int lds[select_lds_words<NW>()];
+  __shared__ SelectSmem<NW> lds;
+  __shared__ int bl[kMaxSelBlocks];
   const int q = blockIdx.x;
   const int i = q % nq;
   const int t = query_pos(L, nq, i);
   int c, n_sel, n_valid;
   candidate_count(t, B, m, c, n_sel, n_valid);
-  const int32_t* bl = blk + (size_t)q * m;
   int32_t* out = tok + (size_t)q * k;
   if (n_valid <= k) {
+    const int32_t* blq = blk + (size_t)q * m;
     for (int slot = threadIdx.x; slot < k; slot += NW * 64)
-      out[slot] = slot < n_valid ? bl[slot / B] * B + slot % B : -1;
+      out[slot] = slot < n_valid ? blq[slot / B] * B + slot % B : -1;
     return;
   }
+  // scoring path: m * B <= 32768 (checked at the API), so n_sel <= kMaxSelBlocks
+  for (int p = threadIdx.x; p < n_sel; p += NW * 64) bl[p] = blk[(size_t)q * m + p];
+  __syncthreads();
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const float* sc = scores + (size_t)q * m * B;
@@ -99,7 +352,8 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int idx = wave * kWave * R + r * kWave + lane;
-    key[r] = idx < n_valid ? score_key(sc[idx]) : 0u;
+    const float v = sc[idx < n_valid ? idx : 0];  // branch-free: all loads in flight together
+    key[r] = idx < n_valid ? score_key(v) : 0u;
   }
   select_top<NW, R>(key, k, lds, [&](int pos, int idx) { out[pos] = bl[idx / B] * B + idx % B; });
 }
@@ -117,11 +371,61 @@ static hipError_t launch_tsel(int R, const Dims& s, const float* sc, const int32
     hipLaunchKernelGGL((k_token_select<NW, RR>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, s.m, s.k); \
     break;
   switch (R) {
-    HSA_TS(1) HSA_TS(2) HSA_TS(4) HSA_TS(8) HSA_TS(16) HSA_TS(32) HSA_TS(64)
+    HSA_TS(1) HSA_TS(2) HSA_TS(4) HSA_TS(8) HSA_TS(16) HSA_TS(32)
+    case 64:
+      if constexpr (NW <= 4) {
+        hipLaunchKernelGGL((k_token_select<NW, 64>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, s.m, s.k);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 #undef HSA_TS
   return hipGetLastError();
+}
+
+constexpr size_t kMaxLds = 160 * 1024;
+
+// Queries per tile of the tiled scorer (64 * QW), or 0 when the per-query
+// scorer is used (few queries per sequence, small blocks, or no LDS room).
+static int tiled_qw(const Dims& s) {
+  if (s.B < 16 || s.nq < 64) return 0;
+  for (int qw = 4; qw >= 1; qw >>= 1) {
+    if (qw > 1 && s.nq < 64 * qw) continue;
+    if (tiled_layout(s.nb, qw, s.m, s.dI).total <= kMaxLds) return qw;
+  }
+  return 0;
+}
+
+template <int DI, int QW>
+static hipError_t launch_tiled_t(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
+                                 float* scores, hipStream_t st) {
+  const int QT = 64 * QW;
+  const int tiles_per_seq = (s.nq + QT - 1) / QT;
+  const int n_tiles = tiles_per_seq * s.b;
+  const size_t lds = tiled_layout(s.nb, QW, s.m, DI).total;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_token_scores_tiled<DI, QW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_token_scores_tiled<DI, QW>), dim3(n_tiles), dim3(kTiledWaves * 64), lds, st, qI, kI, blk,
+                     scores, s.L, s.nq, s.B, s.m, s.k, tiles_per_seq, n_tiles, s.nb);
+  return hipGetLastError();
+}
+
+static hipError_t launch_tiled(const Dims& s, int qw, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
+                               float* scores, hipStream_t st) {
+  if (s.dI == 64) {
+    if (qw == 4) return launch_tiled_t<64, 4>(s, qI, kI, blk, scores, st);
+    if (qw == 2) return launch_tiled_t<64, 2>(s, qI, kI, blk, scores, st);
+    return launch_tiled_t<64, 1>(s, qI, kI, blk, scores, st);
+  }
+  if (qw == 4) return launch_tiled_t<128, 4>(s, qI, kI, blk, scores, st);
+  if (qw == 2) return launch_tiled_t<128, 2>(s, qI, kI, blk, scores, st);
+  return launch_tiled_t<128, 1>(s, qI, kI, blk, scores, st);
 }
 
 hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk, int32_t* tok,
@@ -132,12 +436,20 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
   const bool any_scoring = (long long)s.k < (long long)s.m * s.B && s.L > s.k;
   int n_max = s.m * s.B;
   if (any_scoring) {
-    dim3 grid(s.m, nq_total);
-    if (s.dI == 64)
-      hipLaunchKernelGGL((k_token_scores<64>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m, s.k);
-    else
-      hipLaunchKernelGGL((k_token_scores<128>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m, s.k);
-    hipError_t e = hipGetLastError();
+    const int qw = tiled_qw(s);
+    hipError_t e;
+    if (qw > 0) {
+      e = launch_tiled(s, qw, qI, kI, blk, scores, st);
+    } else {
+      dim3 grid(s.m, nq_total);
+      if (s.dI == 64)
+        hipLaunchKernelGGL((k_token_scores<64>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
+                           s.k);
+      else
+        hipLaunchKernelGGL((k_token_scores<128>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
+                           s.k);
+      e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
   } else {
     n_max = 1;  // every query keeps all of its candidates
