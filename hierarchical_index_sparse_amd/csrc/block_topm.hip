@@ -71,53 +71,69 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
   }
 }
 
+// NW == 1: each of the 4 waves of a workgroup selects for its own query;
+// NW > 1: the NW waves of a workgroup select for one query together.
 template <int NW, int R>
-__global__ __launch_bounds__(NW * 64) void k_block_select(const float* __restrict__ scores, int32_t* __restrict__ blk,
-                                                          int L, int nq, int B, int nb, int m) {
-  __shared__ SelectSmem<NW> lds;
-  const int q = blockIdx.x;
+__global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const float* __restrict__ scores,
+                                                                          int32_t* __restrict__ blk, int L, int nq,
+                                                                          int B, int nb, int m, int nq_total) {
+  constexpr int QPB = NW == 1 ? 4 : 1;  // queries per workgroup
+  constexpr int GT = NW * kWave;        // threads per select group
+  __shared__ SelectSmem<NW> lds[QPB];
+  const int wave = threadIdx.x / kWave;
+  const int q = NW == 1 ? (int)blockIdx.x * 4 + wave : (int)blockIdx.x;
+  if (q >= nq_total) return;  // wave-uniform (NW == 1 only)
+  SelectSmem<NW>& sm = lds[NW == 1 ? wave : 0];
+  const int gtid = NW == 1 ? lane_id() : (int)threadIdx.x;
   const int i = q % nq;
   const int t = query_pos(L, nq, i);
   const int c = t / B;
   int32_t* out = blk + (size_t)q * m;
   if (c + 1 <= m) {
-    for (int j = threadIdx.x; j < m; j += NW * 64) out[j] = j <= c ? j : -1;
+    for (int j = gtid; j < m; j += GT) out[j] = j <= c ? j : -1;
     return;
   }
   const int want = m - 2;
   const int n = c - 1;  // candidates: blocks 1 .. c-1 (index = block - 1)
-  if (threadIdx.x == 0) {
+  if (gtid == 0) {
     out[0] = 0;
     out[m - 1] = c;
   }
   if (want == 0) return;
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
   const float* sc = scores + (size_t)q * nb + 1;
   uint32_t key[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int idx = wave * kWave * R + r * kWave + lane;
+    const int idx = gtid * R + r;
     const float v = sc[idx < n ? idx : 0];  // branch-free: all loads in flight together
     key[r] = idx < n ? score_key(v) : 0u;
   }
-  select_top<NW, R>(key, want, lds, [&](int pos, int idx) { out[1 + pos] = 1 + idx; });
+  select_top<NW, R>(key, want, sm, [&](int pos, int idx) { out[1 + pos] = 1 + idx; });
+}
+
+template <int NW, int R>
+static hipError_t launch_select_r(int nq_total, const float* scores, int32_t* blk, const Dims& s, hipStream_t st) {
+  dim3 grid(NW == 1 ? (nq_total + 3) / 4 : nq_total), block(NW == 1 ? 256 : NW * 64);
+  hipLaunchKernelGGL((k_block_select<NW, R>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m, nq_total);
+  return hipGetLastError();
 }
 
 template <int NW>
 static hipError_t launch_select(int R, int nq_total, const float* scores, int32_t* blk, const Dims& s,
                                 hipStream_t st) {
-  dim3 grid(nq_total), block(NW * 64);
-#define HSA_SEL(RR)                                                                                  \
-  case RR:                                                                                          \
-    hipLaunchKernelGGL((k_block_select<NW, RR>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m); \
-    break;
   switch (R) {
-    HSA_SEL(1) HSA_SEL(2) HSA_SEL(4) HSA_SEL(8) HSA_SEL(16) HSA_SEL(32)
+    case 1: return launch_select_r<NW, 1>(nq_total, scores, blk, s, st);
+    case 2: return launch_select_r<NW, 2>(nq_total, scores, blk, s, st);
+    case 4: return launch_select_r<NW, 4>(nq_total, scores, blk, s, st);
+    case 8: return launch_select_r<NW, 8>(nq_total, scores, blk, s, st);
+    case 16:
+      if constexpr (NW > 1) return launch_select_r<NW, 16>(nq_total, scores, blk, s, st);
+      return hipErrorInvalidValue;
+    case 32:
+      if constexpr (NW > 1) return launch_select_r<NW, 32>(nq_total, scores, blk, s, st);
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
-#undef HSA_SEL
-  return hipGetLastError();
 }
 
 size_t block_topm_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq * s.nb * sizeof(float)); }
@@ -149,7 +165,9 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // many queries: a 4-wave workgroup per query; few queries: 16 waves
+  // many queries: one wave per query (<= 512 candidates) or a 4-wave
+  // workgroup per query; few queries: 16 waves per query
+  if (nq_total >= 512 && n_max <= 64 * 8) return launch_select<1>(pick_r(n_max, 1), nq_total, scores, blk, s, st);
   if (nq_total >= 512 && n_max <= 4 * 64 * 32) return launch_select<4>(pick_r(n_max, 4), nq_total, scores, blk, s, st);
   return launch_select<16>(pick_r(n_max, 16), nq_total, scores, blk, s, st);
 }

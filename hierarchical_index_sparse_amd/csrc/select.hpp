@@ -1,27 +1,29 @@
 // Exact top-`want` selection with ties broken toward the lower index.
 //
-// The keys live in registers.  A workgroup of NW waves holds up to
-// NW * 64 * R keys; wave w owns the contiguous index range
-// [w * 64 * R, (w + 1) * 64 * R) and key[r] of lane l has index
-// w * 64 * R + r * 64 + l.  Key 0 marks an empty slot; keys come from
-// score_key() of finite scores.
+// The keys live in registers, thread-major: a group of NW waves holds up to
+// NW * 64 * R keys and thread x of the group owns the consecutive indices
+// [x * R, x * R + R) (key[r] has index x * R + r).  Key 0 marks an empty
+// slot; keys come from score_key() of finite scores.  With NW == 1 a single
+// wave selects on its own (several waves of one workgroup may then run
+// independent selects, each with its own SelectSmem); with NW > 1 the whole
+// workgroup takes part.
 //
-// 1. Threshold T = the want-th largest key, found in two phases:
-//    a. the scores are dropped into 256 linear bins between their minimum
-//       and maximum (bin = floor((x - min) * 256 / (max - min)), a
+// 1. Threshold T = the want-th largest key:
+//    a. (R >= 8) the scores are dropped into 256 linear bins between their
+//       minimum and maximum (bin = floor((x - min) * 256 / (max - min)), a
 //       non-decreasing function of x, so a key in a higher bin is strictly
 //       larger than every key in a lower one and equal keys share a bin);
 //       a suffix scan of the LDS histogram finds the bin holding T and the
-//       count of keys above it;
-//    b. that bin's keys are compacted into LDS and one wave finds T exactly
-//       by a bitwise binary search (largest x with count(key >= x) >= need;
-//       one compare + ballot + popcount per key and bit).
-//    When the bin is too full for the LDS buffer, or the score range is not
-//    finite, the bitwise search runs over all keys instead.
+//       count of keys above it; that bin's keys are compacted into LDS and
+//       one wave finds T by a bitwise binary search over the bits below the
+//       candidates' common prefix (largest x with count(key >= x) >= need,
+//       one compare + ballot + popcount per key and bit);
+//    b. (R < 8, a target bin too full for the LDS buffer, or a score range
+//       that is not finite) the bitwise search runs over all keys.
 // 2. Every key > T is kept; of the keys equal to T, the first
-//    want - count(> T) in index order are kept.  The kept indices are
-//    compacted in ascending index order with ballot/mbcnt, so emit(pos,
-//    index) receives pos = 0 .. want-1 in index order.
+//    want - count(> T) in index order are kept.  Per-thread counts and wave
+//    prefix scans give every thread its output offset, so emit(pos, index)
+//    receives pos = 0 .. want-1 in ascending index order.
 #pragma once
 
 #include "common.hpp"
@@ -40,12 +42,63 @@ struct SelectSmem {
   uint32_t cand[kBinCap];
 };
 
+// Barrier among the threads taking part in one select.
+template <int NW>
+__device__ __forceinline__ void sel_sync() {
+  if constexpr (NW == 1) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ int sel_wave() {
+  if constexpr (NW == 1) return 0;
+  else return threadIdx.x / kWave;
+}
+
 __device__ __forceinline__ float key_to_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
+__device__ __forceinline__ int wave_excl_scan(int v, int& total) {
+  const int lane = lane_id();
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  total = __shfl(x, kWave - 1, kWave);
+  return x - v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = min(v, (uint32_t)shfl_xor((int)v, o));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_and_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v &= (uint32_t)shfl_xor((int)v, o);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v |= (uint32_t)shfl_xor((int)v, o);
+  return v;
+}
+
 template <int NW>
-__device__ __forceinline__ int wg_sum(int v, int* red, int parity) {
+__device__ __forceinline__ int group_sum(int v, int* red, int parity) {
   if constexpr (NW == 1) {
     return v;
   } else {
@@ -60,18 +113,7 @@ __device__ __forceinline__ int wg_sum(int v, int* red, int parity) {
   }
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)shfl_xor((int)v, o));
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = min(v, (uint32_t)shfl_xor((int)v, o));
-  return v;
-}
-
-// Bitwise search over all registers of all waves: T and count(key > T).
+// Bitwise search over all keys of the group.
 template <int NW, int R>
 __device__ __forceinline__ uint32_t full_threshold(const uint32_t (&key)[R], int want, int* red) {
   uint32_t T = 0;
@@ -81,26 +123,35 @@ __device__ __forceinline__ uint32_t full_threshold(const uint32_t (&key)[R], int
     int cnt = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) cnt += __popcll(ballot(key[r] >= cand));
-    cnt = wg_sum<NW>(cnt, red, parity);
+    cnt = group_sum<NW>(cnt, red, parity);
     parity ^= 1;
     if (cnt >= want) T = cand;
   }
   return T;
 }
 
-// The want-th largest key (1 <= want <= number of non-empty keys).
-// Exact search over the n compacted keys of the target bin by wave 0.
+// Exact search over the n compacted keys of the target bin (one wave).
 template <int R2>
 __device__ __forceinline__ uint32_t bin_threshold(const uint32_t* cand, int n, int need) {
   const int lane = lane_id();
   uint32_t ck[R2];
+  uint32_t all_and = 0xFFFFFFFFu, all_or = 0u;
 #pragma unroll
   for (int r = 0; r < R2; ++r) {
     const int idx = r * kWave + lane;
     ck[r] = idx < n ? cand[idx] : 0u;
+    if (idx < n) {
+      all_and &= ck[r];
+      all_or |= ck[r];
+    }
   }
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
+  all_and = wave_and_u32(all_and);
+  all_or = wave_or_u32(all_or);
+  const uint32_t diff = all_and ^ all_or;
+  if (diff == 0u) return all_and;  // every candidate is equal
+  const int top = 31 - __builtin_clz(diff);
+  uint32_t T = all_and & ~((2u << top) - 1u);  // the common prefix
+  for (int b = top; b >= 0; --b) {
     const uint32_t c = T | (1u << b);
     int cnt = 0;
 #pragma unroll
@@ -110,147 +161,153 @@ __device__ __forceinline__ uint32_t bin_threshold(const uint32_t* cand, int n, i
   return T;
 }
 
+// The want-th largest key (1 <= want <= number of non-empty keys).
 template <int NW, int R>
 __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int want, SelectSmem<NW>& sm) {
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  constexpr int NT = NW * kWave;
-  // few keys per lane: the plain bitwise search is cheaper than the histogram
-  if constexpr (R < 8) return full_threshold<NW, R>(key, want, sm.red);
+  if constexpr (R < 8) {
+    return full_threshold<NW, R>(key, want, sm.red);
+  } else {
+    const int wave = sel_wave<NW>();
+    const int lane = lane_id();
+    const int tid = wave * kWave + lane;
+    constexpr int NT = NW * kWave;
 
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    hi = max(hi, key[r]);
-    lo = min(lo, key[r] ? key[r] : 0xFFFFFFFFu);
-  }
-  hi = wave_max_u32(hi);
-  lo = wave_min_u32(lo);
-  for (int b = threadIdx.x; b < kBins; b += NT) sm.hist[b] = 0;
-  if (lane == 0) {
-    sm.kmin[wave] = lo;
-    sm.kmax[wave] = hi;
-  }
-  if (threadIdx.x == 0) sm.info[2] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    lo = min(lo, sm.kmin[w]);
-    hi = max(hi, sm.kmax[w]);
-  }
-  if (lo == hi) return hi;  // every non-empty key is equal
-  const float smin = key_to_score(lo);
-  const float range = key_to_score(hi) - smin;
-  if (!(range < INFINITY)) {
-    __syncthreads();
-    return full_threshold<NW, R>(key, want, sm.red);
-  }
-  const float scale = (float)kBins / range;
-  auto bin_of = [&](uint32_t k) { return min((int)((key_to_score(k) - smin) * scale), kBins - 1); };
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-    if (key[r]) atomicAdd(&sm.hist[bin_of(key[r])], 1);
-  __syncthreads();
-  if (wave == 0) {
-    // suffix sums over bins: lane l holds bins 4l .. 4l+3
-    const int c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
-              c3 = sm.hist[4 * lane + 3];
-    const int mine = c0 + c1 + c2 + c3;
-    int incl = mine;  // sum over lanes >= l
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int v = __shfl_down(incl, o, kWave);
-      if (lane + o < kWave) incl += v;
+    for (int r = 0; r < R; ++r) {
+      hi = max(hi, key[r]);
+      lo = min(lo, key[r] ? key[r] : 0xFFFFFFFFu);
     }
-    int above = incl - mine;  // keys in bins of higher lanes
-    const int cs[4] = {c0, c1, c2, c3};
+    hi = wave_max_u32(hi);
+    lo = wave_min_u32(lo);
+    for (int b = tid; b < kBins; b += NT) sm.hist[b] = 0;
+    if (lane == 0) {
+      sm.kmin[wave] = lo;
+      sm.kmax[wave] = hi;
+    }
+    if (tid == 0) sm.info[2] = 0;
+    sel_sync<NW>();
 #pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      if (above < want && want <= above + cs[e]) {
-        sm.info[0] = 4 * lane + e;
-        sm.info[1] = above;
+    for (int w = 0; w < NW; ++w) {
+      lo = min(lo, sm.kmin[w]);
+      hi = max(hi, sm.kmax[w]);
+    }
+    if (lo == hi) return hi;  // every non-empty key is equal
+    const float smin = key_to_score(lo);
+    const float range = key_to_score(hi) - smin;
+    if (!(range < INFINITY)) {
+      sel_sync<NW>();
+      return full_threshold<NW, R>(key, want, sm.red);
+    }
+    const float scale = (float)kBins / range;
+    auto bin_of = [&](uint32_t k) { return min((int)((key_to_score(k) - smin) * scale), kBins - 1); };
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (key[r]) atomicAdd(&sm.hist[bin_of(key[r])], 1);
+    sel_sync<NW>();
+    if (wave == 0) {
+      // suffix sums over bins: lane l holds bins 4l .. 4l+3
+      const int c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
+                c3 = sm.hist[4 * lane + 3];
+      const int mine = c0 + c1 + c2 + c3;
+      int incl = mine;  // sum over lanes >= l
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_down(incl, o, kWave);
+        if (lane + o < kWave) incl += v;
       }
-      above += cs[e];
-    }
-  }
-  __syncthreads();
-  const int tb = sm.info[0];
-  const int above = sm.info[1];
-  const int need = want - above;
-  if (sm.hist[tb] > kBinCap) {
-    __syncthreads();
-    return full_threshold<NW, R>(key, want, sm.red);
-  }
-  // compact the target bin's keys (any order)
+      int above = incl - mine;  // keys in bins of higher lanes
+      const int cs[4] = {c0, c1, c2, c3};
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const bool in = key[r] != 0u && bin_of(key[r]) == tb;
-    const uint64_t m = ballot(in);
-    if (m) {
-      const int first = __builtin_ctzll(m);
-      int base = 0;
-      if (lane == first) base = atomicAdd(&sm.info[2], __popcll(m));
-      base = __shfl(base, first, kWave);
-      if (in) sm.cand[base + lanes_below(m)] = key[r];
+      for (int e = 3; e >= 0; --e) {
+        if (above < want && want <= above + cs[e]) {
+          sm.info[0] = 4 * lane + e;
+          sm.info[1] = above;
+        }
+        above += cs[e];
+      }
     }
+    sel_sync<NW>();
+    const int tb = sm.info[0];
+    const int need = want - sm.info[1];
+    if (sm.hist[tb] > kBinCap) {
+      sel_sync<NW>();
+      return full_threshold<NW, R>(key, want, sm.red);
+    }
+    // compact the target bin's keys (any order)
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cnt += (key[r] != 0u && bin_of(key[r]) == tb);
+    int wtot;
+    int pos = wave_excl_scan(cnt, wtot);
+    int base = 0;
+    if (lane == 0 && wtot) base = atomicAdd(&sm.info[2], wtot);
+    pos += __shfl(base, 0, kWave);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (key[r] != 0u && bin_of(key[r]) == tb) sm.cand[pos++] = key[r];
+    sel_sync<NW>();
+    if (wave == 0) {
+      const int n = sm.hist[tb];
+      uint32_t T;
+      if (n <= 64) T = bin_threshold<1>(sm.cand, n, need);
+      else if (n <= 256) T = bin_threshold<4>(sm.cand, n, need);
+      else T = bin_threshold<kBinCap / kWave>(sm.cand, n, need);
+      if (lane == 0) sm.info[3] = (int)T;
+    }
+    sel_sync<NW>();
+    return (uint32_t)sm.info[3];
   }
-  __syncthreads();
-  if (wave == 0) {
-    const int n = sm.info[2];
-    uint32_t T;
-    if (n <= 64) T = bin_threshold<1>(sm.cand, n, need);
-    else if (n <= 256) T = bin_threshold<4>(sm.cand, n, need);
-    else T = bin_threshold<kBinCap / kWave>(sm.cand, n, need);
-    if (lane == 0) sm.info[3] = (int)T;
-  }
-  __syncthreads();
-  return (uint32_t)sm.info[3];
 }
 
-// Requires: 1 <= want < number of non-empty keys.  Must be called by every
-// thread of the workgroup (it contains barriers).
+// Requires: 1 <= want < number of non-empty keys.  Every thread of the
+// group must call it (it synchronises the group).
 template <int NW, int R, typename Emit>
 __device__ __forceinline__ void select_top(const uint32_t (&key)[R], int want, SelectSmem<NW>& sm, Emit&& emit) {
-  const int wave = threadIdx.x / kWave;
+  const int wave = sel_wave<NW>();
   const int lane = lane_id();
   const uint32_t T = find_threshold<NW, R>(key, want, sm);
 
   int gt = 0, eq = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    gt += __popcll(ballot(key[r] > T));
-    eq += __popcll(ballot(key[r] == T));
+    gt += key[r] > T;
+    eq += key[r] == T;
   }
-  int* g = sm.red + 2 * NW;  // the search passes use red[0 .. 2 NW)
-  int* e = sm.red + 3 * NW;
-  if (lane == 0) {
-    g[wave] = gt;
-    e[wave] = eq;
-  }
-  __syncthreads();
-  int gt_total = 0;
+  int gt_w, eq_w;
+  (void)wave_excl_scan(gt, gt_w);
+  const int eq_ex = wave_excl_scan(eq, eq_w);
+  int gt_total = gt_w, eq_before = 0, sel_before = 0;
+  if constexpr (NW > 1) {
+    int* g = sm.red + 2 * NW;  // the search passes use red[0 .. 2 NW)
+    int* e = sm.red + 3 * NW;
+    if (lane == 0) {
+      g[wave] = gt_w;
+      e[wave] = eq_w;
+    }
+    __syncthreads();
+    gt_total = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) gt_total += g[w];
-  const int need_eq = want - gt_total;
-  int eq_before = 0, sel_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    const int take = min(max(need_eq - eq_before, 0), e[w]);
-    sel_before += g[w] + take;
-    eq_before += e[w];
+    for (int w = 0; w < NW; ++w) gt_total += g[w];
+    const int need_all = want - gt_total;
+    for (int w = 0; w < wave; ++w) {
+      sel_before += g[w] + min(max(need_all - eq_before, 0), e[w]);
+      eq_before += e[w];
+    }
   }
-
-  int e_run = eq_before, o_run = sel_before;
+  const int need_eq = want - gt_total;
+  int ties = min(max(need_eq - (eq_before + eq_ex), 0), eq);  // ties this thread keeps
+  int sel_w;
+  int pos = sel_before + wave_excl_scan(gt + ties, sel_w);
+  const int idx0 = (wave * kWave + lane) * R;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const bool is_eq = key[r] == T;
-    const uint64_t eqm = ballot(is_eq);
-    const bool take = key[r] > T || (is_eq && e_run + (int)lanes_below(eqm) < need_eq);
-    const uint64_t selm = ballot(take);
-    if (take) emit(o_run + (int)lanes_below(selm), wave * kWave * R + r * kWave + lane);
-    o_run += __popcll(selm);
-    e_run += __popcll(eqm);
+    const bool take = key[r] > T || (is_eq && ties > 0);
+    ties -= (is_eq && ties > 0);
+    if (take) emit(pos++, idx0 + r);
   }
-  __syncthreads();  // LDS may be reused by the caller
+  sel_sync<NW>();  // LDS may be reused by the caller
 }
 
 }  // namespace hsa

@@ -31,7 +31,7 @@ constexpr int kPartStride = 130;  // 128 dims + running max + running sum
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 template <bool SPLIT>
-__global__ __launch_bounds__(256) void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                      const uint16_t* __restrict__ V, const int32_t* __restrict__ tok,
                                                      float* __restrict__ O, float* __restrict__ lse,
                                                      float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
@@ -74,39 +74,44 @@ __global__ __launch_bounds__(256) void k_sparse_attn(const uint16_t* __restrict_
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int p0 = start; p0 < end; p0 += 32) {
-    const int pos = p0 + (lane & 31);
-    int my = pos < end ? tl[pos] : -1;
-    if (my >= L) my = -1;
-    const uint32_t vmask = (uint32_t)ballot(my >= 0);
-    if (vmask == 0u) continue;
+  // index of list entry `pos` if it is a valid token of this sequence, else -1
+  auto entry = [&](int pos) {
+    int v = pos < end ? tl[pos] : -1;
+    return (v >= L) ? -1 : v;
+  };
+  // K rows (A operand of S^T) and V column pairs of the tile whose entries are `my`
+  auto load_tile = [&](int my, u32x4 (&ka)[4], u32x4 (&kb)[4], uint32_t (&w)[4][8]) {
     const int mine = my < 0 ? 0 : my;
-
-    // ---- S^T = K Q^T over two 16-token tiles
     const int t0 = __shfl(mine, jl, kWave);
     const int t1 = __shfl(mine, 16 + jl, kWave);
     const uint16_t* k0 = Kg + (kv_row0 + t0) * row_stride + 8 * gq;
     const uint16_t* k1 = Kg + (kv_row0 + t1) * row_stride + 8 * gq;
-    u32x4 ka[4], kb[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       ka[ks] = *reinterpret_cast<const u32x4*>(k0 + 32 * ks);
       kb[ks] = *reinterpret_cast<const u32x4*>(k1 + 32 * ks);
     }
-    // V tokens of this lane's 8 P slots: 4 gq + e and 16 + 4 gq + e
-    int vt[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vt[e] = __shfl(mine, 4 * gq + e, kWave);
-      vt[4 + e] = __shfl(mine, 16 + 4 * gq + e, kWave);
-    }
-    uint32_t w[4][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t* vrow = reinterpret_cast<const uint32_t*>(Vg + (kv_row0 + vt[e]) * row_stride) + jl;
+      const int src = (e < 4) ? 4 * gq + e : 16 + 4 * gq + (e - 4);
+      const int vt = __shfl(mine, src, kWave);
+      const uint32_t* vrow = reinterpret_cast<const uint32_t*>(Vg + (kv_row0 + vt) * row_stride) + jl;
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) w[pr][e] = vrow[16 * pr];
     }
+  };
+
+  // software pipeline: tile i's K/V are in registers while tile i+1's loads
+  // are in flight and tile i+2's list entries are being fetched
+  u32x4 ka[4], kb[4];
+  uint32_t w[4][8], w2[4][8];
+  int my = entry(start + (lane & 31));
+  int my_next = entry(start + 32 + (lane & 31));
+  load_tile(my, ka, kb, w);
+  for (int p0 = start; p0 < end; p0 += 32) {
+    const uint32_t vmask = (uint32_t)ballot(my >= 0);
+    const bool has_next = p0 + 32 < end;
+    const int my_next2 = entry(p0 + 64 + (lane & 31));
 
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -114,63 +119,72 @@ __global__ __launch_bounds__(256) void k_sparse_attn(const uint16_t* __restrict_
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), qf[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), qf[ks], s1, 0, 0, 0);
     }
+    if (has_next) load_tile(my_next, ka, kb, w2);
 
-    // ---- online softmax (lane: head jl, tokens 4gq+e and 16+4gq+e)
-    float sv[8];
+    if (vmask != 0u) {
+      // ---- online softmax (lane: head jl, tokens 4gq+e and 16+4gq+e)
+      float sv[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sv[e] = ((vmask >> (4 * gq + e)) & 1u) ? s0[e] * scale_log2 : -INFINITY;
-      sv[4 + e] = ((vmask >> (16 + 4 * gq + e)) & 1u) ? s1[e] * scale_log2 : -INFINITY;
-    }
-    float mx = sv[0];
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = ((vmask >> (4 * gq + e)) & 1u) ? s0[e] * scale_log2 : -INFINITY;
+        sv[4 + e] = ((vmask >> (16 + 4 * gq + e)) & 1u) ? s1[e] * scale_log2 : -INFINITY;
+      }
+      float mx = sv[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    float psum = 0.f;
-    uint32_t ph[4], pl[4];
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      float psum = 0.f;
+      uint32_t ph[4], pl[4];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float pa = exp2f(sv[e] - m_new);
-      const float pb = exp2f(sv[e + 1] - m_new);
-      psum += pa + pb;
-      const uint32_t ha = f32_to_bf16_rne(pa), hb = f32_to_bf16_rne(pb);
-      const uint32_t la = f32_to_bf16_rne(pa - __uint_as_float(ha << 16));
-      const uint32_t lb = f32_to_bf16_rne(pb - __uint_as_float(hb << 16));
-      ph[e / 2] = ha | (hb << 16);
-      pl[e / 2] = la | (lb << 16);
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const bf16x8 p_hi = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
-    const bf16x8 p_lo = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
+      for (int e = 0; e < 8; e += 2) {
+        const float pa = exp2f(sv[e] - m_new);
+        const float pb = exp2f(sv[e + 1] - m_new);
+        psum += pa + pb;
+        const uint32_t ha = f32_to_bf16_rne(pa), hb = f32_to_bf16_rne(pb);
+        const uint32_t la = f32_to_bf16_rne(pa - __uint_as_float(ha << 16));
+        const uint32_t lb = f32_to_bf16_rne(pb - __uint_as_float(hb << 16));
+        ph[e / 2] = ha | (hb << 16);
+        pl[e / 2] = la | (lb << 16);
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      const bf16x8 p_hi = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
+      const bf16x8 p_lo = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
 
-    // ---- rescale O (rows = heads 4gq+i) and accumulate P V
-    float a_i[4];
+      // ---- rescale O (rows = heads 4gq+i) and accumulate P V
+      float a_i[4];
 #pragma unroll
-    for (int i2 = 0; i2 < 4; ++i2) a_i[i2] = __shfl(alpha, 4 * gq + i2, kWave);
+      for (int i2 = 0; i2 < 4; ++i2) a_i[i2] = __shfl(alpha, 4 * gq + i2, kWave);
 #pragma unroll
-    for (int pr = 0; pr < 4; ++pr) {
-      u32x4 ev, od;
+      for (int pr = 0; pr < 4; ++pr) {
+        u32x4 ev, od;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const uint32_t x0 = w[pr][2 * e2], x1 = w[pr][2 * e2 + 1];
-        ev[e2] = (x0 & 0xFFFFu) | (x1 << 16);
-        od[e2] = (x0 >> 16) | (x1 & 0xFFFF0000u);
-      }
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint32_t x0 = w[pr][2 * e2], x1 = w[pr][2 * e2 + 1];
+          ev[e2] = (x0 & 0xFFFFu) | (x1 << 16);
+          od[e2] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        }
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x4 acc = o[2 * pr + hh];
+        for (int hh = 0; hh < 2; ++hh) {
+          f32x4 acc = o[2 * pr + hh];
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) acc[i2] *= a_i[i2];
-        const bf16x8 vb = as_bf16x8(hh ? od : ev);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc, 0, 0, 0);
-        o[2 * pr + hh] = acc;
+          for (int i2 = 0; i2 < 4; ++i2) acc[i2] *= a_i[i2];
+          const bf16x8 vb = as_bf16x8(hh ? od : ev);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc, 0, 0, 0);
+          o[2 * pr + hh] = acc;
+        }
       }
     }
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[pr][e] = w2[pr][e];
+    my = my_next;
+    my_next = my_next2;
   }
 
   l_run += shfl_xor(l_run, 16);
@@ -206,36 +220,69 @@ __global__ __launch_bounds__(256) void k_sparse_attn(const uint16_t* __restrict_
   }
 }
 
-__global__ __launch_bounds__(128) void k_attn_merge(const float* __restrict__ part, float* __restrict__ O,
+// Log-sum-exp merge of the splits of one (query, head): 256 threads = 8
+// split groups x 32 float4 column groups; the groups meet in LDS.
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, float* __restrict__ O,
                                                     float* __restrict__ lse, int Hq, int Hkv, int nsplit) {
+  __shared__ float red[8][129];
+  __shared__ float wmax[4];
   const int qh = blockIdx.x;
   const int q = qh / Hq, h = qh % Hq;
   const int G = Hq / Hkv;
   const int g = h / G, head = h % G;
-  const int dim = threadIdx.x;
+  const int tid = threadIdx.x;
   const float* base = part + ((size_t)(q * Hkv + g) * nsplit * 16 + head) * kPartStride;
   const size_t sstride = (size_t)16 * kPartStride;
+
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * sstride + 128]);
-  float acc = 0.f, Lt = 0.f;
+  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, base[s * sstride + 128]);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
+  if (lane_id() == 0) wmax[tid / kWave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+
+  const int sg = tid / 32, dq = tid % 32;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float Lt = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
+    for (int s = sg; s < nsplit; s += 8) {
       const float* p = base + s * sstride;
       const float wgt = exp2f(p[128] - M);
-      acc += wgt * p[dim];
+      const float4 v = *reinterpret_cast<const float4*>(p + 4 * dq);
+      acc.x += wgt * v.x;
+      acc.y += wgt * v.y;
+      acc.z += wgt * v.z;
+      acc.w += wgt * v.w;
       Lt += wgt * p[129];
     }
   }
-  O[(size_t)qh * 128 + dim] = Lt > 0.f ? acc / Lt : 0.f;
-  if (lse && dim == 0) lse[qh] = Lt > 0.f ? (M + log2f(Lt)) * 0.69314718055994531f : -INFINITY;
+  red[sg][4 * dq] = acc.x;
+  red[sg][4 * dq + 1] = acc.y;
+  red[sg][4 * dq + 2] = acc.z;
+  red[sg][4 * dq + 3] = acc.w;
+  if (dq == 0) red[sg][128] = Lt;
+  __syncthreads();
+  if (tid < 128) {
+    float a = 0.f, l = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a += red[k][tid];
+      l += red[k][128];
+    }
+    O[(size_t)qh * 128 + tid] = l > 0.f ? a / l : 0.f;
+    if (lse && tid == 0) lse[qh] = l > 0.f ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
+  }
 }
 
 // Split plan: enough waves to fill the chip when there are few queries.
 static void split_plan(const Dims& s, int& nsplit, int& chunk) {
+  // at least 4 tiles (128 entries) per split; at most ~2048 waves in total
   const long long items = (long long)s.b * s.nq * s.Hkv;
   const int tiles = (s.k + 31) / 32;
   long long want = (items <= 0 || items >= 2048) ? 1 : (2048 + items - 1) / items;
-  if (want > (tiles + 1) / 2) want = (tiles + 1) / 2;  // at least 2 tiles per split
+  const long long cap = (tiles + 3) / 4;
+  if (want > cap) want = cap;
   if (want < 1) want = 1;
   const int tiles_per = (int)((tiles + want - 1) / want);
   chunk = tiles_per * 32;
@@ -268,7 +315,7 @@ hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* 
                      s.k, chunk, nsplit, scale_log2, n_items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(nq_total * s.Hq)), dim3(128), 0, st, part, O, lse, s.Hq, s.Hkv,
+  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(nq_total * s.Hq)), dim3(256), 0, st, part, O, lse, s.Hq, s.Hkv,
                      nsplit);
   return hipGetLastError();
 }

@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) void k_token_scores_tiled(
 template <int NW, int R>
 __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ blk, int32_t* __restrict__ tok,
-                                                          int L, int nq, int B, int m, int k) {
+                                                          int L, int nq, int B, int log2B, int m, int k) {
   __shared__ SelectSmem<NW> lds;
   __shared__ int bl[kMaxSelBlocks];
   const int q = blockIdx.x;
@@ -345,17 +345,34 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   // scoring path: m * B <= 32768 (checked at the API), so n_sel <= kMaxSelBlocks
   for (int p = threadIdx.x; p < n_sel; p += NW * 64) bl[p] = blk[(size_t)q * m + p];
   __syncthreads();
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const float* sc = scores + (size_t)q * m * B;
+  const float* sc = scores + (size_t)q * m * B;  // 32-byte aligned: m * B is a multiple of 8
+  const int idx0 = threadIdx.x * R;
   uint32_t key[R];
+  if constexpr (R >= 4) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int idx = wave * kWave * R + r * kWave + lane;
-    const float v = sc[idx < n_valid ? idx : 0];  // branch-free: all loads in flight together
-    key[r] = idx < n_valid ? score_key(v) : 0u;
+    for (int r = 0; r < R; r += 4) {
+      if (idx0 + r + 3 < n_valid) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[r + e] = score_key(v[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = idx0 + r + e;
+          key[r + e] = idx < n_valid ? score_key(sc[idx]) : 0u;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = idx0 + r;
+      const float v = sc[idx < n_valid ? idx : 0];
+      key[r] = idx < n_valid ? score_key(v) : 0u;
+    }
   }
-  select_top<NW, R>(key, k, lds, [&](int pos, int idx) { out[pos] = bl[idx / B] * B + idx % B; });
+  const int bmask = B - 1;
+  select_top<NW, R>(key, k, lds, [&](int pos, int idx) { out[pos] = (bl[idx >> log2B] << log2B) | (idx & bmask); });
 }
 
 size_t token_topk_ws_bytes(const Dims& s) {
@@ -366,15 +383,18 @@ size_t token_topk_ws_bytes(const Dims& s) {
 template <int NW>
 static hipError_t launch_tsel(int R, const Dims& s, const float* sc, const int32_t* blk, int32_t* tok, hipStream_t st) {
   dim3 grid(s.b * s.nq), block(NW * 64);
+  const int log2B = __builtin_ctz((unsigned)s.B);  // B is a power of two
 #define HSA_TS(RR)                                                                                          \
   case RR:                                                                                                  \
-    hipLaunchKernelGGL((k_token_select<NW, RR>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, s.m, s.k); \
+    hipLaunchKernelGGL((k_token_select<NW, RR>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, log2B, s.m, \
+                       s.k); \
     break;
   switch (R) {
     HSA_TS(1) HSA_TS(2) HSA_TS(4) HSA_TS(8) HSA_TS(16) HSA_TS(32)
     case 64:
       if constexpr (NW <= 4) {
-        hipLaunchKernelGGL((k_token_select<NW, 64>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, s.m, s.k);
+        hipLaunchKernelGGL((k_token_select<NW, 64>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, log2B, s.m,
+                           s.k);
         break;
       }
       return hipErrorInvalidValue;
