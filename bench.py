@@ -165,6 +165,9 @@ def main():
     ap.add_argument("--workload", default="prefill_64k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-sample", type=int, default=1024, help="queries the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a kernel of known "
+                         "traffic, to scale hardware byte counters against)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -194,6 +197,15 @@ def main():
     def step():
         _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), start_block, out["S"], dev["Q"], dev["K"],
                          dev["V"], None, None, out["O"], out["lse"], ws)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

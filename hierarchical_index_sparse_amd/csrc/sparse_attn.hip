@@ -15,10 +15,12 @@
 //     A-operand layout P needs for P V, so no shuffle of P is required.
 //   * online softmax in the exp2 domain (running max and sum per head).
 //   * O += P V (8 output tiles of 16 dims): each lane gathers, for its 8
-//     tokens, the 32-bit pair (dim 2j, dim 2j+1) of 4 column groups and
-//     splits the pairs into the even-dim and odd-dim B operands, so V needs
-//     no LDS transpose.  P is split into bf16 hi + lo parts (two MFMAs),
-//     which keeps P's rounding error near 2^-17 instead of bf16's 2^-9.
+//     tokens, 16 contiguous bytes (dims 8j .. 8j+7) of each V row; output
+//     tile c takes dims 8j + c, so its B operand is element c of those 8
+//     chunks (16-bit packing only; no LDS transpose, and V costs the same 8
+//     16-byte loads per tile as K).  P is split into bf16 hi + lo parts
+//     (two MFMAs), which keeps P's rounding error near 2^-17 instead of
+//     bf16's 2^-9.
 // Splits (decode) write unnormalised partial results with their running max
 // and sum; k_attn_merge combines them (log-sum-exp merge).
 #include "common.hpp"
@@ -27,6 +29,8 @@
 namespace hsa {
 
 constexpr int kPartStride = 130;  // 128 dims + running max + running sum
+constexpr int kRowBytes = 272;    // staged kv row: 256 bytes + 16 bytes of padding
+constexpr int kStageBytes = 32 * kRowBytes;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -36,6 +40,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                                      float* __restrict__ O, float* __restrict__ lse,
                                                      float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
                                                      int chunk, int nsplit, float scale_log2, int n_items) {
+  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * 2 * kStageBytes];
   const int wave = threadIdx.x / kWave;
   const int item = blockIdx.x * 4 + wave;
   if (item >= n_items) return;
@@ -79,49 +84,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     int v = pos < end ? tl[pos] : -1;
     return (v >= L) ? -1 : v;
   };
-  // K rows (A operand of S^T) and V column pairs of the tile whose entries are `my`
-  auto load_tile = [&](int my, u32x4 (&ka)[4], u32x4 (&kb)[4], uint32_t (&w)[4][8]) {
+  // Coalesced gather of one tile's 32 K rows and 32 V rows: instruction i
+  // reads rows 4i .. 4i+3, 16 lanes (16 bytes each) per 256-byte row.
+  auto gload = [&](int my, u32x4 (&kr)[8], u32x4 (&vr)[8]) {
     const int mine = my < 0 ? 0 : my;
-    const int t0 = __shfl(mine, jl, kWave);
-    const int t1 = __shfl(mine, 16 + jl, kWave);
-    const uint16_t* k0 = Kg + (kv_row0 + t0) * row_stride + 8 * gq;
-    const uint16_t* k1 = Kg + (kv_row0 + t1) * row_stride + 8 * gq;
+    const int c = lane & 15;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      ka[ks] = *reinterpret_cast<const u32x4*>(k0 + 32 * ks);
-      kb[ks] = *reinterpret_cast<const u32x4*>(k1 + 32 * ks);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int src = (e < 4) ? 4 * gq + e : 16 + 4 * gq + (e - 4);
-      const int vt = __shfl(mine, src, kWave);
-      const uint32_t* vrow = reinterpret_cast<const uint32_t*>(Vg + (kv_row0 + vt) * row_stride) + jl;
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr) w[pr][e] = vrow[16 * pr];
+    for (int i = 0; i < 8; ++i) {
+      const int tr = __shfl(mine, 4 * i + (lane >> 4), kWave);
+      const size_t off = (kv_row0 + tr) * row_stride + 8 * c;
+      kr[i] = *reinterpret_cast<const u32x4*>(Kg + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(Vg + off);
     }
   };
+  // this wave's staging buffers: 32 rows of 272 bytes (256 + 16 pad, which
+  // makes the 16-row MFMA operand reads bank-conflict free)
+  unsigned char* kst = stage_lds + (size_t)wave * 2 * kStageBytes;
+  unsigned char* vst = kst + kStageBytes;
+  auto stage = [&](const u32x4 (&kr)[8], const u32x4 (&vr)[8]) {
+    const int off = (lane >> 4) * kRowBytes + 16 * (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<u32x4*>(kst + off + 4 * i * kRowBytes) = kr[i];
+      *reinterpret_cast<u32x4*>(vst + off + 4 * i * kRowBytes) = vr[i];
+    }
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 
-  // software pipeline: tile i's K/V are in registers while tile i+1's loads
-  // are in flight and tile i+2's list entries are being fetched
-  u32x4 ka[4], kb[4];
-  uint32_t w[4][8], w2[4][8];
+  // pipeline: tile i in LDS, tile i+1 in flight to registers, list entries
+  // of tile i+2 in flight
+  u32x4 kr[8], vr[8];
   int my = entry(start + (lane & 31));
   int my_next = entry(start + 32 + (lane & 31));
-  load_tile(my, ka, kb, w);
+  gload(my, kr, vr);
+  stage(kr, vr);
+  if (start + 32 < end) gload(my_next, kr, vr);
+  wave_sync();
   for (int p0 = start; p0 < end; p0 += 32) {
     const uint32_t vmask = (uint32_t)ballot(my >= 0);
-    const bool has_next = p0 + 32 < end;
     const int my_next2 = entry(p0 + 64 + (lane & 31));
 
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[ks]), qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[ks]), qf[ks], s1, 0, 0, 0);
-    }
-    if (has_next) load_tile(my_next, ka, kb, w2);
-
     if (vmask != 0u) {
+      // ---- S^T = K Q^T over two 16-token tiles (A = staged K rows)
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kst + jl * kRowBytes + 16 * (gq + 4 * ks));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kst + (16 + jl) * kRowBytes + 16 * (gq + 4 * ks));
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), qf[ks], s1, 0, 0, 0);
+      }
+      // V chunks (dims 8jl .. 8jl+7) of this lane's 8 P tokens
+      u32x4 w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tr = (e < 4) ? 4 * gq + e : 16 + 4 * gq + (e - 4);
+        w[e] = *reinterpret_cast<const u32x4*>(vst + tr * kRowBytes + 16 * jl);
+      }
+
       // ---- online softmax (lane: head jl, tokens 4gq+e and 16+4gq+e)
       float sv[8];
 #pragma unroll
@@ -154,7 +178,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       const bf16x8 p_hi = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
       const bf16x8 p_lo = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
 
-      // ---- rescale O (rows = heads 4gq+i) and accumulate P V
+      // ---- rescale O (rows = heads 4gq+i) and accumulate P V; output
+      // tile c holds dims 8 jl + c, so its B operand is element c of the
+      // lane's 8 V chunks, packed two tokens per register
       float a_i[4];
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) a_i[i2] = __shfl(alpha, 4 * gq + i2, kWave);
@@ -163,7 +189,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         u32x4 ev, od;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
-          const uint32_t x0 = w[pr][2 * e2], x1 = w[pr][2 * e2 + 1];
+          const uint32_t x0 = w[2 * e2][pr], x1 = w[2 * e2 + 1][pr];
           ev[e2] = (x0 & 0xFFFFu) | (x1 << 16);
           od[e2] = (x0 >> 16) | (x1 & 0xFFFF0000u);
         }
@@ -179,35 +205,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
       }
     }
-#pragma unroll
-    for (int pr = 0; pr < 4; ++pr)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) w[pr][e] = w2[pr][e];
+    wave_sync();  // tile i's LDS reads are done
+    if (p0 + 32 < end) stage(kr, vr);
+    wave_sync();
+    if (p0 + 64 < end) gload(my_next2, kr, vr);
     my = my_next;
     my_next = my_next2;
   }
 
   l_run += shfl_xor(l_run, 16);
   l_run += shfl_xor(l_run, 32);
-  // outputs: lane holds heads 4gq+i, dims 32 pr + 2 jl + hh
+  // outputs: lane holds heads 4gq+i, dims 8 jl + c (c = output tile)
 #pragma unroll
   for (int i2 = 0; i2 < 4; ++i2) {
     const int head = 4 * gq + i2;
     const float l_h = __shfl(l_run, head, kWave);
     if (head >= G) continue;
-    if constexpr (SPLIT) {
-      float* dst = part + ((size_t)item * 16 + head) * kPartStride;
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr)
-        *reinterpret_cast<float2*>(dst + 32 * pr + 2 * jl) = make_float2(o[2 * pr][i2], o[2 * pr + 1][i2]);
-    } else {
-      const float inv = l_h > 0.f ? 1.f / l_h : 0.f;
-      float* dst = O + ((size_t)q * Hq + (size_t)g * G + head) * 128;
-#pragma unroll
-      for (int pr = 0; pr < 4; ++pr)
-        *reinterpret_cast<float2*>(dst + 32 * pr + 2 * jl) =
-            make_float2(o[2 * pr][i2] * inv, o[2 * pr + 1][i2] * inv);
-    }
+    const float inv = SPLIT ? 1.f : (l_h > 0.f ? 1.f / l_h : 0.f);
+    float* dst = SPLIT ? part + ((size_t)item * 16 + head) * kPartStride
+                       : O + ((size_t)q * Hq + (size_t)g * G + head) * 128;
+    *reinterpret_cast<f32x4*>(dst + 8 * jl) =
+        f32x4{o[0][i2] * inv, o[1][i2] * inv, o[2][i2] * inv, o[3][i2] * inv};
+    *reinterpret_cast<f32x4*>(dst + 8 * jl + 4) =
+        f32x4{o[4][i2] * inv, o[5][i2] * inv, o[6][i2] * inv, o[7][i2] * inv};
   }
   if (gq == 0 && jl < G) {
     if constexpr (SPLIT) {
