@@ -73,6 +73,50 @@ def algorithmic_work(w: Workload) -> dict:
     }
 
 
+# ----------------------------------------------------- hardware traffic
+
+
+# kernel sources that define each stage's dominant kernel
+STAGE_SOURCES = {
+    "block_summary": ["block_summary.hip", "common.hpp"],
+    "block_topm": ["block_topm.hip", "select.hpp", "common.hpp"],
+    "token_topk": ["token_topk.hip", "select.hpp", "common.hpp"],
+    "sparse_attn": ["sparse_attn.hip", "common.hpp"],
+}
+
+
+def stage_source_hash(stage: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in STAGE_SOURCES[stage]:
+        with open(os.path.join(ROOT, "hierarchical_index_sparse_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str, stage: str):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE record
+    (profiles/<workload>_traffic.txt), each scaled by what the same counter
+    read for a device copy of known size; None if there is no record or the
+    kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        rec[k.strip()] = v.strip()
+    if rec.get("stage") != stage or rec.get("source_sha256") != stage_source_hash(stage):
+        return None
+    copy_kib = float(rec["copy_bytes"]) / 1024.0
+    fetch_scale = copy_kib / float(rec["copy_fetch_size_kib"])
+    write_scale = copy_kib / float(rec["copy_write_size_kib"])
+    return 1024.0 * (float(rec["fetch_size_kib_per_dispatch"]) * fetch_scale
+                     + float(rec["write_size_kib_per_dispatch"]) * write_scale)
+
+
 # -------------------------------------------------------------- CPU oracle
 
 
@@ -244,6 +288,7 @@ def main():
         achieved = work[dom]["bytes"] / dom_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    roof["traffic"] = recorded_traffic(w.name, dom)
     roof["stage"] = dom
     roof["algorithmic_per_launch"] = work[dom]["flops"] if dom == "block_topm" else work[dom]["bytes"]
 

@@ -6,7 +6,8 @@
 // holding the query) are always kept.  HiLS page (section 2.2): a chunk's
 // coarse score comes from its landmark vectors; here the maximum over them.
 //
-// Kernel 1 (k_block_scores): score_j = max_l qI . S[j, l] for the causal
+// Kernel 1 (k_block_scores_mfma for >= 64 queries per sequence, else the
+// GEMV k_block_scores): score_j = max_l qI . S[j, l] for the causal
 // blocks 1..c-1 of every query that needs scoring (c + 1 > m), written as
 // fp32 to the workspace.  Each wave streams summary rows with 16-byte loads
 // (d_index/8 lanes per row), multiplies by the query chunk it holds in
@@ -73,6 +74,76 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
 
 // NW == 1: each of the 4 waves of a workgroup selects for its own query;
 // NW > 1: the NW waves of a workgroup select for one query together.
+// MFMA block scores for many queries: one workgroup scores 64 consecutive
+// queries of one sequence against 128 summary rows (128 / NL blocks); wave w
+// takes rows 32w .. 32w+31 for all 64 queries.  C = qI S^T with
+// v_mfma_f32_16x16x32_bf16: A = 16 queries' indexer vectors, B = 16 summary
+// rows; the accumulator holds 4 queries x 1 row per lane, the max over a
+// block's NL landmark rows is an xor shuffle across adjacent lanes.  Tiles
+// above the causal diagonal are skipped and only the scores the select reads
+// (blocks 1 .. c-1 of queries with c + 1 > m) are written.
+template <int DI, int NL>
+__global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __restrict__ qI,
+                                                           const uint16_t* __restrict__ S,
+                                                           float* __restrict__ scores, int L, int nq, int B,
+                                                           int nb, int m, int qtiles_per_seq) {
+  constexpr int KS = DI / 32;
+  const int b = blockIdx.y / qtiles_per_seq;
+  const int i0 = (blockIdx.y % qtiles_per_seq) * 64;
+  const int i_last = min(nq, i0 + 64) - 1;
+  const int c_last = query_pos(L, nq, i_last) / B;
+  if (c_last + 1 <= m) return;  // no query of the tile needs scores
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int jl = lane & 15, gq = lane >> 4;
+  const int row0 = blockIdx.x * 128 + wave * 32;  // first summary row of this wave
+  if (row0 / NL >= c_last) return;                // every block is non-causal or forced
+  const int nrows = nb * NL;
+
+  // B operands: 2 tiles of 16 summary rows
+  u32x4 bs[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = min(row0 + 16 * nt + jl, nrows - 1);
+    const uint16_t* src = S + ((size_t)b * nrows + row) * DI + 8 * gq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bs[nt][ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    // A operand: 16 queries
+    const int qa = min(i0 + 16 * mt + jl, nq - 1);
+    const uint16_t* qsrc = qI + ((size_t)b * nq + qa) * DI + 8 * gq;
+    u32x4 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
+                                                      __builtin_bit_cast(bf16x8, bs[nt][ks]), acc, 0, 0, 0);
+      // lane: queries 16mt + 4gq + e, summary row row0 + 16nt + jl
+#pragma unroll
+      for (int o = 1; o < NL; o <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = fmaxf(acc[e], shfl_xor(acc[e], o));
+      const int row = row0 + 16 * nt + jl;
+      const int j = row / NL;
+      if (row % NL == 0 && row < nrows) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + 16 * mt + 4 * gq + e;
+          if (i >= nq) continue;
+          const int c = query_pos(L, nq, i) / B;
+          if (c + 1 > m && j >= 1 && j < c) scores[((size_t)b * nq + i) * nb + j] = acc[e];
+        }
+      }
+    }
+  }
+}
+
 template <int NW, int R>
 __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const float* __restrict__ scores,
                                                                           int32_t* __restrict__ blk, int L, int nq,
@@ -126,9 +197,7 @@ static hipError_t launch_select(int R, int nq_total, const float* scores, int32_
     case 2: return launch_select_r<NW, 2>(nq_total, scores, blk, s, st);
     case 4: return launch_select_r<NW, 4>(nq_total, scores, blk, s, st);
     case 8: return launch_select_r<NW, 8>(nq_total, scores, blk, s, st);
-    case 16:
-      if constexpr (NW > 1) return launch_select_r<NW, 16>(nq_total, scores, blk, s, st);
-      return hipErrorInvalidValue;
+    case 16: return launch_select_r<NW, 16>(nq_total, scores, blk, s, st);
     case 32:
       if constexpr (NW > 1) return launch_select_r<NW, 32>(nq_total, scores, blk, s, st);
       return hipErrorInvalidValue;
@@ -152,7 +221,21 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
   // the last query has the most causal blocks
   const int c_max = (s.L - 1) / s.B;
   const int n_max = c_max - 1;
-  if (c_max + 1 > s.m) {
+  if (c_max + 1 > s.m && s.nq >= 64) {
+    const int qtiles = (s.nq + 63) / 64;
+    dim3 grid((s.nb * s.nL + 127) / 128, qtiles * s.b);
+#define HSA_SM(DI, NL)                                                                                      \
+  hipLaunchKernelGGL((k_block_scores_mfma<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, \
+                     s.nb, s.m, qtiles)
+    if (s.dI == 64) {
+      if (s.nL == 1) HSA_SM(64, 1); else if (s.nL == 2) HSA_SM(64, 2); else HSA_SM(64, 4);
+    } else {
+      if (s.nL == 1) HSA_SM(128, 1); else if (s.nL == 2) HSA_SM(128, 2); else HSA_SM(128, 4);
+    }
+#undef HSA_SM
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (c_max + 1 > s.m) {
     dim3 grid((c_max + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG, nq_total);
     hipError_t e = hipSuccess;
 #define HSA_SC(DI, NL) hipLaunchKernelGGL((k_block_scores<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, s.nb, s.m)
@@ -166,7 +249,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     if (e != hipSuccess) return e;
   }
   // many queries: one wave per query (<= 512 candidates) or a 4-wave
-  // workgroup per query; few queries: 16 waves per query
+  // workgroup per query; few queries: 16 waves per query (shortest latency)
   if (nq_total >= 512 && n_max <= 64 * 8) return launch_select<1>(pick_r(n_max, 1), nq_total, scores, blk, s, st);
   if (nq_total >= 512 && n_max <= 4 * 64 * 32) return launch_select<4>(pick_r(n_max, 4), nq_total, scores, blk, s, st);
   return launch_select<16>(pick_r(n_max, 16), nq_total, scores, blk, s, st);

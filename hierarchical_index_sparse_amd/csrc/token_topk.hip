@@ -474,7 +474,7 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
   } else {
     n_max = 1;  // every query keeps all of its candidates
   }
-  if (nq_total >= 512 && n_max <= 4 * 64 * 64) {
+  if (nq_total >= 512 && n_max <= 4 * 64 * 64) {  // many queries: a 4-wave workgroup per query
     int r = 1;
     while (r * 256 < n_max) r <<= 1;
     return launch_tsel<4>(r, s, scores, blk, tok, st);
