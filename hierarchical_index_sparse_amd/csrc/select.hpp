@@ -9,8 +9,8 @@
 // workgroup takes part.
 //
 // 1. Threshold T = the want-th largest key:
-//    a. (R >= 8) the scores are dropped into 256 linear bins between their
-//       minimum and maximum (bin = floor((x - min) * 256 / (max - min)), a
+//    a. (NW * R >= 8) the scores are dropped into 256 linear bins between
+//       their minimum and maximum (bin = floor((x - min) * 256 / (max - min)), a
 //       non-decreasing function of x, so a key in a higher bin is strictly
 //       larger than every key in a lower one and equal keys share a bin);
 //       a suffix scan of the LDS histogram finds the bin holding T and the
@@ -18,8 +18,8 @@
 //       one wave finds T by a bitwise binary search over the bits below the
 //       candidates' common prefix (largest x with count(key >= x) >= need,
 //       one compare + ballot + popcount per key and bit);
-//    b. (R < 8, a target bin too full for the LDS buffer, or a score range
-//       that is not finite) the bitwise search runs over all keys.
+//    b. (fewer keys, a target bin too full for the LDS buffer, or a score
+//       range that is not finite) the bitwise search runs over all keys.
 // 2. Every key > T is kept; of the keys equal to T, the first
 //    want - count(> T) in index order are kept.  Per-thread counts and wave
 //    prefix scans give every thread its output offset, so emit(pos, index)
@@ -164,7 +164,10 @@ __device__ __forceinline__ uint32_t bin_threshold(const uint32_t* cand, int n, i
 // The want-th largest key (1 <= want <= number of non-empty keys).
 template <int NW, int R>
 __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int want, SelectSmem<NW>& sm) {
-  if constexpr (R < 8) {
+  // Few keys in a single wave: the bitwise search has no barriers and is
+  // cheapest.  Otherwise (many keys, or many waves whose every bitwise pass
+  // would need a workgroup barrier) the histogram path is used.
+  if constexpr (R < 8 && NW * R < 8) {
     return full_threshold<NW, R>(key, want, sm.red);
   } else {
     const int wave = sel_wave<NW>();

@@ -90,9 +90,9 @@ __global__ __launch_bounds__(256) void k_token_scores(const uint16_t* __restrict
 // times B rows instead of m blocks per query.
 // ---------------------------------------------------------------------------
 
-constexpr int kTiledWaves = 16;
+constexpr int kTiledWaves = 8;
 
-// Exclusive scan of two counters over the 1024 threads of the workgroup.
+// Exclusive scan of two counters over the threads of the workgroup.
 __device__ __forceinline__ void wg_scan2(int a, int b, int* lds, int& a_ex, int& b_ex, int& a_tot, int& b_tot) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   int ai = a, bi = b;
@@ -156,7 +156,7 @@ __host__ __device__ inline TiledLayout tiled_layout(int nJ, int QW, int m, int D
 }
 
 template <int DI, int QW>
-__global__ __launch_bounds__(kTiledWaves * 64) void k_token_scores_tiled(
+__global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_token_scores_tiled(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI, const int32_t* __restrict__ blk,
     float* __restrict__ scores, int L, int nq, int B, int m, int k, int tiles_per_seq, int n_tiles, int nJ_max) {
   constexpr int QT = 64 * QW;
@@ -249,7 +249,11 @@ __global__ __launch_bounds__(kTiledWaves * 64) void k_token_scores_tiled(
   }
   __syncthreads();
 
-  // 4. score every union block against the queries that kept it
+  // 4. score every union block against the queries that kept it.  A wave
+  // loads all of a block's kI rows at once (one memory latency per block),
+  // then, per group of 16 queries, loads the group's indexer vectors from
+  // LDS once and runs the block's m-tiles back to back.
+  constexpr int kMaxMT = 8;  // B <= 128
   const int wave = tid / kWave;
   const int lane = lane_id();
   const int slot = lane & 15;
@@ -272,48 +276,52 @@ __global__ __launch_bounds__(kTiledWaves * 64) void k_token_scores_tiled(
       }
       pc += __popcll(word);
     }
+    const uint16_t* blk_rows = kI + (kseq + (size_t)j * B) * DI + 8 * kgrp;
+    const int max_row = L - 1 - j * B;  // rows past the sequence end are clamped (their scores are unused)
+    u32x4 a[kMaxMT][KS];
+#pragma unroll
+    for (int mt = 0; mt < kMaxMT; ++mt) {
+      if (mt < n_mt) {
+        const int r = min(16 * mt + slot, max_row);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[mt][ks] = *reinterpret_cast<const u32x4*>(blk_rows + (size_t)r * DI + 32 * ks);
+      }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    const uint16_t* blk_rows = kI + (kseq + (size_t)j * B) * DI + 8 * kgrp;
-    const int max_row = L - 1 - j * B;  // rows past the sequence end are clamped (their scores are unused)
-    u32x4 a_next[KS];
+    for (int g = 0; g * 16 < pc; ++g) {
+      const int rank = g * 16 + slot;
+      const bool valid = rank < pc;
+      const int qq = valid ? sq[rank] : 0;
+      const int pos = valid ? sp[rank] : 0;
+      bf16x8 bq[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      a_next[ks] = *reinterpret_cast<const u32x4*>(blk_rows + (size_t)min(slot, max_row) * DI + 32 * ks);
-    for (int mt = 0; mt < n_mt; ++mt) {
-      bf16x8 a_cur[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) a_cur[ks] = __builtin_bit_cast(bf16x8, a_next[ks]);
-      if (mt + 1 < n_mt) {
-        const int r = min(16 * (mt + 1) + slot, max_row);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          a_next[ks] = *reinterpret_cast<const u32x4*>(blk_rows + (size_t)r * DI + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (valid) v = *reinterpret_cast<const u32x4*>(qtile + qq * DI + 8 * kgrp + 32 * ks);
+        bq[ks] = __builtin_bit_cast(bf16x8, v);
       }
-      const int r0 = 16 * mt + 4 * kgrp;  // token offset inside the block of this lane's 4 scores
-      const int s0 = j * B + r0;
-      for (int g = 0; g * 16 < pc; ++g) {
-        const int rank = g * 16 + slot;
-        const bool valid = rank < pc;
-        const int qq = valid ? sq[rank] : 0;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int t = query_pos(L, nq, i0 + qq);
+      float* dst = scores + (qrow0 + qq) * (size_t)m * B + (size_t)pos * B + 4 * kgrp;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (valid) v = *reinterpret_cast<const u32x4*>(qtile + qq * DI + 8 * kgrp + 32 * ks);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur[ks], __builtin_bit_cast(bf16x8, v), acc, 0, 0, 0);
-        }
-        if (valid) {
-          const int t = query_pos(L, nq, i0 + qq);
-          float* dst = scores + (qrow0 + qq) * (size_t)m * B + (size_t)sp[rank] * B + r0;
-          if (s0 + 3 <= t) {
-            *reinterpret_cast<f32x4*>(dst) = acc;
-          } else {
+      for (int mt = 0; mt < kMaxMT; ++mt) {
+        if (mt < n_mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (s0 + e <= t) dst[e] = acc[e];
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][ks]), bq[ks], acc, 0, 0, 0);
+          // acc[e]: token j*B + 16 mt + 4 kgrp + e of query qq
+          if (valid) {
+            const int s0 = j * B + 16 * mt + 4 * kgrp;
+            if (s0 + 3 <= t) {
+              *reinterpret_cast<f32x4*>(dst + 16 * mt) = acc;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (s0 + e <= t) dst[16 * mt + e] = acc[e];
+            }
           }
         }
       }

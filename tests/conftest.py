@@ -10,3 +10,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+
+
+def pytest_collection_modifyitems(config, items):
+    # Initialise the GPU runtime once, before any test generates inputs (with
+    # worker threads), when GPU tests are about to run.
+    if any(item.get_closest_marker("gpu") for item in items):
+        import torch
+        if torch.cuda.is_available():
+            torch.zeros(1, device="cuda")
+            torch.cuda.synchronize()
