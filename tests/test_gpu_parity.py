@@ -87,6 +87,56 @@ def test_empty_calls_write_nothing():
     assert torch.all(out["blk"] == -7) and torch.all(out["tok"] == -7)
 
 
+def test_incremental_summaries():
+    # hsa_forward with summary_start_block > 0 recomputes only the newest
+    # blocks: with the earlier summaries already in S the results equal a
+    # full forward (the decode / chunked-prefill state update)
+    w = small("incremental", batch=2, seq_len=3000, n_q=200, d_index=128, block=32, top_m=6,
+              top_k=150, n_heads_q=4, n_heads_kv=1, n_landmarks=2)
+    inp = datagen.make_inputs(w, q_range=4, centre_range=2, noise_range=2)
+    dev = pipeline.to_device(inp)
+    full = pipeline.to_host(pipeline.run_forward(w, dev))
+    start = (w.seq_len - w.n_q) // w.block
+    out = pipeline.alloc_outputs(w)
+    shape = _lib.shape_of(w)
+    _lib.hsa_block_summary(shape, dev["kI"], dev["W"], 0, out["S"])
+    out["S"][:, start:] = 0  # stale state for the blocks the new queries touch
+    inc = pipeline.to_host(pipeline.run_forward(w, dev, out, summary_start_block=start))
+    for key in ("S", "blk", "tok", "O", "lse"):
+        assert np.array_equal(inc[key], full[key], equal_nan=True), key
+
+
+def test_attention_lists_with_holes():
+    # hsa_sparse_attn skips -1 entries and entries >= seq_len anywhere in a
+    # list (the lists the indexer writes only pad at the end)
+    rng = np.random.default_rng(11)
+    b, L, nq, Hq, Hkv, k = 2, 700, 9, 8, 2, 512  # 16 tiles: the split + merge path
+    w = small("holes", batch=b, seq_len=L, n_q=nq, d_index=64, block=16, top_m=4, top_k=k,
+              n_heads_q=Hq, n_heads_kv=Hkv)
+    inp = datagen.make_inputs(w)
+    tok = np.full((b, nq, k), -1, np.int32)
+    for bb in range(b):
+        for i in range(nq):
+            n = int(rng.integers(1, k + 1))
+            sel = np.sort(rng.choice(L, size=n, replace=False)).astype(np.int32)
+            pos = np.sort(rng.choice(k, size=n, replace=False))
+            tok[bb, i, pos] = sel
+            junk = rng.random(k) < 0.05
+            tok[bb, i, junk & (tok[bb, i] < 0)] = L + 5  # out of range: skipped
+    dev = pipeline.to_device(inp)
+    shape = _lib.shape_of(w)
+    O = torch.empty((b, nq, Hq, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((b, nq, Hq), dtype=torch.float32, device="cuda")
+    _lib.hsa_sparse_attn(shape, dev["Q"], dev["K"], dev["V"], torch.from_numpy(tok).cuda(), O, lse)
+    O, lse = O.cpu().numpy(), lse.cpu().numpy()
+    for bb in range(b):
+        for i in range(nq):
+            valid = tok[bb, i][(tok[bb, i] >= 0) & (tok[bb, i] < L)]
+            ro, rl = orc.sparse_attention(inp["Q"][bb, i], inp["K"][bb], inp["V"][bb], valid, w.scale)
+            assert np.abs(O[bb, i] - ro).max() <= 2e-3
+            assert np.abs(lse[bb, i] - rl).max() <= 2e-3
+
+
 def test_repeat_runs_are_bitwise_identical():
     w = WORKLOADS["tiny_prefill_4k"]
     dev = pipeline.to_device(datagen.make_inputs(w))
