@@ -172,7 +172,8 @@ def hsa_forward(shape, qI, kI, W, summary_start_block, S, Q, K, V, blk_out, tok_
 
 
 def hsa_sparse_set_stage_events(events):
-    """events: 5 raw hipEvent_t handles (ints), or None to stop recording."""
+    """events: 5 raw hipEvent_t handles (ints; None entries are not recorded),
+    or None to stop recording."""
     lib = load()
     if events is None:
         _check(lib.hsa_sparse_set_stage_events(None, 0), "hsa_sparse_set_stage_events")

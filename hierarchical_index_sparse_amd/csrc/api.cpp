@@ -131,10 +131,12 @@ hsa_sparse_status_t hsa_sparse_set_stage_events(hsa_sparse_event_t const* events
     return HSA_SPARSE_OK;
   }
   if (n_events != 5 || !events) return fail(HSA_SPARSE_INVALID_ARG, "need 5 events (or 0 and NULL)");
+  bool any = false;
   for (int i = 0; i < 5; ++i) {
-    if (!events[i]) return fail(HSA_SPARSE_INVALID_ARG, "event %d is NULL", i);
     g_stage_events[i] = events[i];
+    any = any || events[i];
   }
+  if (!any) return fail(HSA_SPARSE_INVALID_ARG, "all 5 events are NULL");
   g_record_stages = true;
   return HSA_SPARSE_OK;
 }
@@ -235,15 +237,21 @@ hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape, const uint16_t*
   void* stage = ws + f.stage_off;
   const bool rec = g_record_stages;
 #define HSA_MARK(i)                                                              \
-  if (rec) {                                                                     \
+  if (rec && g_stage_events[i]) {                                               \
     hipError_t er = hipEventRecord((hipEvent_t)g_stage_events[i], stream);       \
     if (er != hipSuccess) return hip_fail(er, "hsa_forward (stage event)");      \
   }
   HSA_MARK(0)
-  hipError_t e = hsa::launch_block_summary(d, kI, landmark_W, summary_start_block, S, stream);
+  // Decode: the only re-summarised block is each query's own, always-kept
+  // block, whose score is never read, so its summary is folded into the
+  // block-score launch instead of preceding it.
+  const bool fold = hsa::block_topm_can_fold(d, summary_start_block);
+  hipError_t e = hipSuccess;
+  if (!fold) e = hsa::launch_block_summary(d, kI, landmark_W, summary_start_block, S, stream);
   if (e != hipSuccess) return hip_fail(e, "hsa_forward (block summary)");
   HSA_MARK(1)
-  e = hsa::launch_block_topm(d, qI, S, blk, stage, stream);
+  const hsa::SummaryFold sf{kI, landmark_W, S, summary_start_block};
+  e = hsa::launch_block_topm(d, qI, S, blk, stage, stream, fold ? &sf : nullptr);
   if (e != hipSuccess) return hip_fail(e, "hsa_forward (block top-m)");
   HSA_MARK(2)
   e = hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);

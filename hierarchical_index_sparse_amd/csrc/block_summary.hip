@@ -13,6 +13,7 @@
 // HBM-bound: B * d_index * 2 bytes read per nL * d_index * 2 bytes written.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "summary.hpp"
 
 namespace hsa {
 
@@ -20,54 +21,8 @@ template <int DI, int NL>
 __global__ __launch_bounds__(256) void k_block_summary(const uint16_t* __restrict__ kI,
                                                        const int8_t* __restrict__ W, uint16_t* __restrict__ S,
                                                        int L, int B, int nb, int start_block) {
-  constexpr int LPR = DI / 8;       // lanes per row
-  constexpr int RPI = 256 / LPR;    // rows per iteration of the workgroup
-  __shared__ float red[NL][RPI][DI];
-
-  const int j = start_block + blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int col8 = tid % LPR;
-  const int r0 = tid / LPR;
-
-  float acc[NL][8];
-#pragma unroll
-  for (int l = 0; l < NL; ++l)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
-
-  const size_t seq_base = (size_t)b * L;
-  for (int r = r0; r < B; r += RPI) {
-    const int s = j * B + r;
-    if (s >= L) break;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(kI + (seq_base + s) * DI + col8 * 8);
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_lo(v[e]);
-      x[2 * e + 1] = bf16_hi(v[e]);
-    }
-#pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      const float w = W ? (float)W[l * B + r] : 1.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[l][e] += w * x[e];
-    }
-  }
-#pragma unroll
-  for (int l = 0; l < NL; ++l)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[l][r0][col8 * 8 + e] = acc[l][e];
-  __syncthreads();
-
-  const float inv_b = 1.f / (float)B;  // exact: B is a power of two
-  for (int o = tid; o < NL * DI; o += 256) {
-    const int l = o / DI, d = o % DI;
-    float total = 0.f;
-#pragma unroll 4
-    for (int r = 0; r < RPI; ++r) total += red[l][r][d];
-    S[(((size_t)b * nb + j) * NL + l) * DI + d] = (uint16_t)f32_to_bf16_rne(total * inv_b);
-  }
+  __shared__ float red[NL][256 / (DI / 8)][DI];
+  summarise_block<DI, NL>(kI, W, S, L, B, nb, start_block + blockIdx.x, blockIdx.y, red);
 }
 
 template <int DI>

@@ -17,25 +17,44 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
+#include "summary.hpp"
 
 namespace hsa {
 
 constexpr int kScoreBlocksPerWG = 64;
 
+// GEMV block scores for few queries per sequence (decode).  Each workgroup
+// takes 64 blocks of one query; its 4 waves issue every summary-row load
+// first (16-byte loads, d_index/8 lanes per row) and then reduce.  With
+// blockIdx.z == 1 the workgroup instead summarises block sum_start +
+// blockIdx.x of sequence blockIdx.y: the host folds the newest blocks'
+// summaries in here only when no query scores them (they are its own,
+// always-kept block), which saves a dependent launch per decode step.
 template <int DI, int NL>
 __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict__ qI,
                                                       const uint16_t* __restrict__ S, float* __restrict__ scores,
-                                                      int L, int nq, int B, int nb, int m) {
+                                                      int L, int nq, int B, int nb, int m,
+                                                      const uint16_t* __restrict__ kI, const int8_t* __restrict__ W,
+                                                      uint16_t* __restrict__ S_out, int sum_start, int batch) {
   constexpr int LPR = DI / 8;     // lanes per summary row
   constexpr int RPL = kWave / LPR;  // rows per wave load
+  constexpr int ITER = kScoreBlocksPerWG * NL / (4 * RPL);
   static_assert(RPL % NL == 0, "a block's landmarks must share one wave load");
 
+  if (blockIdx.z == 1) {
+    __shared__ float red[NL][256 / LPR][DI];
+    const int jb = sum_start + (int)blockIdx.x;
+    if (jb >= nb || (int)blockIdx.y >= batch) return;  // uniform
+    summarise_block<DI, NL>(kI, W, S_out, L, B, nb, jb, blockIdx.y, red);
+    return;
+  }
   const int q = blockIdx.y;  // b * nq + i
+  if (q >= batch * nq) return;
   const int b = q / nq, i = q % nq;
   const int t = query_pos(L, nq, i);
   const int c = t / B;
   if (c + 1 <= m) return;
-  const int j0 = max(1, blockIdx.x * kScoreBlocksPerWG);
+  const int j0 = max(1, (int)blockIdx.x * kScoreBlocksPerWG);
   const int j1 = min(c, (int)(blockIdx.x + 1) * kScoreBlocksPerWG);  // exclusive
   if (j0 >= j1) return;
 
@@ -52,17 +71,22 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
     }
   }
   const uint16_t* Sb = S + (size_t)b * nb * NL * DI;
+  const int row_begin = j0 * NL + wave * RPL + lane / LPR;
   const int row_end = j1 * NL;
-  for (int row0 = j0 * NL + wave * RPL; row0 < row_end; row0 += 4 * RPL) {
-    const int row = row0 + lane / LPR;
-    float dot = 0.f;
-    if (row < row_end) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + col8 * 8);
+  u32x4 v[ITER];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dot += qv[2 * e] * bf16_lo(v[e]);
-        dot += qv[2 * e + 1] * bf16_hi(v[e]);
-      }
+  for (int it = 0; it < ITER; ++it) {
+    const int row = min(row_begin + it * 4 * RPL, row_end - 1);
+    v[it] = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + col8 * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int row = row_begin + it * 4 * RPL;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot += qv[2 * e] * bf16_lo(v[it][e]);
+      dot += qv[2 * e + 1] * bf16_hi(v[it][e]);
     }
 #pragma unroll
     for (int o = 1; o < LPR; o <<= 1) dot += shfl_xor(dot, o);
@@ -72,8 +96,6 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
   }
 }
 
-// NW == 1: each of the 4 waves of a workgroup selects for its own query;
-// NW > 1: the NW waves of a workgroup select for one query together.
 // MFMA block scores for many queries: one workgroup scores 64 consecutive
 // queries of one sequence against 128 summary rows (128 / NL blocks); wave w
 // takes rows 32w .. 32w+31 for all 64 queries.  C = qI S^T with
@@ -213,8 +235,15 @@ static int pick_r(int n, int nw) {
   return r;
 }
 
+bool block_topm_can_fold(const Dims& s, int start_block) {
+  const int c_max = (s.L - 1) / s.B;
+  // the GEMV kernel runs (few queries, some query scores blocks) and no
+  // query scores a block >= start_block (the highest scored is c_max - 1)
+  return s.nq < 64 && c_max + 1 > s.m && start_block >= c_max && start_block < s.nb;
+}
+
 hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk, void* ws,
-                             hipStream_t st) {
+                             hipStream_t st, const SummaryFold* fold) {
   const int nq_total = s.b * s.nq;
   if (nq_total == 0) return hipSuccess;
   float* scores = static_cast<float*>(ws);
@@ -236,16 +265,23 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (c_max + 1 > s.m) {
-    dim3 grid((c_max + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG, nq_total);
-    hipError_t e = hipSuccess;
-#define HSA_SC(DI, NL) hipLaunchKernelGGL((k_block_scores<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, s.nb, s.m)
+    const int xs = (c_max + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG;
+    const int nsum = fold ? s.nb - fold->start_block : 0;
+    dim3 grid(max(xs, nsum), max(nq_total, fold ? s.b : 0), fold ? 2 : 1);
+    const uint16_t* kI = fold ? fold->kI : nullptr;
+    const int8_t* W = fold ? fold->W : nullptr;
+    uint16_t* S_out = fold ? fold->S : nullptr;
+    const int start = fold ? fold->start_block : s.nb;
+#define HSA_SC(DI, NL)                                                                                          \
+  hipLaunchKernelGGL((k_block_scores<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, s.nb, s.m, \
+                     kI, W, S_out, start, s.b)
     if (s.dI == 64) {
       if (s.nL == 1) HSA_SC(64, 1); else if (s.nL == 2) HSA_SC(64, 2); else HSA_SC(64, 4);
     } else {
       if (s.nL == 1) HSA_SC(128, 1); else if (s.nL == 2) HSA_SC(128, 2); else HSA_SC(128, 4);
     }
 #undef HSA_SC
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // many queries: one wave per query (<= 512 candidates) or a 4-wave

@@ -20,10 +20,19 @@ struct Dims {
 hipError_t launch_block_summary(const Dims& s, const uint16_t* kI, const int8_t* W, int start_block,
                                 uint16_t* S, hipStream_t st);
 
-// step 2: scores into `scores` [b*nq, nb] fp32, then the top-m select
+// step 2: scores into `scores` [b*nq, nb] fp32, then the top-m select.
+// With `fold`, the score kernel also summarises blocks fold->start_block ..
+// nb-1 (allowed only when block_topm_can_fold says no query scores them).
+struct SummaryFold {
+  const uint16_t* kI;
+  const int8_t* W;
+  uint16_t* S;
+  int start_block;
+};
 size_t block_topm_ws_bytes(const Dims& s);
+bool block_topm_can_fold(const Dims& s, int start_block);
 hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk,
-                             void* ws, hipStream_t st);
+                             void* ws, hipStream_t st, const SummaryFold* fold = nullptr);
 
 // step 3: scores into [b*nq, m*B] fp32, then the top-k select
 size_t token_topk_ws_bytes(const Dims& s);

@@ -1,0 +1,67 @@
+// Summary of one key block (step 1), shared by the summary kernel and the
+// decode block-score kernel that folds the newest block's summary in.
+//
+// HISA page (two-step method, step one): one summary vector per block,
+// read here as the block mean; HiLS page (section 2.1): landmark l =
+// sum_r W[l, r] kI[r] / B.  The block's B rows (d_index bf16 each) are read
+// once with 16-byte loads, d_index/8 lanes per row; per-thread fp32 partial
+// sums meet in LDS, are scaled by the exact power of two 1/B and rounded
+// once to bf16 (nearest even).  Rows beyond L count as zero.
+#pragma once
+
+#include "common.hpp"
+
+namespace hsa {
+
+// Called by all 256 threads of a workgroup; red is the workgroup's LDS.
+template <int DI, int NL>
+__device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI, const int8_t* __restrict__ W,
+                                                uint16_t* __restrict__ S, int L, int B, int nb, int j, int b,
+                                                float (&red)[NL][256 / (DI / 8)][DI]) {
+  constexpr int LPR = DI / 8;     // lanes per row
+  constexpr int RPI = 256 / LPR;  // rows per iteration of the workgroup
+  const int tid = threadIdx.x;
+  const int col8 = tid % LPR;
+  const int r0 = tid / LPR;
+
+  float acc[NL][8];
+#pragma unroll
+  for (int l = 0; l < NL; ++l)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
+
+  const size_t seq_base = (size_t)b * L;
+  for (int r = r0; r < B; r += RPI) {
+    const int s = j * B + r;
+    if (s >= L) break;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(kI + (seq_base + s) * DI + col8 * 8);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(v[e]);
+      x[2 * e + 1] = bf16_hi(v[e]);
+    }
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      const float w = W ? (float)W[l * B + r] : 1.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[l][e] += w * x[e];
+    }
+  }
+#pragma unroll
+  for (int l = 0; l < NL; ++l)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[l][r0][col8 * 8 + e] = acc[l][e];
+  __syncthreads();
+
+  const float inv_b = 1.f / (float)B;  // exact: B is a power of two
+  for (int o = tid; o < NL * DI; o += 256) {
+    const int l = o / DI, d = o % DI;
+    float total = 0.f;
+#pragma unroll 4
+    for (int r = 0; r < RPI; ++r) total += red[l][r][d];
+    S[(((size_t)b * nb + j) * NL + l) * DI + d] = (uint16_t)f32_to_bf16_rne(total * inv_b);
+  }
+}
+
+}  // namespace hsa

@@ -38,6 +38,7 @@ __global__ __launch_bounds__(256) void k_token_scores(const uint16_t* __restrict
                                                       int L, int nq, int B, int m, int k) {
   constexpr int LPR = DI / 8;
   constexpr int RPI = 256 / LPR;  // rows per workgroup iteration
+  constexpr int NIT = 128 / RPI;  // iterations for the largest block (B = 128)
   const int p = blockIdx.x;
   const int q = blockIdx.y;
   const int b = q / nq, i = q % nq;
@@ -61,20 +62,29 @@ __global__ __launch_bounds__(256) void k_token_scores(const uint16_t* __restrict
   const uint16_t* kb = kI + ((size_t)b * L + (size_t)j * B) * DI;
   float* out = scores + (size_t)q * m * B + (size_t)p * B;
   const int rows = min(B, t - j * B + 1);
-  for (int r0 = 0; r0 < B; r0 += RPI) {
-    const int r = r0 + tid / LPR;
-    float dot = 0.f;
-    if (r < rows) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(kb + (size_t)r * DI + col8 * 8);
+  // every row load in flight at once, then the dot products
+  u32x4 v[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if (it * RPI < B) {
+      const int r = min(it * RPI + tid / LPR, rows - 1);
+      v[it] = *reinterpret_cast<const u32x4*>(kb + (size_t)r * DI + col8 * 8);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if (it * RPI < B) {
+      const int r = it * RPI + tid / LPR;
+      float dot = 0.f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dot += qv[2 * e] * bf16_lo(v[e]);
-        dot += qv[2 * e + 1] * bf16_hi(v[e]);
+        dot += qv[2 * e] * bf16_lo(v[it][e]);
+        dot += qv[2 * e + 1] * bf16_hi(v[it][e]);
       }
-    }
 #pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) dot += shfl_xor(dot, o);
-    if (r < rows && col8 == 0) out[r] = dot;
+      for (int o = 1; o < LPR; o <<= 1) dot += shfl_xor(dot, o);
+      if (r < rows && col8 == 0) out[r] = dot;
+    }
   }
 }
 

@@ -189,9 +189,12 @@ hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape,
 /*
  * Per-step timing of hsa_forward (profiling aid).  After this call, every
  * hsa_forward made by the calling thread records events[0] on its stream
- * before step 1 and events[s] after step s (s = 1..4).  The events are the
- * caller's hipEvent_t handles and must stay valid while such calls are
- * made.  n_events must be 5, or 0 with events == NULL to stop recording.
+ * before step 1 and events[s] after step s (s = 1..4); a NULL entry is not
+ * recorded.  Each recorded event costs the stream a few microseconds, which
+ * matters for short (decode) steps, so record only the boundaries needed.
+ * The events are the caller's hipEvent_t handles and must stay valid while
+ * such calls are made.  n_events must be 5 with at least one non-NULL
+ * entry, or 0 with events == NULL to stop recording.
  */
 typedef struct ihipEvent_t* hsa_sparse_event_t;
 hsa_sparse_status_t hsa_sparse_set_stage_events(hsa_sparse_event_t const* events, int n_events);

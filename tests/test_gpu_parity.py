@@ -106,6 +106,39 @@ def test_incremental_summaries():
         assert np.array_equal(inc[key], full[key], equal_nan=True), key
 
 
+DECODE_FOLD_CASES = [
+    # (seq_len, n_q, block, d_index, n_landmarks): the first three put every
+    # query in the last block, so the newest block's summary is folded into
+    # the block-score launch; the last spans two blocks (separate launch)
+    (5000, 1, 32, 64, 1),
+    (5000, 5, 32, 128, 4),
+    (5024, 1, 32, 128, 2),
+    (5000, 40, 32, 64, 2),
+]
+
+
+@pytest.mark.parametrize("L,nq,B,dI,nL", DECODE_FOLD_CASES)
+def test_incremental_decode_summaries(L, nq, B, dI, nL):
+    # decode-shaped calls with only the newest blocks re-summarised: the same
+    # bits as a full forward, and every query equal to the oracle
+    w = small("decode_inc", batch=3, seq_len=L, n_q=nq, d_index=dI, block=B, top_m=6, top_k=150,
+              n_heads_q=8, n_heads_kv=2, n_landmarks=nL)
+    inp = datagen.make_inputs(w, q_range=3, centre_range=2, noise_range=2)
+    dev = pipeline.to_device(inp)
+    full = pipeline.to_host(pipeline.run_forward(w, dev))
+    start = (L - nq) // B
+    out = pipeline.alloc_outputs(w)
+    _lib.hsa_block_summary(_lib.shape_of(w), dev["kI"], dev.get("W"), 0, out["S"])
+    out["S"][:, start:] = 0
+    inc = pipeline.to_host(pipeline.run_forward(w, dev, out, summary_start_block=start))
+    for key in ("S", "blk", "tok", "O", "lse"):
+        assert np.array_equal(inc[key], full[key], equal_nan=True), key
+    S = oracle_summaries(inp, w)
+    check_summaries(inc["S"], S)
+    check_list_invariants(inc, w)
+    check_queries(inc, inp, w, S, [(b, i) for b in range(w.batch) for i in range(nq)])
+
+
 def test_attention_lists_with_holes():
     # hsa_sparse_attn skips -1 entries and entries >= seq_len anywhere in a
     # list (the lists the indexer writes only pad at the end)
