@@ -1,0 +1,63 @@
+"""Run the GPU parity tests of test_gpu_parity.py without pytest.
+
+    python3 tests/run_gpu_parity.py [name-substring ...]
+
+Calls the same test functions (parametrised cases expanded) in one plain
+Python process, prints PASS/FAIL per case as it ends, stops at the first
+failure and exits non-zero on it.  Full-size workloads run last.
+"""
+import inspect
+import os
+import sys
+import time
+import traceback
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.dirname(HERE))
+sys.path.insert(0, HERE)
+
+import torch  # noqa: E402
+
+torch.zeros(1, device="cuda")
+torch.cuda.synchronize()
+
+import test_gpu_parity as T  # noqa: E402
+
+
+def cases():
+    out = []
+    for name, fn in inspect.getmembers(T, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not marks:
+            out.append((name, fn))
+            continue
+        names, vals = marks[0].args[0], marks[0].args[1]
+        names = [n.strip() for n in names.split(",")] if isinstance(names, str) else list(names)
+        for v in vals:
+            v = v if len(names) > 1 else (v,)
+            kw = dict(zip(names, v))
+            label = getattr(v[0], "name", None) or "-".join(str(x) for x in v)
+            out.append((f"{name}[{label}]", lambda fn=fn, kw=kw: fn(**kw)))
+    out.sort(key=lambda c: c[0].startswith("test_full_size"))
+    return out
+
+
+def main(only):
+    for name, fn in cases():
+        if only and not any(o in name for o in only):
+            continue
+        print(f"RUN  {name}", flush=True)
+        t = time.time()
+        try:
+            fn()
+        except Exception:
+            print(f"FAIL {name}\n{traceback.format_exc()}", flush=True)
+            return 1
+        print(f"PASS {name} ({time.time() - t:.1f}s)", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
