@@ -68,6 +68,9 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
     if (s->n_heads_q / s->n_heads_kv > 16)
       return fail(HSA_SPARSE_UNSUPPORTED, "at most 16 query heads per kv head");
     if (!(s->scale == s->scale)) return fail(HSA_SPARSE_INVALID_ARG, "scale is NaN");
+    // a kv row's byte offset inside its sequence is a 31-bit integer
+    if ((long long)s->seq_len * s->n_heads_kv * 256 > 0x7FFFFFFFll)
+      return fail(HSA_SPARSE_UNSUPPORTED, "seq_len * n_heads_kv * 256 bytes exceeds 2^31");
   }
   const long long nq_total = (long long)s->batch * s->n_q;
   if (nq_total > (1ll << 30)) return fail(HSA_SPARSE_UNSUPPORTED, "batch * n_q too large");

@@ -9,11 +9,13 @@
 // workgroup takes part.
 //
 // 1. Threshold T = the want-th largest key:
-//    a. (NW * R >= 8) the scores are dropped into 256 linear bins between
-//       their minimum and maximum (bin = floor((x - min) * 256 / (max - min)), a
-//       non-decreasing function of x, so a key in a higher bin is strictly
-//       larger than every key in a lower one and equal keys share a bin);
-//       a suffix scan of the LDS histogram finds the bin holding T and the
+//    a. (NW * R >= 8) the scores are dropped into 255 linear bins between
+//       their minimum and maximum (bin = min(floor((x - min) * 255 / (max -
+//       min)), 254), a non-decreasing function of x, so a key in a higher bin
+//       is strictly larger than every key in a lower one and equal keys share
+//       a bin; empty slots go to bin 255, which is never scanned).  Each
+//       key's bin is computed once and kept as one byte in registers.  A
+//       suffix scan of the LDS histogram finds the bin holding T and the
 //       count of keys above it; that bin's keys are compacted into LDS and
 //       one wave finds T by a bitwise binary search over the bits below the
 //       candidates' common prefix (largest x with count(key >= x) >= need,
@@ -60,8 +62,11 @@ __device__ __forceinline__ int sel_wave() {
   else return threadIdx.x / kWave;
 }
 
+// Inverse of score_key for non-empty keys: a set top bit marks a
+// non-negative score (flip it back), a clear one a negative score (flip all).
 __device__ __forceinline__ float key_to_score(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+  const uint32_t flip = ~(uint32_t)((int32_t)k >> 31) | 0x80000000u;
+  return __uint_as_float(k ^ flip);
 }
 
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
@@ -202,16 +207,30 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
       sel_sync<NW>();
       return full_threshold<NW, R>(key, want, sm.red);
     }
-    const float scale = (float)kBins / range;
-    auto bin_of = [&](uint32_t k) { return min((int)((key_to_score(k) - smin) * scale), kBins - 1); };
+    const float scale = (float)(kBins - 1) / range;
+    // bins of all keys, one byte each (4 per register), computed once; the
+    // histogram counts empty slots in the unscanned bin kBins - 1
+    constexpr int RP = (R + 3) / 4;
+    uint32_t binp[RP];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (key[r]) atomicAdd(&sm.hist[bin_of(key[r])], 1);
+    for (int p = 0; p < RP; ++p) binp[p] = 0u;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      // max(key, lo) keeps an empty slot's arithmetic finite; its bin is
+      // then overridden (kBins - 1 has every bit of the byte set)
+      const uint32_t kk = max(key[r], lo);
+      int bn = min((int)((key_to_score(kk) - smin) * scale), kBins - 2);
+      bn |= (int)(key[r] == 0u) * (kBins - 1);
+      binp[r / 4] |= (uint32_t)bn << (8 * (r % 4));
+      atomicAdd(&sm.hist[bn], 1);
+    }
+    auto bin_at = [&](int r) { return (int)((binp[r / 4] >> (8 * (r % 4))) & 0xFFu); };
     sel_sync<NW>();
     if (wave == 0) {
-      // suffix sums over bins: lane l holds bins 4l .. 4l+3
+      // suffix sums over bins: lane l holds bins 4l .. 4l+3 (the last is
+      // the empty-slot bin, left out)
       const int c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
-                c3 = sm.hist[4 * lane + 3];
+                c3 = lane == kWave - 1 ? 0 : sm.hist[4 * lane + 3];
       const int mine = c0 + c1 + c2 + c3;
       int incl = mine;  // sum over lanes >= l
 #pragma unroll
@@ -240,7 +259,7 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
     // compact the target bin's keys (any order)
     int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) cnt += (key[r] != 0u && bin_of(key[r]) == tb);
+    for (int r = 0; r < R; ++r) cnt += bin_at(r) == tb;
     int wtot;
     int pos = wave_excl_scan(cnt, wtot);
     int base = 0;
@@ -248,7 +267,7 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
     pos += __shfl(base, 0, kWave);
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (key[r] != 0u && bin_of(key[r]) == tb) sm.cand[pos++] = key[r];
+      if (bin_at(r) == tb) sm.cand[pos++] = key[r];
     sel_sync<NW>();
     if (wave == 0) {
       const int n = sm.hist[tb];
@@ -264,7 +283,9 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
 }
 
 // Requires: 1 <= want < number of non-empty keys.  Every thread of the
-// group must call it (it synchronises the group).
+// group must call it (it synchronises the group).  emit(pos, idx, take) is
+// called for every key of the thread in index order; `take` says whether
+// the key is kept, and then pos (0 .. want-1) is its output slot.
 template <int NW, int R, typename Emit>
 __device__ __forceinline__ void select_top(const uint32_t (&key)[R], int want, SelectSmem<NW>& sm, Emit&& emit) {
   const int wave = sel_wave<NW>();
@@ -305,10 +326,11 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[R], int want, S
   const int idx0 = (wave * kWave + lane) * R;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const bool is_eq = key[r] == T;
-    const bool take = key[r] > T || (is_eq && ties > 0);
-    ties -= (is_eq && ties > 0);
-    if (take) emit(pos++, idx0 + r);
+    const int is_eq = key[r] == T;
+    const int tk = (int)(key[r] > T) | (is_eq & (int)(ties > 0));
+    ties -= is_eq & tk;
+    emit(pos, idx0 + r, tk != 0);
+    pos += tk;
   }
   sel_sync<NW>();  // LDS may be reused by the caller
 }

@@ -31,8 +31,31 @@ namespace hsa {
 constexpr int kPartStride = 130;  // 128 dims + running max + running sum
 constexpr int kRowBytes = 272;    // staged kv row: 256 bytes + 16 bytes of padding
 constexpr int kStageBytes = 32 * kRowBytes;
+// The running max per head is only moved when a tile's max exceeds it by more
+// than this (log2 units), so O is rescaled on few tiles; P = exp2(s - max)
+// then stays below 2^kLazyMax.
+constexpr float kLazyMax = 8.f;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Reductions over the lanes l, l^16, l^32, l^48 (the four lane rows that
+// hold one head's tokens), with gfx950's row-swap permutes.
+__device__ __forceinline__ float max_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -69,32 +92,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   const int start = split * chunk;
   const int end = min(k, start + chunk);
   const int32_t* tl = tok + (size_t)q * k;
-  const size_t kv_row0 = (size_t)b * L;
-  const uint16_t* Kg = K + (size_t)g * 128;
-  const uint16_t* Vg = V + (size_t)g * 128;
-  const size_t row_stride = (size_t)Hkv * 128;
+  // this (sequence, kv head)'s rows; a row's byte offset fits 31 bits
+  // (seq_len * n_heads_kv * 256 < 2^31, checked at the API)
+  const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + ((size_t)b * L * Hkv + g) * 128);
+  const unsigned char* Vb = reinterpret_cast<const unsigned char*>(V + ((size_t)b * L * Hkv + g) * 128);
+  const int row_bytes = Hkv * 256;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // index of list entry `pos` if it is a valid token of this sequence, else -1
+  // byte offset of list entry `pos`'s row if it is a valid token of this
+  // sequence, else -1
   auto entry = [&](int pos) {
-    int v = pos < end ? tl[pos] : -1;
-    return (v >= L) ? -1 : v;
+    const int v = pos < end ? tl[pos] : -1;
+    return (v >= 0 && v < L) ? (int)__umul24((unsigned)v, (unsigned)row_bytes) : -1;
   };
   // Coalesced gather of one tile's 32 K rows and 32 V rows: instruction i
   // reads rows 4i .. 4i+3, 16 lanes (16 bytes each) per 256-byte row.
   auto gload = [&](int my, u32x4 (&kr)[8], u32x4 (&vr)[8]) {
-    const int mine = my < 0 ? 0 : my;
-    const int c = lane & 15;
+    const int mine = max(my, 0);  // an invalid entry loads row 0 (masked later)
+    const unsigned col = 16u * (unsigned)(lane & 15);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int tr = __shfl(mine, 4 * i + (lane >> 4), kWave);
-      const size_t off = (kv_row0 + tr) * row_stride + 8 * c;
-      kr[i] = *reinterpret_cast<const u32x4*>(Kg + off);
-      vr[i] = *reinterpret_cast<const u32x4*>(Vg + off);
+      const unsigned off = (unsigned)__shfl(mine, 4 * i + (lane >> 4), kWave) + col;
+      kr[i] = *reinterpret_cast<const u32x4*>(Kb + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(Vb + off);
     }
   };
   // this wave's staging buffers: 32 rows of 272 bytes (256 + 16 pad, which
@@ -150,55 +174,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       float sv[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sv[e] = ((vmask >> (4 * gq + e)) & 1u) ? s0[e] * scale_log2 : -INFINITY;
-        sv[4 + e] = ((vmask >> (16 + 4 * gq + e)) & 1u) ? s1[e] * scale_log2 : -INFINITY;
+        sv[e] = s0[e] * scale_log2;
+        sv[4 + e] = s1[e] * scale_log2;
       }
-      float mx = sv[0];
+      if (vmask != 0xFFFFFFFFu) {  // holes or the list's tail
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, shfl_xor(mx, 16));
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
+        for (int e = 0; e < 4; ++e) {
+          if (!((vmask >> (4 * gq + e)) & 1u)) sv[e] = -INFINITY;
+          if (!((vmask >> (16 + 4 * gq + e)) & 1u)) sv[4 + e] = -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mx = max_x32(max_x16(mx));
+      if (ballot(mx > m_run + kLazyMax)) {
+        // move the running max of every head that grew, rescale O and l
+        const float m_new = mx > m_run + kLazyMax ? mx : m_run;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const float a = __shfl(alpha, 4 * gq + i2, kWave);  // rows of O are heads 4gq+i2
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) o[nt][i2] *= a;
+        }
+      }
+      // P = exp2(s - m_run) <= 2^kLazyMax, split into bf16 hi (truncated)
+      // + lo (the exact remainder, truncated): relative error <= 2^-16
       float psum = 0.f;
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float pa = exp2f(sv[e] - m_new);
-        const float pb = exp2f(sv[e + 1] - m_new);
+        const float pa = __builtin_amdgcn_exp2f(sv[e] - m_run);
+        const float pb = __builtin_amdgcn_exp2f(sv[e + 1] - m_run);
         psum += pa + pb;
-        const uint32_t ha = f32_to_bf16_rne(pa), hb = f32_to_bf16_rne(pb);
-        const uint32_t la = f32_to_bf16_rne(pa - __uint_as_float(ha << 16));
-        const uint32_t lb = f32_to_bf16_rne(pb - __uint_as_float(hb << 16));
-        ph[e / 2] = ha | (hb << 16);
-        pl[e / 2] = la | (lb << 16);
+        const float ra = pa - __uint_as_float(__float_as_uint(pa) & 0xFFFF0000u);
+        const float rb = pb - __uint_as_float(__float_as_uint(pb) & 0xFFFF0000u);
+        ph[e / 2] = __builtin_amdgcn_perm(__float_as_uint(pb), __float_as_uint(pa), 0x07060302u);
+        pl[e / 2] = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run += psum;
       const bf16x8 p_hi = as_bf16x8(u32x4{ph[0], ph[1], ph[2], ph[3]});
       const bf16x8 p_lo = as_bf16x8(u32x4{pl[0], pl[1], pl[2], pl[3]});
 
-      // ---- rescale O (rows = heads 4gq+i) and accumulate P V; output
-      // tile c holds dims 8 jl + c, so its B operand is element c of the
-      // lane's 8 V chunks, packed two tokens per register
-      float a_i[4];
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) a_i[i2] = __shfl(alpha, 4 * gq + i2, kWave);
+      // ---- O += P V; output tile c holds dims 8 jl + c, so its B operand is
+      // element c of the lane's 8 V chunks, packed two tokens per register
 #pragma unroll
       for (int pr = 0; pr < 4; ++pr) {
         u32x4 ev, od;
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const uint32_t x0 = w[2 * e2][pr], x1 = w[2 * e2 + 1][pr];
-          ev[e2] = (x0 & 0xFFFFu) | (x1 << 16);
-          od[e2] = (x0 >> 16) | (x1 & 0xFFFF0000u);
+          ev[e2] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+          od[e2] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          f32x4 acc = o[2 * pr + hh];
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) acc[i2] *= a_i[i2];
           const bf16x8 vb = as_bf16x8(hh ? od : ev);
+          f32x4 acc = o[2 * pr + hh];
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_hi, vb, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(p_lo, vb, acc, 0, 0, 0);
           o[2 * pr + hh] = acc;
@@ -213,8 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     my_next = my_next2;
   }
 
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  l_run = sum_x32(sum_x16(l_run));
   // outputs: lane holds heads 4gq+i, dims 8 jl + c (c = output tile)
 #pragma unroll
   for (int i2 = 0; i2 < 4; ++i2) {

@@ -23,7 +23,6 @@
 namespace hsa {
 
 // Largest m with m * B <= 32768 candidates at the smallest block size.
-constexpr int kMaxSelBlocks = 32768 / 8;
 
 __device__ __forceinline__ void candidate_count(int t, int B, int m, int& c, int& n_sel, int& n_valid) {
   c = t / B;
@@ -342,12 +341,26 @@ __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_e
   }
 }
 
-template <int NW, int R>
+// Dynamic LDS of the select: the query's block list (m entries, padded to a
+// multiple of 4) and, when k <= kStageMax (STAGED), the output list plus one
+// dummy slot per lane, so that the list leaves in coalesced 16-byte stores
+// instead of one 4-byte store per kept token and emission needs no branch.
+constexpr int kStageMax = 8192;
+static inline size_t tsel_lds_bytes(int m, int k) {
+  return sizeof(int) * ((size_t)((m + 3) & ~3) + (k <= kStageMax ? (size_t)k + kWave : 0));
+}
+
+// ONEBLK: R <= B (both powers of two), so a thread's R slots lie in one
+// kept block and its tokens are one base plus the slot offset.
+template <int NW, int R, bool STAGED, bool ONEBLK>
 __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ blk, int32_t* __restrict__ tok,
                                                           int L, int nq, int B, int log2B, int m, int k) {
+  constexpr int NT = NW * 64;
   __shared__ SelectSmem<NW> lds;
-  __shared__ int bl[kMaxSelBlocks];
+  extern __shared__ int dyn_lds[];
+  int* bl = dyn_lds;
+  int* stage = dyn_lds + ((m + 3) & ~3);
   const int q = blockIdx.x;
   const int i = q % nq;
   const int t = query_pos(L, nq, i);
@@ -356,12 +369,11 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   int32_t* out = tok + (size_t)q * k;
   if (n_valid <= k) {
     const int32_t* blq = blk + (size_t)q * m;
-    for (int slot = threadIdx.x; slot < k; slot += NW * 64)
+    for (int slot = threadIdx.x; slot < k; slot += NT)
       out[slot] = slot < n_valid ? blq[slot / B] * B + slot % B : -1;
     return;
   }
-  // scoring path: m * B <= 32768 (checked at the API), so n_sel <= kMaxSelBlocks
-  for (int p = threadIdx.x; p < n_sel; p += NW * 64) bl[p] = blk[(size_t)q * m + p];
+  for (int p = threadIdx.x; p < n_sel; p += NT) bl[p] = blk[(size_t)q * m + p];
   __syncthreads();
   const float* sc = scores + (size_t)q * m * B;  // 32-byte aligned: m * B is a multiple of 8
   const int idx0 = threadIdx.x * R;
@@ -390,7 +402,22 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
     }
   }
   const int bmask = B - 1;
-  select_top<NW, R>(key, k, lds, [&](int pos, int idx) { out[pos] = (bl[idx >> log2B] << log2B) | (idx & bmask); });
+  const int tbase = ONEBLK ? (bl[min(idx0 >> log2B, n_sel - 1)] << log2B) | (idx0 & bmask) : 0;
+  const int dummy = k + lane_id();
+  select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take) {
+    const int v = ONEBLK ? tbase + (idx - idx0) : (bl[idx >> log2B] << log2B) | (idx & bmask);
+    if constexpr (STAGED) stage[take ? pos : dummy] = v;
+    else if (take) out[pos] = v;
+  });
+  if constexpr (STAGED) {
+    // select_top ends with a barrier: the staged list is complete
+    if ((k & 3) == 0) {
+      for (int p = threadIdx.x * 4; p < k; p += NT * 4)
+        *reinterpret_cast<u32x4*>(out + p) = *reinterpret_cast<const u32x4*>(stage + p);
+    } else {
+      for (int p = threadIdx.x; p < k; p += NT) out[p] = stage[p];
+    }
+  }
 }
 
 size_t token_topk_ws_bytes(const Dims& s) {
@@ -398,28 +425,58 @@ size_t token_topk_ws_bytes(const Dims& s) {
   return align_up((size_t)s.b * s.nq * s.m * s.B * sizeof(float));
 }
 
-template <int NW>
-static hipError_t launch_tsel(int R, const Dims& s, const float* sc, const int32_t* blk, int32_t* tok, hipStream_t st) {
-  dim3 grid(s.b * s.nq), block(NW * 64);
+template <int NW, int R, bool STAGED, bool ONEBLK>
+static void launch_tsel_k(const Dims& s, size_t dyn, int log2B, const float* sc, const int32_t* blk, int32_t* tok,
+                          hipStream_t st) {
+  hipLaunchKernelGGL((k_token_select<NW, R, STAGED, ONEBLK>), dim3(s.b * s.nq), dim3(NW * 64), dyn, st, sc, blk, tok,
+                     s.L, s.nq, s.B, log2B, s.m, s.k);
+}
+
+// Variants: a thread's slots span several blocks only when R > B (R > 8,
+// since B >= 8); the list exceeds the staging limit only when the group
+// can hold more than kStageMax candidates.
+template <int NW, int R>
+static hipError_t launch_tsel_r(bool scoring, const Dims& s, const float* sc, const int32_t* blk, int32_t* tok,
+                                hipStream_t st) {
   const int log2B = __builtin_ctz((unsigned)s.B);  // B is a power of two
-#define HSA_TS(RR)                                                                                          \
-  case RR:                                                                                                  \
-    hipLaunchKernelGGL((k_token_select<NW, RR>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, log2B, s.m, \
-                       s.k); \
-    break;
+  const bool staged = s.k <= kStageMax;
+  const bool oneblk = R <= s.B;
+  // without scoring every query takes the keep-all path, which uses no LDS;
+  // with scoring m * B <= 32768 (checked at the API), so m <= 4096
+  const size_t dyn = scoring ? tsel_lds_bytes(s.m, s.k) : 0;
+  constexpr bool kMulti = R > 8;
+  constexpr bool kLong = NW * 64 * R > kStageMax;
+  if (!scoring || (staged && oneblk)) {
+    // (without scoring the variant does not matter: the keep-all path)
+    launch_tsel_k<NW, R, true, true>(s, dyn, log2B, sc, blk, tok, st);
+  } else if (staged) {
+    if constexpr (kMulti) launch_tsel_k<NW, R, true, false>(s, dyn, log2B, sc, blk, tok, st);
+    else return hipErrorInvalidValue;
+  } else if (oneblk) {
+    if constexpr (kLong) launch_tsel_k<NW, R, false, true>(s, dyn, log2B, sc, blk, tok, st);
+    else return hipErrorInvalidValue;
+  } else {
+    if constexpr (kLong && kMulti) launch_tsel_k<NW, R, false, false>(s, dyn, log2B, sc, blk, tok, st);
+    else return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_tsel(int R, bool scoring, const Dims& s, const float* sc, const int32_t* blk, int32_t* tok,
+                              hipStream_t st) {
   switch (R) {
-    HSA_TS(1) HSA_TS(2) HSA_TS(4) HSA_TS(8) HSA_TS(16) HSA_TS(32)
+    case 1: return launch_tsel_r<NW, 1>(scoring, s, sc, blk, tok, st);
+    case 2: return launch_tsel_r<NW, 2>(scoring, s, sc, blk, tok, st);
+    case 4: return launch_tsel_r<NW, 4>(scoring, s, sc, blk, tok, st);
+    case 8: return launch_tsel_r<NW, 8>(scoring, s, sc, blk, tok, st);
+    case 16: return launch_tsel_r<NW, 16>(scoring, s, sc, blk, tok, st);
+    case 32: return launch_tsel_r<NW, 32>(scoring, s, sc, blk, tok, st);
     case 64:
-      if constexpr (NW <= 4) {
-        hipLaunchKernelGGL((k_token_select<NW, 64>), grid, block, 0, st, sc, blk, tok, s.L, s.nq, s.B, log2B, s.m,
-                           s.k);
-        break;
-      }
+      if constexpr (NW <= 4) return launch_tsel_r<NW, 64>(scoring, s, sc, blk, tok, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
-#undef HSA_TS
-  return hipGetLastError();
 }
 
 constexpr size_t kMaxLds = 160 * 1024;
@@ -495,12 +552,12 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
   if (nq_total >= 512 && n_max <= 4 * 64 * 64) {  // many queries: a 4-wave workgroup per query
     int r = 1;
     while (r * 256 < n_max) r <<= 1;
-    return launch_tsel<4>(r, s, scores, blk, tok, st);
+    return launch_tsel<4>(r, any_scoring, s, scores, blk, tok, st);
   }
   int r = 1;
   while (r * 1024 < n_max) r <<= 1;
   if (r > 32) return hipErrorInvalidValue;
-  return launch_tsel<16>(r, s, scores, blk, tok, st);
+  return launch_tsel<16>(r, any_scoring, s, scores, blk, tok, st);
 }
 
 }  // namespace hsa

@@ -67,8 +67,16 @@ def call_forward(lib, s, ws_bytes=1 << 40, W=None, qI=FAKE):
     (dict(n_heads_q=64, n_heads_kv=2), 2),
     (dict(top_k=0), 1),
     (dict(n_q=5000), 1),
+    # kv row offsets are 31-bit: seq_len * n_heads_kv * 256 must stay below 2^31
+    (dict(seq_len=1 << 22, n_q=1, n_heads_q=16, n_heads_kv=2), 2),
+    (dict(seq_len=(1 << 23) - 1, n_q=1, n_heads_q=16, n_heads_kv=1, top_k=1 << 20), 0),
 ])
 def test_attention_validation(lib, kw, status):
+    if status == 0:
+        # valid: the call would launch, so only the shape check is exercised
+        # (zero queries: nothing is enqueued)
+        assert call_attn(lib, shape(**dict(kw, batch=0))) == 0
+        return
     assert call_attn(lib, shape(**kw)) == status
     assert lib.hsa_sparse_last_error() != b""
 
