@@ -200,6 +200,47 @@ class HipEvents:
     def destroy(self, ev):
         self.hip.hipEventDestroy(ev)
 
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+
+# ------------------------------------------------------- flat indexer
+
+
+def flat_comparison(w: Workload, dev: dict, shape, stage_ms: dict, steps: int, hip) -> dict | None:
+    """Time hsa_flat_topk (score every causal token, keep top-k) on the same
+    indexer inputs, against the hierarchical indexer's stages of hsa_forward
+    (summary + block top-m + token top-k) - the comparison the HISA page
+    reports.  None when the flat indexer does not support the shape."""
+    import torch
+
+    from hierarchical_index_sparse_amd import _lib
+    need = _lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_FLAT_TOPK)
+    if need == 0 and w.top_k < w.seq_len:
+        return None  # unsupported shape
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    tok = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device="cuda")
+    _lib.hsa_flat_topk(shape, dev["qI"], dev["kI"], tok, ws)
+    torch.cuda.synchronize()
+    n = max(3, min(steps, 10))
+    ev = [(hip.create(), hip.create()) for _ in range(n)]
+    stream = torch.cuda.current_stream().cuda_stream
+    for a, b in ev:
+        hip.record(a, stream)
+        _lib.hsa_flat_topk(shape, dev["qI"], dev["kI"], tok, ws)
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    flat_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev]))
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    del ws, tok
+    torch.cuda.empty_cache()
+    hier_ms = stage_ms["block_summary"] + stage_ms["block_topm"] + stage_ms["token_topk"]
+    return {"flat_indexer_ms": flat_ms, "hierarchical_indexer_ms": hier_ms, "speedup": flat_ms / hier_ms,
+            "note": "same inputs and output form; hierarchical = summary + block top-m + token top-k stages "
+                    "of hsa_forward"}
+
 
 # ------------------------------------------------------------------- main
 
@@ -212,6 +253,8 @@ def main():
     ap.add_argument("--workload", default="prefill_64k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-sample", type=int, default=1024, help="queries the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flat", action="store_true",
+                    help="skip timing the flat indexer (every causal token scored) on the same inputs")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of known "
                          "traffic, to scale hardware byte counters against)")
@@ -296,6 +339,8 @@ def main():
         hip.destroy(a)
         hip.destroy(b)
 
+    flat = None if args.no_flat else flat_comparison(w, dev, shape, stage_ms, args.steps, hip)
+
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     queries = w.batch * w.n_q
     value = queries / (ms_per_step / 1000.0)
@@ -336,6 +381,7 @@ def main():
         "gpu_step_ms_all_stage_events": gpu_step_ms,
         "stage_hbm_frac": {n: work[n]["bytes"] / (stage_ms[n] / 1000.0) / 1e9 / HBM_PEAK_GBS for n in STAGES},
         "roofline": roof,
+        "indexer_vs_flat": flat,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

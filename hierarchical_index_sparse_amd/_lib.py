@@ -21,12 +21,13 @@ HSA_SPARSE_OP_BLOCK_TOPM = 1
 HSA_SPARSE_OP_TOKEN_TOPK = 2
 HSA_SPARSE_OP_SPARSE_ATTN = 3
 HSA_SPARSE_OP_FORWARD = 4
+HSA_SPARSE_OP_FLAT_TOPK = 5
 
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "HIP_ERROR"}
 
 EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_error",
            "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
-           "hsa_sparse_set_stage_events")
+           "hsa_sparse_set_stage_events", "hsa_flat_topk")
 
 
 class HsaSparseShape(ctypes.Structure):
@@ -67,8 +68,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_sparse_attn.argtypes = [S, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward.argtypes = [S, P, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_sparse_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.hsa_flat_topk.argtypes = [S, P, P, P, P, SZ, P]
     for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
-                 "hsa_sparse_set_stage_events"):
+                 "hsa_sparse_set_stage_events", "hsa_flat_topk"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -149,6 +151,13 @@ def hsa_token_topk(shape, qI, kI, blk, tok, workspace=None, stream=None):
                                _ptr(blk, "blk", _I32), _ptr(tok, "tok", _I32), ws.data_ptr(), nbytes,
                                _stream(stream))
     _check(st, "hsa_token_topk")
+
+
+def hsa_flat_topk(shape, qI, kI, tok, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_FLAT_TOPK, workspace, qI.device)
+    st = load().hsa_flat_topk(ctypes.byref(shape), _ptr(qI, "qI", _BF16), _ptr(kI, "kI", _BF16),
+                              _ptr(tok, "tok", _I32), ws.data_ptr(), nbytes, _stream(stream))
+    _check(st, "hsa_flat_topk")
 
 
 def hsa_sparse_attn(shape, Q, K, V, tok, O, lse=None, workspace=None, stream=None):

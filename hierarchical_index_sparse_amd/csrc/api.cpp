@@ -32,7 +32,7 @@ hsa_sparse_status_t hip_fail(hipError_t e, const char* where) {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
-enum : unsigned { kSummary = 1u, kSelect = 2u, kAttn = 4u };
+enum : unsigned { kSummary = 1u, kSelect = 2u, kAttn = 4u, kFlat = 8u };
 
 // Checks shared by every entry point; `parts` names the fields the entry
 // point reads.  Fills `d` on success.
@@ -46,6 +46,11 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
   if (parts & kSelect) {
     if (s->top_m < 2) return fail(HSA_SPARSE_INVALID_ARG, "top_m must be >= 2 (first and last block are kept)");
     if (s->top_k < 1) return fail(HSA_SPARSE_INVALID_ARG, "top_k must be >= 1");
+  }
+  if (parts & kFlat) {
+    if (s->top_k < 1) return fail(HSA_SPARSE_INVALID_ARG, "top_k must be >= 1");
+    if (s->d_index != 64 && s->d_index != 128)
+      return fail(HSA_SPARSE_UNSUPPORTED, "d_index must be 64 or 128 (got %d)", s->d_index);
   }
   if (need_index) {
     if (s->d_index != 64 && s->d_index != 128)
@@ -87,6 +92,9 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
   d.d = s->head_dim;
   d.scale = s->scale;
   d.nb = (int)(((long long)s->seq_len + d.B - 1) / d.B);
+  if ((parts & kFlat) && !hsa::flat_topk_supported(d))
+    return fail(HSA_SPARSE_UNSUPPORTED, "flat top-k needs top_k <= 8192 when top_k < seq_len (got %d)",
+                s->top_k);
   g_last_error.clear();
   return HSA_SPARSE_OK;
 }
@@ -156,6 +164,8 @@ size_t hsa_sparse_workspace_size(const hsa_sparse_shape_t* shape, int op) {
       return check_shape(shape, d, kAttn) == HSA_SPARSE_OK ? hsa::sparse_attn_ws_bytes(d) : 0;
     case HSA_SPARSE_OP_FORWARD:
       return check_shape(shape, d, kSummary | kSelect | kAttn) == HSA_SPARSE_OK ? forward_layout(d).total : 0;
+    case HSA_SPARSE_OP_FLAT_TOPK:
+      return check_shape(shape, d, kFlat) == HSA_SPARSE_OK ? hsa::flat_topk_ws_bytes(d) : 0;
     default: return 0;
   }
 }
@@ -201,6 +211,20 @@ hsa_sparse_status_t hsa_token_topk(const hsa_sparse_shape_t* shape, const uint16
     return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "token_topk needs %zu workspace bytes", need);
   hipError_t e = hsa::launch_token_topk(d, qI, kI, blk, tok, workspace, stream);
   return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_token_topk");
+}
+
+hsa_sparse_status_t hsa_flat_topk(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,
+                                  int32_t* tok, void* workspace, size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kFlat);
+  if (st != HSA_SPARSE_OK) return st;
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!qI || !kI || !tok) return fail(HSA_SPARSE_INVALID_ARG, "qI, kI or tok is NULL");
+  const size_t need = hsa::flat_topk_ws_bytes(d);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "flat_topk needs %zu workspace bytes", need);
+  hipError_t e = hsa::launch_flat_topk(d, qI, kI, tok, workspace, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_flat_topk");
 }
 
 hsa_sparse_status_t hsa_sparse_attn(const hsa_sparse_shape_t* shape, const uint16_t* Q, const uint16_t* K,

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
     const float v = sc[idx < n ? idx : 0];  // branch-free: all loads in flight together
     key[r] = idx < n ? score_key(v) : 0u;
   }
-  select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take) {
+  select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = 1 + idx;
   });
 }

@@ -1,0 +1,323 @@
+// The flat indexer: for every query, score every causal token s <= t with
+// the indexer's dot product and keep the top-k.
+//
+// HISA page (the problem and the original method): the indexer scores each
+// query against all previous tokens and keeps the most relevant ones; the
+// hierarchical method replaces exactly this step, and degrades to it when
+// every block is kept.  Built here as the baseline the hierarchical path is
+// measured against, with the same output form (ascending token lists,
+// padded with -1; ties to the lower index).
+//
+// Kernel 1 (k_flat_scores): S^T = kI qI^T on v_mfma_f32_16x16x32_bf16 for
+// 64 queries x 512 tokens per workgroup (A = 16 key rows, B = 16 queries);
+// each wave keeps the 64 queries in registers over its 128 tokens, and each
+// lane holds 4 consecutive tokens of one query and writes them with one
+// 16-byte store.  Tiles after the tile's last query are skipped.  Bound by
+// the score writes (4 bytes per causal pair).
+//
+// Kernel 2 (k_flat_chunk_select): the t+1 candidates of a query are cut into
+// chunks of kFlatChunk tokens (what one 4-wave select holds in registers);
+// each chunk keeps its own top-min(k, n) with the exact select of
+// select.hpp.  A query with a single chunk writes its list directly.
+// Kernel 3 (k_flat_merge): groups of up to 8192 / k (k <= 2048, 4 waves) or
+// 32768 / k (16 waves) chunk winners are
+// merged by the same select until one list per query remains.  The global
+// top-k under (score desc, index asc) is contained in the union of the
+// chunks' top-k under the same order, and every level keeps the lists in
+// ascending index order, so ties resolve exactly as in one select.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "select.hpp"
+
+namespace hsa {
+
+constexpr int kFlatChunk = 4 * 64 * 32;   // 8192 keys per chunk select: 4 waves x 64 lanes x 32
+// merge selects: 4 waves (8192 keys) while that holds four lists of k, else 16 waves (32768 keys)
+constexpr int kFlatMergeSmall = 4 * 64 * 32;
+constexpr int kFlatMergeLarge = 16 * 64 * 32;
+constexpr int kFlatStageMax = 8192;
+constexpr int kFlatKeysPerWG = 512;  // score tile: 64 queries x 512 tokens (128 per wave)
+
+template <int DI>
+__global__ __launch_bounds__(256) void k_flat_scores(const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI,
+                                                     float* __restrict__ scores, int L, int nq, int Lp,
+                                                     int qtiles_per_seq) {
+  constexpr int KS = DI / 32;
+  const int b = blockIdx.y / qtiles_per_seq;
+  const int i0 = (blockIdx.y % qtiles_per_seq) * 64;
+  const int t_last = query_pos(L, nq, min(nq, i0 + 64) - 1);
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int jl = lane & 15, gq = lane >> 4;
+  const int wkey0 = blockIdx.x * kFlatKeysPerWG + wave * (kFlatKeysPerWG / 4);  // this wave's first token
+  if (wkey0 > t_last) return;
+
+  // B operands: the 64 queries (4 tiles of 16), kept for all of the wave's keys
+  u32x4 qb[4][KS];
+  int tq[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int i = min(i0 + 16 * mt + jl, nq - 1);
+    const uint16_t* qsrc = qI + ((size_t)b * nq + i) * DI + 8 * gq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[mt][ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
+    tq[mt] = i0 + 16 * mt + jl < nq ? query_pos(L, nq, i) : -1;  // -1: no such query
+  }
+  for (int key0 = wkey0; key0 < wkey0 + kFlatKeysPerWG / 4 && key0 <= t_last; key0 += 32) {
+    // A operands: 2 tiles of 16 key rows
+    u32x4 ka[2][KS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int row = min(key0 + 16 * kt + jl, L - 1);
+      const uint16_t* src = kI + ((size_t)b * L + row) * DI + 8 * gq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float* dst = scores + ((size_t)b * nq + i0 + 16 * mt + jl) * Lp;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kt][ks]),
+                                                        __builtin_bit_cast(bf16x8, qb[mt][ks]), acc, 0, 0, 0);
+        // lane: tokens s0 .. s0+3 of query i0 + 16mt + jl
+        const int s0 = key0 + 16 * kt + 4 * gq;
+        if (s0 <= tq[mt]) *reinterpret_cast<f32x4*>(dst + s0) = acc;
+      }
+    }
+  }
+}
+
+// One (query, chunk).  Lists of chunk winners are (key, token) pairs in
+// ascending token order with their count.
+template <int NW, int R>
+__global__ __launch_bounds__(NW * 64) void k_flat_chunk_select(const float* __restrict__ scores,
+                                                               uint2* __restrict__ lists, int* __restrict__ counts,
+                                                               int32_t* __restrict__ tok, int L, int nq, int Lp,
+                                                               int k, int nchunk) {
+  constexpr int NT = NW * 64;
+  static_assert(NT * R <= kFlatChunk, "a chunk must fit the group");
+  __shared__ SelectSmem<NW> lds;
+  extern __shared__ int stage[];  // k + 64 ints (final lists are staged)
+  const int q = blockIdx.x;
+  const int c = blockIdx.y;
+  const int t = query_pos(L, nq, q % nq);
+  const int n_all = t + 1;
+  int32_t* out = tok + (size_t)q * k;
+  if (n_all <= k) {  // every causal token is kept
+    if (c == 0)
+      for (int s = threadIdx.x; s < k; s += NT) out[s] = s < n_all ? s : -1;
+    return;
+  }
+  const int lo = c * kFlatChunk;
+  if (lo >= n_all) return;
+  const int n = min(kFlatChunk, n_all - lo);
+  const bool single = n_all <= kFlatChunk;  // then c == 0 and the list is final
+  const float* sc = scores + (size_t)q * Lp + lo;
+  const int idx0 = threadIdx.x * R;
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; r += 4) {
+    if (idx0 + r + 3 < n) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[r + e] = score_key(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[r + e] = idx0 + r + e < n ? score_key(sc[idx0 + r + e]) : 0u;
+    }
+  }
+  uint2* lst = lists + ((size_t)q * nchunk + c) * k;
+  if (n <= k) {  // a short last chunk: all of it goes to the merge
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (idx0 + r < n) lst[idx0 + r] = make_uint2(key[r], (unsigned)(lo + idx0 + r));
+    if (threadIdx.x == 0) counts[(size_t)q * nchunk + c] = n;
+    return;
+  }
+  if (single) {  // k <= kFlatStageMax (checked at the API): the list is staged in LDS
+    const int dummy = k + lane_id();
+    select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) { stage[take ? pos : dummy] = lo + idx; });
+    for (int p = threadIdx.x; p < k; p += NT) out[p] = stage[p];
+    return;
+  }
+  select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t kv) {
+    if (take) lst[pos] = make_uint2(kv, (unsigned)(lo + idx));
+  });
+  if (threadIdx.x == 0) counts[(size_t)q * nchunk + c] = k;
+}
+
+// One (query, group of up to G lists) of a merge level: n_in lists per query
+// at this level (fewer for early queries), n_in = ceil(n_chunks_of_query /
+// G^level).  Writes list `grp` of the next level, or the final tokens when
+// this group is the query's only one.
+template <int NW, int R>
+__global__ __launch_bounds__(NW * 64) void k_flat_merge(const uint2* __restrict__ lin, const int* __restrict__ cin,
+                                                        uint2* __restrict__ lout, int* __restrict__ cout,
+                                                        int32_t* __restrict__ tok, int L, int nq, int k, int nchunk,
+                                                        int G, int level) {
+  constexpr int NT = NW * 64;
+  __shared__ SelectSmem<NW> lds;
+  extern __shared__ int stage[];  // k + 64 ints
+  const int q = blockIdx.x;
+  const int grp = blockIdx.y;
+  const int t = query_pos(L, nq, q % nq);
+  const int n_all = t + 1;
+  if (n_all <= k || n_all <= kFlatChunk) return;  // finished by the chunk select
+  int n_in = (n_all + kFlatChunk - 1) / kFlatChunk;
+  for (int l = 0; l < level; ++l) n_in = (n_in + G - 1) / G;
+  if (n_in <= 1) return;  // finished at an earlier level
+  const int first = grp * G;
+  if (first >= n_in) return;
+  const int nl = min(G, n_in - first);
+  const bool final_list = n_in <= G;
+  // candidates: lists first .. first+nl-1; every list but the last holds k
+  const int cnt_last = cin[(size_t)q * nchunk + first + nl - 1];
+  const int n = (nl - 1) * k + cnt_last;
+  const uint2* src = lin + ((size_t)q * nchunk + first) * k;
+  const int idx0 = threadIdx.x * R;
+  uint32_t key[R];
+  int tk[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int s = idx0 + r;
+    uint2 v = make_uint2(0u, 0u);
+    if (s < n) v = src[s];  // list j of the group starts at j * k
+    key[r] = v.x;
+    tk[r] = (int)v.y;
+  }
+  if (final_list) {
+    int32_t* out = tok + (size_t)q * k;
+    if (n <= k) {  // every candidate is kept (in index order)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (idx0 + r < k) out[idx0 + r] = idx0 + r < n ? tk[r] : -1;
+      for (int p = NT * R + threadIdx.x; p < k; p += NT) out[p] = -1;
+      return;
+    }
+    const int dummy = k + lane_id();
+    select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) { stage[take ? pos : dummy] = tk[idx - idx0]; });
+    for (int p = threadIdx.x; p < k; p += NT) out[p] = stage[p];
+    return;
+  }
+  uint2* dst = lout + ((size_t)q * nchunk + grp) * k;
+  if (n <= k) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (idx0 + r < n) dst[idx0 + r] = make_uint2(key[r], (unsigned)tk[r]);
+    if (threadIdx.x == 0) cout[(size_t)q * nchunk + grp] = n;
+    return;
+  }
+  select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t kv) {
+    if (take) dst[pos] = make_uint2(kv, (unsigned)tk[idx - idx0]);
+  });
+  if (threadIdx.x == 0) cout[(size_t)q * nchunk + grp] = k;
+}
+
+// ----------------------------------------------------------------- host side
+
+static int flat_nchunk(const Dims& s) { return (s.L + kFlatChunk - 1) / kFlatChunk; }
+static int flat_lp(const Dims& s) { return (s.L + 3) & ~3; }
+static bool flat_needs_lists(const Dims& s) { return s.k < s.L && flat_nchunk(s) > 1; }
+
+bool flat_topk_supported(const Dims& s) {
+  if (s.k >= s.L) return true;  // everything is kept: no select
+  // final lists are staged in LDS; a merge group holds at least two lists
+  return s.k <= kFlatStageMax;  // a merge group then holds at least 32768 / 8192 = 4 lists
+}
+
+size_t flat_topk_ws_bytes(const Dims& s) {
+  const size_t nqt = (size_t)s.b * s.nq;
+  if (s.k >= s.L) return 0;
+  size_t bytes = align_up(nqt * flat_lp(s) * sizeof(float));
+  if (flat_needs_lists(s)) {
+    const size_t lists = nqt * flat_nchunk(s) * s.k;
+    bytes += 2 * align_up(lists * sizeof(uint2)) + 2 * align_up(nqt * flat_nchunk(s) * sizeof(int));
+  }
+  return bytes;
+}
+
+template <int NW, int R>
+static void launch_merge(dim3 grid, size_t dyn, const uint2* lin, const int* cin, uint2* lout, int* cout,
+                         int32_t* tok, const Dims& s, int nchunk, int G, int level, hipStream_t st) {
+  hipLaunchKernelGGL((k_flat_merge<NW, R>), grid, dim3(NW * 64), dyn, st, lin, cin, lout, cout, tok, s.L, s.nq, s.k,
+                     nchunk, G, level);
+}
+
+hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, int32_t* tok, void* ws,
+                            hipStream_t st) {
+  const int nq_total = s.b * s.nq;
+  if (nq_total == 0) return hipSuccess;
+  const int nchunk = flat_nchunk(s);
+  const int Lp = flat_lp(s);
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  float* scores = reinterpret_cast<float*>(p);
+  if (s.k < s.L) {
+    const int qtiles = (s.nq + 63) / 64;
+    dim3 grid((s.L + kFlatKeysPerWG - 1) / kFlatKeysPerWG, qtiles * s.b);
+    if (s.dI == 64)
+      hipLaunchKernelGGL((k_flat_scores<64>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+    else
+      hipLaunchKernelGGL((k_flat_scores<128>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    p += align_up((size_t)nq_total * Lp * sizeof(float));
+  }
+  uint2* lists[2] = {nullptr, nullptr};
+  int* counts[2] = {nullptr, nullptr};
+  if (flat_needs_lists(s)) {
+    const size_t nl = (size_t)nq_total * nchunk;
+    for (int i = 0; i < 2; ++i) {
+      lists[i] = reinterpret_cast<uint2*>(p);
+      p += align_up(nl * s.k * sizeof(uint2));
+      counts[i] = reinterpret_cast<int*>(p);
+      p += align_up(nl * sizeof(int));
+    }
+  }
+  // staged final lists: k + 64 ints (k <= kFlatStageMax when a select runs)
+  const size_t dyn = s.k < s.L ? sizeof(int) * ((size_t)s.k + kWave) : 0;
+  hipLaunchKernelGGL((k_flat_chunk_select<4, 32>), dim3(nq_total, s.k < s.L ? nchunk : 1), dim3(256), dyn, st,
+                     scores, lists[0], counts[0], tok, s.L, s.nq, Lp, s.k, nchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !flat_needs_lists(s)) return e;
+  // merge levels until one list per query remains
+  const bool small = 4 * s.k <= kFlatMergeSmall;  // 4-wave merges only when a group holds 4+ lists
+  const int G = (small ? kFlatMergeSmall : kFlatMergeLarge) / s.k;  // >= 2
+  int n_lists = nchunk, level = 0, cur = 0;
+  while (n_lists > 1) {
+    const int groups = (n_lists + G - 1) / G;
+    const int n_max = min(G, n_lists) * s.k;  // candidates of the fullest group
+    dim3 grid(nq_total, groups);
+    const uint2* lin = lists[cur];
+    const int* cin = counts[cur];
+    uint2* lout = lists[cur ^ 1];
+    int* cout = counts[cur ^ 1];
+    int r = 1;
+    while (r * (small ? 256 : 1024) < n_max) r <<= 1;
+#define HSA_MG(NW, RR) \
+  case RR: launch_merge<NW, RR>(grid, dyn, lin, cin, lout, cout, tok, s, nchunk, G, level, st); break;
+    if (small) {
+      switch (r) {
+        HSA_MG(4, 1) HSA_MG(4, 2) HSA_MG(4, 4) HSA_MG(4, 8) HSA_MG(4, 16) HSA_MG(4, 32)
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      switch (r) {
+        HSA_MG(16, 1) HSA_MG(16, 2) HSA_MG(16, 4) HSA_MG(16, 8) HSA_MG(16, 16) HSA_MG(16, 32)
+        default: return hipErrorInvalidValue;
+      }
+    }
+#undef HSA_MG
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    n_lists = groups;
+    cur ^= 1;
+    ++level;
+  }
+  return hipSuccess;
+}
+
+}  // namespace hsa

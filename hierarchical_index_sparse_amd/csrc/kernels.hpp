@@ -44,6 +44,12 @@ size_t sparse_attn_ws_bytes(const Dims& s);
 hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                               const int32_t* tok, float* O, float* lse, void* ws, hipStream_t st);
 
+// the flat indexer (every causal token scored), the baseline of step 3
+bool flat_topk_supported(const Dims& s);
+size_t flat_topk_ws_bytes(const Dims& s);
+hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, int32_t* tok, void* ws,
+                            hipStream_t st);
+
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
 }  // namespace hsa

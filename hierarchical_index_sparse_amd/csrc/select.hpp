@@ -283,7 +283,7 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
 }
 
 // Requires: 1 <= want < number of non-empty keys.  Every thread of the
-// group must call it (it synchronises the group).  emit(pos, idx, take) is
+// group must call it (it synchronises the group).  emit(pos, idx, take, key) is
 // called for every key of the thread in index order; `take` says whether
 // the key is kept, and then pos (0 .. want-1) is its output slot.
 template <int NW, int R, typename Emit>
@@ -329,7 +329,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[R], int want, S
     const int is_eq = key[r] == T;
     const int tk = (int)(key[r] > T) | (is_eq & (int)(ties > 0));
     ties -= is_eq & tk;
-    emit(pos, idx0 + r, tk != 0);
+    emit(pos, idx0 + r, tk != 0, key[r]);
     pos += tk;
   }
   sel_sync<NW>();  // LDS may be reused by the caller

@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   const int bmask = B - 1;
   const int tbase = ONEBLK ? (bl[min(idx0 >> log2B, n_sel - 1)] << log2B) | (idx0 & bmask) : 0;
   const int dummy = k + lane_id();
-  select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take) {
+  select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) {
     const int v = ONEBLK ? tbase + (idx - idx0) : (bl[idx >> log2B] << log2B) | (idx & bmask);
     if constexpr (STAGED) stage[take ? pos : dummy] = v;
     else if (take) out[pos] = v;

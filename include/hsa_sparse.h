@@ -84,7 +84,8 @@ enum {
   HSA_SPARSE_OP_BLOCK_TOPM = 1,
   HSA_SPARSE_OP_TOKEN_TOPK = 2,
   HSA_SPARSE_OP_SPARSE_ATTN = 3,
-  HSA_SPARSE_OP_FORWARD = 4
+  HSA_SPARSE_OP_FORWARD = 4,
+  HSA_SPARSE_OP_FLAT_TOPK = 5
 };
 
 /* Bytes of device workspace the operation `op` needs for `shape`
@@ -187,6 +188,30 @@ hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape,
                                 int32_t* tok_out, float* O, float* lse,
                                 void* workspace, size_t workspace_bytes,
                                 hsa_sparse_stream_t stream);
+
+/*
+ * The flat indexer, the method the hierarchical one replaces (HISA page:
+ * the indexer scores each query against every previous token and keeps
+ * the most relevant; with every block kept the hierarchical selection
+ * reduces to it).  Provided as the baseline the hierarchical path is
+ * measured against, and as a check of that reduction.
+ *   Reads batch, seq_len, n_q, d_index and top_k of the shape.
+ *   qI, kI  as for hsa_token_topk.
+ *   tok     [batch, n_q, top_k] int32 output: for the query at t, all of
+ *           0..t if t + 1 <= top_k, else the best top_k tokens of 0..t by
+ *           qI . kI[s] (ties to the lower index); ascending, -1 padded.
+ *   workspace  >= hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_FLAT_TOPK):
+ *           every causal score in fp32 ([batch * n_q, seq_len] rounded up to
+ *           a multiple of 4 per row) plus the chunk winners' lists when
+ *           seq_len > 32768.
+ * Supported: d_index in {64, 128}; top_k <= 8192 when top_k < seq_len.
+ * Errors: as for the other entry points; nothing is launched on an error.
+ */
+hsa_sparse_status_t hsa_flat_topk(const hsa_sparse_shape_t* shape,
+                                  const uint16_t* qI, const uint16_t* kI,
+                                  int32_t* tok, void* workspace,
+                                  size_t workspace_bytes,
+                                  hsa_sparse_stream_t stream);
 
 /*
  * Per-step timing of hsa_forward (profiling aid).  After this call, every

@@ -1,8 +1,9 @@
-"""Run the GPU parity tests of test_gpu_parity.py without pytest.
+"""Run the GPU parity tests without pytest.
 
     python3 tests/run_gpu_parity.py [name-substring ...]
 
-Calls the same test functions (parametrised cases expanded) in one plain
+Calls the same test functions of test_gpu_parity.py and test_gpu_flat.py
+(parametrised cases expanded) in one plain
 Python process, prints PASS/FAIL per case as it ends, stops at the first
 failure and exits non-zero on it.  Full-size workloads run last.
 """
@@ -21,12 +22,16 @@ import torch  # noqa: E402
 torch.zeros(1, device="cuda")
 torch.cuda.synchronize()
 
-import test_gpu_parity as T  # noqa: E402
+import test_gpu_flat  # noqa: E402
+import test_gpu_parity  # noqa: E402
+
+MODULES = (test_gpu_parity, test_gpu_flat)
 
 
 def cases():
     out = []
-    for name, fn in inspect.getmembers(T, inspect.isfunction):
+    members = [m for T in MODULES for m in inspect.getmembers(T, inspect.isfunction) if m[1].__module__ == T.__name__]
+    for name, fn in members:
         if not name.startswith("test_"):
             continue
         marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
@@ -40,7 +45,7 @@ def cases():
             kw = dict(zip(names, v))
             label = getattr(v[0], "name", None) or "-".join(str(x) for x in v)
             out.append((f"{name}[{label}]", lambda fn=fn, kw=kw: fn(**kw)))
-    out.sort(key=lambda c: c[0].startswith("test_full_size"))
+    out.sort(key=lambda c: c[0].startswith(("test_full_size", "test_flat_prefill")))
     return out
 
 

@@ -148,3 +148,40 @@ def test_workspace_sizes(lib):
         assert fwd % 256 == 0
     assert lib.hsa_sparse_workspace_size(None, _lib.HSA_SPARSE_OP_FORWARD) == 0
     assert lib.hsa_sparse_workspace_size(ctypes.byref(shape()), 42) == 0
+
+
+def call_flat(lib, s, ws_bytes=1 << 44, tok=FAKE):
+    return lib.hsa_flat_topk(ctypes.byref(s), FAKE, FAKE, tok, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), 1),
+    (dict(d_index=32), 2),
+    (dict(n_q=5000), 1),
+    (dict(seq_len=65536, n_q=1, top_k=8193), 2),        # list longer than the LDS stage
+    (dict(seq_len=8000, n_q=1, top_k=8193), 0),         # keeps everything: no select
+    (dict(seq_len=200000, n_q=1, top_k=8192), 0),       # several merge levels
+    (dict(seq_len=4096, n_q=16, block=0, top_m=0), 0),  # block fields are not read
+])
+def test_flat_validation(lib, kw, status):
+    if status == 0:
+        assert call_flat(lib, shape(**dict(kw, batch=0))) == 0
+        assert lib.hsa_sparse_workspace_size(ctypes.byref(shape(**kw)), _lib.HSA_SPARSE_OP_FLAT_TOPK) >= 0
+        return
+    assert call_flat(lib, shape(**kw)) == status
+    assert lib.hsa_sparse_last_error() != b""
+
+
+def test_flat_workspace(lib):
+    # every causal score in fp32, rows padded to a multiple of 4; plus two
+    # ping-pong buffers of chunk winners (8-byte pairs and a count per list)
+    # when a query's candidates span several 8192-token chunks
+    s = shape(batch=2, seq_len=4097, n_q=3, top_k=100)
+    need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FLAT_TOPK)
+    assert need >= 2 * 3 * 4100 * 4 and need % 256 == 0
+    s = shape(batch=1, seq_len=70000, n_q=2, top_k=1000)
+    need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FLAT_TOPK)
+    assert need >= 2 * 70000 * 4 + 2 * (2 * 9 * 1000 * 8)
+    assert call_flat(lib, s, ws_bytes=need - 1) == 3
+    assert lib.hsa_sparse_workspace_size(ctypes.byref(shape(top_k=5000)), _lib.HSA_SPARSE_OP_FLAT_TOPK) == 0
+    assert lib.hsa_flat_topk(ctypes.byref(shape(batch=0)), None, None, None, None, 0, None) == 0
