@@ -88,10 +88,8 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
       dot += qv[2 * e] * bf16_lo(v[it][e]);
       dot += qv[2 * e + 1] * bf16_hi(v[it][e]);
     }
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) dot += shfl_xor(dot, o);
-#pragma unroll
-    for (int o = LPR; o < LPR * NL; o <<= 1) dot = fmaxf(dot, shfl_xor(dot, o));
+    dot = group_sum_f<LPR>(dot);
+    if constexpr (NL > 1) dot = group_max_f<LPR * NL>(dot);  // a block's landmark rows are adjacent
     if (row < row_end && (lane % (LPR * NL)) == 0) scores[(size_t)q * nb + row / NL] = dot;
   }
 }
@@ -147,10 +145,10 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
                                                       __builtin_bit_cast(bf16x8, bs[nt][ks]), acc, 0, 0, 0);
       // lane: queries 16mt + 4gq + e, summary row row0 + 16nt + jl
+      if constexpr (NL > 1) {
 #pragma unroll
-      for (int o = 1; o < NL; o <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = fmaxf(acc[e], shfl_xor(acc[e], o));
+        for (int e = 0; e < 4; ++e) acc[e] = group_max_f<NL>(acc[e]);
+      }
       const int row = row0 + 16 * nt + jl;
       const int j = row / NL;
       if (row % NL == 0 && row < nrows) {
@@ -202,6 +200,93 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
     key[r] = idx < n ? score_key(v) : 0u;
   }
   select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+    if (take) out[1 + pos] = 1 + idx;
+  });
+}
+
+// Decode block top-m in one launch (few queries, at most kFusedMaxBlocks
+// scored blocks, one summary vector per block): one 1024-thread workgroup
+// per query scores its causal blocks 1..c-1 into LDS (16-byte summary-row
+// loads, d_index/8 lanes per row, 8 rounds of loads in flight, dot products
+// reduced by xor shuffles) and runs the 16-wave select on them, so the
+// scores never leave the chip.  Workgroups past the queries summarise the
+// newest blocks when the host folds that in (as for k_block_scores).
+constexpr int kFusedMaxBlocks = 2048;
+
+template <int DI, int R>
+__global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __restrict__ qI,
+                                                            const uint16_t* __restrict__ S, int32_t* __restrict__ blk,
+                                                            int L, int nq, int B, int nb, int m, int nq_total,
+                                                            const uint16_t* __restrict__ kI,
+                                                            uint16_t* __restrict__ S_out, int sum_start, int nsum) {
+  constexpr int LPR = DI / 8;      // lanes per summary row
+  constexpr int RPI = 1024 / LPR;  // rows per round of the workgroup
+  constexpr int U = 8;             // rounds of loads in flight
+  __shared__ float sc[kFusedMaxBlocks];
+  __shared__ SelectSmem<16> sm;
+  __shared__ float red[1][1024 / LPR][DI];
+  if ((int)blockIdx.x >= nq_total) {  // folded summary of a newest block (uniform)
+    const int w = (int)blockIdx.x - nq_total;
+    summarise_block<DI, 1, 1024>(kI, nullptr, S_out, L, B, nb, sum_start + w % nsum, w / nsum, red);
+    return;
+  }
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int b = q / nq;
+  const int t = query_pos(L, nq, q % nq);
+  const int c = t / B;
+  int32_t* out = blk + (size_t)q * m;
+  if (c + 1 <= m) {
+    for (int j = tid; j < m; j += 1024) out[j] = j <= c ? j : -1;
+    return;
+  }
+  const int want = m - 2;
+  const int n = c - 1;  // candidates: blocks 1 .. c-1 (index = block - 1)
+  if (tid == 0) {
+    out[0] = 0;
+    out[m - 1] = c;
+  }
+  if (want == 0) return;
+
+  const int col8 = tid % LPR, r0 = tid / LPR;
+  float qv[8];
+  {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(qI + (size_t)q * DI + col8 * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_lo(v[e]);
+      qv[2 * e + 1] = bf16_hi(v[e]);
+    }
+  }
+  const uint16_t* Sb = S + ((size_t)b * nb + 1) * DI;  // row j-1 = block j
+  for (int base = 0; base < n; base += U * RPI) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(base + u * RPI + r0, n - 1);
+      v[u] = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + col8 * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot += qv[2 * e] * bf16_lo(v[u][e]);
+        dot += qv[2 * e + 1] * bf16_hi(v[u][e]);
+      }
+      dot = group_sum_f<LPR>(dot);
+      const int row = base + u * RPI + r0;
+      if (col8 == 0 && row < n) sc[row] = dot;
+    }
+  }
+  __syncthreads();
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = tid * R + r;
+    key[r] = idx < n ? score_key(sc[idx]) : 0u;
+  }
+  select_top<16, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = 1 + idx;
   });
 }
@@ -266,6 +351,23 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
 #undef HSA_SM
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  } else if (c_max + 1 > s.m && s.nL == 1 && n_max <= kFusedMaxBlocks && nq_total < 512) {
+    const int nsum = fold ? s.nb - fold->start_block : 0;
+    dim3 grid(nq_total + (fold ? s.b * nsum : 0));
+    const uint16_t* kI = fold ? fold->kI : nullptr;
+    uint16_t* S_out = fold ? fold->S : nullptr;
+    const int start = fold ? fold->start_block : s.nb;
+    const int ns = max(nsum, 1);
+#define HSA_FD(DI, RR)                                                                                             \
+  hipLaunchKernelGGL((k_block_topm_decode<DI, RR>), grid, dim3(1024), 0, st, qI, S, blk, s.L, s.nq, s.B, s.nb, s.m, \
+                     nq_total, kI, S_out, start, ns)
+    if (s.dI == 64) {
+      if (n_max <= 1024) HSA_FD(64, 1); else HSA_FD(64, 2);
+    } else {
+      if (n_max <= 1024) HSA_FD(128, 1); else HSA_FD(128, 2);
+    }
+#undef HSA_FD
+    return hipGetLastError();
   } else if (c_max + 1 > s.m) {
     const int xs = (c_max + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG;
     const int nsum = fold ? s.nb - fold->start_block : 0;

@@ -70,36 +70,22 @@ __device__ __forceinline__ float key_to_score(uint32_t k) {
 }
 
 __device__ __forceinline__ int wave_excl_scan(int v, int& total) {
-  const int lane = lane_id();
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  total = __shfl(x, kWave - 1, kWave);
-  return x - v;
+  const int incl = wave_incl_scan(v);
+  total = __builtin_amdgcn_readlane(incl, kWave - 1);
+  return incl - v;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = max(v, (uint32_t)shfl_xor((int)v, o));
-  return v;
+  return group_reduce<kWave>(v, [](uint32_t a, uint32_t b) { return max(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = min(v, (uint32_t)shfl_xor((int)v, o));
-  return v;
+  return group_reduce<kWave>(v, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_and_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v &= (uint32_t)shfl_xor((int)v, o);
-  return v;
+  return group_reduce<kWave>(v, [](uint32_t a, uint32_t b) { return a & b; });
 }
 __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v |= (uint32_t)shfl_xor((int)v, o);
-  return v;
+  return group_reduce<kWave>(v, [](uint32_t a, uint32_t b) { return a | b; });
 }
 
 template <int NW>
@@ -156,7 +142,11 @@ __device__ __forceinline__ uint32_t bin_threshold(const uint32_t* cand, int n, i
   if (diff == 0u) return all_and;  // every candidate is equal
   const int top = 31 - __builtin_clz(diff);
   uint32_t T = all_and & ~((2u << top) - 1u);  // the common prefix
-  for (int b = top; b >= 0; --b) {
+  // T is one of the candidates, so the bits below the lowest bit set in any
+  // candidate are 0 in T too: the search stops there (integer-valued scores
+  // leave many low mantissa bits clear)
+  const int low = __builtin_ctz(all_or);
+  for (int b = top; b >= low; --b) {
     const uint32_t c = T | (1u << b);
     int cnt = 0;
 #pragma unroll
@@ -232,13 +222,8 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
       const int c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
                 c3 = lane == kWave - 1 ? 0 : sm.hist[4 * lane + 3];
       const int mine = c0 + c1 + c2 + c3;
-      int incl = mine;  // sum over lanes >= l
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const int v = __shfl_down(incl, o, kWave);
-        if (lane + o < kWave) incl += v;
-      }
-      int above = incl - mine;  // keys in bins of higher lanes
+      const int pre = wave_incl_scan(mine);  // sum over lanes <= l
+      int above = __builtin_amdgcn_readlane(pre, kWave - 1) - pre;  // keys in bins of higher lanes
       const int cs[4] = {c0, c1, c2, c3};
 #pragma unroll
       for (int e = 3; e >= 0; --e) {
@@ -264,7 +249,7 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
     int pos = wave_excl_scan(cnt, wtot);
     int base = 0;
     if (lane == 0 && wtot) base = atomicAdd(&sm.info[2], wtot);
-    pos += __shfl(base, 0, kWave);
+    pos += __builtin_amdgcn_readlane(base, 0);
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (bin_at(r) == tb) sm.cand[pos++] = key[r];

@@ -288,8 +288,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 
   float M = -INFINITY;
   for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, base[s * sstride + 128]);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
+  M = group_max_f<kWave>(M);
   if (lane_id() == 0) wmax[tid / kWave] = M;
   __syncthreads();
   M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));

@@ -13,13 +13,13 @@
 
 namespace hsa {
 
-// Called by all 256 threads of a workgroup; red is the workgroup's LDS.
-template <int DI, int NL>
+// Called by all NTH threads of a workgroup; red is the workgroup's LDS.
+template <int DI, int NL, int NTH = 256>
 __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI, const int8_t* __restrict__ W,
                                                 uint16_t* __restrict__ S, int L, int B, int nb, int j, int b,
-                                                float (&red)[NL][256 / (DI / 8)][DI]) {
+                                                float (&red)[NL][NTH / (DI / 8)][DI]) {
   constexpr int LPR = DI / 8;     // lanes per row
-  constexpr int RPI = 256 / LPR;  // rows per iteration of the workgroup
+  constexpr int RPI = NTH / LPR;  // rows per iteration of the workgroup
   const int tid = threadIdx.x;
   const int col8 = tid % LPR;
   const int r0 = tid / LPR;
@@ -55,7 +55,7 @@ __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI,
   __syncthreads();
 
   const float inv_b = 1.f / (float)B;  // exact: B is a power of two
-  for (int o = tid; o < NL * DI; o += 256) {
+  for (int o = tid; o < NL * DI; o += NTH) {
     const int l = o / DI, d = o % DI;
     float total = 0.f;
 #pragma unroll 4

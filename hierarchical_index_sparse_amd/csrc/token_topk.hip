@@ -80,8 +80,7 @@ __global__ __launch_bounds__(256) void k_token_scores(const uint16_t* __restrict
         dot += qv[2 * e] * bf16_lo(v[it][e]);
         dot += qv[2 * e + 1] * bf16_hi(v[it][e]);
       }
-#pragma unroll
-      for (int o = 1; o < LPR; o <<= 1) dot += shfl_xor(dot, o);
+      dot = group_sum_f<LPR>(dot);
       if (r < rows && col8 == 0) out[r] = dot;
     }
   }
