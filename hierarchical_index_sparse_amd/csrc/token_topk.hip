@@ -16,6 +16,8 @@
 // Kernel 2 (k_token_select): one workgroup per query; when n_valid <= k all
 // candidates are written, otherwise the exact select of select.hpp runs over
 // the slot scores.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -340,6 +342,140 @@ __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_e
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block-major scoring (many queries per kept block, e.g. a chunk of new
+// queries against a long context).  The kept (query, slot) pairs are
+// inverted into one list per (sequence, block): counted with atomics,
+// offsets by a one-workgroup scan, lists filled through per-block cursors
+// (their order varies, but every score goes to its fixed slot, so results
+// are deterministic).  Then each workgroup loads one block's kI rows and
+// scores up to kBmChunk of its queries with MFMA, so each block's keys are
+// read once per kBmChunk queries instead of once per query.
+constexpr int kBmChunk = 64;
+
+__device__ __forceinline__ bool bm_entry(const int32_t* __restrict__ blk, long long e, int L, int nq, int B, int m,
+                                         int k, int nb, int& bj) {
+  const int q = (int)(e / m), p = (int)(e % m);
+  int c, n_sel, n_valid;
+  candidate_count(query_pos(L, nq, q % nq), B, m, c, n_sel, n_valid);
+  if (n_valid <= k || p >= n_sel) return false;
+  bj = (q / nq) * nb + blk[e];
+  return true;
+}
+
+__global__ __launch_bounds__(256) void k_bm_zero(int* __restrict__ counts, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) counts[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_bm_count(const int32_t* __restrict__ blk, int* __restrict__ counts, int L,
+                                                  int nq, int B, int m, int k, int nb, long long total) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+    int bj;
+    if (bm_entry(blk, e, L, nq, B, m, k, nb, bj)) atomicAdd(&counts[bj], 1);
+  }
+}
+
+// One workgroup: offsets[i] = sum of counts before i, chunk_off[i] = sum of
+// ceil(count / kBmChunk) before i (both with a final total), cursor = offsets.
+__global__ __launch_bounds__(1024) void k_bm_scan(const int* __restrict__ counts, int* __restrict__ offsets,
+                                                  int* __restrict__ chunk_off, int* __restrict__ cursor, int n) {
+  __shared__ int s_cnt[16], s_chk[16];
+  const int tid = threadIdx.x;
+  const int per = (n + 1023) / 1024;
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  int a = 0, ch = 0;
+  for (int i = lo; i < hi; ++i) {
+    a += counts[i];
+    ch += (counts[i] + kBmChunk - 1) / kBmChunk;
+  }
+  const int ia = wave_incl_scan(a), ic = wave_incl_scan(ch);
+  const int wave = tid / kWave;
+  if (lane_id() == kWave - 1) {
+    s_cnt[wave] = ia;
+    s_chk[wave] = ic;
+  }
+  __syncthreads();
+  int ba = 0, bc = 0;
+  for (int w = 0; w < wave; ++w) {
+    ba += s_cnt[w];
+    bc += s_chk[w];
+  }
+  int ra = ba + ia - a, rc = bc + ic - ch;  // exclusive prefix at lo
+  for (int i = lo; i < hi; ++i) {
+    offsets[i] = ra;
+    cursor[i] = ra;
+    chunk_off[i] = rc;
+    ra += counts[i];
+    rc += (counts[i] + kBmChunk - 1) / kBmChunk;
+  }
+  if (tid == 1023) {
+    offsets[n] = ra;
+    chunk_off[n] = rc;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_bm_fill(const int32_t* __restrict__ blk, int* __restrict__ cursor,
+                                                 int2* __restrict__ entries, int L, int nq, int B, int m, int k,
+                                                 int nb, long long total) {
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+    int bj;
+    if (bm_entry(blk, e, L, nq, B, m, k, nb, bj))
+      entries[atomicAdd(&cursor[bj], 1)] = make_int2((int)(e / m), (int)(e % m));
+  }
+}
+
+// One workgroup = one chunk of up to kBmChunk entries of one (sequence,
+// block) list; wave w takes entries 16w .. 16w+15.  S^T = kI_block qI^T per
+// 16-token tile (A = 16 key rows, B = 16 queries): each lane holds 4
+// consecutive tokens of one query and writes them with one 16-byte store to
+// that query's slots p*B + r.  Rows past L are clamped (their slots lie past
+// the query's candidates and are never read).
+template <int DI>
+__global__ __launch_bounds__(256) void k_bm_scores(const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI,
+                                                   const int2* __restrict__ entries, const int* __restrict__ offsets,
+                                                   const int* __restrict__ chunk_off, float* __restrict__ scores,
+                                                   int L, int nq, int B, int m, int nb, int nlist) {
+  constexpr int KS = DI / 32;
+  const int wg = blockIdx.x;
+  if (wg >= chunk_off[nlist]) return;
+  int lo = 0, hi = nlist;  // the list whose chunk range holds wg
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (chunk_off[mid] <= wg) lo = mid; else hi = mid;
+  }
+  const int bj = lo;
+  const int e0 = offsets[bj] + (wg - chunk_off[bj]) * kBmChunk;
+  const int e1 = min(e0 + kBmChunk, offsets[bj + 1]);
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int jl = lane & 15, gq = lane >> 4;
+  const int w0 = e0 + 16 * wave;
+  if (w0 >= e1) return;
+  const int b = bj / nb, j = bj % nb;
+  const int2 ent = entries[min(w0 + jl, e1 - 1)];  // this lane's query and slot (column jl)
+  const bool live = w0 + jl < e1;
+  u32x4 qb[KS];
+  {
+    const uint16_t* src = qI + (size_t)ent.x * DI + 8 * gq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
+  }
+  float* dst = scores + (size_t)ent.x * m * B + (size_t)ent.y * B + 4 * gq;
+  const uint16_t* kb = kI + (size_t)b * L * DI;
+  for (int r0 = 0; r0 < B; r0 += 16) {
+    const int row = min(j * B + r0 + jl, L - 1);
+    u32x4 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * DI + 8 * gq + 32 * ks);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
+                                                    __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
+    if (live) *reinterpret_cast<f32x4*>(dst + r0) = acc;
+  }
+}
+
 // Dynamic LDS of the select: the query's block list (m entries, padded to a
 // multiple of 4) and, when k <= kStageMax (STAGED), the output list plus one
 // dummy slot per lane, so that the list leaves in coalesced 16-byte stores
@@ -419,9 +555,48 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   }
 }
 
+// Workspace: the slot-ordered scores, then (block-major scoring) the list
+// counts, offsets, chunk offsets, cursors and the (query, slot) entries.
+struct BmLayout {
+  size_t counts, offsets, chunk_off, cursor, entries, total;
+};
+static BmLayout bm_layout(const Dims& s, size_t base) {
+  const size_t nl = (size_t)s.b * s.nb;
+  BmLayout t;
+  size_t o = base;
+  t.counts = o;
+  o += align_up(nl * 4);
+  t.offsets = o;
+  o += align_up((nl + 1) * 4);
+  t.chunk_off = o;
+  o += align_up((nl + 1) * 4);
+  t.cursor = o;
+  o += align_up(nl * 4);
+  t.entries = o;
+  o += align_up((size_t)s.b * s.nq * s.m * sizeof(int2));
+  t.total = o;
+  return t;
+}
+
+static int tiled_qw(const Dims& s);
+
+// Block-major scoring pays off when a query tile of the tiled scorer would
+// keep each block only a few times (a chunk of queries against a long
+// context: 64 queries x 128 kept blocks out of 4096), so that every block's
+// keys would be streamed for very few queries; when tiles amortise well
+// (prefill, where consecutive queries keep 32 of a tile's blocks on average)
+// the tiled scorer stays.  Decode keeps the per-query scorer.
+static bool use_block_major(const Dims& s) {
+  if (s.B < 16 || s.nq < 64 || (long long)s.b * s.nq * s.m >= (1ll << 30) || (long long)s.b * s.nb >= (1ll << 24))
+    return false;
+  const int qw = tiled_qw(s);
+  return qw == 0 || 64ll * qw * s.m < 8ll * s.nb;
+}
+
 size_t token_topk_ws_bytes(const Dims& s) {
   if ((long long)s.k >= (long long)s.m * s.B) return 0;
-  return align_up((size_t)s.b * s.nq * s.m * s.B * sizeof(float));
+  const size_t scores = align_up((size_t)s.b * s.nq * s.m * s.B * sizeof(float));
+  return use_block_major(s) ? bm_layout(s, scores).total : scores;
 }
 
 template <int NW, int R, bool STAGED, bool ONEBLK>
@@ -532,7 +707,31 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
   if (any_scoring) {
     const int qw = tiled_qw(s);
     hipError_t e;
-    if (qw > 0) {
+    if (use_block_major(s)) {
+      unsigned char* base = static_cast<unsigned char*>(ws);
+      const BmLayout lay = bm_layout(s, align_up((size_t)nq_total * s.m * s.B * sizeof(float)));
+      int* counts = reinterpret_cast<int*>(base + lay.counts);
+      int* offsets = reinterpret_cast<int*>(base + lay.offsets);
+      int* chunk_off = reinterpret_cast<int*>(base + lay.chunk_off);
+      int* cursor = reinterpret_cast<int*>(base + lay.cursor);
+      int2* entries = reinterpret_cast<int2*>(base + lay.entries);
+      const int nl = s.b * s.nb;
+      const long long total = (long long)nq_total * s.m;
+      const int g1 = (int)std::min<long long>((total + 255) / 256, 8192);
+      hipLaunchKernelGGL(k_bm_zero, dim3(std::min((nl + 255) / 256, 1024)), dim3(256), 0, st, counts, nl);
+      hipLaunchKernelGGL(k_bm_count, dim3(g1), dim3(256), 0, st, blk, counts, s.L, s.nq, s.B, s.m, s.k, s.nb, total);
+      hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(1024), 0, st, counts, offsets, chunk_off, cursor, nl);
+      hipLaunchKernelGGL(k_bm_fill, dim3(g1), dim3(256), 0, st, blk, cursor, entries, s.L, s.nq, s.B, s.m, s.k, s.nb,
+                         total);
+      const int gs = (int)((total + kBmChunk - 1) / kBmChunk + nl);
+      if (s.dI == 64)
+        hipLaunchKernelGGL((k_bm_scores<64>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off, scores,
+                           s.L, s.nq, s.B, s.m, s.nb, nl);
+      else
+        hipLaunchKernelGGL((k_bm_scores<128>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off,
+                           scores, s.L, s.nq, s.B, s.m, s.nb, nl);
+      e = hipGetLastError();
+    } else if (qw > 0) {
       e = launch_tiled(s, qw, qI, kI, blk, scores, st);
     } else {
       dim3 grid(s.m, nq_total);

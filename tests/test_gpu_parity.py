@@ -41,6 +41,9 @@ SMALL_CASES = [
            top_k=1000, n_heads_q=16, n_heads_kv=1), 2),
     (small("prefill_r64_select", seq_len=20000, n_q=512, d_index=128, block=128, top_m=100,
            top_k=300, n_heads_q=2, n_heads_kv=1), 2),
+    # a chunk of queries against a long context: block-major token scoring
+    (small("chunk_block_major", seq_len=20000, n_q=300, d_index=64, block=16, top_m=40, top_k=200,
+           n_heads_q=2, n_heads_kv=1), 2),
     # decode with 2048 scored blocks: the one-launch block top-m at its limit (R = 2)
     (small("decode_fused_r2", batch=3, seq_len=32790, n_q=2, d_index=128, block=16, top_m=40, top_k=300,
            n_heads_q=4, n_heads_kv=1), 2),
