@@ -81,8 +81,8 @@ def algorithmic_work(w: Workload) -> dict:
 
 # kernel sources that define each stage's dominant kernel
 STAGE_SOURCES = {
-    "block_summary": ["block_summary.hip", "common.hpp"],
-    "block_topm": ["block_topm.hip", "select.hpp", "common.hpp"],
+    "block_summary": ["block_summary.hip", "summary.hpp", "common.hpp"],
+    "block_topm": ["block_topm.hip", "select.hpp", "summary.hpp", "common.hpp"],
     "token_topk": ["token_topk.hip", "select.hpp", "common.hpp"],
     "sparse_attn": ["sparse_attn.hip", "common.hpp"],
 }
