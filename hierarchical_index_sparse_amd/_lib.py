@@ -27,7 +27,7 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL",
 
 EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_error",
            "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
-           "hsa_sparse_set_stage_events", "hsa_flat_topk")
+           "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step")
 
 
 class HsaSparseShape(ctypes.Structure):
@@ -69,8 +69,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_forward.argtypes = [S, P, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_sparse_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.hsa_flat_topk.argtypes = [S, P, P, P, P, SZ, P]
+    lib.hsa_decode_step.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
-                 "hsa_sparse_set_stage_events", "hsa_flat_topk"):
+                 "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -151,6 +152,17 @@ def hsa_token_topk(shape, qI, kI, blk, tok, workspace=None, stream=None):
                                _ptr(blk, "blk", _I32), _ptr(tok, "tok", _I32), ws.data_ptr(), nbytes,
                                _stream(stream))
     _check(st, "hsa_token_topk")
+
+
+def hsa_decode_step(shape, seq_lens, qI, kI, W, S, Q, K, V, blk_out, tok_out, O, lse, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_FORWARD, workspace, Q.device)
+    st = load().hsa_decode_step(ctypes.byref(shape), _ptr(seq_lens, "seq_lens", _I32), _ptr(qI, "qI", _BF16),
+                                _ptr(kI, "kI", _BF16), _ptr(W, "W", _I8, True), _ptr(S, "S", _BF16),
+                                _ptr(Q, "Q", _BF16), _ptr(K, "K", _BF16), _ptr(V, "V", _BF16),
+                                _ptr(blk_out, "blk_out", _I32, True), _ptr(tok_out, "tok_out", _I32, True),
+                                _ptr(O, "O", _F32), _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes,
+                                _stream(stream))
+    _check(st, "hsa_decode_step")
 
 
 def hsa_flat_topk(shape, qI, kI, tok, workspace=None, stream=None):

@@ -242,6 +242,56 @@ hsa_sparse_status_t hsa_sparse_attn(const hsa_sparse_shape_t* shape, const uint1
   return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_sparse_attn");
 }
 
+// Steps 1-4 on one stream for validated dims (d.lens set for per-sequence
+// lengths).  `who` names the entry point in error messages.
+static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, const uint16_t* qI,
+                                        const uint16_t* kI, const int8_t* landmark_W, int32_t summary_start_block,
+                                        uint16_t* S, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                        int32_t* blk_out, int32_t* tok_out, float* O, float* lse, void* workspace,
+                                        size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!qI || !kI || !S || !Q || !K || !V || !O)
+    return fail(HSA_SPARSE_INVALID_ARG, "qI, kI, S, Q, K, V or O is NULL");
+  const ForwardLayout f = forward_layout(d);
+  if (workspace_bytes < f.total || !workspace)
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "%s needs %zu workspace bytes", who, f.total);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* blk = blk_out ? blk_out : reinterpret_cast<int32_t*>(ws + f.blk_off);
+  int32_t* tok = tok_out ? tok_out : reinterpret_cast<int32_t*>(ws + f.tok_off);
+  void* stage = ws + f.stage_off;
+  const bool rec = g_record_stages;
+  auto hf = [&](hipError_t err, const char* step) {
+    return fail(HSA_SPARSE_HIP_ERROR, "%s (%s): %s", who, step, hipGetErrorString(err));
+  };
+#define HSA_MARK(i)                                                              \
+  if (rec && g_stage_events[i]) {                                               \
+    hipError_t er = hipEventRecord((hipEvent_t)g_stage_events[i], stream);       \
+    if (er != hipSuccess) return hf(er, "stage event");                    \
+  }
+  HSA_MARK(0)
+  // Decode: the only re-summarised block is each query's own, always-kept
+  // block, whose score is never read, so its summary is folded into the
+  // block-score launch instead of preceding it.
+  const bool fold = hsa::block_topm_can_fold(d, summary_start_block);
+  hipError_t e = hipSuccess;
+  if (!fold) e = hsa::launch_block_summary(d, kI, landmark_W, summary_start_block, S, stream);
+  if (e != hipSuccess) return hf(e, "block summary");
+  HSA_MARK(1)
+  const hsa::SummaryFold sf{kI, landmark_W, S, summary_start_block};
+  e = hsa::launch_block_topm(d, qI, S, blk, stage, stream, fold ? &sf : nullptr);
+  if (e != hipSuccess) return hf(e, "block top-m");
+  HSA_MARK(2)
+  e = hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
+  if (e != hipSuccess) return hf(e, "token top-k");
+  HSA_MARK(3)
+  e = hsa::launch_sparse_attn(d, Q, K, V, tok, O, lse, stage, stream);
+  if (e != hipSuccess) return hf(e, "sparse attention");
+  HSA_MARK(4)
+#undef HSA_MARK
+  return HSA_SPARSE_OK;
+}
+
 hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,
                                 const int8_t* landmark_W, int32_t summary_start_block, uint16_t* S,
                                 const uint16_t* Q, const uint16_t* K, const uint16_t* V, int32_t* blk_out,
@@ -251,44 +301,23 @@ hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape, const uint16_t*
   hsa_sparse_status_t st = check_shape(shape, d, kSummary | kSelect | kAttn);
   if (st != HSA_SPARSE_OK) return st;
   if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
-  if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
-  if (empty(d)) return HSA_SPARSE_OK;
-  if (!qI || !kI || !S || !Q || !K || !V || !O)
-    return fail(HSA_SPARSE_INVALID_ARG, "qI, kI, S, Q, K, V or O is NULL");
-  const ForwardLayout f = forward_layout(d);
-  if (workspace_bytes < f.total || !workspace)
-    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "forward needs %zu workspace bytes", f.total);
-  char* ws = static_cast<char*>(workspace);
-  int32_t* blk = blk_out ? blk_out : reinterpret_cast<int32_t*>(ws + f.blk_off);
-  int32_t* tok = tok_out ? tok_out : reinterpret_cast<int32_t*>(ws + f.tok_off);
-  void* stage = ws + f.stage_off;
-  const bool rec = g_record_stages;
-#define HSA_MARK(i)                                                              \
-  if (rec && g_stage_events[i]) {                                               \
-    hipError_t er = hipEventRecord((hipEvent_t)g_stage_events[i], stream);       \
-    if (er != hipSuccess) return hip_fail(er, "hsa_forward (stage event)");      \
-  }
-  HSA_MARK(0)
-  // Decode: the only re-summarised block is each query's own, always-kept
-  // block, whose score is never read, so its summary is folded into the
-  // block-score launch instead of preceding it.
-  const bool fold = hsa::block_topm_can_fold(d, summary_start_block);
-  hipError_t e = hipSuccess;
-  if (!fold) e = hsa::launch_block_summary(d, kI, landmark_W, summary_start_block, S, stream);
-  if (e != hipSuccess) return hip_fail(e, "hsa_forward (block summary)");
-  HSA_MARK(1)
-  const hsa::SummaryFold sf{kI, landmark_W, S, summary_start_block};
-  e = hsa::launch_block_topm(d, qI, S, blk, stage, stream, fold ? &sf : nullptr);
-  if (e != hipSuccess) return hip_fail(e, "hsa_forward (block top-m)");
-  HSA_MARK(2)
-  e = hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
-  if (e != hipSuccess) return hip_fail(e, "hsa_forward (token top-k)");
-  HSA_MARK(3)
-  e = hsa::launch_sparse_attn(d, Q, K, V, tok, O, lse, stage, stream);
-  if (e != hipSuccess) return hip_fail(e, "hsa_forward (sparse attention)");
-  HSA_MARK(4)
-#undef HSA_MARK
-  return HSA_SPARSE_OK;
+  return forward_impl(d, "hsa_forward", qI, kI, landmark_W, summary_start_block, S, Q, K, V, blk_out, tok_out, O,
+                      lse, workspace, workspace_bytes, stream);
+}
+
+hsa_sparse_status_t hsa_decode_step(const hsa_sparse_shape_t* shape, const int32_t* seq_lens, const uint16_t* qI,
+                                    const uint16_t* kI, const int8_t* landmark_W, uint16_t* S, const uint16_t* Q,
+                                    const uint16_t* K, const uint16_t* V, int32_t* blk_out, int32_t* tok_out,
+                                    float* O, float* lse, void* workspace, size_t workspace_bytes,
+                                    hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSummary | kSelect | kAttn);
+  if (st != HSA_SPARSE_OK) return st;
+  if (d.nq != 1 && d.b != 0) return fail(HSA_SPARSE_INVALID_ARG, "hsa_decode_step takes n_q == 1 (got %d)", d.nq);
+  if (!seq_lens && d.b != 0) return fail(HSA_SPARSE_INVALID_ARG, "seq_lens is NULL");
+  d.lens = seq_lens;
+  return forward_impl(d, "hsa_decode_step", qI, kI, landmark_W, 0, S, Q, K, V, blk_out, tok_out, O, lse, workspace,
+                      workspace_bytes, stream);
 }
 
 }  // extern "C"

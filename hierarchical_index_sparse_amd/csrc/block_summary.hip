@@ -17,22 +17,31 @@
 
 namespace hsa {
 
+// Workgroup (x, b) summarises block start + x of sequence b.  With
+// per-sequence lengths, start is the block of sequence b's first new query,
+// (Lb - nq) / B, and blocks at or past ceil(Lb / B) are skipped.
 template <int DI, int NL>
 __global__ __launch_bounds__(256) void k_block_summary(const uint16_t* __restrict__ kI,
                                                        const int8_t* __restrict__ W, uint16_t* __restrict__ S,
-                                                       int L, int B, int nb, int start_block) {
+                                                       int L, int B, int nb, int start_block,
+                                                       const int32_t* __restrict__ lens, int nq) {
   __shared__ float red[NL][256 / (DI / 8)][DI];
-  summarise_block<DI, NL>(kI, W, S, L, B, nb, start_block + blockIdx.x, blockIdx.y, red);
+  const int b = blockIdx.y;
+  const int Lb = seq_len_of(lens, L, b);
+  const int j = (lens ? (Lb - nq) / B : start_block) + (int)blockIdx.x;
+  if (j >= nb || j * B >= Lb) return;  // uniform
+  summarise_block<DI, NL>(kI, W, S, L, Lb, B, nb, j, b, red);
 }
 
 template <int DI>
 static hipError_t launch_di(const Dims& s, const uint16_t* kI, const int8_t* W, int start, uint16_t* S,
                             hipStream_t st) {
-  dim3 grid(s.nb - start, s.b);
+  // blocks the new queries touch: at most ceil(nq / B) + 1 per sequence
+  dim3 grid(s.lens ? (s.nq + s.B - 1) / s.B + 1 : s.nb - start, s.b);
   switch (s.nL) {
-    case 1: hipLaunchKernelGGL((k_block_summary<DI, 1>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start); break;
-    case 2: hipLaunchKernelGGL((k_block_summary<DI, 2>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start); break;
-    case 4: hipLaunchKernelGGL((k_block_summary<DI, 4>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start); break;
+    case 1: hipLaunchKernelGGL((k_block_summary<DI, 1>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
+    case 2: hipLaunchKernelGGL((k_block_summary<DI, 2>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
+    case 4: hipLaunchKernelGGL((k_block_summary<DI, 4>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -40,7 +49,7 @@ static hipError_t launch_di(const Dims& s, const uint16_t* kI, const int8_t* W, 
 
 hipError_t launch_block_summary(const Dims& s, const uint16_t* kI, const int8_t* W, int start_block, uint16_t* S,
                                 hipStream_t st) {
-  if (start_block >= s.nb || s.b == 0) return hipSuccess;
+  if (s.b == 0 || (!s.lens && start_block >= s.nb)) return hipSuccess;
   return s.dI == 64 ? launch_di<64>(s, kI, W, start_block, S, st) : launch_di<128>(s, kI, W, start_block, S, st);
 }
 

@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ S, float* __restrict__ scores,
                                                       int L, int nq, int B, int nb, int m,
                                                       const uint16_t* __restrict__ kI, const int8_t* __restrict__ W,
-                                                      uint16_t* __restrict__ S_out, int sum_start, int batch) {
+                                                      uint16_t* __restrict__ S_out, int sum_start, int batch,
+                                                      const int32_t* __restrict__ lens) {
   constexpr int LPR = DI / 8;     // lanes per summary row
   constexpr int RPL = kWave / LPR;  // rows per wave load
   constexpr int ITER = kScoreBlocksPerWG * NL / (4 * RPL);
@@ -43,15 +44,18 @@ __global__ __launch_bounds__(256) void k_block_scores(const uint16_t* __restrict
 
   if (blockIdx.z == 1) {
     __shared__ float red[NL][256 / LPR][DI];
-    const int jb = sum_start + (int)blockIdx.x;
-    if (jb >= nb || (int)blockIdx.y >= batch) return;  // uniform
-    summarise_block<DI, NL>(kI, W, S_out, L, B, nb, jb, blockIdx.y, red);
+    if ((int)blockIdx.y >= batch) return;  // uniform
+    const int Lb = seq_len_of(lens, L, blockIdx.y);
+    // per-sequence lengths (n_q == 1): the block of the sequence's query
+    const int jb = (lens ? (Lb - 1) / B : sum_start) + (int)blockIdx.x;
+    if (jb >= nb || jb * B >= Lb) return;  // uniform
+    summarise_block<DI, NL>(kI, W, S_out, L, Lb, B, nb, jb, blockIdx.y, red);
     return;
   }
   const int q = blockIdx.y;  // b * nq + i
   if (q >= batch * nq) return;
   const int b = q / nq, i = q % nq;
-  const int t = query_pos(L, nq, i);
+  const int t = query_pos(seq_len_of(lens, L, b), nq, i);
   const int c = t / B;
   if (c + 1 <= m) return;
   const int j0 = max(1, (int)blockIdx.x * kScoreBlocksPerWG);
@@ -167,7 +171,8 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
 template <int NW, int R>
 __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const float* __restrict__ scores,
                                                                           int32_t* __restrict__ blk, int L, int nq,
-                                                                          int B, int nb, int m, int nq_total) {
+                                                                          int B, int nb, int m, int nq_total,
+                                                                          const int32_t* __restrict__ lens) {
   constexpr int QPB = NW == 1 ? 4 : 1;  // queries per workgroup
   constexpr int GT = NW * kWave;        // threads per select group
   __shared__ SelectSmem<NW> lds[QPB];
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
   SelectSmem<NW>& sm = lds[NW == 1 ? wave : 0];
   const int gtid = NW == 1 ? lane_id() : (int)threadIdx.x;
   const int i = q % nq;
-  const int t = query_pos(L, nq, i);
+  const int t = query_pos(seq_len_of(lens, L, q / nq), nq, i);
   const int c = t / B;
   int32_t* out = blk + (size_t)q * m;
   if (c + 1 <= m) {
@@ -218,7 +223,8 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
                                                             const uint16_t* __restrict__ S, int32_t* __restrict__ blk,
                                                             int L, int nq, int B, int nb, int m, int nq_total,
                                                             const uint16_t* __restrict__ kI,
-                                                            uint16_t* __restrict__ S_out, int sum_start, int nsum) {
+                                                            uint16_t* __restrict__ S_out, int sum_start, int nsum,
+                                                            const int32_t* __restrict__ lens) {
   constexpr int LPR = DI / 8;      // lanes per summary row
   constexpr int RPI = 1024 / LPR;  // rows per round of the workgroup
   constexpr int U = 8;             // rounds of loads in flight
@@ -227,13 +233,18 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
   __shared__ float red[1][1024 / LPR][DI];
   if ((int)blockIdx.x >= nq_total) {  // folded summary of a newest block (uniform)
     const int w = (int)blockIdx.x - nq_total;
-    summarise_block<DI, 1, 1024>(kI, nullptr, S_out, L, B, nb, sum_start + w % nsum, w / nsum, red);
+    const int bs = w / nsum;
+    const int Lb = seq_len_of(lens, L, bs);
+    // per-sequence lengths (n_q == 1): the block of the sequence's query
+    const int jb = (lens ? (Lb - 1) / B : sum_start) + w % nsum;
+    if (jb >= nb || jb * B >= Lb) return;
+    summarise_block<DI, 1, 1024>(kI, nullptr, S_out, L, Lb, B, nb, jb, bs, red);
     return;
   }
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const int b = q / nq;
-  const int t = query_pos(L, nq, q % nq);
+  const int t = query_pos(seq_len_of(lens, L, b), nq, q % nq);
   const int c = t / B;
   int32_t* out = blk + (size_t)q * m;
   if (c + 1 <= m) {
@@ -294,7 +305,8 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
 template <int NW, int R>
 static hipError_t launch_select_r(int nq_total, const float* scores, int32_t* blk, const Dims& s, hipStream_t st) {
   dim3 grid(NW == 1 ? (nq_total + 3) / 4 : nq_total), block(NW == 1 ? 256 : NW * 64);
-  hipLaunchKernelGGL((k_block_select<NW, R>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m, nq_total);
+  hipLaunchKernelGGL((k_block_select<NW, R>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m, nq_total,
+                     s.lens);
   return hipGetLastError();
 }
 
@@ -325,7 +337,10 @@ static int pick_r(int n, int nw) {
 bool block_topm_can_fold(const Dims& s, int start_block) {
   const int c_max = (s.L - 1) / s.B;
   // the GEMV kernel runs (few queries, some query scores blocks) and no
-  // query scores a block >= start_block (the highest scored is c_max - 1)
+  // query scores a block >= start_block (the highest scored is c_max - 1);
+  // with per-sequence lengths (one query each) the re-summarised block is
+  // always the query's own, never scored
+  if (s.lens) return s.nq == 1 && c_max + 1 > s.m;
   return s.nq < 64 && c_max + 1 > s.m && start_block >= c_max && start_block < s.nb;
 }
 
@@ -352,7 +367,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   } else if (c_max + 1 > s.m && s.nL == 1 && n_max <= kFusedMaxBlocks && nq_total < 512) {
-    const int nsum = fold ? s.nb - fold->start_block : 0;
+    const int nsum = fold ? (s.lens ? 1 : s.nb - fold->start_block) : 0;
     dim3 grid(nq_total + (fold ? s.b * nsum : 0));
     const uint16_t* kI = fold ? fold->kI : nullptr;
     uint16_t* S_out = fold ? fold->S : nullptr;
@@ -360,7 +375,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     const int ns = max(nsum, 1);
 #define HSA_FD(DI, RR)                                                                                             \
   hipLaunchKernelGGL((k_block_topm_decode<DI, RR>), grid, dim3(1024), 0, st, qI, S, blk, s.L, s.nq, s.B, s.nb, s.m, \
-                     nq_total, kI, S_out, start, ns)
+                     nq_total, kI, S_out, start, ns, s.lens)
     if (s.dI == 64) {
       if (n_max <= 1024) HSA_FD(64, 1); else HSA_FD(64, 2);
     } else {
@@ -370,7 +385,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     return hipGetLastError();
   } else if (c_max + 1 > s.m) {
     const int xs = (c_max + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG;
-    const int nsum = fold ? s.nb - fold->start_block : 0;
+    const int nsum = fold ? (s.lens ? 1 : s.nb - fold->start_block) : 0;
     dim3 grid(max(xs, nsum), max(nq_total, fold ? s.b : 0), fold ? 2 : 1);
     const uint16_t* kI = fold ? fold->kI : nullptr;
     const int8_t* W = fold ? fold->W : nullptr;
@@ -378,7 +393,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     const int start = fold ? fold->start_block : s.nb;
 #define HSA_SC(DI, NL)                                                                                          \
   hipLaunchKernelGGL((k_block_scores<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, s.nb, s.m, \
-                     kI, W, S_out, start, s.b)
+                     kI, W, S_out, start, s.b, s.lens)
     if (s.dI == 64) {
       if (s.nL == 1) HSA_SC(64, 1); else if (s.nL == 2) HSA_SC(64, 2); else HSA_SC(64, 4);
     } else {

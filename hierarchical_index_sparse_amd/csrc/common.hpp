@@ -112,4 +112,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // Query position t of query i (queries are the last n_q tokens).
 __device__ __forceinline__ int query_pos(int L, int nq, int i) { return L - nq + i; }
 
+// Current length of sequence b: lens[b] for a batch of different lengths
+// (clamped to [1, L], so a bad value cannot address past the cache), else L.
+// L stays the row stride of the per-sequence arrays either way.
+__device__ __forceinline__ int seq_len_of(const int32_t* __restrict__ lens, int L, int b) {
+  return lens ? min(max(lens[b], 1), L) : L;
+}
+
 }  // namespace hsa

@@ -14,6 +14,10 @@ struct Dims {
   int b, L, nq, dI, B, nL, m, k, Hq, Hkv, d;
   float scale;
   int nb;  // ceil(L / B)
+  // device [b]: current length of each sequence (decode over a batch of
+  // different lengths, n_q == 1); nullptr: every sequence has length L.
+  // L stays the capacity and row stride.
+  const int32_t* lens = nullptr;
 };
 
 // step 1

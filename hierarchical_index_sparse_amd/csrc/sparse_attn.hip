@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                                      const uint16_t* __restrict__ V, const int32_t* __restrict__ tok,
                                                      float* __restrict__ O, float* __restrict__ lse,
                                                      float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
-                                                     int chunk, int nsplit, float scale_log2, int n_items) {
+                                                     int chunk, int nsplit, float scale_log2, int n_items,
+                                                     const int32_t* __restrict__ lens) {
   __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * 2 * kStageBytes];
   const int wave = threadIdx.x / kWave;
   const int item = blockIdx.x * 4 + wave;
@@ -105,9 +106,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 
   // byte offset of list entry `pos`'s row if it is a valid token of this
   // sequence, else -1
+  const int Lb = seq_len_of(lens, L, b);  // entries at or past the sequence's length are skipped
   auto entry = [&](int pos) {
     const int v = pos < end ? tl[pos] : -1;
-    return (v >= 0 && v < L) ? (int)__umul24((unsigned)v, (unsigned)row_bytes) : -1;
+    return (v >= 0 && v < Lb) ? (int)__umul24((unsigned)v, (unsigned)row_bytes) : -1;
   };
   // Coalesced gather of one tile's 32 K rows and 32 V rows: instruction i
   // reads rows 4i .. 4i+3, 16 lanes (16 bytes each) per 256-byte row.
@@ -359,12 +361,12 @@ hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* 
   dim3 grid((n_items + 3) / 4), block(256);
   if (nsplit == 1) {
     hipLaunchKernelGGL((k_sparse_attn<false>), grid, block, 0, st, Q, K, V, tok, O, lse, nullptr, s.L, s.nq, s.Hq,
-                       s.Hkv, s.k, chunk, nsplit, scale_log2, n_items);
+                       s.Hkv, s.k, chunk, nsplit, scale_log2, n_items, s.lens);
     return hipGetLastError();
   }
   float* part = static_cast<float*>(ws);
   hipLaunchKernelGGL((k_sparse_attn<true>), grid, block, 0, st, Q, K, V, tok, O, lse, part, s.L, s.nq, s.Hq, s.Hkv,
-                     s.k, chunk, nsplit, scale_log2, n_items);
+                     s.k, chunk, nsplit, scale_log2, n_items, s.lens);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(nq_total * s.Hq)), dim3(256), 0, st, part, O, lse, s.Hq, s.Hkv,

@@ -14,9 +14,11 @@
 namespace hsa {
 
 // Called by all NTH threads of a workgroup; red is the workgroup's LDS.
+// L is the row stride of kI per sequence, Lb the sequence's length (rows
+// at or past Lb count as zero).
 template <int DI, int NL, int NTH = 256>
 __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI, const int8_t* __restrict__ W,
-                                                uint16_t* __restrict__ S, int L, int B, int nb, int j, int b,
+                                                uint16_t* __restrict__ S, int L, int Lb, int B, int nb, int j, int b,
                                                 float (&red)[NL][NTH / (DI / 8)][DI]) {
   constexpr int LPR = DI / 8;     // lanes per row
   constexpr int RPI = NTH / LPR;  // rows per iteration of the workgroup
@@ -33,7 +35,7 @@ __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI,
   const size_t seq_base = (size_t)b * L;
   for (int r = r0; r < B; r += RPI) {
     const int s = j * B + r;
-    if (s >= L) break;
+    if (s >= Lb) break;
     const u32x4 v = *reinterpret_cast<const u32x4*>(kI + (seq_base + s) * DI + col8 * 8);
     float x[8];
 #pragma unroll

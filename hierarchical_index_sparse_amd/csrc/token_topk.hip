@@ -36,14 +36,15 @@ template <int DI>
 __global__ __launch_bounds__(256) void k_token_scores(const uint16_t* __restrict__ qI,
                                                       const uint16_t* __restrict__ kI,
                                                       const int32_t* __restrict__ blk, float* __restrict__ scores,
-                                                      int L, int nq, int B, int m, int k) {
+                                                      int L, int nq, int B, int m, int k,
+                                                      const int32_t* __restrict__ lens) {
   constexpr int LPR = DI / 8;
   constexpr int RPI = 256 / LPR;  // rows per workgroup iteration
   constexpr int NIT = 128 / RPI;  // iterations for the largest block (B = 128)
   const int p = blockIdx.x;
   const int q = blockIdx.y;
   const int b = q / nq, i = q % nq;
-  const int t = query_pos(L, nq, i);
+  const int t = query_pos(seq_len_of(lens, L, b), nq, i);
   int c, n_sel, n_valid;
   candidate_count(t, B, m, c, n_sel, n_valid);
   if (n_valid <= k || p >= n_sel) return;
@@ -490,7 +491,8 @@ static inline size_t tsel_lds_bytes(int m, int k) {
 template <int NW, int R, bool STAGED, bool ONEBLK>
 __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ blk, int32_t* __restrict__ tok,
-                                                          int L, int nq, int B, int log2B, int m, int k) {
+                                                          int L, int nq, int B, int log2B, int m, int k,
+                                                          const int32_t* __restrict__ lens) {
   constexpr int NT = NW * 64;
   __shared__ SelectSmem<NW> lds;
   extern __shared__ int dyn_lds[];
@@ -498,7 +500,7 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   int* stage = dyn_lds + ((m + 3) & ~3);
   const int q = blockIdx.x;
   const int i = q % nq;
-  const int t = query_pos(L, nq, i);
+  const int t = query_pos(seq_len_of(lens, L, q / nq), nq, i);
   int c, n_sel, n_valid;
   candidate_count(t, B, m, c, n_sel, n_valid);
   int32_t* out = tok + (size_t)q * k;
@@ -603,7 +605,7 @@ template <int NW, int R, bool STAGED, bool ONEBLK>
 static void launch_tsel_k(const Dims& s, size_t dyn, int log2B, const float* sc, const int32_t* blk, int32_t* tok,
                           hipStream_t st) {
   hipLaunchKernelGGL((k_token_select<NW, R, STAGED, ONEBLK>), dim3(s.b * s.nq), dim3(NW * 64), dyn, st, sc, blk, tok,
-                     s.L, s.nq, s.B, log2B, s.m, s.k);
+                     s.L, s.nq, s.B, log2B, s.m, s.k, s.lens);
 }
 
 // Variants: a thread's slots span several blocks only when R > B (R > 8,
@@ -737,10 +739,10 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
       dim3 grid(s.m, nq_total);
       if (s.dI == 64)
         hipLaunchKernelGGL((k_token_scores<64>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
-                           s.k);
+                           s.k, s.lens);
       else
         hipLaunchKernelGGL((k_token_scores<128>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
-                           s.k);
+                           s.k, s.lens);
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

@@ -190,6 +190,37 @@ hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape,
                                 hsa_sparse_stream_t stream);
 
 /*
+ * One decode step over a batch of sequences of different lengths (HISA
+ * page: the drop-in indexer leaves the KV cache and the attention as they
+ * are, and decode is where its per-token cost matters; the summary of the
+ * partial last block is kept up to date as tokens are appended).
+ *   shape      seq_len is the capacity: the row stride of kI, K and V per
+ *              sequence and ceil(seq_len / block) summary blocks per
+ *              sequence in S; n_q must be 1.
+ *   seq_lens   device int32 [batch]: the current length L_b of sequence b,
+ *              1 <= L_b <= seq_len (values outside are clamped).  The
+ *              caller has written the new token's rows kI, K, V at L_b - 1.
+ *   qI, Q      the new token of each sequence ([batch, 1, ...]).
+ *   S          in-out summary state: on entry it must hold the summaries of
+ *              the blocks before each sequence's last block (from earlier
+ *              steps or hsa_block_summary); this call recomputes block
+ *              (L_b - 1) / block of every sequence from its rows < L_b.
+ *   The rest, and the results (for the query at t = L_b - 1, candidates
+ *   limited to s <= t), are as for hsa_forward.  Workspace:
+ *   hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_FORWARD).
+ * Errors: as for hsa_forward; n_q != 1 or seq_lens == NULL is INVALID_ARG.
+ */
+hsa_sparse_status_t hsa_decode_step(const hsa_sparse_shape_t* shape,
+                                    const int32_t* seq_lens,
+                                    const uint16_t* qI, const uint16_t* kI,
+                                    const int8_t* landmark_W, uint16_t* S,
+                                    const uint16_t* Q, const uint16_t* K,
+                                    const uint16_t* V, int32_t* blk_out,
+                                    int32_t* tok_out, float* O, float* lse,
+                                    void* workspace, size_t workspace_bytes,
+                                    hsa_sparse_stream_t stream);
+
+/*
  * The flat indexer, the method the hierarchical one replaces (HISA page:
  * the indexer scores each query against every previous token and keeps
  * the most relevant; with every block kept the hierarchical selection

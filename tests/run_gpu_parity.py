@@ -2,7 +2,7 @@
 
     python3 tests/run_gpu_parity.py [name-substring ...]
 
-Calls the same test functions of test_gpu_parity.py and test_gpu_flat.py
+Calls the same test functions of every tests/test_gpu_*.py module
 (parametrised cases expanded) in one plain
 Python process, prints PASS/FAIL per case as it ends, stops at the first
 failure and exits non-zero on it.  Full-size workloads run last.
@@ -22,10 +22,11 @@ import torch  # noqa: E402
 torch.zeros(1, device="cuda")
 torch.cuda.synchronize()
 
-import test_gpu_flat  # noqa: E402
-import test_gpu_parity  # noqa: E402
+import importlib  # noqa: E402
+import glob  # noqa: E402
 
-MODULES = (test_gpu_parity, test_gpu_flat)
+MODULES = [importlib.import_module(os.path.basename(f)[:-3])
+           for f in sorted(glob.glob(os.path.join(HERE, "test_gpu_*.py")))]
 
 
 def cases():

@@ -185,3 +185,17 @@ def test_flat_workspace(lib):
     assert call_flat(lib, s, ws_bytes=need - 1) == 3
     assert lib.hsa_sparse_workspace_size(ctypes.byref(shape(top_k=5000)), _lib.HSA_SPARSE_OP_FLAT_TOPK) == 0
     assert lib.hsa_flat_topk(ctypes.byref(shape(batch=0)), None, None, None, None, 0, None) == 0
+
+
+def test_decode_step_validation(lib):
+    def call(s, lens=FAKE):
+        return lib.hsa_decode_step(ctypes.byref(s), lens, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                                   None, FAKE, 1 << 40, None)
+    assert call(shape(n_q=2)) == 1          # one new query per sequence
+    assert call(shape(n_q=1), lens=None) == 1
+    assert call(shape(n_q=1, head_dim=64)) == 2
+    assert call(shape(batch=0, n_q=1), lens=None) == 0
+    s = shape(n_q=1)
+    need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FORWARD)
+    assert lib.hsa_decode_step(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
+                               None, FAKE, need - 1, None) == 3
