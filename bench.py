@@ -42,9 +42,12 @@ STAGES = ("block_summary", "block_topm", "token_topk", "sparse_attn")
 # --------------------------------------------------------------- work model
 
 
-def per_query_counts(w: Workload):
-    """Closed-form per-query sizes: scored blocks, candidate tokens, kept tokens."""
-    t = w.seq_len - w.n_q + np.arange(w.n_q, dtype=np.int64)
+def per_query_counts(w: Workload, t=None):
+    """Closed-form per-query sizes: scored blocks, candidate tokens, kept tokens
+    (queries at positions t; by default the last n_q positions)."""
+    if t is None:
+        t = w.seq_len - w.n_q + np.arange(w.n_q, dtype=np.int64)
+    t = np.asarray(t, dtype=np.int64)
     c = t // w.block
     scored_blocks = np.where(c + 1 <= w.top_m, 0, c - 1)
     n_sel = np.minimum(c + 1, w.top_m)
@@ -54,24 +57,33 @@ def per_query_counts(w: Workload):
     return scored_blocks, scored_tokens, kept
 
 
-def algorithmic_work(w: Workload) -> dict:
-    """Bytes each step must move (and flops it must do), per stage."""
-    sb, st, kept = per_query_counts(w)
+def algorithmic_work(w: Workload, lens=None) -> dict:
+    """Bytes each step must move (and flops it must do), per stage.  With
+    per-sequence lengths (one query each) every sequence counts at its own
+    length and re-summarises its own last block."""
     b, nq = w.batch, w.n_q
     dI, nL, d = w.d_index, w.n_landmarks, w.head_dim
-    start = (w.seq_len - nq) // w.block
-    summ_rows = min(w.seq_len, w.n_blocks * w.block) - start * w.block
-    summ_bytes = b * summ_rows * dI * 2 + b * (w.n_blocks - start) * nL * dI * 2
-    topm_flops = 2.0 * dI * nL * b * sb.sum()
-    topm_bytes = b * (nq * dI * 2 + sb.sum() * nL * dI * 2 + nq * w.top_m * 4)
-    topk_bytes = b * (st.sum() * dI * 2 + nq * w.top_k * 4 + nq * w.top_m * 4)
-    attn_bytes = b * (kept.sum() * w.n_heads_kv * d * 2 * 2 + nq * w.n_heads_q * d * (2 + 4)
-                      + nq * w.top_k * 4)
-    attn_flops = 4.0 * d * w.n_heads_q * b * kept.sum()
+    if lens is None:
+        sb, st, kept = (x * b for x in per_query_counts(w))
+        start = (w.seq_len - nq) // w.block
+        summ_rows = b * (min(w.seq_len, w.n_blocks * w.block) - start * w.block)
+        summ_blocks = b * (w.n_blocks - start)
+    else:
+        t = np.asarray(lens, dtype=np.int64) - 1
+        sb, st, kept = per_query_counts(w, t)
+        summ_rows = int((t + 1 - (t // w.block) * w.block).sum())
+        summ_blocks = b
+    summ_bytes = summ_rows * dI * 2 + summ_blocks * nL * dI * 2
+    topm_flops = 2.0 * dI * nL * sb.sum()
+    topm_bytes = b * nq * dI * 2 + sb.sum() * nL * dI * 2 + b * nq * w.top_m * 4
+    topk_bytes = st.sum() * dI * 2 + b * nq * w.top_k * 4 + b * nq * w.top_m * 4
+    attn_bytes = (kept.sum() * w.n_heads_kv * d * 2 * 2 + b * nq * w.n_heads_q * d * (2 + 4)
+                  + b * nq * w.top_k * 4)
+    attn_flops = 4.0 * d * w.n_heads_q * kept.sum()
     return {
         "block_summary": {"bytes": float(summ_bytes), "flops": 0.0},
         "block_topm": {"bytes": float(topm_bytes), "flops": float(topm_flops)},
-        "token_topk": {"bytes": float(topk_bytes), "flops": float(2.0 * dI * b * st.sum())},
+        "token_topk": {"bytes": float(topk_bytes), "flops": float(2.0 * dI * st.sum())},
         "sparse_attn": {"bytes": float(attn_bytes), "flops": float(attn_flops)},
     }
 
@@ -138,7 +150,9 @@ def _oracle_one(args):
     from oracle import hisa_oracle as orc
     b, i = args
     w, inp, S = _ORC_STATE["w"], _ORC_STATE["inp"], _ORC_STATE["S"]
-    orc.forward_query(inp, b, i, w.query_pos(i), w.block, w.top_m, w.top_k, w.scale, S_bits=S[b])
+    lens = inp.get("seq_lens")
+    t = w.query_pos(i) if lens is None else int(lens[b]) - 1
+    orc.forward_query(inp, b, i, t, w.block, w.top_m, w.top_k, w.scale, S_bits=S[b])
     return 1
 
 
@@ -150,7 +164,9 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     cores = max(1, min(cores, 16))
     t0 = time.perf_counter()
-    S = [orc.block_summary(inp["kI"][b], w.block, inp.get("W")) for b in range(w.batch)]
+    lens = inp.get("seq_lens")
+    S = [orc.block_summary(inp["kI"][b] if lens is None else inp["kI"][b, :int(lens[b])], w.block, inp.get("W"))
+         for b in range(w.batch)]
     t_summary = time.perf_counter() - t0
     total = w.batch * w.n_q
     n = min(sample, total)
@@ -284,9 +300,15 @@ def main():
     start_block = (w.seq_len - w.n_q) // w.block
     _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), 0, out["S"])
 
+    lens = inp.get("seq_lens")
+
     def step():
-        _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), start_block, out["S"], dev["Q"], dev["K"],
-                         dev["V"], None, None, out["O"], out["lse"], ws)
+        if lens is None:
+            _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), start_block, out["S"], dev["Q"], dev["K"],
+                             dev["V"], None, None, out["O"], out["lse"], ws)
+        else:  # one decode step over sequences of different lengths
+            _lib.hsa_decode_step(shape, dev["seq_lens"], dev["qI"], dev["kI"], dev.get("W"), out["S"], dev["Q"],
+                                 dev["K"], dev["V"], None, None, out["O"], out["lse"], ws)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -339,13 +361,14 @@ def main():
         hip.destroy(a)
         hip.destroy(b)
 
-    flat = None if args.no_flat else flat_comparison(w, dev, shape, stage_ms, args.steps, hip)
+    # the flat indexer takes one length for the batch
+    flat = None if (args.no_flat or lens is not None) else flat_comparison(w, dev, shape, stage_ms, args.steps, hip)
 
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     queries = w.batch * w.n_q
     value = queries / (ms_per_step / 1000.0)
 
-    work = algorithmic_work(w)
+    work = algorithmic_work(w, lens)
     dom_s = dom_ms / 1000.0
     if dom == "block_topm":
         achieved = work[dom]["flops"] / dom_s / 1e12
@@ -373,7 +396,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16 in, fp32 accumulate",
         "data": "synthetic (seeded; integer-valued bf16 indexer vectors, N(0,1) bf16 Q/K/V)",
-        "config": {"workload": w.name, "summary_start_block": start_block, "batch": w.batch, "seq_len": w.seq_len, "n_q": w.n_q,
+        "config": {"workload": w.name,
+                   "summary_start_block": start_block if lens is None else "each sequence's last block",
+                   "seq_lens": None if lens is None else f"uniform in [{w.varlen_min}, {w.seq_len}], "
+                                                         f"mean {float(np.mean(lens)):.0f} (seeded)",
+                   "batch": w.batch, "seq_len": w.seq_len, "n_q": w.n_q,
                    "d_index": w.d_index, "block": w.block, "top_m": w.top_m, "top_k": w.top_k,
                    "heads_q": w.n_heads_q, "heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
                    "n_landmarks": w.n_landmarks, "parallelism": "single GPU"},

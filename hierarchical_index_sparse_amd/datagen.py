@@ -28,7 +28,7 @@ import torch
 from .workloads import Workload
 
 _TID = {"qI": 1, "kI_centre": 2, "kI_noise": 3, "Q": 4, "K": 5, "V": 6, "W": 7,
-        "needles": 8}
+        "needles": 8, "seq_lens": 9}
 _CHUNK = 1 << 22  # elements per independent stream chunk
 
 
@@ -140,12 +140,21 @@ def gen_landmark_projection(w: Workload) -> np.ndarray | None:
     return g.integers(0, 2, size=(w.n_landmarks, w.block), dtype=np.int8)
 
 
+def gen_seq_lens(w: Workload) -> np.ndarray | None:
+    """Current length of each sequence, uniform in [varlen_min, seq_len], for
+    workloads of different lengths (decode); None when all are seq_len."""
+    if not w.varlen_min:
+        return None
+    g = _rng(w.seed, "seq_lens", 0)
+    return g.integers(w.varlen_min, w.seq_len + 1, size=w.batch).astype(np.int32)
+
+
 def make_inputs(w: Workload, attention: bool = True, **kw) -> dict[str, np.ndarray]:
     """All inputs of one workload as host arrays (bf16 as uint16 bits)."""
     q_range = kw.pop("q_range", 8)
     qI = gen_index_queries(w, q_range=q_range)
     kI, needles = gen_index_keys(w, qI, q_range=q_range, **kw)
-    res = {"qI": qI, "kI": kI, "needles": needles, "W": gen_landmark_projection(w)}
+    res = {"qI": qI, "kI": kI, "needles": needles, "W": gen_landmark_projection(w), "seq_lens": gen_seq_lens(w)}
     if attention:
         res.update(gen_attention_inputs(w))
     return res

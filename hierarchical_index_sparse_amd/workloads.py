@@ -31,6 +31,9 @@ class Workload:
     head_dim: int = 128
     n_landmarks: int = 1
     needles: int = 0
+    # > 0: decode over sequences of different lengths, uniform in
+    # [varlen_min, seq_len] (seq_len is then the cache capacity; n_q == 1)
+    varlen_min: int = 0
     seed: int = 0
     description: str = ""
 
@@ -74,6 +77,10 @@ WORKLOADS = {
         name="decode_512k", batch=4, seq_len=524288, n_q=1, d_index=128,
         block=128, top_m=128, top_k=4096, n_heads_q=32, n_heads_kv=2,
         description="decode, batch 4, L=524288"),
+    "decode_varlen_128k": Workload(
+        name="decode_varlen_128k", batch=32, seq_len=131072, n_q=1, d_index=128,
+        block=128, top_m=64, top_k=2048, n_heads_q=16, n_heads_kv=1, varlen_min=65536,
+        description="decode, batch 32, cache capacity 131072, lengths uniform in [65536, 131072]"),
     "landmark_decode_1m": Workload(
         name="landmark_decode_1m", batch=2, seq_len=1048576, n_q=1, d_index=128,
         block=128, top_m=256, top_k=256 * 128, n_heads_q=16, n_heads_kv=1,

@@ -109,3 +109,28 @@ def test_decode_step_equals_forward_at_full_length():
     got = run_step(w, dev, c, [w.seq_len] * w.batch)
     for key in ("S", "blk", "tok", "O", "lse"):
         assert np.array_equal(got[key], ref[key], equal_nan=True), key
+
+
+def test_decode_varlen_128k_sampled():
+    # the bench configuration: batch 32, capacity 131072, seeded lengths in
+    # [65536, 131072]; every list checked for invariants, 6 sequences against
+    # the oracle
+    from hierarchical_index_sparse_amd.workloads import WORKLOADS
+    w = WORKLOADS["decode_varlen_128k"]
+    inp = datagen.make_inputs(w)
+    lens = [int(x) for x in inp["seq_lens"]]
+    dev = pipeline.to_device(inp)
+    out = pipeline.alloc_outputs(w)
+    _lib.hsa_block_summary(_lib.shape_of(w), dev["kI"], None, 0, out["S"])
+    gpu = run_step(w, dev, out, lens)
+    for b, Lb in enumerate(lens):
+        c = (Lb - 1) // w.block
+        blk = gpu["blk"][b, 0]
+        assert blk[0] == 0 and blk[-1] == c and np.all(np.diff(blk) > 0), b
+        tok = gpu["tok"][b, 0]
+        assert np.all(np.diff(tok) > 0) and tok[-1] <= Lb - 1 and set(tok // w.block) <= set(blk.tolist()), b
+    picks = sorted({0, w.batch - 1, int(np.argmin(lens)), int(np.argmax(lens)), 7, 19})
+    sub = {"S": gpu["S"][picks], "blk": gpu["blk"][picks], "tok": gpu["tok"][picks], "O": gpu["O"][picks],
+           "lse": gpu["lse"][picks]}
+    sub_inp = {k: (v[picks] if isinstance(v, np.ndarray) and v.ndim >= 2 else v) for k, v in inp.items()}
+    check_step(w.with_(batch=len(picks)), sub_inp, sub, [lens[b] for b in picks])
