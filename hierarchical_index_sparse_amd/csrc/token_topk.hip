@@ -169,7 +169,8 @@ __host__ __device__ inline TiledLayout tiled_layout(int nJ, int QW, int m, int D
 template <int DI, int QW>
 __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_token_scores_tiled(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI, const int32_t* __restrict__ blk,
-    float* __restrict__ scores, int L, int nq, int B, int m, int k, int tiles_per_seq, int n_tiles, int nJ_max) {
+    float* __restrict__ scores, int L, int nq, int B, int m, int k, int tiles_per_seq, int n_tiles, int nJ_max,
+    int parts) {
   constexpr int QT = 64 * QW;
   constexpr int KS = DI / 32;
   constexpr int NT = kTiledWaves * 64;
@@ -183,7 +184,10 @@ __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_e
   uint16_t* qtile = reinterpret_cast<uint16_t*>(smem + lay.qtile);
   int* scan = reinterpret_cast<int*>(smem + lay.scan);
 
-  const int tile = n_tiles - 1 - (int)blockIdx.x;  // longest tiles first
+  // `parts` workgroups share a tile, each scoring every parts-th union block
+  // (the union grows with the tile's position; late tiles hold every block)
+  const int tile = n_tiles - 1 - (int)blockIdx.x / parts;  // longest tiles first
+  const int part = (int)blockIdx.x % parts;
   const int b = tile / tiles_per_seq;
   const int i0 = (tile % tiles_per_seq) * QT;
   const int nqt = min(nq - i0, QT);
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_e
   uint16_t* sq = reinterpret_cast<uint16_t*>(smem + lay.wscratch) + (size_t)wave * 2 * QT;
   uint16_t* sp = sq + QT;
   const int n_mt = B / 16;
-  for (int u = wave; u < nU; u += kTiledWaves) {
+  for (int u = part * kTiledWaves + wave; u < nU; u += parts * kTiledWaves) {
     const int j = ulist[u];
     const int off = uoff[u];
     int pc = 0;
@@ -675,15 +679,13 @@ static hipError_t launch_tiled_t(const Dims& s, const uint16_t* qI, const uint16
   const int tiles_per_seq = (s.nq + QT - 1) / QT;
   const int n_tiles = tiles_per_seq * s.b;
   const size_t lds = tiled_layout(s.nb, QW, s.m, DI).total;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_token_scores_tiled<DI, QW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL((k_token_scores_tiled<DI, QW>), dim3(n_tiles), dim3(kTiledWaves * 64), lds, st, qI, kI, blk,
-                     scores, s.L, s.nq, s.B, s.m, s.k, tiles_per_seq, n_tiles, s.nb);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_token_scores_tiled<DI, QW>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  if (e != hipSuccess) return e;
+  // about two workgroups per CU in total, at most 4 per tile
+  const int parts = std::max(1, std::min(4, (512 + n_tiles - 1) / n_tiles));
+  hipLaunchKernelGGL((k_token_scores_tiled<DI, QW>), dim3(n_tiles * parts), dim3(kTiledWaves * 64), lds, st, qI, kI,
+                     blk, scores, s.L, s.nq, s.B, s.m, s.k, tiles_per_seq, n_tiles, s.nb, parts);
   return hipGetLastError();
 }
 
