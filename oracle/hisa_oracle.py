@@ -137,6 +137,63 @@ def select_blocks(q_bits: np.ndarray, S_bits: np.ndarray, t: int, block: int, m:
 
 
 # ---------------------------------------------------------------------------
+# a third, coarser level: super-blocks of G blocks  [LSA page, latent space
+# and hierarchical clustering: the query walks a tree from the root and
+# scores only a few nodes per level; here the tree is fixed, contiguous
+# runs of blocks, not learned]
+# ---------------------------------------------------------------------------
+
+
+def super_summary(S_bits: np.ndarray, group: int) -> np.ndarray:
+    """Summaries of super-blocks of `group` consecutive blocks.
+
+    Reading: a super-block summary is the mean of its blocks' summaries
+    (landmark by landmark), summed exactly and rounded once to bf16; missing
+    blocks past the end count as zero and the divisor is always `group`,
+    like the token rule of block_summary.  S_bits [nb, nL, d] ->
+    [ceil(nb / group), nL, d].
+    """
+    nb, nL, d = S_bits.shape
+    nsb = (nb + group - 1) // group
+    x = np.zeros((nsb * group, nL, d), np.float64)
+    x[:nb] = bf16_to_f64(S_bits)
+    x = x.reshape(nsb, group, nL, d)
+    out = np.empty((nsb, nL, d), np.uint16)
+    for J in range(nsb):
+        out[J] = f64_to_bf16_rne(x[J].sum(axis=0) / group)
+    return out
+
+
+def select_blocks_3level(q_bits: np.ndarray, S_bits: np.ndarray, S2_bits: np.ndarray, t: int, block: int,
+                         group: int, m2: int, m: int) -> np.ndarray:
+    """Kept blocks of the query at position t through a super-block level.
+
+    Reading: the super-blocks are selected exactly like blocks (select_blocks
+    at super-block size block * group with m2 kept, the first and the
+    query's own super-block forced); the candidate blocks are the blocks
+    j <= c = t // block inside the kept super-blocks; all of them are kept if
+    they number at most m, else blocks 0 and c plus the best m - 2 of the
+    other candidates by block score (ties to the lower index).  Ascending,
+    padded with -1 to m.
+    """
+    assert m >= 2 and m2 >= 2
+    c = t // block
+    sup = select_blocks(q_bits, S2_bits, t, block * group, m2)
+    sup = sup[sup >= 0]
+    cand = (sup[:, None] * group + np.arange(group)[None, :]).reshape(-1)
+    cand = cand[cand <= c]
+    out = np.full(m, -1, np.int32)
+    if cand.size <= m:
+        out[:cand.size] = cand
+        return out
+    scores = block_scores(q_bits, S_bits, c)
+    mid = cand[(cand != 0) & (cand != c)]
+    kept = top_by_score(scores[mid], mid, m - 2)
+    out[:] = np.sort(np.concatenate([[0, c], kept]))
+    return out
+
+
+# ---------------------------------------------------------------------------
 # step 3: token scores and token selection  [HISA step two]
 # ---------------------------------------------------------------------------
 
@@ -209,6 +266,18 @@ def sparse_attention(Q_bits: np.ndarray, K_bits: np.ndarray, V_bits: np.ndarray,
 # ---------------------------------------------------------------------------
 # the whole path for one query
 # ---------------------------------------------------------------------------
+
+
+def forward_query_3level(seq: dict, b: int, i: int, t: int, block: int, group: int, m2: int, m: int, k: int,
+                         scale: float, S_bits: np.ndarray, S2_bits: np.ndarray, attention: bool = True) -> dict:
+    """forward_query with the block list chosen through super-blocks."""
+    q = seq["qI"][b, i]
+    blk = select_blocks_3level(q, S_bits, S2_bits, t, block, group, m2, m)
+    tok = select_tokens(q, seq["kI"][b], blk, t, block, k)
+    res = {"blk": blk, "tok": tok}
+    if attention:
+        res["O"], res["lse"] = sparse_attention(seq["Q"][b, i], seq["K"][b], seq["V"][b], tok, scale)
+    return res
 
 
 def forward_query(seq: dict, b: int, i: int, t: int, block: int, m: int, k: int,
