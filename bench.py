@@ -2,8 +2,10 @@
 """Throughput of hierarchical block-then-token sparse attention on one GPU.
 
 One step = one hsa_forward call over the workload's whole batch: block
-summaries of every block, block top-m, token top-k and sparse attention,
-with inputs already resident in HBM.  Prints one JSON line.
+summaries of the blocks the queries touch, block top-m, token top-k and
+sparse attention, with inputs already resident in HBM (hsa_decode_step for
+sequences of different lengths, hsa_forward_3level for workloads with
+super-blocks).  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
@@ -42,15 +44,33 @@ STAGES = ("block_summary", "block_topm", "token_topk", "sparse_attn")
 # --------------------------------------------------------------- work model
 
 
+def level1_counts(w: Workload, t):
+    """Three-level selection: super-blocks scored at level 1 and candidate
+    blocks scored at level 2 per query at position t."""
+    c = t // w.block
+    C = c // w.group
+    scored_super = np.where(C + 1 <= w.top_m2, 0, C - 1)
+    n_cand = (np.minimum(C + 1, w.top_m2) - 1) * w.group + (c - C * w.group) + 1
+    scored_blocks = np.where(n_cand <= w.top_m, 0, n_cand)
+    return scored_super, scored_blocks
+
+
 def per_query_counts(w: Workload, t=None):
     """Closed-form per-query sizes: scored blocks, candidate tokens, kept tokens
-    (queries at positions t; by default the last n_q positions)."""
+    (queries at positions t; by default the last n_q positions).  With
+    super-blocks the scored "blocks" are the level-1 super-blocks plus the
+    level-2 candidate blocks."""
     if t is None:
         t = w.seq_len - w.n_q + np.arange(w.n_q, dtype=np.int64)
     t = np.asarray(t, dtype=np.int64)
     c = t // w.block
-    scored_blocks = np.where(c + 1 <= w.top_m, 0, c - 1)
-    n_sel = np.minimum(c + 1, w.top_m)
+    if w.group:
+        scored_blocks = sum(level1_counts(w, t))
+        n_cand = (np.minimum(c // w.group + 1, w.top_m2) - 1) * w.group + (c - c // w.group * w.group) + 1
+        n_sel = np.minimum(n_cand, w.top_m)
+    else:
+        scored_blocks = np.where(c + 1 <= w.top_m, 0, c - 1)
+        n_sel = np.minimum(c + 1, w.top_m)
     n_valid = (n_sel - 1) * w.block + (t - c * w.block + 1)
     scored_tokens = np.where(n_valid <= w.top_k, 0, n_valid)
     kept = np.minimum(n_valid, w.top_k)
@@ -76,6 +96,14 @@ def algorithmic_work(w: Workload, lens=None) -> dict:
     summ_bytes = summ_rows * dI * 2 + summ_blocks * nL * dI * 2
     topm_flops = 2.0 * dI * nL * sb.sum()
     topm_bytes = b * nq * dI * 2 + sb.sum() * nL * dI * 2 + b * nq * w.top_m * 4
+    if w.group:
+        # super-blocks from the first touched block's on are re-summarised
+        # (their G block summaries read, one row written); level 1 writes and
+        # level 2 reads the top_m2 lists
+        start = (w.seq_len - nq) // w.block
+        n_super = b * (w.n_super - start // w.group)
+        summ_bytes += n_super * (w.group + 1) * nL * dI * 2
+        topm_bytes += 2 * b * nq * w.top_m2 * 4
     topk_bytes = st.sum() * dI * 2 + b * nq * w.top_k * 4 + b * nq * w.top_m * 4
     attn_bytes = (kept.sum() * w.n_heads_kv * d * 2 * 2 + b * nq * w.n_heads_q * d * (2 + 4)
                   + b * nq * w.top_k * 4)
@@ -93,8 +121,8 @@ def algorithmic_work(w: Workload, lens=None) -> dict:
 
 # kernel sources that define each stage's dominant kernel
 STAGE_SOURCES = {
-    "block_summary": ["block_summary.hip", "summary.hpp", "common.hpp"],
-    "block_topm": ["block_topm.hip", "select.hpp", "summary.hpp", "common.hpp"],
+    "block_summary": ["block_summary.hip", "summary.hpp", "block_topm_3level.hip", "common.hpp"],
+    "block_topm": ["block_topm.hip", "block_topm_3level.hip", "select.hpp", "summary.hpp", "common.hpp"],
     "token_topk": ["token_topk.hip", "select.hpp", "common.hpp"],
     "sparse_attn": ["sparse_attn.hip", "common.hpp"],
 }
@@ -152,7 +180,11 @@ def _oracle_one(args):
     w, inp, S = _ORC_STATE["w"], _ORC_STATE["inp"], _ORC_STATE["S"]
     lens = inp.get("seq_lens")
     t = w.query_pos(i) if lens is None else int(lens[b]) - 1
-    orc.forward_query(inp, b, i, t, w.block, w.top_m, w.top_k, w.scale, S_bits=S[b])
+    if w.group:
+        orc.forward_query_3level(inp, b, i, t, w.block, w.group, w.top_m2, w.top_m, w.top_k, w.scale, S[b],
+                                 _ORC_STATE["S2"][b])
+    else:
+        orc.forward_query(inp, b, i, t, w.block, w.top_m, w.top_k, w.scale, S_bits=S[b])
     return 1
 
 
@@ -167,12 +199,13 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
     lens = inp.get("seq_lens")
     S = [orc.block_summary(inp["kI"][b] if lens is None else inp["kI"][b, :int(lens[b])], w.block, inp.get("W"))
          for b in range(w.batch)]
+    S2 = [orc.super_summary(x, w.group) for x in S] if w.group else None
     t_summary = time.perf_counter() - t0
     total = w.batch * w.n_q
     n = min(sample, total)
     flat = np.unique(np.linspace(0, total - 1, n).round().astype(np.int64))
     queries = [(int(x // w.n_q), int(x % w.n_q)) for x in flat]
-    _ORC_STATE.update(w=w, inp=inp, S=S)
+    _ORC_STATE.update(w=w, inp=inp, S=S, S2=S2)
     ctx = mp.get_context("fork")
     t0 = time.perf_counter()
     with ctx.Pool(cores, initializer=_oracle_worker_init) as pool:
@@ -186,7 +219,8 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
         "cores": cores,
         "kind": "oracle",
         "sample": f"{done} of {total} queries, evenly spaced over the batch and positions; "
-                  f"block summaries of all {w.batch} sequence(s) built once ({t_summary:.2f} s); "
+                  f"block{' and super-block' if w.group else ''} summaries of all {w.batch} sequence(s) "
+                  f"built once ({t_summary:.2f} s); "
                   f"{wall:.1f} s wall on {cores} worker processes",
     }
 
@@ -258,6 +292,53 @@ def flat_comparison(w: Workload, dev: dict, shape, stage_ms: dict, steps: int, h
                     "of hsa_forward"}
 
 
+def two_level_comparison(w: Workload, dev: dict, shape, stage_ms: dict, blk3, steps: int, hip) -> dict:
+    """Time the two-level hsa_forward (every causal block scored) on the same
+    inputs, m and k, against the three-level stages, and report how many of
+    its kept blocks the three-level selection also keeps."""
+    import torch
+
+    from hierarchical_index_sparse_amd import _lib, pipeline
+    w2 = w.with_(group=0, top_m2=0)
+    out = pipeline.alloc_outputs(w2)
+    ws = torch.empty(_lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_FORWARD), dtype=torch.uint8,
+                     device="cuda")
+    start = (w.seq_len - w.n_q) // w.block
+    _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), 0, out["S"])
+
+    def run(lists):
+        _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), start, out["S"], dev["Q"], dev["K"], dev["V"],
+                         out["blk"] if lists else None, None, out["O"], out["lse"], ws)
+
+    run(True)
+    torch.cuda.synchronize()
+    blk2 = out["blk"].cpu().numpy().reshape(-1, w.top_m)
+    b3 = blk3.reshape(-1, w.top_m)
+    overlap = float(np.mean([np.intersect1d(x[x >= 0], y[y >= 0]).size / max(1, (x >= 0).sum())
+                             for x, y in zip(blk2, b3)]))
+    n = max(3, min(steps, 10))
+    events = [[hip.create() for _ in range(5)] for _ in range(n)]
+    for s in range(n):
+        _lib.hsa_sparse_set_stage_events(events[s])
+        run(False)
+    torch.cuda.synchronize()
+    _lib.hsa_sparse_set_stage_events(None)
+    st2 = {name: float(np.mean([hip.elapsed_ms(ev[i], ev[i + 1]) for ev in events]))
+           for i, name in enumerate(STAGES)}
+    step2 = float(np.mean([hip.elapsed_ms(ev[0], ev[4]) for ev in events]))
+    for ev in events:
+        for e in ev:
+            hip.destroy(e)
+    del out, ws
+    torch.cuda.empty_cache()
+    return {"two_level_stage_ms": st2, "two_level_step_ms": step2,
+            "three_level_block_stages_ms": stage_ms["block_summary"] + stage_ms["block_topm"],
+            "two_level_block_stages_ms": st2["block_summary"] + st2["block_topm"],
+            "block_list_overlap": overlap,
+            "note": "same inputs, m and k; block stages = summaries + block selection; overlap = mean fraction "
+                    "of the two-level kept blocks that the three-level selection also keeps"}
+
+
 # ------------------------------------------------------------------- main
 
 
@@ -302,8 +383,15 @@ def main():
 
     lens = inp.get("seq_lens")
 
+    if w.group:
+        _lib.hsa_super_summary(shape, w.group, out["S"], 0, out["S2"])
+
     def step():
-        if lens is None:
+        if w.group:
+            _lib.hsa_forward_3level(shape, w.group, w.top_m2, dev["qI"], dev["kI"], dev.get("W"), start_block,
+                                    out["S"], out["S2"], dev["Q"], dev["K"], dev["V"], out["sup"], None, None,
+                                    out["O"], out["lse"], ws)
+        elif lens is None:
             _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), start_block, out["S"], dev["Q"], dev["K"],
                              dev["V"], None, None, out["O"], out["lse"], ws)
         else:  # one decode step over sequences of different lengths
@@ -362,7 +450,14 @@ def main():
         hip.destroy(b)
 
     # the flat indexer takes one length for the batch
-    flat = None if (args.no_flat or lens is not None) else flat_comparison(w, dev, shape, stage_ms, args.steps, hip)
+    flat = None if (args.no_flat or lens is not None or w.group) else flat_comparison(w, dev, shape, stage_ms,
+                                                                                      args.steps, hip)
+    two = None
+    if w.group:
+        blk3 = pipeline.alloc_outputs(w)["blk"]
+        _lib.hsa_block_topm_3level(shape, w.group, w.top_m2, dev["qI"], out["S"], out["S2"], out["sup"], blk3)
+        torch.cuda.synchronize()
+        two = two_level_comparison(w, dev, shape, stage_ms, blk3.cpu().numpy(), args.steps, hip)
 
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     queries = w.batch * w.n_q
@@ -403,12 +498,15 @@ def main():
                    "batch": w.batch, "seq_len": w.seq_len, "n_q": w.n_q,
                    "d_index": w.d_index, "block": w.block, "top_m": w.top_m, "top_k": w.top_k,
                    "heads_q": w.n_heads_q, "heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
-                   "n_landmarks": w.n_landmarks, "parallelism": "single GPU"},
+                   "n_landmarks": w.n_landmarks,
+                   **({"group": w.group, "top_m2": w.top_m2} if w.group else {}),
+                   "parallelism": "single GPU"},
         "stage_ms": stage_ms,
         "gpu_step_ms_all_stage_events": gpu_step_ms,
         "stage_hbm_frac": {n: work[n]["bytes"] / (stage_ms[n] / 1000.0) / 1e9 / HBM_PEAK_GBS for n in STAGES},
         "roofline": roof,
         "indexer_vs_flat": flat,
+        **({"three_level_vs_two_level": two} if w.group else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

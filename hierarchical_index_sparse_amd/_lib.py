@@ -27,7 +27,8 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL",
 
 EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_error",
            "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
-           "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step")
+           "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_super_summary",
+           "hsa_block_topm_3level", "hsa_forward_3level")
 
 
 class HsaSparseShape(ctypes.Structure):
@@ -70,6 +71,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_sparse_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.hsa_flat_topk.argtypes = [S, P, P, P, P, SZ, P]
     lib.hsa_decode_step.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_super_summary.argtypes = [S, I32, P, I32, P, P]
+    lib.hsa_block_topm_3level.argtypes = [S, I32, I32, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_3level.argtypes = [S, I32, I32, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
                  "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
@@ -190,6 +194,33 @@ def hsa_forward(shape, qI, kI, W, summary_start_block, S, Q, K, V, blk_out, tok_
                             _ptr(O, "O", _F32), _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes,
                             _stream(stream))
     _check(st, "hsa_forward")
+
+
+def hsa_super_summary(shape, group, S, start_super, S2, stream=None):
+    st = load().hsa_super_summary(ctypes.byref(shape), int(group), _ptr(S, "S", _BF16), int(start_super),
+                                  _ptr(S2, "S2", _BF16), _stream(stream))
+    _check(st, "hsa_super_summary")
+
+
+def hsa_block_topm_3level(shape, group, top_m2, qI, S, S2, sup, blk, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_BLOCK_TOPM, workspace, qI.device)
+    st = load().hsa_block_topm_3level(ctypes.byref(shape), int(group), int(top_m2), _ptr(qI, "qI", _BF16),
+                                      _ptr(S, "S", _BF16), _ptr(S2, "S2", _BF16), _ptr(sup, "sup", _I32),
+                                      _ptr(blk, "blk", _I32), ws.data_ptr(), nbytes, _stream(stream))
+    _check(st, "hsa_block_topm_3level")
+
+
+def hsa_forward_3level(shape, group, top_m2, qI, kI, W, summary_start_block, S, S2, Q, K, V, sup_out, blk_out,
+                       tok_out, O, lse=None, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_FORWARD, workspace, Q.device)
+    st = load().hsa_forward_3level(ctypes.byref(shape), int(group), int(top_m2), _ptr(qI, "qI", _BF16),
+                                   _ptr(kI, "kI", _BF16), _ptr(W, "W", _I8, True), int(summary_start_block),
+                                   _ptr(S, "S", _BF16), _ptr(S2, "S2", _BF16), _ptr(Q, "Q", _BF16),
+                                   _ptr(K, "K", _BF16), _ptr(V, "V", _BF16), _ptr(sup_out, "sup_out", _I32),
+                                   _ptr(blk_out, "blk_out", _I32, True), _ptr(tok_out, "tok_out", _I32, True),
+                                   _ptr(O, "O", _F32), _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes,
+                                   _stream(stream))
+    _check(st, "hsa_forward_3level")
 
 
 def hsa_sparse_set_stage_events(events):

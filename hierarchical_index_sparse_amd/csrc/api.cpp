@@ -101,6 +101,28 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
 
 bool empty(const hsa::Dims& d) { return d.b == 0 || d.nq == 0; }
 
+// Super-block level of the three-level selection.
+struct Level3 {
+  int lgG, m2;
+  uint16_t* S2;
+  int32_t* sup;
+};
+
+constexpr int kMaxGroup = 4096;
+constexpr int kMaxLevel2Slots = 8192;
+
+// group: blocks per super-block; top_m2: kept super-blocks.  Sets lgG.
+hsa_sparse_status_t check_level3(int32_t group, int32_t top_m2, int& lgG) {
+  if (!is_pow2(group) || group > kMaxGroup)
+    return fail(HSA_SPARSE_UNSUPPORTED, "group must be a power of two in [1, %d] (got %d)", kMaxGroup, group);
+  if (top_m2 < 2) return fail(HSA_SPARSE_INVALID_ARG, "top_m2 must be >= 2 (first and last super-block are kept)");
+  if ((long long)top_m2 * group > kMaxLevel2Slots)
+    return fail(HSA_SPARSE_UNSUPPORTED, "top_m2 * group > %d candidate blocks", kMaxLevel2Slots);
+  lgG = 0;
+  while ((1 << lgG) < group) ++lgG;
+  return HSA_SPARSE_OK;
+}
+
 struct ForwardLayout {
   size_t blk_off, tok_off, stage_off, total;
 };
@@ -244,15 +266,18 @@ hsa_sparse_status_t hsa_sparse_attn(const hsa_sparse_shape_t* shape, const uint1
 
 // Steps 1-4 on one stream for validated dims (d.lens set for per-sequence
 // lengths).  `who` names the entry point in error messages.
+// With `l3`, step 2 selects through super-blocks.
 static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, const uint16_t* qI,
                                         const uint16_t* kI, const int8_t* landmark_W, int32_t summary_start_block,
                                         uint16_t* S, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                                         int32_t* blk_out, int32_t* tok_out, float* O, float* lse, void* workspace,
-                                        size_t workspace_bytes, hsa_sparse_stream_t stream) {
+                                        size_t workspace_bytes, hsa_sparse_stream_t stream,
+                                        const Level3* l3 = nullptr) {
   if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
   if (empty(d)) return HSA_SPARSE_OK;
   if (!qI || !kI || !S || !Q || !K || !V || !O)
     return fail(HSA_SPARSE_INVALID_ARG, "qI, kI, S, Q, K, V or O is NULL");
+  if (l3 && (!l3->S2 || !l3->sup)) return fail(HSA_SPARSE_INVALID_ARG, "S2 or sup_out is NULL");
   const ForwardLayout f = forward_layout(d);
   if (workspace_bytes < f.total || !workspace)
     return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "%s needs %zu workspace bytes", who, f.total);
@@ -273,13 +298,23 @@ static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, con
   // Decode: the only re-summarised block is each query's own, always-kept
   // block, whose score is never read, so its summary is folded into the
   // block-score launch instead of preceding it.
-  const bool fold = hsa::block_topm_can_fold(d, summary_start_block);
+  // (With super-blocks the query's own super-block is always kept too, and
+  // its summary is rebuilt in the same folded workgroup.)
+  const bool fold = l3 ? hsa::block_topm_3level_can_fold(d, l3->lgG, l3->m2, summary_start_block)
+                       : hsa::block_topm_can_fold(d, summary_start_block);
   hipError_t e = hipSuccess;
   if (!fold) e = hsa::launch_block_summary(d, kI, landmark_W, summary_start_block, S, stream);
   if (e != hipSuccess) return hf(e, "block summary");
+  if (l3 && !fold) e = hsa::launch_super_summary(d, l3->lgG, S, summary_start_block >> l3->lgG, l3->S2, stream);
+  if (e != hipSuccess) return hf(e, "super-block summary");
   HSA_MARK(1)
   const hsa::SummaryFold sf{kI, landmark_W, S, summary_start_block};
-  e = hsa::launch_block_topm(d, qI, S, blk, stage, stream, fold ? &sf : nullptr);
+  if (l3) {
+    e = hsa::launch_block_topm_3level(d, l3->lgG, l3->m2, qI, S, l3->S2, l3->sup, blk, stage, stream,
+                                      fold ? &sf : nullptr, l3->S2);
+  } else {
+    e = hsa::launch_block_topm(d, qI, S, blk, stage, stream, fold ? &sf : nullptr);
+  }
   if (e != hipSuccess) return hf(e, "block top-m");
   HSA_MARK(2)
   e = hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
@@ -318,6 +353,58 @@ hsa_sparse_status_t hsa_decode_step(const hsa_sparse_shape_t* shape, const int32
   d.lens = seq_lens;
   return forward_impl(d, "hsa_decode_step", qI, kI, landmark_W, 0, S, Q, K, V, blk_out, tok_out, O, lse, workspace,
                       workspace_bytes, stream);
+}
+
+hsa_sparse_status_t hsa_super_summary(const hsa_sparse_shape_t* shape, int32_t group, const uint16_t* S,
+                                      int32_t start_super, uint16_t* S2, hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSummary);
+  if (st != HSA_SPARSE_OK) return st;
+  int lgG = 0;
+  st = check_level3(group, 2, lgG);
+  if (st != HSA_SPARSE_OK) return st;
+  if (start_super < 0) return fail(HSA_SPARSE_INVALID_ARG, "start_super < 0");
+  const int nsb = (d.nb + group - 1) / group;
+  if (d.b == 0 || d.L == 0 || start_super >= nsb) return HSA_SPARSE_OK;
+  if (!S || !S2) return fail(HSA_SPARSE_INVALID_ARG, "S or S2 is NULL");
+  hipError_t e = hsa::launch_super_summary(d, lgG, S, start_super, S2, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_super_summary");
+}
+
+hsa_sparse_status_t hsa_block_topm_3level(const hsa_sparse_shape_t* shape, int32_t group, int32_t top_m2,
+                                          const uint16_t* qI, const uint16_t* S, const uint16_t* S2, int32_t* sup,
+                                          int32_t* blk, void* workspace, size_t workspace_bytes,
+                                          hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSelect | kSummary);
+  if (st != HSA_SPARSE_OK) return st;
+  int lgG = 0;
+  st = check_level3(group, top_m2, lgG);
+  if (st != HSA_SPARSE_OK) return st;
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!qI || !S || !S2 || !sup || !blk) return fail(HSA_SPARSE_INVALID_ARG, "qI, S, S2, sup or blk is NULL");
+  const size_t need = hsa::block_topm_3level_ws_bytes(d, lgG);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "block_topm_3level needs %zu workspace bytes", need);
+  hipError_t e = hsa::launch_block_topm_3level(d, lgG, top_m2, qI, S, S2, sup, blk, workspace, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_block_topm_3level");
+}
+
+hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape, int32_t group, int32_t top_m2,
+                                       const uint16_t* qI, const uint16_t* kI, const int8_t* landmark_W,
+                                       int32_t summary_start_block, uint16_t* S, uint16_t* S2, const uint16_t* Q,
+                                       const uint16_t* K, const uint16_t* V, int32_t* sup_out, int32_t* blk_out,
+                                       int32_t* tok_out, float* O, float* lse, void* workspace,
+                                       size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSummary | kSelect | kAttn);
+  if (st != HSA_SPARSE_OK) return st;
+  Level3 l3{0, top_m2, S2, sup_out};
+  st = check_level3(group, top_m2, l3.lgG);
+  if (st != HSA_SPARSE_OK) return st;
+  if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
+  return forward_impl(d, "hsa_forward_3level", qI, kI, landmark_W, summary_start_block, S, Q, K, V, blk_out,
+                      tok_out, O, lse, workspace, workspace_bytes, stream, &l3);
 }
 
 }  // extern "C"

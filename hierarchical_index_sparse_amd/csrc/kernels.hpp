@@ -38,6 +38,20 @@ bool block_topm_can_fold(const Dims& s, int start_block);
 hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk,
                              void* ws, hipStream_t st, const SummaryFold* fold = nullptr);
 
+// step 2 through super-blocks of 2^lgG blocks: S2 summaries of the
+// super-blocks from start_super on, then level 1 (top-m2 super-blocks into
+// sup [b*nq, m2]) and level 2 (top-m blocks among theirs into blk)
+hipError_t launch_super_summary(const Dims& s, int lgG, const uint16_t* S, int start_super, uint16_t* S2,
+                                hipStream_t st);
+// With `fold`, the newest block's summary and its super-block's (into
+// S2_out) are rebuilt inside the selection launch; allowed only when
+// block_topm_3level_can_fold says no query reads them.
+size_t block_topm_3level_ws_bytes(const Dims& s, int lgG);
+bool block_topm_3level_can_fold(const Dims& s, int lgG, int m2, int start_block);
+hipError_t launch_block_topm_3level(const Dims& s, int lgG, int m2, const uint16_t* qI, const uint16_t* S,
+                                    const uint16_t* S2, int32_t* sup, int32_t* blk, void* ws, hipStream_t st,
+                                    const SummaryFold* fold = nullptr, uint16_t* S2_out = nullptr);
+
 // step 3: scores into [b*nq, m*B] fp32, then the top-k select
 size_t token_topk_ws_bytes(const Dims& s);
 hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,

@@ -15,11 +15,17 @@ namespace hsa {
 
 // Called by all NTH threads of a workgroup; red is the workgroup's LDS.
 // L is the row stride of kI per sequence, Lb the sequence's length (rows
-// at or past Lb count as zero).
+// at or past Lb count as zero).  With S2, the summary of the super-block of
+// 2^lgG blocks holding block j is rebuilt too: the mean of its blocks'
+// summaries (block j's fresh value, the others read from S; blocks past nb
+// count as zero), summed in block order in fp32 and rounded once, the same
+// arithmetic as the super-block summary kernel.  No other workgroup may be
+// writing that super-block's blocks in S.
 template <int DI, int NL, int NTH = 256>
 __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI, const int8_t* __restrict__ W,
                                                 uint16_t* __restrict__ S, int L, int Lb, int B, int nb, int j, int b,
-                                                float (&red)[NL][NTH / (DI / 8)][DI]) {
+                                                float (&red)[NL][NTH / (DI / 8)][DI],
+                                                uint16_t* __restrict__ S2 = nullptr, int lgG = 0) {
   constexpr int LPR = DI / 8;     // lanes per row
   constexpr int RPI = NTH / LPR;  // rows per iteration of the workgroup
   const int tid = threadIdx.x;
@@ -62,7 +68,18 @@ __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI,
     float total = 0.f;
 #pragma unroll 4
     for (int r = 0; r < RPI; ++r) total += red[l][r][d];
-    S[(((size_t)b * nb + j) * NL + l) * DI + d] = (uint16_t)f32_to_bf16_rne(total * inv_b);
+    const uint32_t own = f32_to_bf16_rne(total * inv_b);
+    S[(((size_t)b * nb + j) * NL + l) * DI + d] = (uint16_t)own;
+    if (S2) {
+      const int J = j >> lgG, g0 = J << lgG, g1 = min(nb, g0 + (1 << lgG));
+      const int nsb = (nb + (1 << lgG) - 1) >> lgG;
+      float sum = 0.f;
+      for (int g = g0; g < g1; ++g) {
+        const uint32_t v = g == j ? own : (uint32_t)S[(((size_t)b * nb + g) * NL + l) * DI + d];
+        sum += __uint_as_float(v << 16);
+      }
+      S2[(((size_t)b * nsb + J) * NL + l) * DI + d] = (uint16_t)f32_to_bf16_rne(sum * __builtin_ldexpf(1.f, -lgG));
+    }
   }
 }
 

@@ -30,13 +30,17 @@ def to_device(inp: dict, device="cuda") -> dict:
 
 def alloc_outputs(w: Workload, device="cuda") -> dict:
     nqt = (w.batch, w.n_q)
-    return {
+    res = {
         "S": torch.zeros((w.batch, w.n_blocks, w.n_landmarks, w.d_index), dtype=torch.bfloat16, device=device),
         "blk": torch.full(nqt + (w.top_m,), -7, dtype=torch.int32, device=device),
         "tok": torch.full(nqt + (w.top_k,), -7, dtype=torch.int32, device=device),
         "O": torch.full(nqt + (w.n_heads_q, w.head_dim), float("nan"), dtype=torch.float32, device=device),
         "lse": torch.full(nqt + (w.n_heads_q,), float("nan"), dtype=torch.float32, device=device),
     }
+    if w.group:
+        res["S2"] = torch.zeros((w.batch, w.n_super, w.n_landmarks, w.d_index), dtype=torch.bfloat16, device=device)
+        res["sup"] = torch.full(nqt + (w.top_m2,), -7, dtype=torch.int32, device=device)
+    return res
 
 
 def run_stages(w: Workload, dev: dict, out: dict | None = None, attention: bool = True) -> dict:
@@ -59,6 +63,18 @@ def run_forward(w: Workload, dev: dict, out: dict | None = None, keep_lists: boo
     _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), summary_start_block, out["S"], dev["Q"],
                      dev["K"], dev["V"], out["blk"] if keep_lists else None,
                      out["tok"] if keep_lists else None, out["O"], out["lse"], workspace)
+    return out
+
+
+def run_forward_3level(w: Workload, dev: dict, out: dict | None = None, keep_lists: bool = True,
+                       workspace: torch.Tensor | None = None, summary_start_block: int = 0) -> dict:
+    """Steps 1-4 through hsa_forward_3level (super-blocks of w.group blocks)."""
+    shape = _lib.shape_of(w)
+    out = out or alloc_outputs(w, dev["qI"].device)
+    _lib.hsa_forward_3level(shape, w.group, w.top_m2, dev["qI"], dev["kI"], dev.get("W"), summary_start_block,
+                            out["S"], out["S2"], dev["Q"], dev["K"], dev["V"], out["sup"],
+                            out["blk"] if keep_lists else None, out["tok"] if keep_lists else None, out["O"],
+                            out["lse"], workspace)
     return out
 
 

@@ -34,6 +34,10 @@ class Workload:
     # > 0: decode over sequences of different lengths, uniform in
     # [varlen_min, seq_len] (seq_len is then the cache capacity; n_q == 1)
     varlen_min: int = 0
+    # > 0: three-level selection, super-blocks of `group` blocks of which
+    # `top_m2` are kept before the blocks are chosen among theirs
+    group: int = 0
+    top_m2: int = 0
     seed: int = 0
     description: str = ""
 
@@ -47,6 +51,10 @@ class Workload:
     @property
     def n_blocks(self) -> int:
         return (self.seq_len + self.block - 1) // self.block
+
+    @property
+    def n_super(self) -> int:
+        return (self.n_blocks + self.group - 1) // self.group if self.group else 0
 
     def query_pos(self, i: int) -> int:
         """Absolute position of query i (queries are the last n_q tokens)."""
@@ -81,6 +89,11 @@ WORKLOADS = {
         name="decode_varlen_128k", batch=32, seq_len=131072, n_q=1, d_index=128,
         block=128, top_m=64, top_k=2048, n_heads_q=16, n_heads_kv=1, varlen_min=65536,
         description="decode, batch 32, cache capacity 131072, lengths uniform in [65536, 131072]"),
+    "decode_3level_1m": Workload(
+        name="decode_3level_1m", batch=8, seq_len=1048576, n_q=1, d_index=128,
+        block=128, top_m=64, top_k=2048, n_heads_q=16, n_heads_kv=1, needles=4,
+        group=16, top_m2=32,
+        description="decode, batch 8, L=1048576, super-blocks of 16 blocks, 32 kept, then 64 blocks"),
     "landmark_decode_1m": Workload(
         name="landmark_decode_1m", batch=2, seq_len=1048576, n_q=1, d_index=128,
         block=128, top_m=256, top_k=256 * 128, n_heads_q=16, n_heads_kv=1,

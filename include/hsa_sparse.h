@@ -245,10 +245,80 @@ hsa_sparse_status_t hsa_flat_topk(const hsa_sparse_shape_t* shape,
                                   hsa_sparse_stream_t stream);
 
 /*
+ * Three-level selection: super-blocks -> blocks -> tokens (LSA page, latent
+ * space and hierarchical clustering: the query descends a tree of key
+ * groups from the root and scores only a few nodes per level).  Here the
+ * tree is fixed: a super-block is `group` consecutive blocks, summarised by
+ * the mean of their summaries and selected like a block (HISA page, step
+ * one, with the first and the query's own super-block always kept); the
+ * blocks are then selected among the blocks of the kept super-blocks only,
+ * which bounds the per-query block work by ceil(nb / group) + top_m2 * group
+ * instead of nb.  Supported: group a power of two in [1, 4096],
+ * top_m2 >= 2, top_m2 * group <= 8192; the shape as for hsa_forward.
+ *
+ * hsa_super_summary: S [batch, nb, n_landmarks, d_index] bf16 block
+ *   summaries (step 1) -> S2 [batch, nsb, n_landmarks, d_index] bf16 with
+ *   nsb = ceil(nb / group):
+ *   S2[J, l] = bf16_rne(sum_{g < group} S[J*group + g, l] / group), blocks
+ *   past nb counted as 0 (sums in fp32: exact when the summaries' partial
+ *   sums fit 24 bits, as for the integer-valued workloads).  Super-blocks
+ *   start_super .. nsb-1 are written; earlier ones are left as they are.
+ *
+ * hsa_block_topm_3level: step 2 through super-blocks.
+ *   qI, S as for hsa_block_topm; S2 from hsa_super_summary.
+ *   sup  [batch, n_q, top_m2] int32 output, level 1: for the query at t
+ *        with C = t / (block * group), all of 0..C if C + 1 <= top_m2,
+ *        else {0, C} plus the best top_m2 - 2 of 1..C-1 by
+ *        max_l qI . S2[J, l]; ascending, -1 padded.
+ *   blk  [batch, n_q, top_m] int32 output, level 2: the candidates are the
+ *        blocks j <= c = t / block of the super-blocks in sup; all of them
+ *        if at most top_m, else {0, c} plus the best top_m - 2 of the other
+ *        candidates by max_l qI . S[j, l]; ascending, -1 padded.
+ *   workspace  the size hsa_sparse_workspace_size(shape,
+ *        HSA_SPARSE_OP_BLOCK_TOPM) gives is enough for any group.
+ *
+ * hsa_forward_3level: hsa_forward with step 2 replaced by the two levels
+ *   above.  S and S2 are in-out summary state: block summaries from
+ *   summary_start_block on and super-block summaries from
+ *   summary_start_block / group on are recomputed first.  sup_out is
+ *   required; blk_out, tok_out, lse may be NULL.  Workspace:
+ *   hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_FORWARD).  Stage events
+ *   (hsa_sparse_set_stage_events) mark the same four steps, step 1 ending
+ *   after the super-block summaries.
+ * Errors: as for the other entry points; nothing is launched on an error.
+ */
+hsa_sparse_status_t hsa_super_summary(const hsa_sparse_shape_t* shape,
+                                      int32_t group, const uint16_t* S,
+                                      int32_t start_super, uint16_t* S2,
+                                      hsa_sparse_stream_t stream);
+
+hsa_sparse_status_t hsa_block_topm_3level(const hsa_sparse_shape_t* shape,
+                                          int32_t group, int32_t top_m2,
+                                          const uint16_t* qI,
+                                          const uint16_t* S,
+                                          const uint16_t* S2, int32_t* sup,
+                                          int32_t* blk, void* workspace,
+                                          size_t workspace_bytes,
+                                          hsa_sparse_stream_t stream);
+
+hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape,
+                                       int32_t group, int32_t top_m2,
+                                       const uint16_t* qI, const uint16_t* kI,
+                                       const int8_t* landmark_W,
+                                       int32_t summary_start_block,
+                                       uint16_t* S, uint16_t* S2,
+                                       const uint16_t* Q, const uint16_t* K,
+                                       const uint16_t* V, int32_t* sup_out,
+                                       int32_t* blk_out, int32_t* tok_out,
+                                       float* O, float* lse, void* workspace,
+                                       size_t workspace_bytes,
+                                       hsa_sparse_stream_t stream);
+
+/*
  * Per-step timing of hsa_forward (profiling aid).  After this call, every
- * hsa_forward made by the calling thread records events[0] on its stream
- * before step 1 and events[s] after step s (s = 1..4); a NULL entry is not
- * recorded.  Each recorded event costs the stream a few microseconds, which
+ * hsa_forward, hsa_decode_step and hsa_forward_3level made by the calling
+ * thread records events[0] on its stream before step 1 and events[s] after
+ * step s (s = 1..4); a NULL entry is not recorded.  Each recorded event costs the stream a few microseconds, which
  * matters for short (decode) steps, so record only the boundaries needed.
  * The events are the caller's hipEvent_t handles and must stay valid while
  * such calls are made.  n_events must be 5 with at least one non-NULL

@@ -199,3 +199,36 @@ def test_decode_step_validation(lib):
     need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FORWARD)
     assert lib.hsa_decode_step(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE,
                                None, FAKE, need - 1, None) == 3
+
+
+def test_three_level_validation(lib):
+    def fwd(s, group=16, m2=8, S2=FAKE, sup=FAKE, ws=1 << 40):
+        return lib.hsa_forward_3level(ctypes.byref(s), group, m2, FAKE, FAKE, None, 0, FAKE, S2, FAKE, FAKE, FAKE,
+                                      sup, None, None, FAKE, None, FAKE, ws, None)
+
+    def sel(s, group=16, m2=8, ws=1 << 40):
+        return lib.hsa_block_topm_3level(ctypes.byref(s), group, m2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
+
+    s = shape()
+    assert fwd(s, group=12) == 2             # not a power of two
+    assert fwd(s, group=8192) == 2           # above 4096
+    assert fwd(s, group=0) == 2
+    assert fwd(s, m2=1) == 1                 # first and last super-block are kept
+    assert fwd(s, group=64, m2=256) == 2     # 16384 level-2 candidates > 8192
+    assert fwd(s, S2=None) == 1
+    assert fwd(s, sup=None) == 1
+    assert fwd(shape(head_dim=64)) == 2
+    need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FORWARD)
+    assert fwd(s, ws=need - 1) == 3
+    assert sel(s, group=3) == 2 and sel(s, m2=0) == 1
+    need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_BLOCK_TOPM)
+    # level 1 scores ceil(nb / group) super-blocks: the block top-m size is enough
+    assert sel(s, group=1, ws=need - 1) == 3
+    assert b"workspace" in lib.hsa_sparse_last_error()
+    assert sel(shape(batch=0), ws=0) == 0
+    assert lib.hsa_super_summary(ctypes.byref(s), 16, FAKE, -1, FAKE, None) == 1
+    assert lib.hsa_super_summary(ctypes.byref(s), 5, FAKE, 0, FAKE, None) == 2
+    assert lib.hsa_super_summary(ctypes.byref(shape(batch=0)), 16, None, 0, None, None) == 0
+    # start past the last super-block (4096 / 64 = 64 blocks, 4 super-blocks of 16): nothing to do
+    assert lib.hsa_super_summary(ctypes.byref(s), 16, None, 4, None, None) == 0
+    assert lib.hsa_super_summary(ctypes.byref(s), 16, None, 3, None, None) == 1
