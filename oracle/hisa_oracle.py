@@ -264,6 +264,53 @@ def sparse_attention(Q_bits: np.ndarray, K_bits: np.ndarray, V_bits: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# per-head selection from the attention queries  [HiLS pseudocode: the
+# landmark scores come from Q itself against the chunks' landmarks, and the
+# exact attention runs over the concatenated K/V of the kept chunks]
+# ---------------------------------------------------------------------------
+
+
+def head_landmarks(K_bits: np.ndarray, block: int, W: np.ndarray | None = None) -> np.ndarray:
+    """Landmarks of one sequence's attention keys, per kv head.
+
+    K_bits [L, Hkv, d] -> [nb, nL, Hkv, d]: kv head g's landmarks are the
+    block summary (block_summary) of its key rows K[:, g].  The float64 sums
+    of bf16 keys are exact while the values' exponents span < 45 bits (true
+    for the N(0, 1) keys of every workload), so one rounding to bf16.
+    """
+    return np.stack([block_summary(K_bits[:, g, :], block, W) for g in range(K_bits.shape[1])], axis=2)
+
+
+def forward_query_heads(seq: dict, b: int, i: int, t: int, block: int, m: int, scale: float,
+                        LK_bits: np.ndarray, attention: bool = True, blk_override: np.ndarray | None = None) -> dict:
+    """Per-head chunk selection and attention for query i (position t) of sequence b.
+
+    Query head h (kv head g = h // (Hq / Hkv)) ranks the causal chunks by
+    max_l Q[h] . LK[j, l, g] with the block rule of select_blocks (first and
+    own chunk kept, m in all), then attends over every token s <= t of its
+    kept chunks.  blk_override [Hq, m] replaces the selection (to evaluate
+    the attention of a given selection).  Returns blk [Hq, m], O [Hq, d],
+    lse [Hq].
+    """
+    Q = seq["Q"][b, i]
+    Hq, Hkv = Q.shape[0], seq["K"].shape[2]
+    group = Hq // Hkv
+    blk = np.empty((Hq, m), np.int32)
+    res = {"blk": blk}
+    if attention:
+        res["O"] = np.empty((Hq, Q.shape[1]), np.float64)
+        res["lse"] = np.empty(Hq, np.float64)
+    for h in range(Hq):
+        g = h // group
+        blk[h] = select_blocks(Q[h], LK_bits[:, :, g, :], t, block, m) if blk_override is None else blk_override[h]
+        if attention:
+            tok = candidate_tokens(blk[h], t, block)
+            O, lse = sparse_attention(Q[h:h + 1], seq["K"][b][:, g:g + 1], seq["V"][b][:, g:g + 1], tok, scale)
+            res["O"][h], res["lse"][h] = O[0], lse[0]
+    return res
+
+
+# ---------------------------------------------------------------------------
 # the whole path for one query
 # ---------------------------------------------------------------------------
 

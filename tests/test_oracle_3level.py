@@ -11,35 +11,14 @@ from fractions import Fraction
 
 import numpy as np
 import pytest
-import torch
 
 from oracle import hisa_oracle as orc
 from hierarchical_index_sparse_amd import datagen
+from exact_bf16 import bf16_rne_of_fraction as _bf16_rne_of_fraction
 
 
 def bits_of_ints(a):
     return datagen.int_to_bf16_bits(np.asarray(a))
-
-
-def _bf16_rne_of_fraction(fr: Fraction) -> int:
-    """bf16 bits of the exact rational fr rounded to 8 significant bits, ties to even."""
-    if fr == 0:
-        return 0
-    a = abs(fr)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if Fraction(2) ** e > a:
-        e -= 1
-    assert Fraction(2) ** e <= a < Fraction(2) ** (e + 1)
-    unit = Fraction(2) ** (e - 7)
-    n = a / unit                      # in [128, 256)
-    fl = n.numerator // n.denominator
-    rem = n - fl
-    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
-        fl += 1
-    v = float(fl * unit) * (-1 if fr < 0 else 1)
-    assert Fraction(v) == fl * unit * (-1 if fr < 0 else 1)
-    t = torch.tensor([v], dtype=torch.float32).to(torch.bfloat16).view(torch.int16)
-    return int(t.numpy().view(np.uint16)[0])
 
 
 def test_fraction_rounding_helper():
