@@ -77,10 +77,38 @@ def per_query_counts(w: Workload, t=None):
     return scored_blocks, scored_tokens, kept
 
 
+def head_work(w: Workload) -> dict:
+    """Per-head selection: landmarks of the touched chunks (K rows of every kv
+    head read, nL landmark rows written), chunk scores (each kv head's
+    landmark rows read once per query for its QPG heads), no token stage,
+    attention over every causal token of each head's kept chunks (one kv
+    head's K and V row per token and head)."""
+    b, nq, Hq, Hkv, nL, d = w.batch, w.n_q, w.n_heads_q, w.n_heads_kv, w.n_landmarks, w.head_dim
+    t = w.seq_len - nq + np.arange(nq, dtype=np.int64)
+    c = t // w.block
+    scored = np.where(c + 1 <= w.top_m, 0, c - 1)
+    n_valid = (np.minimum(c + 1, w.top_m) - 1) * w.block + (t - c * w.block + 1)
+    start = (w.seq_len - nq) // w.block
+    rows = min(w.seq_len, w.n_blocks * w.block) - start * w.block
+    lm_bytes = b * (rows * Hkv * d * 2 + (w.n_blocks - start) * nL * Hkv * d * 2)
+    sel_bytes = b * (scored.sum() * nL * Hkv * d * 2 + nq * Hq * d * 2 + nq * Hq * w.top_m * 4)
+    sel_flops = 2.0 * d * nL * Hq * b * scored.sum()
+    attn_bytes = b * Hq * (n_valid.sum() * d * 2 * 2 + nq * d * (2 + 4))
+    attn_flops = 4.0 * d * Hq * b * n_valid.sum()
+    return {
+        "block_summary": {"bytes": float(lm_bytes), "flops": 0.0},
+        "block_topm": {"bytes": float(sel_bytes), "flops": float(sel_flops)},
+        "token_topk": {"bytes": 0.0, "flops": 0.0},
+        "sparse_attn": {"bytes": float(attn_bytes), "flops": float(attn_flops)},
+    }
+
+
 def algorithmic_work(w: Workload, lens=None) -> dict:
     """Bytes each step must move (and flops it must do), per stage.  With
     per-sequence lengths (one query each) every sequence counts at its own
     length and re-summarises its own last block."""
+    if w.per_head:
+        return head_work(w)
     b, nq = w.batch, w.n_q
     dI, nL, d = w.d_index, w.n_landmarks, w.head_dim
     if lens is None:
@@ -121,8 +149,9 @@ def algorithmic_work(w: Workload, lens=None) -> dict:
 
 # kernel sources that define each stage's dominant kernel
 STAGE_SOURCES = {
-    "block_summary": ["block_summary.hip", "summary.hpp", "block_topm_3level.hip", "common.hpp"],
-    "block_topm": ["block_topm.hip", "block_topm_3level.hip", "select.hpp", "summary.hpp", "common.hpp"],
+    "block_summary": ["block_summary.hip", "summary.hpp", "block_topm_3level.hip", "head_select.hip", "common.hpp"],
+    "block_topm": ["block_topm.hip", "block_topm_3level.hip", "head_select.hip", "select.hpp", "summary.hpp",
+                   "common.hpp"],
     "token_topk": ["token_topk.hip", "select.hpp", "common.hpp"],
     "sparse_attn": ["sparse_attn.hip", "common.hpp"],
 }
@@ -180,7 +209,9 @@ def _oracle_one(args):
     w, inp, S = _ORC_STATE["w"], _ORC_STATE["inp"], _ORC_STATE["S"]
     lens = inp.get("seq_lens")
     t = w.query_pos(i) if lens is None else int(lens[b]) - 1
-    if w.group:
+    if w.per_head:
+        orc.forward_query_heads(inp, b, i, t, w.block, w.top_m, w.scale, S[b])
+    elif w.group:
         orc.forward_query_3level(inp, b, i, t, w.block, w.group, w.top_m2, w.top_m, w.top_k, w.scale, S[b],
                                  _ORC_STATE["S2"][b])
     else:
@@ -197,8 +228,11 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
     cores = max(1, min(cores, 16))
     t0 = time.perf_counter()
     lens = inp.get("seq_lens")
-    S = [orc.block_summary(inp["kI"][b] if lens is None else inp["kI"][b, :int(lens[b])], w.block, inp.get("W"))
-         for b in range(w.batch)]
+    if w.per_head:
+        S = [orc.head_landmarks(inp["K"][b], w.block, inp.get("W")) for b in range(w.batch)]
+    else:
+        S = [orc.block_summary(inp["kI"][b] if lens is None else inp["kI"][b, :int(lens[b])], w.block,
+                               inp.get("W")) for b in range(w.batch)]
     S2 = [orc.super_summary(x, w.group) for x in S] if w.group else None
     t_summary = time.perf_counter() - t0
     total = w.batch * w.n_q
@@ -219,7 +253,8 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
         "cores": cores,
         "kind": "oracle",
         "sample": f"{done} of {total} queries, evenly spaced over the batch and positions; "
-                  f"block{' and super-block' if w.group else ''} summaries of all {w.batch} sequence(s) "
+                  f"{'landmarks' if w.per_head else 'block summaries'}"
+                  f"{' and super-block summaries' if w.group else ''} of all {w.batch} sequence(s) "
                   f"built once ({t_summary:.2f} s); "
                   f"{wall:.1f} s wall on {cores} worker processes",
     }
@@ -339,6 +374,45 @@ def two_level_comparison(w: Workload, dev: dict, shape, stage_ms: dict, blk3, st
                     "of the two-level kept blocks that the three-level selection also keeps"}
 
 
+def dense_comparison(w: Workload, dev: dict, steps: int, hip, step_ms: float) -> dict:
+    """Time exact attention over every causal token (the full attention the
+    HiLS page measures its decode speedup against) on the same Q, K, V with
+    hsa_sparse_attn and a list 0..t per query."""
+    import torch
+
+    from hierarchical_index_sparse_amd import _lib
+    wd = w.with_(per_head=False, top_k=w.seq_len)
+    shape = _lib.shape_of(wd)
+    t = w.seq_len - w.n_q + torch.arange(w.n_q, device="cuda", dtype=torch.int32)
+    s = torch.arange(w.seq_len, device="cuda", dtype=torch.int32)
+    tok = torch.where(s[None, :] <= t[:, None], s[None, :], torch.full_like(s[None, :], -1))
+    tok = tok[None].expand(w.batch, -1, -1).contiguous()
+    O = torch.empty((w.batch, w.n_q, w.n_heads_q, w.head_dim), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, _lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_SPARSE_ATTN)),
+                     dtype=torch.uint8, device="cuda")
+    _lib.hsa_sparse_attn(shape, dev["Q"], dev["K"], dev["V"], tok, O, None, ws)
+    torch.cuda.synchronize()
+    n = max(3, min(steps, 10))
+    ev = [(hip.create(), hip.create()) for _ in range(n)]
+    stream = torch.cuda.current_stream().cuda_stream
+    for a, b in ev:
+        hip.record(a, stream)
+        _lib.hsa_sparse_attn(shape, dev["Q"], dev["K"], dev["V"], tok, O, None, ws)
+        hip.record(b, stream)
+    torch.cuda.synchronize()
+    dense_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev]))
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    kv_bytes = w.batch * w.n_q * w.seq_len * w.n_heads_kv * w.head_dim * 2 * 2
+    del tok, O, ws
+    torch.cuda.empty_cache()
+    return {"dense_attention_ms": dense_ms, "dense_hbm_frac": kv_bytes / (dense_ms / 1000.0) / 1e9 / HBM_PEAK_GBS,
+            "sparse_step_ms": step_ms, "speedup": dense_ms / step_ms,
+            "note": "dense = exact attention of every query over all causal tokens (hsa_sparse_attn, same Q/K/V); "
+                    "sparse = the whole per-head step (landmarks of the touched chunk, selection, attention)"}
+
+
 # ------------------------------------------------------------------- main
 
 
@@ -373,13 +447,16 @@ def main():
     dev = pipeline.to_device(inp)
     out = pipeline.alloc_outputs(w)
     shape = _lib.shape_of(w)
-    ws = torch.empty(_lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_FORWARD), dtype=torch.uint8,
-                     device="cuda")
+    op = _lib.HSA_SPARSE_OP_FORWARD_HEADS if w.per_head else _lib.HSA_SPARSE_OP_FORWARD
+    ws = torch.empty(_lib.hsa_sparse_workspace_size(shape, op), dtype=torch.uint8, device="cuda")
 
     # summaries of blocks before the new queries are state (built once at
     # ingest); each step re-summarises the blocks the queries' tokens touch
     start_block = (w.seq_len - w.n_q) // w.block
-    _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), 0, out["S"])
+    if w.per_head:
+        _lib.hsa_head_landmarks(shape, dev["K"], dev.get("W"), 0, out["LK"])
+    else:
+        _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), 0, out["S"])
 
     lens = inp.get("seq_lens")
 
@@ -387,7 +464,10 @@ def main():
         _lib.hsa_super_summary(shape, w.group, out["S"], 0, out["S2"])
 
     def step():
-        if w.group:
+        if w.per_head:
+            _lib.hsa_forward_heads(shape, dev.get("W"), start_block, dev["Q"], dev["K"], dev["V"], out["LK"], None,
+                                   out["O"], out["lse"], ws)
+        elif w.group:
             _lib.hsa_forward_3level(shape, w.group, w.top_m2, dev["qI"], dev["kI"], dev.get("W"), start_block,
                                     out["S"], out["S2"], dev["Q"], dev["K"], dev["V"], out["sup"], None, None,
                                     out["O"], out["lse"], ws)
@@ -450,14 +530,15 @@ def main():
         hip.destroy(b)
 
     # the flat indexer takes one length for the batch
-    flat = None if (args.no_flat or lens is not None or w.group) else flat_comparison(w, dev, shape, stage_ms,
-                                                                                      args.steps, hip)
+    flat = None if (args.no_flat or lens is not None or w.group or w.per_head) else flat_comparison(
+        w, dev, shape, stage_ms, args.steps, hip)
     two = None
     if w.group:
         blk3 = pipeline.alloc_outputs(w)["blk"]
         _lib.hsa_block_topm_3level(shape, w.group, w.top_m2, dev["qI"], out["S"], out["S2"], out["sup"], blk3)
         torch.cuda.synchronize()
         two = two_level_comparison(w, dev, shape, stage_ms, blk3.cpu().numpy(), args.steps, hip)
+    dense = dense_comparison(w, dev, args.steps, hip, gpu_step_ms) if w.per_head else None
 
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     queries = w.batch * w.n_q
@@ -494,7 +575,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 in, fp32 accumulate",
-        "data": "synthetic (seeded; integer-valued bf16 indexer vectors, N(0,1) bf16 Q/K/V)",
+        "data": ("synthetic (seeded; N(0,1) bf16 Q/K/V, one planted needle chunk per sequence and kv head)"
+                 if w.per_head else "synthetic (seeded; integer-valued bf16 indexer vectors, N(0,1) bf16 Q/K/V)"),
         "config": {"workload": w.name,
                    "summary_start_block": start_block if lens is None else "each sequence's last block",
                    "seq_lens": None if lens is None else f"uniform in [{w.varlen_min}, {w.seq_len}], "
@@ -504,6 +586,7 @@ def main():
                    "heads_q": w.n_heads_q, "heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
                    "n_landmarks": w.n_landmarks,
                    **({"group": w.group, "top_m2": w.top_m2} if w.group else {}),
+                   **({"selection": "per query head from Q and landmarks of K"} if w.per_head else {}),
                    "parallelism": "single GPU"},
         "stage_ms": stage_ms,
         "gpu_step_ms_all_stage_events": gpu_step_ms,
@@ -511,6 +594,7 @@ def main():
         "roofline": roof,
         "indexer_vs_flat": flat,
         **({"three_level_vs_two_level": two} if w.group else {}),
+        **({"per_head_vs_dense_attention": dense} if w.per_head else {}),
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -22,13 +22,16 @@ HSA_SPARSE_OP_TOKEN_TOPK = 2
 HSA_SPARSE_OP_SPARSE_ATTN = 3
 HSA_SPARSE_OP_FORWARD = 4
 HSA_SPARSE_OP_FLAT_TOPK = 5
+HSA_SPARSE_OP_HEAD_TOPM = 6
+HSA_SPARSE_OP_FORWARD_HEADS = 7
 
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "HIP_ERROR"}
 
 EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_error",
            "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
            "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_super_summary",
-           "hsa_block_topm_3level", "hsa_forward_3level")
+           "hsa_block_topm_3level", "hsa_forward_3level", "hsa_head_landmarks", "hsa_head_topm",
+           "hsa_forward_heads")
 
 
 class HsaSparseShape(ctypes.Structure):
@@ -74,6 +77,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_super_summary.argtypes = [S, I32, P, I32, P, P]
     lib.hsa_block_topm_3level.argtypes = [S, I32, I32, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward_3level.argtypes = [S, I32, I32, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_head_landmarks.argtypes = [S, P, P, I32, P, P]
+    lib.hsa_head_topm.argtypes = [S, P, P, P, P, SZ, P]
+    lib.hsa_forward_heads.argtypes = [S, P, I32, P, P, P, P, P, P, P, P, SZ, P]
     for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
                  "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
@@ -221,6 +227,29 @@ def hsa_forward_3level(shape, group, top_m2, qI, kI, W, summary_start_block, S, 
                                    _ptr(O, "O", _F32), _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes,
                                    _stream(stream))
     _check(st, "hsa_forward_3level")
+
+
+def hsa_head_landmarks(shape, K, W, start_block, LK, stream=None):
+    st = load().hsa_head_landmarks(ctypes.byref(shape), _ptr(K, "K", _BF16), _ptr(W, "W", _I8, True),
+                                   int(start_block), _ptr(LK, "LK", _BF16), _stream(stream))
+    _check(st, "hsa_head_landmarks")
+
+
+def hsa_head_topm(shape, Q, LK, blk, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_HEAD_TOPM, workspace, Q.device)
+    st = load().hsa_head_topm(ctypes.byref(shape), _ptr(Q, "Q", _BF16), _ptr(LK, "LK", _BF16),
+                              _ptr(blk, "blk", _I32), ws.data_ptr(), nbytes, _stream(stream))
+    _check(st, "hsa_head_topm")
+
+
+def hsa_forward_heads(shape, W, summary_start_block, Q, K, V, LK, blk_out, O, lse=None, workspace=None,
+                      stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_FORWARD_HEADS, workspace, Q.device)
+    st = load().hsa_forward_heads(ctypes.byref(shape), _ptr(W, "W", _I8, True), int(summary_start_block),
+                                  _ptr(Q, "Q", _BF16), _ptr(K, "K", _BF16), _ptr(V, "V", _BF16),
+                                  _ptr(LK, "LK", _BF16), _ptr(blk_out, "blk_out", _I32, True), _ptr(O, "O", _F32),
+                                  _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes, _stream(stream))
+    _check(st, "hsa_forward_heads")
 
 
 def hsa_sparse_set_stage_events(events):

@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhsa_sparse.so")
 
 SOURCES = ["api.cpp", "block_summary.hip", "block_topm.hip", "block_topm_3level.hip", "token_topk.hip", "sparse_attn.hip",
-           "flat_topk.hip"]
+           "flat_topk.hip", "head_select.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

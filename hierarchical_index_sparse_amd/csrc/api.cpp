@@ -32,7 +32,9 @@ hsa_sparse_status_t hip_fail(hipError_t e, const char* where) {
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
-enum : unsigned { kSummary = 1u, kSelect = 2u, kAttn = 4u, kFlat = 8u };
+enum : unsigned { kSummary = 1u, kSelect = 2u, kAttn = 4u, kFlat = 8u, kHeads = 16u, kHeadSel = 32u };
+
+constexpr long long kMaxHeadTokens = 131072;  // top_m * block of a per-head list
 
 // Checks shared by every entry point; `parts` names the fields the entry
 // point reads.  Fills `d` on success.
@@ -65,7 +67,28 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
         (long long)s->top_k < (long long)s->top_m * s->block)
       return fail(HSA_SPARSE_UNSUPPORTED, "top_m * block > 32768 candidates with top_k < top_m * block");
   }
-  if (!(parts & kSelect) && need_attn && s->top_k < 1) return fail(HSA_SPARSE_INVALID_ARG, "top_k must be >= 1");
+  if (parts & kHeads) {
+    // per-head selection: the landmarks come from K (head_dim wide rows)
+    if (s->head_dim != 128) return fail(HSA_SPARSE_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
+    if (!is_pow2(s->block) || s->block < 8 || s->block > 128)
+      return fail(HSA_SPARSE_UNSUPPORTED, "block must be a power of two in [8, 128] (got %d)", s->block);
+    if (s->n_landmarks != 1 && s->n_landmarks != 2 && s->n_landmarks != 4)
+      return fail(HSA_SPARSE_UNSUPPORTED, "n_landmarks must be 1, 2 or 4 (got %d)", s->n_landmarks);
+    if (s->n_heads_q < 1 || s->n_heads_kv < 1 || s->n_heads_q % s->n_heads_kv != 0)
+      return fail(HSA_SPARSE_INVALID_ARG, "n_heads_kv must divide n_heads_q");
+    if (s->n_heads_kv > 16) return fail(HSA_SPARSE_UNSUPPORTED, "at most 16 kv heads (got %d)", s->n_heads_kv);
+  }
+  if (parts & kHeadSel) {
+    if (s->top_m < 2) return fail(HSA_SPARSE_INVALID_ARG, "top_m must be >= 2 (first and last chunk are kept)");
+    const long long nb = ((long long)s->seq_len + s->block - 1) / s->block;
+    if (nb - 2 > 32768) return fail(HSA_SPARSE_UNSUPPORTED, "too many chunks (%lld > 32770)", nb);
+    if ((long long)s->top_m * s->block > kMaxHeadTokens)
+      return fail(HSA_SPARSE_UNSUPPORTED, "top_m * block > %lld tokens per head", kMaxHeadTokens);
+    if ((long long)s->batch * s->n_q * s->n_heads_q > (1ll << 30))
+      return fail(HSA_SPARSE_UNSUPPORTED, "batch * n_q * n_heads_q too large");
+  }
+  if (!(parts & (kSelect | kHeads)) && need_attn && s->top_k < 1)
+    return fail(HSA_SPARSE_INVALID_ARG, "top_k must be >= 1");
   if (need_attn) {
     if (s->head_dim != 128) return fail(HSA_SPARSE_UNSUPPORTED, "head_dim must be 128 (got %d)", s->head_dim);
     if (s->n_heads_q < 1 || s->n_heads_kv < 1 || s->n_heads_q % s->n_heads_kv != 0)
@@ -126,6 +149,19 @@ hsa_sparse_status_t check_level3(int32_t group, int32_t top_m2, int& lgG) {
 struct ForwardLayout {
   size_t blk_off, tok_off, stage_off, total;
 };
+
+// per-head forward: chunk lists, token lists, then scores / attention
+// scratch (never live at the same time)
+ForwardLayout heads_layout(const hsa::Dims& d) {
+  using hsa::align_up;
+  ForwardLayout f;
+  const size_t rows = (size_t)d.b * d.nq * d.Hq;
+  f.blk_off = 0;
+  f.tok_off = align_up(rows * d.m * sizeof(int32_t));
+  f.stage_off = f.tok_off + align_up(rows * d.m * d.B * sizeof(int32_t));
+  f.total = f.stage_off + std::max(hsa::head_scores_ws_bytes(d), hsa::head_attn_ws_bytes(d));
+  return f;
+}
 
 ForwardLayout forward_layout(const hsa::Dims& d) {
   using hsa::align_up;
@@ -188,6 +224,10 @@ size_t hsa_sparse_workspace_size(const hsa_sparse_shape_t* shape, int op) {
       return check_shape(shape, d, kSummary | kSelect | kAttn) == HSA_SPARSE_OK ? forward_layout(d).total : 0;
     case HSA_SPARSE_OP_FLAT_TOPK:
       return check_shape(shape, d, kFlat) == HSA_SPARSE_OK ? hsa::flat_topk_ws_bytes(d) : 0;
+    case HSA_SPARSE_OP_HEAD_TOPM:
+      return check_shape(shape, d, kHeads | kHeadSel) == HSA_SPARSE_OK ? hsa::head_scores_ws_bytes(d) : 0;
+    case HSA_SPARSE_OP_FORWARD_HEADS:
+      return check_shape(shape, d, kHeads | kHeadSel | kAttn) == HSA_SPARSE_OK ? heads_layout(d).total : 0;
     default: return 0;
   }
 }
@@ -405,6 +445,82 @@ hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape, int32_t 
   if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
   return forward_impl(d, "hsa_forward_3level", qI, kI, landmark_W, summary_start_block, S, Q, K, V, blk_out,
                       tok_out, O, lse, workspace, workspace_bytes, stream, &l3);
+}
+
+hsa_sparse_status_t hsa_head_landmarks(const hsa_sparse_shape_t* shape, const uint16_t* K,
+                                       const int8_t* landmark_W, int32_t start_block, uint16_t* LK,
+                                       hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kHeads);
+  if (st != HSA_SPARSE_OK) return st;
+  if (start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "start_block < 0");
+  if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
+  if (d.b == 0 || d.L == 0 || start_block >= d.nb) return HSA_SPARSE_OK;
+  if (!K || !LK) return fail(HSA_SPARSE_INVALID_ARG, "K or LK is NULL");
+  hipError_t e = hsa::launch_head_landmarks(d, K, landmark_W, start_block, LK, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_head_landmarks");
+}
+
+hsa_sparse_status_t hsa_head_topm(const hsa_sparse_shape_t* shape, const uint16_t* Q, const uint16_t* LK,
+                                  int32_t* blk, void* workspace, size_t workspace_bytes,
+                                  hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kHeads | kHeadSel);
+  if (st != HSA_SPARSE_OK) return st;
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!Q || !LK || !blk) return fail(HSA_SPARSE_INVALID_ARG, "Q, LK or blk is NULL");
+  const size_t need = hsa::head_scores_ws_bytes(d);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "head_topm needs %zu workspace bytes", need);
+  hipError_t e = hsa::launch_head_topm(d, Q, LK, blk, workspace, stream, nullptr);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_head_topm");
+}
+
+hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape, const int8_t* landmark_W,
+                                      int32_t summary_start_block, const uint16_t* Q, const uint16_t* K,
+                                      const uint16_t* V, uint16_t* LK, int32_t* blk_out, float* O, float* lse,
+                                      void* workspace, size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kHeads | kHeadSel | kAttn);
+  if (st != HSA_SPARSE_OK) return st;
+  if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
+  if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!Q || !K || !V || !LK || !O) return fail(HSA_SPARSE_INVALID_ARG, "Q, K, V, LK or O is NULL");
+  const ForwardLayout f = heads_layout(d);
+  if (workspace_bytes < f.total || !workspace)
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "hsa_forward_heads needs %zu workspace bytes", f.total);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* blk = blk_out ? blk_out : reinterpret_cast<int32_t*>(ws + f.blk_off);
+  int32_t* tok = reinterpret_cast<int32_t*>(ws + f.tok_off);
+  void* stage = ws + f.stage_off;
+  const bool rec = g_record_stages;
+  auto hf = [&](hipError_t err, const char* step) {
+    return fail(HSA_SPARSE_HIP_ERROR, "hsa_forward_heads (%s): %s", step, hipGetErrorString(err));
+  };
+#define HSA_MARK(i)                                                        \
+  if (rec && g_stage_events[i]) {                                          \
+    hipError_t er = hipEventRecord((hipEvent_t)g_stage_events[i], stream); \
+    if (er != hipSuccess) return hf(er, "stage event");                    \
+  }
+  HSA_MARK(0)
+  // decode: the only rebuilt chunk is every query's own, always-kept chunk,
+  // so its landmarks are folded into the score launch
+  const bool fold = hsa::head_topm_can_fold(d, summary_start_block);
+  hipError_t e = hipSuccess;
+  if (!fold) e = hsa::launch_head_landmarks(d, K, landmark_W, summary_start_block, LK, stream);
+  if (e != hipSuccess) return hf(e, "landmarks");
+  HSA_MARK(1)
+  const hsa::HeadFold hfold{K, landmark_W, LK, summary_start_block};
+  e = hsa::launch_head_topm(d, Q, LK, blk, stage, stream, tok, fold ? &hfold : nullptr);
+  if (e != hipSuccess) return hf(e, "chunk top-m");
+  HSA_MARK(2)
+  HSA_MARK(3)
+  e = hsa::launch_head_attn(d, Q, K, V, tok, O, lse, stage, stream);
+  if (e != hipSuccess) return hf(e, "attention");
+  HSA_MARK(4)
+#undef HSA_MARK
+  return HSA_SPARSE_OK;
 }
 
 }  // extern "C"

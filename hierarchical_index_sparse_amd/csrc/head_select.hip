@@ -1,0 +1,263 @@
+// Per-head chunk selection from the attention queries themselves.
+//
+// HiLS page (hils_attention pseudocode; section 2.1 landmark tokens,
+// section 2.2 two-layer selection): the coarse layer scores each chunk by
+// the attention query Q against the chunk's landmark vectors, keeps the top
+// chunks and runs exact attention over the concatenated K/V of the kept
+// chunks.  Here every query head ranks the chunks by its own Q_h against
+// landmarks of its kv head's keys (max over landmarks), with the block rule
+// of the shared indexer (first chunk and the query's own chunk kept, m in
+// all), and attends over every causal token of its kept chunks.
+//
+// k_head_landmarks: LK[b, j, l, g] = bf16_rne(sum_r W[l, r] K[b, jB + r, g] / B),
+//   accumulated in fp64, which is exact for bf16 keys whose exponents span
+//   fewer than 45 bits, so the one rounding is the only one.  In decode the
+//   newest chunk's landmarks are folded into the score launch.
+// k_head_scores_mfma: per (sequence, kv head) a [chunk landmark rows] x
+//   [(query, head-in-group) columns] contraction on v_mfma_f32_16x16x32_bf16
+//   (fp32 accumulation), max over a chunk's landmarks, scores of the causal
+//   chunks 1..c-1 written per (query, head) row.
+// The exact select then runs per (query, head) row (k_block_select).
+// The select also writes each row's causal tokens of its kept chunks, as
+//   row indices s * Hkv + g of K and V viewed as [L * Hkv, d], so the sparse
+//   attention kernel runs each (query, head) as a one-head query.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace hsa {
+
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
+  // round the 52-bit fraction to 7 bits, ties to even (normal range)
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint64_t lsb = (u >> 45) & 1ull;
+  u += 0x00000FFFFFFFFFFFull + lsb;
+  u &= ~0x00001FFFFFFFFFFFull;
+  return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;  // exact: 8 significant bits
+}
+
+// The landmarks of chunk j of sequence b (all kv heads), computed by the
+// calling waves (wave of nw): a K row (Hkv * 128 bf16) is Hkv groups of 16
+// lanes x 16 bytes; wave w takes groups w, w + nw, ...; lane = (row phase
+// p = lane / 16, 16-byte column chunk lane % 16) sums rows p, p + 4, ...
+// with 8 rows of loads in flight, in fp64; the four row phases meet by lane
+// shuffles.  fp64 sums of bf16 values are exact here, so the result does
+// not depend on this order.  No LDS.
+template <int NL>
+__device__ __forceinline__ void head_landmark_chunk(const uint16_t* __restrict__ K, const int8_t* __restrict__ W,
+                                                    uint16_t* __restrict__ LK, int L, int B, int nb, int Hkv, int j,
+                                                    int b, int wave, int nw) {
+  constexpr int U = 8;
+  const int lane = lane_id();
+  const int p = lane >> 4, cl = lane & 15;
+  const int RW = Hkv * 128;
+  const int rows = min(B, L - j * B);  // rows of the chunk inside the sequence
+  for (int cg = wave; cg < Hkv; cg += nw) {
+    const int col = (cg * 16 + cl) * 8;
+    double acc[NL][8];
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[l][e] = 0.0;
+    for (int r0 = 0; r0 < rows; r0 += 4 * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = min(r0 + 4 * u + p, rows - 1);
+        v[u] = *reinterpret_cast<const u32x4*>(K + ((size_t)b * L + (size_t)j * B + r) * RW + col);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + 4 * u + p;
+        if (r >= rows) continue;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+          const double w = W ? (double)W[l * B + r] : 1.0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[l][2 * e] += w * (double)bf16_lo(v[u][e]);
+            acc[l][2 * e + 1] += w * (double)bf16_hi(v[u][e]);
+          }
+        }
+      }
+    }
+    const double inv_b = 1.0 / (double)B;  // exact: B is a power of two
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        double x = acc[l][e];
+        x += __shfl_xor(x, 16, kWave);
+        x += __shfl_xor(x, 32, kWave);
+        acc[l][e] = x;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = f64_to_bf16_rne(acc[l][2 * e] * inv_b) | (f64_to_bf16_rne(acc[l][2 * e + 1] * inv_b) << 16);
+      if (p == 0) *reinterpret_cast<u32x4*>(LK + (((size_t)b * nb + j) * NL + l) * RW + col) = o;
+    }
+  }
+}
+
+// Workgroup (x, b): the landmarks of chunk start + x of sequence b.
+template <int NL>
+__global__ __launch_bounds__(256) void k_head_landmarks(const uint16_t* __restrict__ K, const int8_t* __restrict__ W,
+                                                        uint16_t* __restrict__ LK, int L, int B, int nb, int Hkv,
+                                                        int start) {
+  const int j = start + (int)blockIdx.x;
+  if (j >= nb) return;
+  head_landmark_chunk<NL>(K, W, LK, L, B, nb, Hkv, j, blockIdx.y, threadIdx.x / kWave, 4);
+}
+
+// Workgroup (x, y): 128 landmark rows (chunk j, landmark l: row j*NL + l) of
+// kv head g against 64 (query, head) columns of sequence b, y = (b * Hkv +
+// g) * ctiles + column tile.  Column p is query p / QPG, head g*QPG + p % QPG.
+// Wave w takes rows 32w .. 32w+31 (two 16-row B operands) for all 64
+// columns (four 16-column A operands); the accumulator holds 4 columns x 1
+// row per lane; a chunk's NL landmark rows sit in adjacent lanes, reduced by
+// an xor-shuffle maximum.  Workgroups past the score tiles (y >= n_score_y,
+// x == 0) compute the landmarks of chunks fold_start .. of sequence
+// (y - n_score_y) / nfold when the host folds them in: only when no query
+// scores them (each is its queries' own, always kept, chunk).
+template <int NL>
+__global__ __launch_bounds__(256) void k_head_scores_mfma(const uint16_t* __restrict__ Q,
+                                                          const uint16_t* __restrict__ LK,
+                                                          float* __restrict__ scores, int L, int nq, int B, int nb,
+                                                          int m, int Hq, int Hkv, int ctiles, int n_score_y,
+                                                          const uint16_t* __restrict__ K, const int8_t* __restrict__ W,
+                                                          uint16_t* __restrict__ LK_out, int fold_start, int nfold) {
+  constexpr int DI = 128, KS = DI / 32;
+  if ((int)blockIdx.y >= n_score_y) {  // folded landmarks (uniform)
+    const int y = (int)blockIdx.y - n_score_y;
+    const int j = fold_start + y % nfold;
+    if (blockIdx.x != 0 || j >= nb) return;
+    head_landmark_chunk<NL>(K, W, LK_out, L, B, nb, Hkv, j, y / nfold, threadIdx.x / kWave, 4);
+    return;
+  }
+  const int QPG = Hq / Hkv;
+  const int ncols = nq * QPG;
+  const int bg = blockIdx.y / ctiles, ct = blockIdx.y % ctiles;
+  const int b = bg / Hkv, g = bg % Hkv;
+  const int col0 = ct * 64;
+  const int c_last = query_pos(L, nq, (min(ncols, col0 + 64) - 1) / QPG) / B;
+  if (c_last + 1 <= m) return;  // no query of the tile needs scores
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int jl = lane & 15, gq = lane >> 4;
+  const int row0 = blockIdx.x * 128 + wave * 32;
+  if (row0 / NL >= c_last) return;  // every chunk is non-causal or forced
+  const int nrows = nb * NL;
+
+  u32x4 bs[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = min(row0 + 16 * nt + jl, nrows - 1);
+    const uint16_t* src = LK + (((size_t)b * nrows + row) * Hkv + g) * DI + 8 * gq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bs[nt][ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
+  }
+  for (int mt = 0; mt < 4; ++mt) {
+    if (col0 + 16 * mt >= ncols) break;  // uniform
+    const int ca = min(col0 + 16 * mt + jl, ncols - 1);
+    const uint16_t* qsrc = Q + (((size_t)b * nq + ca / QPG) * Hq + g * QPG + ca % QPG) * DI + 8 * gq;
+    u32x4 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
+                                                      __builtin_bit_cast(bf16x8, bs[nt][ks]), acc, 0, 0, 0);
+      if constexpr (NL > 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = group_max_f<NL>(acc[e]);
+      }
+      const int row = row0 + 16 * nt + jl;
+      const int j = row / NL;
+      if (row % NL == 0 && row < nrows) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = col0 + 16 * mt + 4 * gq + e;
+          if (col >= ncols) continue;
+          const int i = col / QPG;
+          const int c = query_pos(L, nq, i) / B;
+          if (c + 1 > m && j >= 1 && j < c)
+            scores[(((size_t)b * nq + i) * Hq + g * QPG + col % QPG) * nb + j] = acc[e];
+        }
+      }
+    }
+  }
+}
+
+size_t head_scores_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq * s.Hq * s.nb * sizeof(float)); }
+
+hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t* W, int start, uint16_t* LK,
+                                 hipStream_t st) {
+  if (s.b == 0 || start >= s.nb) return hipSuccess;
+  dim3 grid(s.nb - start, s.b);
+  switch (s.nL) {
+    case 1: hipLaunchKernelGGL((k_head_landmarks<1>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
+    case 2: hipLaunchKernelGGL((k_head_landmarks<2>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
+    case 4: hipLaunchKernelGGL((k_head_landmarks<4>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool head_topm_can_fold(const Dims& s, int start_block) {
+  // the score launch runs and the rebuilt chunks start at the last one,
+  // which no query scores (a query scores chunks below its own)
+  const int c_max = (s.L - 1) / s.B;
+  return c_max + 1 > s.m && start_block >= c_max && start_block < s.nb;
+}
+
+hipError_t launch_head_topm(const Dims& s, const uint16_t* Q, const uint16_t* LK, int32_t* blk, void* ws,
+                            hipStream_t st, int32_t* tok, const HeadFold* fold) {
+  if (s.b == 0 || s.nq == 0) return hipSuccess;
+  float* scores = static_cast<float*>(ws);
+  const int c_max = (s.L - 1) / s.B;
+  if (c_max + 1 > s.m) {
+    const int ctiles = (s.nq * (s.Hq / s.Hkv) + 63) / 64;
+    const int n_score_y = s.b * s.Hkv * ctiles;
+    const int nfold = fold ? s.nb - fold->start_block : 0;
+    dim3 grid((s.nb * s.nL + 127) / 128, n_score_y + s.b * nfold);
+    const uint16_t* K = fold ? fold->K : nullptr;
+    const int8_t* W = fold ? fold->W : nullptr;
+    uint16_t* LK_out = fold ? fold->LK : nullptr;
+    const int fs = fold ? fold->start_block : s.nb;
+#define HSA_HS(NL)                                                                                               \
+  hipLaunchKernelGGL((k_head_scores_mfma<NL>), grid, dim3(256), 0, st, Q, LK, scores, s.L, s.nq, s.B, s.nb, s.m, \
+                     s.Hq, s.Hkv, ctiles, n_score_y, K, W, LK_out, fs, max(nfold, 1))
+    if (s.nL == 1) HSA_HS(1); else if (s.nL == 2) HSA_HS(2); else HSA_HS(4);
+#undef HSA_HS
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (fold) {
+    return hipErrorInvalidValue;  // the host folds only into a score launch
+  }
+  return launch_block_select(s, s.Hq, scores, blk, st, tok, s.Hkv, s.Hq / s.Hkv);
+}
+
+// The attention of the per-head lists: each (query, head) row is a one-head
+// query over K and V viewed as [L * Hkv, 1, d].
+static Dims attn_view(const Dims& s) {
+  Dims v = s;
+  v.nq = s.nq * s.Hq;
+  v.Hq = 1;
+  v.Hkv = 1;
+  v.L = s.L * s.Hkv;
+  v.k = s.m * s.B;
+  return v;
+}
+
+size_t head_attn_ws_bytes(const Dims& s) { return sparse_attn_ws_bytes(attn_view(s)); }
+
+hipError_t launch_head_attn(const Dims& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                            const int32_t* tok, float* O, float* lse, void* ws, hipStream_t st) {
+  if (s.b == 0 || s.nq == 0) return hipSuccess;
+  return launch_sparse_attn(attn_view(s), Q, K, V, tok, O, lse, ws, st);
+}
+
+}  // namespace hsa

@@ -38,6 +38,13 @@ bool block_topm_can_fold(const Dims& s, int start_block);
 hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk,
                              void* ws, hipStream_t st, const SummaryFold* fold = nullptr);
 
+// the exact top-m select over fp32 scores [b*nq*heads, nb] (rows of
+// block 1 .. c-1 filled), `heads` select rows per query; with tok, each
+// row's causal tokens of its kept blocks too (entries s * tok_hkv + g, g =
+// head / tok_qpg, -1 padded to m * B)
+hipError_t launch_block_select(const Dims& s, int heads, const float* scores, int32_t* blk, hipStream_t st,
+                               int32_t* tok = nullptr, int tok_hkv = 1, int tok_qpg = 1);
+
 // step 2 through super-blocks of 2^lgG blocks: S2 summaries of the
 // super-blocks from start_super on, then level 1 (top-m2 super-blocks into
 // sup [b*nq, m2]) and level 2 (top-m blocks among theirs into blk)
@@ -67,6 +74,29 @@ bool flat_topk_supported(const Dims& s);
 size_t flat_topk_ws_bytes(const Dims& s);
 hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, int32_t* tok, void* ws,
                             hipStream_t st);
+
+// per-head selection from the attention queries: landmarks of K per kv
+// head (LK [b, nb, nL, Hkv, 128]), per-(query, head) chunk top-m (scores
+// [b*nq*Hq, nb] fp32 in ws), then the per-head lists' attention (token
+// lists [b*nq*Hq, m*B] in tok)
+hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t* W, int start, uint16_t* LK,
+                                 hipStream_t st);
+size_t head_scores_ws_bytes(const Dims& s);
+// With `fold` the landmarks of chunks fold->start_block .. are rebuilt in
+// the score launch (only when head_topm_can_fold).  tok: the per-head token
+// lists for launch_head_attn, written by the select.
+struct HeadFold {
+  const uint16_t* K;
+  const int8_t* W;
+  uint16_t* LK;
+  int start_block;
+};
+bool head_topm_can_fold(const Dims& s, int start_block);
+hipError_t launch_head_topm(const Dims& s, const uint16_t* Q, const uint16_t* LK, int32_t* blk, void* ws,
+                            hipStream_t st, int32_t* tok, const HeadFold* fold = nullptr);
+size_t head_attn_ws_bytes(const Dims& s);
+hipError_t launch_head_attn(const Dims& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                            const int32_t* tok, float* O, float* lse, void* ws, hipStream_t st);
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 

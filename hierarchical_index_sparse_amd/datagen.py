@@ -28,7 +28,7 @@ import torch
 from .workloads import Workload
 
 _TID = {"qI": 1, "kI_centre": 2, "kI_noise": 3, "Q": 4, "K": 5, "V": 6, "W": 7,
-        "needles": 8, "seq_lens": 9}
+        "needles": 8, "seq_lens": 9, "head_needles": 10}
 _CHUNK = 1 << 22  # elements per independent stream chunk
 
 
@@ -149,8 +149,36 @@ def gen_seq_lens(w: Workload) -> np.ndarray | None:
     return g.integers(w.varlen_min, w.seq_len + 1, size=w.batch).astype(np.int32)
 
 
+def plant_head_needles(w: Workload, att: dict) -> np.ndarray:
+    """Per-head workloads: in every (sequence, kv head g) one chunk j in
+    1 .. nb-2 gets keys K + 2 * sign(Q_h) for one query head h of g (the
+    last query's), so that head h's score for chunk j stands far above the
+    rest.  Modifies att["K"]; returns [b, Hkv, 2] (chunk, head)."""
+    nb, B = w.n_blocks, w.block
+    qpg = w.n_heads_q // w.n_heads_kv
+    assert nb - 2 >= 1
+    out = np.zeros((w.batch, w.n_heads_kv, 2), np.int64)
+    for b in range(w.batch):
+        g_rng = _rng(w.seed, "head_needles", b)
+        for g in range(w.n_heads_kv):
+            j = int(g_rng.integers(1, nb - 1))
+            h = g * qpg + int(g_rng.integers(0, qpg))
+            q = (att["Q"][b, -1, h].astype(np.uint32) << 16).view(np.float32)
+            rows = slice(j * B, min(w.seq_len, j * B + B))
+            k = (att["K"][b, rows, g].astype(np.uint32) << 16).view(np.float32)
+            att["K"][b, rows, g] = f32_to_bf16_bits(k + np.where(q < 0, -2.0, 2.0).astype(np.float32))
+            out[b, g] = (j, h)
+    return out
+
+
 def make_inputs(w: Workload, attention: bool = True, **kw) -> dict[str, np.ndarray]:
     """All inputs of one workload as host arrays (bf16 as uint16 bits)."""
+    if w.per_head:  # no indexer vectors: the selection reads Q and K
+        res = {"W": gen_landmark_projection(w), "seq_lens": gen_seq_lens(w)}
+        res.update(gen_attention_inputs(w))
+        if w.needles:
+            res["head_needles"] = plant_head_needles(w, res)
+        return res
     q_range = kw.pop("q_range", 8)
     qI = gen_index_queries(w, q_range=q_range)
     kI, needles = gen_index_keys(w, qI, q_range=q_range, **kw)

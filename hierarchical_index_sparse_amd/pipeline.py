@@ -16,7 +16,7 @@ def to_device(inp: dict, device="cuda") -> dict:
     """Host arrays (bf16 as uint16 bits, W as int8) -> GPU tensors."""
     out = {}
     for key, arr in inp.items():
-        if arr is None or key == "needles":
+        if arr is None or key.endswith("needles"):
             out[key] = arr
             continue
         a = np.ascontiguousarray(arr)
@@ -37,6 +37,15 @@ def alloc_outputs(w: Workload, device="cuda") -> dict:
         "O": torch.full(nqt + (w.n_heads_q, w.head_dim), float("nan"), dtype=torch.float32, device=device),
         "lse": torch.full(nqt + (w.n_heads_q,), float("nan"), dtype=torch.float32, device=device),
     }
+    if w.per_head:
+        qh = nqt + (w.n_heads_q,)
+        return {
+            "LK": torch.zeros((w.batch, w.n_blocks, w.n_landmarks, w.n_heads_kv, w.head_dim), dtype=torch.bfloat16,
+                              device=device),
+            "blk": torch.full(qh + (w.top_m,), -7, dtype=torch.int32, device=device),
+            "O": res["O"],
+            "lse": res["lse"],
+        }
     if w.group:
         res["S2"] = torch.zeros((w.batch, w.n_super, w.n_landmarks, w.d_index), dtype=torch.bfloat16, device=device)
         res["sup"] = torch.full(nqt + (w.top_m2,), -7, dtype=torch.int32, device=device)
@@ -75,6 +84,16 @@ def run_forward_3level(w: Workload, dev: dict, out: dict | None = None, keep_lis
                             out["S"], out["S2"], dev["Q"], dev["K"], dev["V"], out["sup"],
                             out["blk"] if keep_lists else None, out["tok"] if keep_lists else None, out["O"],
                             out["lse"], workspace)
+    return out
+
+
+def run_forward_heads(w: Workload, dev: dict, out: dict | None = None, keep_lists: bool = True,
+                      workspace: torch.Tensor | None = None, summary_start_block: int = 0) -> dict:
+    """Per-head chunk selection and attention through hsa_forward_heads."""
+    shape = _lib.shape_of(w)
+    out = out or alloc_outputs(w, dev["Q"].device)
+    _lib.hsa_forward_heads(shape, dev.get("W"), summary_start_block, dev["Q"], dev["K"], dev["V"], out["LK"],
+                           out["blk"] if keep_lists else None, out["O"], out["lse"], workspace)
     return out
 
 

@@ -38,6 +38,9 @@ class Workload:
     # `top_m2` are kept before the blocks are chosen among theirs
     group: int = 0
     top_m2: int = 0
+    # True: every query head selects its own chunks from Q against
+    # landmarks of K (no indexer vectors, no token top-k)
+    per_head: bool = False
     seed: int = 0
     description: str = ""
 
@@ -94,6 +97,12 @@ WORKLOADS = {
         block=128, top_m=64, top_k=2048, n_heads_q=16, n_heads_kv=1, needles=4,
         group=16, top_m2=32,
         description="decode, batch 8, L=1048576, super-blocks of 16 blocks, 32 kept, then 64 blocks"),
+    "head_decode_512k": Workload(
+        name="head_decode_512k", batch=4, seq_len=524288, n_q=1, d_index=128,
+        block=64, top_m=32, top_k=32 * 64, n_heads_q=32, n_heads_kv=4, n_landmarks=4,
+        per_head=True, needles=1,
+        description="per-head chunk selection from Q (HiLS-style), decode, batch 4, L=524288, "
+                    "chunks of 64 with 4 landmarks, 32 kept per head, 32 query heads / 4 kv heads"),
     "landmark_decode_1m": Workload(
         name="landmark_decode_1m", batch=2, seq_len=1048576, n_q=1, d_index=128,
         block=128, top_m=256, top_k=256 * 128, n_heads_q=16, n_heads_kv=1,

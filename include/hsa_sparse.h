@@ -85,7 +85,9 @@ enum {
   HSA_SPARSE_OP_TOKEN_TOPK = 2,
   HSA_SPARSE_OP_SPARSE_ATTN = 3,
   HSA_SPARSE_OP_FORWARD = 4,
-  HSA_SPARSE_OP_FLAT_TOPK = 5
+  HSA_SPARSE_OP_FLAT_TOPK = 5,
+  HSA_SPARSE_OP_HEAD_TOPM = 6,
+  HSA_SPARSE_OP_FORWARD_HEADS = 7
 };
 
 /* Bytes of device workspace the operation `op` needs for `shape`
@@ -315,9 +317,74 @@ hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape,
                                        hsa_sparse_stream_t stream);
 
 /*
+ * Per-head chunk selection from the attention queries (HiLS page,
+ * hils_attention pseudocode: landmark scores are Q against the chunks'
+ * landmarks, the top chunks are kept and exact attention runs over the
+ * concatenated K/V of the kept chunks; sections 2.1-2.2).  Every query head
+ * h selects its own chunks (blocks of `block` tokens) with its own Q_h,
+ * against landmarks of its kv head g = h / (n_heads_q / n_heads_kv), and
+ * attends over every causal token of them.  There is no token top-k: a
+ * head's list is all tokens s <= t of its kept chunks.
+ * Shape fields read: batch, seq_len, n_q, block, n_landmarks, top_m,
+ * n_heads_q, n_heads_kv, head_dim, scale (d_index and top_k are not read).
+ * Supported: head_dim 128; block a power of two in [8, 128]; n_landmarks in
+ * {1, 2, 4}; n_heads_kv <= 16 dividing n_heads_q with at most 16 query
+ * heads per kv head; top_m >= 2; top_m * block <= 131072;
+ * ceil(seq_len / block) - 2 <= 32768; seq_len * n_heads_kv * 256 < 2^31.
+ *
+ * hsa_head_landmarks: K [batch, seq_len, n_heads_kv, head_dim] bf16 ->
+ *   LK [batch, nb, n_landmarks, n_heads_kv, head_dim] bf16,
+ *   LK[j, l, g] = bf16_rne(sum_r w[l, r] * K[j*B + r, g] / B) (w = 1 with
+ *   landmark_W NULL, which needs n_landmarks == 1), rows past seq_len
+ *   counted as 0, summed exactly (fp64) and rounded once.  Chunks
+ *   start_block .. nb-1 are written.
+ *
+ * hsa_head_topm: blk [batch, n_q, n_heads_q, top_m] int32 output: for the
+ *   query at t with c = t / block, per head, all of 0..c if c + 1 <= top_m,
+ *   else {0, c} plus the best top_m - 2 chunks of 1..c-1 by
+ *   max_l Q[h] . LK[j, l, g] (fp32 accumulation of bf16 products, so chunks
+ *   whose scores differ by less than the fp32 rounding of the dot product
+ *   may be ordered either way; ties to the lower index); ascending, -1
+ *   padded.  Workspace: hsa_sparse_workspace_size(shape,
+ *   HSA_SPARSE_OP_HEAD_TOPM) (the fp32 chunk scores).
+ *
+ * hsa_forward_heads: landmarks from summary_start_block on (LK is in-out
+ *   state, as S is for hsa_forward), the per-head selection, then for each
+ *   (query, head) exact softmax attention over its tokens:
+ *   O [batch, n_q, n_heads_q, head_dim] fp32 and lse (NULL or
+ *   [batch, n_q, n_heads_q]) as in hsa_sparse_attn.  blk_out: NULL or the
+ *   chunk lists as for hsa_head_topm.  Workspace:
+ *   hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_FORWARD_HEADS) (lists of
+ *   top_m * block tokens per (query, head) plus scratch).  Stage events
+ *   mark landmarks (1), selection (2) and attention (4); event 3 is
+ *   recorded right after 2.
+ * Errors: as for the other entry points; nothing is launched on an error.
+ */
+hsa_sparse_status_t hsa_head_landmarks(const hsa_sparse_shape_t* shape,
+                                       const uint16_t* K,
+                                       const int8_t* landmark_W,
+                                       int32_t start_block, uint16_t* LK,
+                                       hsa_sparse_stream_t stream);
+
+hsa_sparse_status_t hsa_head_topm(const hsa_sparse_shape_t* shape,
+                                  const uint16_t* Q, const uint16_t* LK,
+                                  int32_t* blk, void* workspace,
+                                  size_t workspace_bytes,
+                                  hsa_sparse_stream_t stream);
+
+hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape,
+                                      const int8_t* landmark_W,
+                                      int32_t summary_start_block,
+                                      const uint16_t* Q, const uint16_t* K,
+                                      const uint16_t* V, uint16_t* LK,
+                                      int32_t* blk_out, float* O, float* lse,
+                                      void* workspace, size_t workspace_bytes,
+                                      hsa_sparse_stream_t stream);
+
+/*
  * Per-step timing of hsa_forward (profiling aid).  After this call, every
- * hsa_forward, hsa_decode_step and hsa_forward_3level made by the calling
- * thread records events[0] on its stream before step 1 and events[s] after
+ * hsa_forward, hsa_decode_step, hsa_forward_3level and hsa_forward_heads
+ * made by the calling thread records events[0] on its stream before step 1 and events[s] after
  * step s (s = 1..4); a NULL entry is not recorded.  Each recorded event costs the stream a few microseconds, which
  * matters for short (decode) steps, so record only the boundaries needed.
  * The events are the caller's hipEvent_t handles and must stay valid while

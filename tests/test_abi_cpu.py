@@ -232,3 +232,34 @@ def test_three_level_validation(lib):
     # start past the last super-block (4096 / 64 = 64 blocks, 4 super-blocks of 16): nothing to do
     assert lib.hsa_super_summary(ctypes.byref(s), 16, None, 4, None, None) == 0
     assert lib.hsa_super_summary(ctypes.byref(s), 16, None, 3, None, None) == 1
+
+
+def test_per_head_validation(lib):
+    def fwd(s, ws=1 << 40, W=None, LK=FAKE):
+        return lib.hsa_forward_heads(ctypes.byref(s), W, 0, FAKE, FAKE, FAKE, LK, None, FAKE, None, FAKE, ws, None)
+
+    base = dict(n_q=1, block=64, top_m=8, n_heads_q=8, n_heads_kv=2, d_index=0, top_k=0)
+    assert fwd(shape(**dict(base, top_m=1))) == 1
+    assert fwd(shape(**dict(base, head_dim=64))) == 2
+    assert fwd(shape(**dict(base, block=96))) == 2
+    assert fwd(shape(**dict(base, n_heads_kv=3))) == 1            # does not divide 8
+    assert fwd(shape(**dict(base, n_heads_q=32, n_heads_kv=32))) == 2  # more than 16 kv heads
+    assert fwd(shape(**dict(base, top_m=4096, block=64))) == 2   # 262144 tokens per head
+    assert fwd(shape(**dict(base, n_landmarks=4))) == 1          # needs landmark_W
+    assert fwd(shape(**base), LK=None) == 1
+    s = shape(**base)
+    need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FORWARD_HEADS)
+    # chunk lists + token lists (top_m * block per query head) + scratch
+    rows = 1 * 1 * 8
+    assert need >= rows * 8 * 4 + rows * 8 * 64 * 4
+    assert fwd(s, ws=need - 1) == 3
+    sel = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_HEAD_TOPM)
+    assert sel >= rows * 64 * 4  # fp32 score per (query, head, chunk): 4096 / 64 chunks
+    assert lib.hsa_head_topm(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, sel - 1, None) == 3
+    # landmarks read no selection fields
+    t = shape(**dict(base, top_m=0))
+    assert lib.hsa_head_landmarks(ctypes.byref(t), FAKE, None, -1, FAKE, None) == 1
+    assert lib.hsa_head_landmarks(ctypes.byref(shape(**dict(base, n_landmarks=2))), FAKE, None, 0, FAKE, None) == 1
+    assert lib.hsa_head_landmarks(ctypes.byref(t), None, None, 64, None, None) == 0  # past the last chunk
+    assert lib.hsa_forward_heads(ctypes.byref(shape(**dict(base, batch=0))), None, 0, None, None, None, None, None,
+                                 None, None, None, 0, None) == 0
