@@ -168,18 +168,11 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
   }
 }
 
-// Select rows are (sequence, query, head) with `heads` rows per query (1
-// for the shared indexer): row q belongs to query (q / heads) % nq.  With
-// TOKS (per-head selection) the row's token list is written too: entry e is
-// token s = blk[e / B] * B + e % B if s <= t, stored as s * tok_hkv + g
-// with g = (q % heads) / tok_qpg, else -1 (tok [rows, m * B]).
-template <int NW, int R, bool TOKS>
+template <int NW, int R>
 __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const float* __restrict__ scores,
                                                                           int32_t* __restrict__ blk, int L, int nq,
                                                                           int B, int nb, int m, int nq_total,
-                                                                          const int32_t* __restrict__ lens,
-                                                                          int heads, int32_t* __restrict__ tok,
-                                                                          int tok_hkv, int tok_qpg) {
+                                                                          const int32_t* __restrict__ lens) {
   constexpr int QPB = NW == 1 ? 4 : 1;  // queries per workgroup
   constexpr int GT = NW * kWave;        // threads per select group
   __shared__ SelectSmem<NW> lds[QPB];
@@ -188,17 +181,12 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
   if (q >= nq_total) return;  // wave-uniform (NW == 1 only)
   SelectSmem<NW>& sm = lds[NW == 1 ? wave : 0];
   const int gtid = NW == 1 ? lane_id() : (int)threadIdx.x;
-  const int qi = q / heads;
-  const int i = qi % nq;
-  const int t = query_pos(seq_len_of(lens, L, qi / nq), nq, i);
+  const int i = q % nq;
+  const int t = query_pos(seq_len_of(lens, L, q / nq), nq, i);
   const int c = t / B;
   int32_t* out = blk + (size_t)q * m;
-  int32_t* tq = TOKS ? tok + (size_t)q * m * B : nullptr;
-  const int g = TOKS ? (q % heads) / tok_qpg : 0;
   if (c + 1 <= m) {
     for (int j = gtid; j < m; j += GT) out[j] = j <= c ? j : -1;
-    if constexpr (TOKS)
-      for (int e = gtid; e < m * B; e += GT) tq[e] = e <= t ? e * tok_hkv + g : -1;
     return;
   }
   const int want = m - 2;
@@ -206,14 +194,6 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
   if (gtid == 0) {
     out[0] = 0;
     out[m - 1] = c;
-  }
-  if constexpr (TOKS) {
-    // block 0 (whole: c >= 1) and block c (up to t) at the list's ends
-    for (int e = gtid; e < B; e += GT) {
-      tq[e] = e * tok_hkv + g;
-      const int s = c * B + e;
-      tq[(m - 1) * B + e] = s <= t ? s * tok_hkv + g : -1;
-    }
   }
   if (want == 0) return;
   const float* sc = scores + (size_t)q * nb + 1;
@@ -225,16 +205,7 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
     key[r] = idx < n ? score_key(v) : 0u;
   }
   select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
-    if (take) {
-      out[1 + pos] = 1 + idx;
-      if constexpr (TOKS) {
-        const int s0 = (1 + idx) * B;
-        i32x4* dst = reinterpret_cast<i32x4*>(tq + (size_t)(1 + pos) * B);
-        for (int r = 0; r < B; r += 4)
-          dst[r / 4] = i32x4{(s0 + r) * tok_hkv + g, (s0 + r + 1) * tok_hkv + g, (s0 + r + 2) * tok_hkv + g,
-                             (s0 + r + 3) * tok_hkv + g};
-      }
-    }
+    if (take) out[1 + pos] = 1 + idx;
   });
 }
 
@@ -331,38 +302,25 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
   });
 }
 
-// Launch arguments of the select beyond the scores and lists: rows per
-// query, and the per-head token lists (tok == nullptr: none).
-struct SelectRows {
-  int heads;
-  int32_t* tok;
-  int tok_hkv, tok_qpg;
-};
-
 template <int NW, int R>
-static hipError_t launch_select_r(int nq_total, const float* scores, int32_t* blk, const Dims& s,
-                                  const SelectRows& rw, hipStream_t st) {
+static hipError_t launch_select_r(int nq_total, const float* scores, int32_t* blk, const Dims& s, hipStream_t st) {
   dim3 grid(NW == 1 ? (nq_total + 3) / 4 : nq_total), block(NW == 1 ? 256 : NW * 64);
-  if (rw.tok)
-    hipLaunchKernelGGL((k_block_select<NW, R, true>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m,
-                       nq_total, s.lens, rw.heads, rw.tok, rw.tok_hkv, rw.tok_qpg);
-  else
-    hipLaunchKernelGGL((k_block_select<NW, R, false>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m,
-                       nq_total, s.lens, rw.heads, nullptr, 1, 1);
+  hipLaunchKernelGGL((k_block_select<NW, R>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m, nq_total,
+                     s.lens);
   return hipGetLastError();
 }
 
 template <int NW>
 static hipError_t launch_select(int R, int nq_total, const float* scores, int32_t* blk, const Dims& s,
-                                const SelectRows& rw, hipStream_t st) {
+                                hipStream_t st) {
   switch (R) {
-    case 1: return launch_select_r<NW, 1>(nq_total, scores, blk, s, rw, st);
-    case 2: return launch_select_r<NW, 2>(nq_total, scores, blk, s, rw, st);
-    case 4: return launch_select_r<NW, 4>(nq_total, scores, blk, s, rw, st);
-    case 8: return launch_select_r<NW, 8>(nq_total, scores, blk, s, rw, st);
-    case 16: return launch_select_r<NW, 16>(nq_total, scores, blk, s, rw, st);
+    case 1: return launch_select_r<NW, 1>(nq_total, scores, blk, s, st);
+    case 2: return launch_select_r<NW, 2>(nq_total, scores, blk, s, st);
+    case 4: return launch_select_r<NW, 4>(nq_total, scores, blk, s, st);
+    case 8: return launch_select_r<NW, 8>(nq_total, scores, blk, s, st);
+    case 16: return launch_select_r<NW, 16>(nq_total, scores, blk, s, st);
     case 32:
-      if constexpr (NW > 1) return launch_select_r<NW, 32>(nq_total, scores, blk, s, rw, st);
+      if constexpr (NW > 1) return launch_select_r<NW, 32>(nq_total, scores, blk, s, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -445,21 +403,11 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_block_select(s, 1, scores, blk, st);
-}
-
-hipError_t launch_block_select(const Dims& s, int heads, const float* scores, int32_t* blk, hipStream_t st,
-                               int32_t* tok, int tok_hkv, int tok_qpg) {
-  const int nq_total = s.b * s.nq * heads;
-  const int n_max = (s.L - 1) / s.B - 1;
-  const SelectRows rw{heads, tok, tok_hkv, tok_qpg};
-  // many rows: one wave per row (<= 512 candidates) or a 4-wave workgroup
-  // per row; few rows: 16 waves per row (shortest latency)
-  if (nq_total >= 512 && n_max <= 64 * 8)
-    return launch_select<1>(pick_r(n_max, 1), nq_total, scores, blk, s, rw, st);
-  if (nq_total >= 512 && n_max <= 4 * 64 * 32)
-    return launch_select<4>(pick_r(n_max, 4), nq_total, scores, blk, s, rw, st);
-  return launch_select<16>(pick_r(n_max, 16), nq_total, scores, blk, s, rw, st);
+  // many queries: one wave per query (<= 512 candidates) or a 4-wave
+  // workgroup per query; few queries: 16 waves per query (shortest latency)
+  if (nq_total >= 512 && n_max <= 64 * 8) return launch_select<1>(pick_r(n_max, 1), nq_total, scores, blk, s, st);
+  if (nq_total >= 512 && n_max <= 4 * 64 * 32) return launch_select<4>(pick_r(n_max, 4), nq_total, scores, blk, s, st);
+  return launch_select<16>(pick_r(n_max, 16), nq_total, scores, blk, s, st);
 }
 
 }  // namespace hsa

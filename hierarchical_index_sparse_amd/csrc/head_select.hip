@@ -12,17 +12,18 @@
 // k_head_landmarks: LK[b, j, l, g] = bf16_rne(sum_r W[l, r] K[b, jB + r, g] / B),
 //   accumulated in fp64, which is exact for bf16 keys whose exponents span
 //   fewer than 45 bits, so the one rounding is the only one.  In decode the
-//   newest chunk's landmarks are folded into the score launch.
+//   newest chunk's landmarks are folded into the select launch.
 // k_head_scores_mfma: per (sequence, kv head) a [chunk landmark rows] x
 //   [(query, head-in-group) columns] contraction on v_mfma_f32_16x16x32_bf16
 //   (fp32 accumulation), max over a chunk's landmarks, scores of the causal
 //   chunks 1..c-1 written per (query, head) row.
-// The exact select then runs per (query, head) row (k_block_select).
-// The select also writes each row's causal tokens of its kept chunks, as
-//   row indices s * Hkv + g of K and V viewed as [L * Hkv, d], so the sparse
-//   attention kernel runs each (query, head) as a one-head query.
+// k_head_select: the exact select per (query, head) row; it also writes
+//   each row's causal tokens of its kept chunks, as row indices s * Hkv + g
+//   of K and V viewed as [L * Hkv, d], so the sparse attention kernel runs
+//   each (query, head) as a one-head query.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace hsa {
 
@@ -115,25 +116,13 @@ __global__ __launch_bounds__(256) void k_head_landmarks(const uint16_t* __restri
 // Wave w takes rows 32w .. 32w+31 (two 16-row B operands) for all 64
 // columns (four 16-column A operands); the accumulator holds 4 columns x 1
 // row per lane; a chunk's NL landmark rows sit in adjacent lanes, reduced by
-// an xor-shuffle maximum.  Workgroups past the score tiles (y >= n_score_y,
-// x == 0) compute the landmarks of chunks fold_start .. of sequence
-// (y - n_score_y) / nfold when the host folds them in: only when no query
-// scores them (each is its queries' own, always kept, chunk).
+// an xor-shuffle maximum.
 template <int NL>
 __global__ __launch_bounds__(256) void k_head_scores_mfma(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ LK,
                                                           float* __restrict__ scores, int L, int nq, int B, int nb,
-                                                          int m, int Hq, int Hkv, int ctiles, int n_score_y,
-                                                          const uint16_t* __restrict__ K, const int8_t* __restrict__ W,
-                                                          uint16_t* __restrict__ LK_out, int fold_start, int nfold) {
+                                                          int m, int Hq, int Hkv, int ctiles) {
   constexpr int DI = 128, KS = DI / 32;
-  if ((int)blockIdx.y >= n_score_y) {  // folded landmarks (uniform)
-    const int y = (int)blockIdx.y - n_score_y;
-    const int j = fold_start + y % nfold;
-    if (blockIdx.x != 0 || j >= nb) return;
-    head_landmark_chunk<NL>(K, W, LK_out, L, B, nb, Hkv, j, y / nfold, threadIdx.x / kWave, 4);
-    return;
-  }
   const int QPG = Hq / Hkv;
   const int ncols = nq * QPG;
   const int bg = blockIdx.y / ctiles, ct = blockIdx.y % ctiles;
@@ -191,6 +180,106 @@ __global__ __launch_bounds__(256) void k_head_scores_mfma(const uint16_t* __rest
   }
 }
 
+// The select of the per-head rows (sequence, query, head), one row per
+// group of NW waves (NW == 1: four rows per workgroup, one per wave): the
+// exact top-(m-2) of chunks 1..c-1 by score with chunks 0 and c kept
+// (select_top), the chunk list written ascending and -1 padded, then the
+// row's token list written by the whole group from the list kept in LDS:
+// entry e is token s = list[e / B] * B + e % B if s <= t, stored as
+// s * Hkv + g (g = head / QPG), else -1.  The first nfold_wg workgroups
+// instead rebuild the landmarks of chunks fold_start .. of each sequence
+// when the host folds them in (no row of this launch reads landmarks, and
+// the score launch before it read none of those chunks).
+constexpr int kHeadListMax = 1024;  // chunk lists staged in LDS
+
+template <int NW, int R>
+__global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_head_select(
+    const float* __restrict__ scores, int32_t* __restrict__ blk, int32_t* __restrict__ tok, int L, int nq, int B,
+    int nb, int m, int Hq, int Hkv, int rows, int nfold_wg, const uint16_t* __restrict__ K,
+    const int8_t* __restrict__ W, uint16_t* __restrict__ LK_out, int NL, int fold_start, int nfold) {
+  constexpr int QPB = NW == 1 ? 4 : 1;  // rows per workgroup
+  constexpr int GT = NW * kWave;        // threads per row
+  __shared__ SelectSmem<NW> lds[QPB];
+  __shared__ int32_t list[QPB][kHeadListMax];
+  const int wave = threadIdx.x / kWave;
+  if ((int)blockIdx.x < nfold_wg) {  // folded landmarks (uniform)
+    const int j = fold_start + (int)blockIdx.x % nfold;
+    const int bs = (int)blockIdx.x / nfold;
+    if (j >= nb) return;
+    const int nw = blockDim.x / kWave;
+    if (NL == 1) head_landmark_chunk<1>(K, W, LK_out, L, B, nb, Hkv, j, bs, wave, nw);
+    else if (NL == 2) head_landmark_chunk<2>(K, W, LK_out, L, B, nb, Hkv, j, bs, wave, nw);
+    else head_landmark_chunk<4>(K, W, LK_out, L, B, nb, Hkv, j, bs, wave, nw);
+    return;
+  }
+  const int wg = (int)blockIdx.x - nfold_wg;
+  const int q = NW == 1 ? wg * 4 + wave : wg;
+  if (q >= rows) return;  // wave-uniform (NW == 1 only)
+  SelectSmem<NW>& sm = lds[NW == 1 ? wave : 0];
+  int32_t* lst = list[NW == 1 ? wave : 0];
+  const int gtid = NW == 1 ? lane_id() : (int)threadIdx.x;
+  const int qpg = Hq / Hkv;
+  const int g = (q % Hq) / qpg;
+  const int t = query_pos(L, nq, (q / Hq) % nq);
+  const int c = t / B;
+  int32_t* out = blk + (size_t)q * m;
+  int32_t* tq = tok ? tok + (size_t)q * m * B : nullptr;
+  if (c + 1 <= m) {
+    for (int j = gtid; j < m; j += GT) out[j] = j <= c ? j : -1;
+    if (tq)
+      for (int e = gtid; e < m * B; e += GT) tq[e] = e <= t ? e * Hkv + g : -1;
+    return;
+  }
+  const int want = m - 2;
+  const int n = c - 1;  // candidates: chunks 1 .. c-1 (index = chunk - 1)
+  const bool staged = m <= kHeadListMax;
+  if (gtid == 0) {
+    out[0] = 0;
+    out[m - 1] = c;
+    if (staged) {
+      lst[0] = 0;
+      lst[m - 1] = c;
+    }
+  }
+  if (want > 0) {
+    const float* sc = scores + (size_t)q * nb + 1;
+    uint32_t key[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = gtid * R + r;
+      const float v = sc[idx < n ? idx : 0];  // branch-free: all loads in flight together
+      key[r] = idx < n ? score_key(v) : 0u;
+    }
+    select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+      if (!take) return;
+      out[1 + pos] = 1 + idx;
+      if (staged) {
+        lst[1 + pos] = 1 + idx;
+      } else if (tq) {  // lists too long for LDS: each kept chunk's tokens from its thread
+        for (int r = 0; r < B; ++r) tq[(size_t)(1 + pos) * B + r] = ((1 + idx) * B + r) * Hkv + g;
+      }
+    });
+  }
+  if (!tq) return;
+  sel_sync<NW>();
+  if (staged) {
+    // 4 consecutive entries share a chunk (B is a multiple of 4)
+    for (int e = gtid * 4; e < m * B; e += GT * 4) {
+      const int s0 = lst[e / B] * B + e % B;
+      i32x4 v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = s0 + k <= t ? (s0 + k) * Hkv + g : -1;
+      *reinterpret_cast<i32x4*>(tq + e) = v;
+    }
+  } else {
+    for (int e = gtid; e < B; e += GT) {  // the two forced chunks
+      tq[e] = e * Hkv + g;
+      const int s = c * B + e;
+      tq[(size_t)(m - 1) * B + e] = s <= t ? s * Hkv + g : -1;
+    }
+  }
+}
+
 size_t head_scores_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq * s.Hq * s.nb * sizeof(float)); }
 
 hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t* W, int start, uint16_t* LK,
@@ -207,10 +296,45 @@ hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t*
 }
 
 bool head_topm_can_fold(const Dims& s, int start_block) {
-  // the score launch runs and the rebuilt chunks start at the last one,
-  // which no query scores (a query scores chunks below its own)
+  // the rebuilt chunks start at the last one, which no query scores (a
+  // query scores chunks below its own)
   const int c_max = (s.L - 1) / s.B;
-  return c_max + 1 > s.m && start_block >= c_max && start_block < s.nb;
+  return start_block >= c_max && start_block < s.nb;
+}
+
+template <int NW, int R>
+static hipError_t launch_head_select_r(const Dims& s, const float* scores, int32_t* blk, int32_t* tok,
+                                       const HeadFold* fold, hipStream_t st) {
+  const int rows = s.b * s.nq * s.Hq;
+  const int nfold = fold ? s.nb - fold->start_block : 0;
+  const int nfold_wg = s.b * nfold;
+  dim3 grid(nfold_wg + (NW == 1 ? (rows + 3) / 4 : rows)), block(NW == 1 ? 256 : NW * 64);
+  hipLaunchKernelGGL((k_head_select<NW, R>), grid, block, 0, st, scores, blk, tok, s.L, s.nq, s.B, s.nb, s.m, s.Hq,
+                     s.Hkv, rows, nfold_wg, fold ? fold->K : nullptr, fold ? fold->W : nullptr,
+                     fold ? fold->LK : nullptr, s.nL, fold ? fold->start_block : s.nb, max(nfold, 1));
+  return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_head_select(int R, const Dims& s, const float* scores, int32_t* blk, int32_t* tok,
+                                     const HeadFold* fold, hipStream_t st) {
+  switch (R) {
+    case 1: return launch_head_select_r<NW, 1>(s, scores, blk, tok, fold, st);
+    case 2: return launch_head_select_r<NW, 2>(s, scores, blk, tok, fold, st);
+    case 4: return launch_head_select_r<NW, 4>(s, scores, blk, tok, fold, st);
+    case 8: return launch_head_select_r<NW, 8>(s, scores, blk, tok, fold, st);
+    case 16: return launch_head_select_r<NW, 16>(s, scores, blk, tok, fold, st);
+    case 32:
+      if constexpr (NW > 1) return launch_head_select_r<NW, 32>(s, scores, blk, tok, fold, st);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static int pick_r(int n, int nw) {
+  int r = 1;
+  while (r * 64 * nw < n) r <<= 1;
+  return r;
 }
 
 hipError_t launch_head_topm(const Dims& s, const uint16_t* Q, const uint16_t* LK, int32_t* blk, void* ws,
@@ -220,24 +344,23 @@ hipError_t launch_head_topm(const Dims& s, const uint16_t* Q, const uint16_t* LK
   const int c_max = (s.L - 1) / s.B;
   if (c_max + 1 > s.m) {
     const int ctiles = (s.nq * (s.Hq / s.Hkv) + 63) / 64;
-    const int n_score_y = s.b * s.Hkv * ctiles;
-    const int nfold = fold ? s.nb - fold->start_block : 0;
-    dim3 grid((s.nb * s.nL + 127) / 128, n_score_y + s.b * nfold);
-    const uint16_t* K = fold ? fold->K : nullptr;
-    const int8_t* W = fold ? fold->W : nullptr;
-    uint16_t* LK_out = fold ? fold->LK : nullptr;
-    const int fs = fold ? fold->start_block : s.nb;
+    dim3 grid((s.nb * s.nL + 127) / 128, s.b * s.Hkv * ctiles);
 #define HSA_HS(NL)                                                                                               \
   hipLaunchKernelGGL((k_head_scores_mfma<NL>), grid, dim3(256), 0, st, Q, LK, scores, s.L, s.nq, s.B, s.nb, s.m, \
-                     s.Hq, s.Hkv, ctiles, n_score_y, K, W, LK_out, fs, max(nfold, 1))
+                     s.Hq, s.Hkv, ctiles)
     if (s.nL == 1) HSA_HS(1); else if (s.nL == 2) HSA_HS(2); else HSA_HS(4);
 #undef HSA_HS
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-  } else if (fold) {
-    return hipErrorInvalidValue;  // the host folds only into a score launch
   }
-  return launch_block_select(s, s.Hq, scores, blk, st, tok, s.Hkv, s.Hq / s.Hkv);
+  // many rows: one wave per row (<= 512 candidates) or 4 waves per row;
+  // few rows: 16 waves per row (shortest latency)
+  const int rows = s.b * s.nq * s.Hq;
+  const int n_max = c_max - 1;
+  if (rows >= 512 && n_max <= 64 * 8) return launch_head_select<1>(pick_r(n_max, 1), s, scores, blk, tok, fold, st);
+  if (rows >= 512 && n_max <= 4 * 64 * 32)
+    return launch_head_select<4>(pick_r(n_max, 4), s, scores, blk, tok, fold, st);
+  return launch_head_select<16>(pick_r(n_max, 16), s, scores, blk, tok, fold, st);
 }
 
 // The attention of the per-head lists: each (query, head) row is a one-head

@@ -38,13 +38,6 @@ bool block_topm_can_fold(const Dims& s, int start_block);
 hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk,
                              void* ws, hipStream_t st, const SummaryFold* fold = nullptr);
 
-// the exact top-m select over fp32 scores [b*nq*heads, nb] (rows of
-// block 1 .. c-1 filled), `heads` select rows per query; with tok, each
-// row's causal tokens of its kept blocks too (entries s * tok_hkv + g, g =
-// head / tok_qpg, -1 padded to m * B)
-hipError_t launch_block_select(const Dims& s, int heads, const float* scores, int32_t* blk, hipStream_t st,
-                               int32_t* tok = nullptr, int tok_hkv = 1, int tok_qpg = 1);
-
 // step 2 through super-blocks of 2^lgG blocks: S2 summaries of the
 // super-blocks from start_super on, then level 1 (top-m2 super-blocks into
 // sup [b*nq, m2]) and level 2 (top-m blocks among theirs into blk)
@@ -83,8 +76,8 @@ hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t*
                                  hipStream_t st);
 size_t head_scores_ws_bytes(const Dims& s);
 // With `fold` the landmarks of chunks fold->start_block .. are rebuilt in
-// the score launch (only when head_topm_can_fold).  tok: the per-head token
-// lists for launch_head_attn, written by the select.
+// the select launch (only when head_topm_can_fold).  tok: the per-head token
+// lists for launch_head_attn, written by the select (nullptr: none).
 struct HeadFold {
   const uint16_t* K;
   const int8_t* W;
