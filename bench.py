@@ -5,17 +5,20 @@ One step = one hsa_forward call over the workload's whole batch: block
 summaries of the blocks the queries touch, block top-m, token top-k and
 sparse attention, with inputs already resident in HBM (hsa_decode_step for
 sequences of different lengths, hsa_forward_3level for workloads with
-super-blocks).  Prints one JSON line.
+super-blocks, hsa_forward_heads for per-head selection).  Prints one JSON
+line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
-Stage times come from HIP events that hsa_forward records on its stream
-(hsa_sparse_set_stage_events): an untimed pass records all five stage
-boundaries and names the dominant stage; the timed region records only the
-two events around that stage, since each recorded event costs the stream a
-few microseconds.  The roofline entry uses the dominant stage's algorithmic
-bytes (or flops) per launch, computed in closed form below, divided by its
-average duration over the timed steps.
+Kernel times come from start/stop events that each kernel's dispatch
+carries (hsa_sparse_set_kernel_events, hipExtLaunchKernelGGL), which add no
+work to the stream: an untimed pass times every kernel of a step and names
+the dominant (longest) one; in the timed region only that kernel carries
+events.  The roofline entry divides that kernel's algorithmic bytes (or
+flops) per launch, computed in closed form below, by its average duration
+over the timed steps.  Stage times (an untimed pass with the stage events of
+hsa_sparse_set_stage_events, a few microseconds of stream time each) are
+reported alongside.
 The CPU baseline times the plain CPU oracle on a stratified sample of the
 same workload's queries, before the GPU is touched.
 """
@@ -144,33 +147,82 @@ def algorithmic_work(w: Workload, lens=None) -> dict:
     }
 
 
-# ----------------------------------------------------- hardware traffic
-
-
-# kernel sources that define each stage's dominant kernel
-STAGE_SOURCES = {
-    "block_summary": ["block_summary.hip", "summary.hpp", "block_topm_3level.hip", "head_select.hip", "common.hpp"],
-    "block_topm": ["block_topm.hip", "block_topm_3level.hip", "head_select.hip", "select.hpp", "summary.hpp",
-                   "common.hpp"],
-    "token_topk": ["token_topk.hip", "select.hpp", "common.hpp"],
-    "sparse_attn": ["sparse_attn.hip", "common.hpp"],
+KERNEL_STAGE = {
+    "k_block_summary": "block_summary", "k_super_summary": "block_summary", "k_head_landmarks": "block_summary",
+    "k_block_scores": "block_topm", "k_block_scores_mfma": "block_topm", "k_block_select": "block_topm",
+    "k_block_topm_decode": "block_topm", "k_block_topm_l2": "block_topm", "k_block_topm_3level_decode": "block_topm",
+    "k_head_scores_mfma": "block_topm", "k_head_select": "block_topm",
+    "k_token_scores": "token_topk", "k_token_scores_tiled": "token_topk", "k_bm_scores": "token_topk",
+    "k_token_select": "token_topk",
+    "k_sparse_attn": "sparse_attn", "k_attn_merge": "sparse_attn",
 }
 
 
-def stage_source_hash(stage: str) -> str:
+def kernel_work(w: Workload, kernel: str, lens=None) -> dict:
+    """Algorithmic bytes and flops of one launch of `kernel` in one step, and
+    the roof it is measured against.  Kernels that split a stage in two
+    count the intermediate they hand over (fp32 scores, 4 bytes each) on
+    both sides; a kernel that is the whole stage gets the stage's figure."""
+    stage = KERNEL_STAGE.get(kernel)
+    work = algorithmic_work(w, lens)
+    b, nq, dI, nL = w.batch, w.n_q, w.d_index, w.n_landmarks
+    if w.per_head:
+        t = w.seq_len - nq + np.arange(nq, dtype=np.int64)
+        c = t // w.block
+        scored = float(b * w.n_heads_q * np.where(c + 1 <= w.top_m, 0, c - 1).sum())
+        rows = b * nq * w.n_heads_q
+        sel = work["block_topm"]
+        if kernel == "k_head_scores_mfma":
+            return {"bytes": sel["bytes"] - rows * w.top_m * 4 + scored * 4, "flops": sel["flops"], "bound": "hbm"}
+        if kernel == "k_head_select":
+            return {"bytes": scored * 4 + rows * w.top_m * 4 + rows * w.top_m * w.block * 4, "flops": 0.0,
+                    "bound": "hbm"}
+    else:
+        if lens is None:
+            sb, st, kept = (x * b for x in per_query_counts(w))
+        else:
+            sb, st, kept = per_query_counts(w, np.asarray(lens, dtype=np.int64) - 1)
+        sb, st = float(sb.sum()), float(st.sum())
+        nqt = b * nq
+        if kernel == "k_block_scores_mfma":
+            return {"bytes": sb * 4, "flops": 2.0 * dI * nL * sb, "bound": "mfma"}
+        if kernel == "k_block_scores":
+            return {"bytes": nqt * dI * 2 + sb * nL * dI * 2 + sb * 4, "flops": 2.0 * dI * nL * sb, "bound": "hbm"}
+        if kernel == "k_block_select":
+            return {"bytes": sb * 4 + nqt * w.top_m * 4, "flops": 0.0, "bound": "hbm"}
+        if kernel in ("k_token_scores", "k_token_scores_tiled", "k_bm_scores"):
+            return {"bytes": nqt * dI * 2 + st * dI * 2 + st * 4, "flops": 2.0 * dI * st, "bound": "hbm"}
+        if kernel == "k_token_select":
+            return {"bytes": st * 4 + nqt * w.top_k * 4, "flops": 0.0, "bound": "hbm"}
+    if stage is None:
+        return {"bytes": 0.0, "flops": 0.0, "bound": "hbm"}
+    return {"bytes": work[stage]["bytes"], "flops": work[stage]["flops"], "bound": "hbm"}
+
+
+# ----------------------------------------------------- hardware traffic
+
+
+CSRC = os.path.join(ROOT, "hierarchical_index_sparse_amd", "csrc")
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 of the .hip file that defines `kernel` and of every header."""
+    import glob
     import hashlib
     h = hashlib.sha256()
-    for name in STAGE_SOURCES[stage]:
-        with open(os.path.join(ROOT, "hierarchical_index_sparse_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    defining = [f for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+                if f"void {kernel}(" in open(f).read()]
+    for f in defining + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str, stage: str):
+def recorded_traffic(workload: str, kernel: str):
     """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE record
     (profiles/<workload>_traffic.txt), each scaled by what the same counter
-    read for a device copy of known size; None if there is no record or the
-    kernel's sources changed since it was taken."""
+    read for a device copy of known size; None if there is no record for
+    this kernel or its sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -180,7 +232,7 @@ def recorded_traffic(workload: str, stage: str):
             continue
         k, v = line.split(":", 1)
         rec[k.strip()] = v.strip()
-    if rec.get("stage") != stage or rec.get("source_sha256") != stage_source_hash(stage):
+    if rec.get("kernel") != kernel or rec.get("source_sha256") != kernel_source_hash(kernel):
         return None
     copy_kib = float(rec["copy_bytes"]) / 1024.0
     fetch_scale = copy_kib / float(rec["copy_fetch_size_kib"])
@@ -463,7 +515,7 @@ def main():
     if w.group:
         _lib.hsa_super_summary(shape, w.group, out["S"], 0, out["S2"])
 
-    def step():
+    def checked_step():
         if w.per_head:
             _lib.hsa_forward_heads(shape, dev.get("W"), start_block, dev["Q"], dev["K"], dev["V"], out["LK"], None,
                                    out["O"], out["lse"], ws)
@@ -477,6 +529,44 @@ def main():
         else:  # one decode step over sequences of different lengths
             _lib.hsa_decode_step(shape, dev["seq_lens"], dev["qI"], dev["kI"], dev.get("W"), out["S"], dev["Q"],
                                  dev["K"], dev["V"], None, None, out["O"], out["lse"], ws)
+
+    # After one call through the checking wrappers above, steps call the
+    # entry point with its arguments marshalled once, so that the host's
+    # per-call cost (tens of microseconds of Python checks) does not pace
+    # the short decode steps.
+    checked_step()
+    torch.cuda.synchronize()
+    lib = _lib.load()
+    sref = ctypes.byref(shape)
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes = ws.numel()
+
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+
+    if w.per_head:
+        fn, call_args = lib.hsa_forward_heads, (sref, ptr(dev.get("W")), start_block, ptr(dev["Q"]), ptr(dev["K"]),
+                                           ptr(dev["V"]), ptr(out["LK"]), None, ptr(out["O"]), ptr(out["lse"]),
+                                           ptr(ws), nbytes, stream)
+    elif w.group:
+        fn, call_args = lib.hsa_forward_3level, (sref, w.group, w.top_m2, ptr(dev["qI"]), ptr(dev["kI"]),
+                                            ptr(dev.get("W")), start_block, ptr(out["S"]), ptr(out["S2"]),
+                                            ptr(dev["Q"]), ptr(dev["K"]), ptr(dev["V"]), ptr(out["sup"]), None, None,
+                                            ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes, stream)
+    elif lens is None:
+        fn, call_args = lib.hsa_forward, (sref, ptr(dev["qI"]), ptr(dev["kI"]), ptr(dev.get("W")), start_block,
+                                     ptr(out["S"]), ptr(dev["Q"]), ptr(dev["K"]), ptr(dev["V"]), None, None,
+                                     ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes, stream)
+    else:
+        fn, call_args = lib.hsa_decode_step, (sref, ptr(dev["seq_lens"]), ptr(dev["qI"]), ptr(dev["kI"]),
+                                         ptr(dev.get("W")), ptr(out["S"]), ptr(dev["Q"]), ptr(dev["K"]),
+                                         ptr(dev["V"]), None, None, ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes,
+                                         stream)
+
+    def step():
+        st = fn(*call_args)
+        if st != 0:
+            raise _lib.HsaSparseError(st, fn.__name__, lib.hsa_sparse_last_error().decode())
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -508,22 +598,45 @@ def main():
     for ev in events:
         for e in ev:
             hip.destroy(e)
-    dom = max(STAGES, key=lambda n: stage_ms[n])
-    di = STAGES.index(dom)
+    # Kernel breakdown (untimed): every kernel's dispatch carries its own
+    # start/stop events (hsa_sparse_set_kernel_events), which add no work
+    # to the stream; the longest kernel is the dominant one.
+    n_slots = 32
+    kev = [([hip.create() for _ in range(n_slots)], [hip.create() for _ in range(n_slots)]) for _ in range(n_prof)]
+    for s in range(n_prof):
+        _lib.hsa_sparse_set_kernel_events(kev[s][0], kev[s][1])
+        step()
+    torch.cuda.synchronize()
+    names = _lib.hsa_sparse_last_kernels()
+    _lib.hsa_sparse_set_kernel_events(None, None)
+    nk = min(len(names), n_slots)
+    kernel_us = [float(np.mean([hip.elapsed_ms(kev[s][0][i], kev[s][1][i]) for s in range(n_prof)])) * 1000.0
+                 for i in range(nk)]
+    for a, b in kev:
+        for e in a + b:
+            hip.destroy(e)
+    di = int(np.argmax(kernel_us))
+    dom = names[di]
 
-    # Timed region: K whole steps; the dominant stage's launch duration comes
-    # from the events bracketing it in each of these steps.
+    # Timed region: K whole steps; only the dominant kernel's dispatch
+    # carries events, giving its duration in each step (event arrays built
+    # before the loop).
     timed = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    Ev = ctypes.c_void_p * (di + 1)
+    ev_arrays = []
+    for a, b in timed:
+        st_ev, sp_ev = Ev(), Ev()
+        st_ev[di], sp_ev[di] = a, b
+        ev_arrays.append((st_ev, sp_ev))
+    set_kev = lib.hsa_sparse_set_kernel_events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        ev = [None] * 5
-        ev[di], ev[di + 1] = timed[s]
-        _lib.hsa_sparse_set_stage_events(ev)
+    for st_ev, sp_ev in ev_arrays:
+        set_kev(st_ev, sp_ev, di + 1)
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    _lib.hsa_sparse_set_stage_events(None)
+    _lib.hsa_sparse_set_kernel_events(None, None)
     dom_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in timed]))
     for a, b in timed:
         hip.destroy(a)
@@ -545,23 +658,23 @@ def main():
     value = queries / (ms_per_step / 1000.0)
 
     work = algorithmic_work(w, lens)
+    kw = kernel_work(w, dom, lens)
     dom_s = dom_ms / 1000.0
-    # the block stage is a bf16 MFMA contraction only where the MFMA block
-    # scorer runs (two-level selection, >= 64 queries per sequence); the
-    # decode paths are GEMVs over summary rows
-    mfma_block = dom == "block_topm" and not w.group and w.n_q >= 64
-    if mfma_block:
-        achieved = work[dom]["flops"] / dom_s / 1e12
+    # only the MFMA block scorer is measured against the bf16 MFMA roof;
+    # every other kernel streams its operands and is measured against HBM
+    if kw["bound"] == "mfma":
+        achieved = kw["flops"] / dom_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
     else:
-        achieved = work[dom]["bytes"] / dom_s / 1e9
+        achieved = kw["bytes"] / dom_s / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
     roof["traffic"] = recorded_traffic(w.name, dom)
-    roof["stage"] = dom
-    roof["stage_ms_timed"] = dom_ms
-    roof["algorithmic_per_launch"] = work[dom]["flops"] if mfma_block else work[dom]["bytes"]
+    roof["kernel"] = dom
+    roof["stage"] = KERNEL_STAGE.get(dom)
+    roof["kernel_ms_timed"] = dom_ms
+    roof["algorithmic_per_launch"] = kw["flops"] if kw["bound"] == "mfma" else kw["bytes"]
 
     res = {
         "metric": "queries/sec end-to-end (index+attn)",
@@ -589,6 +702,7 @@ def main():
                    **({"selection": "per query head from Q and landmarks of K"} if w.per_head else {}),
                    "parallelism": "single GPU"},
         "stage_ms": stage_ms,
+        "kernel_us": [[n, round(u, 2)] for n, u in zip(names, kernel_us)],
         "gpu_step_ms_all_stage_events": gpu_step_ms,
         "stage_hbm_frac": {n: work[n]["bytes"] / (stage_ms[n] / 1000.0) / 1e9 / HBM_PEAK_GBS for n in STAGES},
         "roofline": roof,

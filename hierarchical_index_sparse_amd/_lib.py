@@ -31,7 +31,7 @@ EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_
            "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
            "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_super_summary",
            "hsa_block_topm_3level", "hsa_forward_3level", "hsa_head_landmarks", "hsa_head_topm",
-           "hsa_forward_heads")
+           "hsa_forward_heads", "hsa_sparse_set_kernel_events", "hsa_sparse_last_kernels")
 
 
 class HsaSparseShape(ctypes.Structure):
@@ -80,6 +80,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_head_landmarks.argtypes = [S, P, P, I32, P, P]
     lib.hsa_head_topm.argtypes = [S, P, P, P, P, SZ, P]
     lib.hsa_forward_heads.argtypes = [S, P, I32, P, P, P, P, P, P, P, P, SZ, P]
+    EV = ctypes.POINTER(ctypes.c_void_p)
+    lib.hsa_sparse_set_kernel_events.argtypes = [EV, EV, ctypes.c_int]
+    lib.hsa_sparse_last_kernels.argtypes = []
+    lib.hsa_sparse_last_kernels.restype = ctypes.c_char_p
     for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
                  "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step"):
         getattr(lib, name).restype = ctypes.c_int
@@ -250,6 +254,23 @@ def hsa_forward_heads(shape, W, summary_start_block, Q, K, V, LK, blk_out, O, ls
                                   _ptr(LK, "LK", _BF16), _ptr(blk_out, "blk_out", _I32, True), _ptr(O, "O", _F32),
                                   _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes, _stream(stream))
     _check(st, "hsa_forward_heads")
+
+
+def hsa_sparse_set_kernel_events(start, stop):
+    """start, stop: equal-length lists of raw hipEvent_t handles (ints; None
+    entries are not recorded), or None to stop recording."""
+    lib = load()
+    if start is None:
+        _check(lib.hsa_sparse_set_kernel_events(None, None, 0), "hsa_sparse_set_kernel_events")
+        return
+    n = len(start)
+    a = (ctypes.c_void_p * n)(*start)
+    b = (ctypes.c_void_p * n)(*stop)
+    _check(lib.hsa_sparse_set_kernel_events(a, b, n), "hsa_sparse_set_kernel_events")
+
+
+def hsa_sparse_last_kernels():
+    return load().hsa_sparse_last_kernels().decode().split(",")
 
 
 def hsa_sparse_set_stage_events(events):

@@ -16,6 +16,23 @@ thread_local std::string g_last_error;
 thread_local hsa_sparse_event_t g_stage_events[5];
 thread_local bool g_record_stages = false;
 
+// per-kernel timing: start/stop events of kernel i of each call, and the
+// names of the last call's kernels
+constexpr int kMaxKernelEvents = 32;
+thread_local hsa_sparse_event_t g_kernel_start[kMaxKernelEvents];
+thread_local hsa_sparse_event_t g_kernel_stop[kMaxKernelEvents];
+thread_local int g_n_kernel_events = 0;
+thread_local int g_kernel_idx = 0;
+thread_local std::string g_kernel_names;
+
+// Opened by every entry point that launches kernels: numbering restarts.
+struct CallScope {
+  CallScope() {
+    g_kernel_idx = 0;
+    if (g_n_kernel_events) g_kernel_names.clear();
+  }
+};
+
 hsa_sparse_status_t fail(hsa_sparse_status_t st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -179,7 +196,50 @@ ForwardLayout forward_layout(const hsa::Dims& d) {
 
 }  // namespace
 
+namespace hsa {
+
+void kernel_slot(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  *start = nullptr;
+  *stop = nullptr;
+  if (!g_n_kernel_events) return;
+  const int i = g_kernel_idx++;
+  if (i < g_n_kernel_events) {
+    *start = (hipEvent_t)g_kernel_start[i];
+    *stop = (hipEvent_t)g_kernel_stop[i];
+  }
+  // "(k_name<T, U>)" -> "k_name"
+  std::string n(name);
+  const size_t a = n.find_first_not_of("( ");
+  n = n.substr(a == std::string::npos ? 0 : a);
+  const size_t e = n.find_first_of("<) ");
+  if (e != std::string::npos) n.resize(e);
+  if (!g_kernel_names.empty()) g_kernel_names += ",";
+  g_kernel_names += n;
+}
+
+}  // namespace hsa
+
 extern "C" {
+
+hsa_sparse_status_t hsa_sparse_set_kernel_events(hsa_sparse_event_t const* start, hsa_sparse_event_t const* stop,
+                                                 int n_events) {
+  if (n_events == 0 && !start && !stop) {
+    g_n_kernel_events = 0;
+    g_kernel_names.clear();
+    return HSA_SPARSE_OK;
+  }
+  if (n_events < 1 || n_events > kMaxKernelEvents || !start || !stop)
+    return fail(HSA_SPARSE_INVALID_ARG, "need 1 to %d start and stop events (or 0 and NULLs)", kMaxKernelEvents);
+  for (int i = 0; i < n_events; ++i) {
+    g_kernel_start[i] = start[i];
+    g_kernel_stop[i] = stop[i];
+  }
+  g_n_kernel_events = n_events;
+  g_kernel_names.clear();
+  return HSA_SPARSE_OK;
+}
+
+const char* hsa_sparse_last_kernels(void) { return g_kernel_names.c_str(); }
 
 const char* hsa_sparse_strerror(hsa_sparse_status_t status) {
   switch (status) {
@@ -234,6 +294,7 @@ size_t hsa_sparse_workspace_size(const hsa_sparse_shape_t* shape, int op) {
 
 hsa_sparse_status_t hsa_block_summary(const hsa_sparse_shape_t* shape, const uint16_t* kI, const int8_t* landmark_W,
                                       int32_t start_block, uint16_t* S, hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kSummary);
   if (st != HSA_SPARSE_OK) return st;
@@ -248,6 +309,7 @@ hsa_sparse_status_t hsa_block_summary(const hsa_sparse_shape_t* shape, const uin
 hsa_sparse_status_t hsa_block_topm(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* S,
                                    int32_t* blk, void* workspace, size_t workspace_bytes,
                                    hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kSelect | kSummary);
   if (st != HSA_SPARSE_OK) return st;
@@ -263,6 +325,7 @@ hsa_sparse_status_t hsa_block_topm(const hsa_sparse_shape_t* shape, const uint16
 hsa_sparse_status_t hsa_token_topk(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,
                                    const int32_t* blk, int32_t* tok, void* workspace, size_t workspace_bytes,
                                    hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kSelect | kSummary);
   if (st != HSA_SPARSE_OK) return st;
@@ -277,6 +340,7 @@ hsa_sparse_status_t hsa_token_topk(const hsa_sparse_shape_t* shape, const uint16
 
 hsa_sparse_status_t hsa_flat_topk(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,
                                   int32_t* tok, void* workspace, size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kFlat);
   if (st != HSA_SPARSE_OK) return st;
@@ -292,6 +356,7 @@ hsa_sparse_status_t hsa_flat_topk(const hsa_sparse_shape_t* shape, const uint16_
 hsa_sparse_status_t hsa_sparse_attn(const hsa_sparse_shape_t* shape, const uint16_t* Q, const uint16_t* K,
                                     const uint16_t* V, const int32_t* tok, float* O, float* lse, void* workspace,
                                     size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kAttn);
   if (st != HSA_SPARSE_OK) return st;
@@ -313,6 +378,7 @@ static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, con
                                         int32_t* blk_out, int32_t* tok_out, float* O, float* lse, void* workspace,
                                         size_t workspace_bytes, hsa_sparse_stream_t stream,
                                         const Level3* l3 = nullptr) {
+  CallScope calls;
   if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
   if (empty(d)) return HSA_SPARSE_OK;
   if (!qI || !kI || !S || !Q || !K || !V || !O)
@@ -397,6 +463,7 @@ hsa_sparse_status_t hsa_decode_step(const hsa_sparse_shape_t* shape, const int32
 
 hsa_sparse_status_t hsa_super_summary(const hsa_sparse_shape_t* shape, int32_t group, const uint16_t* S,
                                       int32_t start_super, uint16_t* S2, hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kSummary);
   if (st != HSA_SPARSE_OK) return st;
@@ -415,6 +482,7 @@ hsa_sparse_status_t hsa_block_topm_3level(const hsa_sparse_shape_t* shape, int32
                                           const uint16_t* qI, const uint16_t* S, const uint16_t* S2, int32_t* sup,
                                           int32_t* blk, void* workspace, size_t workspace_bytes,
                                           hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kSelect | kSummary);
   if (st != HSA_SPARSE_OK) return st;
@@ -450,6 +518,7 @@ hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape, int32_t 
 hsa_sparse_status_t hsa_head_landmarks(const hsa_sparse_shape_t* shape, const uint16_t* K,
                                        const int8_t* landmark_W, int32_t start_block, uint16_t* LK,
                                        hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kHeads);
   if (st != HSA_SPARSE_OK) return st;
@@ -464,6 +533,7 @@ hsa_sparse_status_t hsa_head_landmarks(const hsa_sparse_shape_t* shape, const ui
 hsa_sparse_status_t hsa_head_topm(const hsa_sparse_shape_t* shape, const uint16_t* Q, const uint16_t* LK,
                                   int32_t* blk, void* workspace, size_t workspace_bytes,
                                   hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kHeads | kHeadSel);
   if (st != HSA_SPARSE_OK) return st;
@@ -480,6 +550,7 @@ hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape, const int
                                       int32_t summary_start_block, const uint16_t* Q, const uint16_t* K,
                                       const uint16_t* V, uint16_t* LK, int32_t* blk_out, float* O, float* lse,
                                       void* workspace, size_t workspace_bytes, hsa_sparse_stream_t stream) {
+  CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kHeads | kHeadSel | kAttn);
   if (st != HSA_SPARSE_OK) return st;

@@ -39,9 +39,9 @@ static hipError_t launch_di(const Dims& s, const uint16_t* kI, const int8_t* W, 
   // blocks the new queries touch: at most ceil(nq / B) + 1 per sequence
   dim3 grid(s.lens ? (s.nq + s.B - 1) / s.B + 1 : s.nb - start, s.b);
   switch (s.nL) {
-    case 1: hipLaunchKernelGGL((k_block_summary<DI, 1>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
-    case 2: hipLaunchKernelGGL((k_block_summary<DI, 2>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
-    case 4: hipLaunchKernelGGL((k_block_summary<DI, 4>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
+    case 1: HSA_LAUNCH((k_block_summary<DI, 1>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
+    case 2: HSA_LAUNCH((k_block_summary<DI, 2>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
+    case 4: HSA_LAUNCH((k_block_summary<DI, 4>), grid, dim3(256), 0, st, kI, W, S, s.L, s.B, s.nb, start, s.lens, s.nq); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
 template <int NW, int R>
 static hipError_t launch_select_r(int nq_total, const float* scores, int32_t* blk, const Dims& s, hipStream_t st) {
   dim3 grid(NW == 1 ? (nq_total + 3) / 4 : nq_total), block(NW == 1 ? 256 : NW * 64);
-  hipLaunchKernelGGL((k_block_select<NW, R>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m, nq_total,
+  HSA_LAUNCH((k_block_select<NW, R>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m, nq_total,
                      s.lens);
   return hipGetLastError();
 }
@@ -356,7 +356,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     const int qtiles = (s.nq + 63) / 64;
     dim3 grid((s.nb * s.nL + 127) / 128, qtiles * s.b);
 #define HSA_SM(DI, NL)                                                                                      \
-  hipLaunchKernelGGL((k_block_scores_mfma<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, \
+  HSA_LAUNCH((k_block_scores_mfma<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, \
                      s.nb, s.m, qtiles)
     if (s.dI == 64) {
       if (s.nL == 1) HSA_SM(64, 1); else if (s.nL == 2) HSA_SM(64, 2); else HSA_SM(64, 4);
@@ -374,7 +374,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     const int start = fold ? fold->start_block : s.nb;
     const int ns = max(nsum, 1);
 #define HSA_FD(DI, RR)                                                                                             \
-  hipLaunchKernelGGL((k_block_topm_decode<DI, RR>), grid, dim3(1024), 0, st, qI, S, blk, s.L, s.nq, s.B, s.nb, s.m, \
+  HSA_LAUNCH((k_block_topm_decode<DI, RR>), grid, dim3(1024), 0, st, qI, S, blk, s.L, s.nq, s.B, s.nb, s.m, \
                      nq_total, kI, S_out, start, ns, s.lens)
     if (s.dI == 64) {
       if (n_max <= 1024) HSA_FD(64, 1); else HSA_FD(64, 2);
@@ -392,7 +392,7 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     uint16_t* S_out = fold ? fold->S : nullptr;
     const int start = fold ? fold->start_block : s.nb;
 #define HSA_SC(DI, NL)                                                                                          \
-  hipLaunchKernelGGL((k_block_scores<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, s.nb, s.m, \
+  HSA_LAUNCH((k_block_scores<DI, NL>), grid, dim3(256), 0, st, qI, S, scores, s.L, s.nq, s.B, s.nb, s.m, \
                      kI, W, S_out, start, s.b, s.lens)
     if (s.dI == 64) {
       if (s.nL == 1) HSA_SC(64, 1); else if (s.nL == 2) HSA_SC(64, 2); else HSA_SC(64, 4);

@@ -310,10 +310,10 @@ hipError_t launch_super_summary(const Dims& s, int lgG, const uint16_t* S, int s
   const int n_items = (int)items;
   dim3 grid((unsigned)((items + 255) / 256));
   if (s.dI == 64)
-    hipLaunchKernelGGL((k_super_summary<64>), grid, dim3(256), 0, st, S, S2, s.nb, nsb, s.nL, lgG, start_super,
+    HSA_LAUNCH((k_super_summary<64>), grid, dim3(256), 0, st, S, S2, s.nb, nsb, s.nL, lgG, start_super,
                        n_items);
   else
-    hipLaunchKernelGGL((k_super_summary<128>), grid, dim3(256), 0, st, S, S2, s.nb, nsb, s.nL, lgG, start_super,
+    HSA_LAUNCH((k_super_summary<128>), grid, dim3(256), 0, st, S, S2, s.nb, nsb, s.nL, lgG, start_super,
                        n_items);
   return hipGetLastError();
 }
@@ -323,7 +323,7 @@ static hipError_t launch_l2_r(const Dims& s, int lgG, int m2, const uint16_t* qI
                               const int32_t* sup, int32_t* blk, hipStream_t st) {
   dim3 grid(s.b * s.nq), block(NW * 64);
 #define HSA_L2(DI, NL)                                                                                   \
-  hipLaunchKernelGGL((k_block_topm_l2<DI, NL, NW, R>), grid, block, 0, st, qI, S, sup, blk, s.L, s.nq, s.B, \
+  HSA_LAUNCH((k_block_topm_l2<DI, NL, NW, R>), grid, block, 0, st, qI, S, sup, blk, s.L, s.nq, s.B, \
                      lgG, s.nb, m2, s.m)
   if (s.dI == 64) {
     if (s.nL == 1) HSA_L2(64, 1); else if (s.nL == 2) HSA_L2(64, 2); else HSA_L2(64, 4);
@@ -364,7 +364,7 @@ static hipError_t launch_fused3_r(const Dims& s, int lgG, int m2, const uint16_t
   const int nsb = (s.nb + (1 << lgG) - 1) >> lgG;
   const int nsum = fold ? s.nb - fold->start_block : 0;
   dim3 grid(nq_total + s.b * nsum);
-  hipLaunchKernelGGL((k_block_topm_3level_decode<DI, R1, R2>), grid, dim3(1024), 0, st, qI, S, S2, sup, blk, s.L,
+  HSA_LAUNCH((k_block_topm_3level_decode<DI, R1, R2>), grid, dim3(1024), 0, st, qI, S, S2, sup, blk, s.L,
                      s.nq, s.B, lgG, s.nb, nsb, m2, s.m, nq_total, fold ? fold->kI : nullptr,
                      fold ? fold->S : nullptr, S2_out, fold ? fold->start_block : s.nb, max(nsum, 1));
   return hipGetLastError();

@@ -243,7 +243,7 @@ size_t flat_topk_ws_bytes(const Dims& s) {
 template <int NW, int R>
 static void launch_merge(dim3 grid, size_t dyn, const uint2* lin, const int* cin, uint2* lout, int* cout,
                          int32_t* tok, const Dims& s, int nchunk, int G, int level, hipStream_t st) {
-  hipLaunchKernelGGL((k_flat_merge<NW, R>), grid, dim3(NW * 64), dyn, st, lin, cin, lout, cout, tok, s.L, s.nq, s.k,
+  HSA_LAUNCH((k_flat_merge<NW, R>), grid, dim3(NW * 64), dyn, st, lin, cin, lout, cout, tok, s.L, s.nq, s.k,
                      nchunk, G, level);
 }
 
@@ -259,9 +259,9 @@ hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* k
     const int qtiles = (s.nq + 63) / 64;
     dim3 grid((s.L + kFlatKeysPerWG - 1) / kFlatKeysPerWG, qtiles * s.b);
     if (s.dI == 64)
-      hipLaunchKernelGGL((k_flat_scores<64>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+      HSA_LAUNCH((k_flat_scores<64>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
     else
-      hipLaunchKernelGGL((k_flat_scores<128>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+      HSA_LAUNCH((k_flat_scores<128>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     p += align_up((size_t)nq_total * Lp * sizeof(float));
@@ -279,7 +279,7 @@ hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* k
   }
   // staged final lists: k + 64 ints (k <= kFlatStageMax when a select runs)
   const size_t dyn = s.k < s.L ? sizeof(int) * ((size_t)s.k + kWave) : 0;
-  hipLaunchKernelGGL((k_flat_chunk_select<4, 32>), dim3(nq_total, s.k < s.L ? nchunk : 1), dim3(256), dyn, st,
+  HSA_LAUNCH((k_flat_chunk_select<4, 32>), dim3(nq_total, s.k < s.L ? nchunk : 1), dim3(256), dyn, st,
                      scores, lists[0], counts[0], tok, s.L, s.nq, Lp, s.k, nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !flat_needs_lists(s)) return e;

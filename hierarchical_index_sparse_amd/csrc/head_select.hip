@@ -287,9 +287,9 @@ hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t*
   if (s.b == 0 || start >= s.nb) return hipSuccess;
   dim3 grid(s.nb - start, s.b);
   switch (s.nL) {
-    case 1: hipLaunchKernelGGL((k_head_landmarks<1>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
-    case 2: hipLaunchKernelGGL((k_head_landmarks<2>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
-    case 4: hipLaunchKernelGGL((k_head_landmarks<4>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
+    case 1: HSA_LAUNCH((k_head_landmarks<1>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
+    case 2: HSA_LAUNCH((k_head_landmarks<2>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
+    case 4: HSA_LAUNCH((k_head_landmarks<4>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -309,7 +309,7 @@ static hipError_t launch_head_select_r(const Dims& s, const float* scores, int32
   const int nfold = fold ? s.nb - fold->start_block : 0;
   const int nfold_wg = s.b * nfold;
   dim3 grid(nfold_wg + (NW == 1 ? (rows + 3) / 4 : rows)), block(NW == 1 ? 256 : NW * 64);
-  hipLaunchKernelGGL((k_head_select<NW, R>), grid, block, 0, st, scores, blk, tok, s.L, s.nq, s.B, s.nb, s.m, s.Hq,
+  HSA_LAUNCH((k_head_select<NW, R>), grid, block, 0, st, scores, blk, tok, s.L, s.nq, s.B, s.nb, s.m, s.Hq,
                      s.Hkv, rows, nfold_wg, fold ? fold->K : nullptr, fold ? fold->W : nullptr,
                      fold ? fold->LK : nullptr, s.nL, fold ? fold->start_block : s.nb, max(nfold, 1));
   return hipGetLastError();
@@ -346,7 +346,7 @@ hipError_t launch_head_topm(const Dims& s, const uint16_t* Q, const uint16_t* LK
     const int ctiles = (s.nq * (s.Hq / s.Hkv) + 63) / 64;
     dim3 grid((s.nb * s.nL + 127) / 128, s.b * s.Hkv * ctiles);
 #define HSA_HS(NL)                                                                                               \
-  hipLaunchKernelGGL((k_head_scores_mfma<NL>), grid, dim3(256), 0, st, Q, LK, scores, s.L, s.nq, s.B, s.nb, s.m, \
+  HSA_LAUNCH((k_head_scores_mfma<NL>), grid, dim3(256), 0, st, Q, LK, scores, s.L, s.nq, s.B, s.nb, s.m, \
                      s.Hq, s.Hkv, ctiles)
     if (s.nL == 1) HSA_HS(1); else if (s.nL == 2) HSA_HS(2); else HSA_HS(4);
 #undef HSA_HS

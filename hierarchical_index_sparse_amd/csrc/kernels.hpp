@@ -2,6 +2,7 @@
 // arguments (see api.cpp) and only enqueues work on `stream`.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -9,6 +10,25 @@
 #include "hsa_sparse.h"
 
 namespace hsa {
+
+// Per-kernel timing (hsa_sparse_set_kernel_events): the start and stop
+// events the next kernel of the current call records with its dispatch
+// (both nullptr when not recording), and its name appended to the call's
+// kernel list.
+void kernel_slot(const char* name, hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through this: with recording on,
+// the dispatch itself carries the kernel's start and stop events
+// (hipExtLaunchKernelGGL), so timing a kernel adds no work to the stream.
+#define HSA_LAUNCH(KERNEL, GRID, BLOCK, LDS, ST, ...)                                                      \
+  do {                                                                                                     \
+    hipEvent_t hsa_ev0_, hsa_ev1_;                                                                         \
+    ::hsa::kernel_slot(#KERNEL, &hsa_ev0_, &hsa_ev1_);                                                     \
+    if (hsa_ev0_ || hsa_ev1_)                                                                              \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, ST, hsa_ev0_, hsa_ev1_, 0, __VA_ARGS__);             \
+    else                                                                                                   \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__);                                       \
+  } while (0)
 
 struct Dims {
   int b, L, nq, dI, B, nL, m, k, Hq, Hkv, d;

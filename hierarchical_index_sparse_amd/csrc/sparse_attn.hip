@@ -360,16 +360,16 @@ hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* 
   const float scale_log2 = s.scale * 1.4426950408889634f;
   dim3 grid((n_items + 3) / 4), block(256);
   if (nsplit == 1) {
-    hipLaunchKernelGGL((k_sparse_attn<false>), grid, block, 0, st, Q, K, V, tok, O, lse, nullptr, s.L, s.nq, s.Hq,
+    HSA_LAUNCH((k_sparse_attn<false>), grid, block, 0, st, Q, K, V, tok, O, lse, nullptr, s.L, s.nq, s.Hq,
                        s.Hkv, s.k, chunk, nsplit, scale_log2, n_items, s.lens);
     return hipGetLastError();
   }
   float* part = static_cast<float*>(ws);
-  hipLaunchKernelGGL((k_sparse_attn<true>), grid, block, 0, st, Q, K, V, tok, O, lse, part, s.L, s.nq, s.Hq, s.Hkv,
+  HSA_LAUNCH((k_sparse_attn<true>), grid, block, 0, st, Q, K, V, tok, O, lse, part, s.L, s.nq, s.Hq, s.Hkv,
                      s.k, chunk, nsplit, scale_log2, n_items, s.lens);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_merge, dim3((unsigned)(nq_total * s.Hq)), dim3(256), 0, st, part, O, lse, s.Hq, s.Hkv,
+  HSA_LAUNCH(k_attn_merge, dim3((unsigned)(nq_total * s.Hq)), dim3(256), 0, st, part, O, lse, s.Hq, s.Hkv,
                      nsplit);
   return hipGetLastError();
 }

@@ -608,7 +608,7 @@ size_t token_topk_ws_bytes(const Dims& s) {
 template <int NW, int R, bool STAGED, bool ONEBLK>
 static void launch_tsel_k(const Dims& s, size_t dyn, int log2B, const float* sc, const int32_t* blk, int32_t* tok,
                           hipStream_t st) {
-  hipLaunchKernelGGL((k_token_select<NW, R, STAGED, ONEBLK>), dim3(s.b * s.nq), dim3(NW * 64), dyn, st, sc, blk, tok,
+  HSA_LAUNCH((k_token_select<NW, R, STAGED, ONEBLK>), dim3(s.b * s.nq), dim3(NW * 64), dyn, st, sc, blk, tok,
                      s.L, s.nq, s.B, log2B, s.m, s.k, s.lens);
 }
 
@@ -684,7 +684,7 @@ static hipError_t launch_tiled_t(const Dims& s, const uint16_t* qI, const uint16
   if (e != hipSuccess) return e;
   // about two workgroups per CU in total, at most 4 per tile
   const int parts = std::max(1, std::min(4, (512 + n_tiles - 1) / n_tiles));
-  hipLaunchKernelGGL((k_token_scores_tiled<DI, QW>), dim3(n_tiles * parts), dim3(kTiledWaves * 64), lds, st, qI, kI,
+  HSA_LAUNCH((k_token_scores_tiled<DI, QW>), dim3(n_tiles * parts), dim3(kTiledWaves * 64), lds, st, qI, kI,
                      blk, scores, s.L, s.nq, s.B, s.m, s.k, tiles_per_seq, n_tiles, s.nb, parts);
   return hipGetLastError();
 }
@@ -722,17 +722,17 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
       const int nl = s.b * s.nb;
       const long long total = (long long)nq_total * s.m;
       const int g1 = (int)std::min<long long>((total + 255) / 256, 8192);
-      hipLaunchKernelGGL(k_bm_zero, dim3(std::min((nl + 255) / 256, 1024)), dim3(256), 0, st, counts, nl);
-      hipLaunchKernelGGL(k_bm_count, dim3(g1), dim3(256), 0, st, blk, counts, s.L, s.nq, s.B, s.m, s.k, s.nb, total);
-      hipLaunchKernelGGL(k_bm_scan, dim3(1), dim3(1024), 0, st, counts, offsets, chunk_off, cursor, nl);
-      hipLaunchKernelGGL(k_bm_fill, dim3(g1), dim3(256), 0, st, blk, cursor, entries, s.L, s.nq, s.B, s.m, s.k, s.nb,
+      HSA_LAUNCH(k_bm_zero, dim3(std::min((nl + 255) / 256, 1024)), dim3(256), 0, st, counts, nl);
+      HSA_LAUNCH(k_bm_count, dim3(g1), dim3(256), 0, st, blk, counts, s.L, s.nq, s.B, s.m, s.k, s.nb, total);
+      HSA_LAUNCH(k_bm_scan, dim3(1), dim3(1024), 0, st, counts, offsets, chunk_off, cursor, nl);
+      HSA_LAUNCH(k_bm_fill, dim3(g1), dim3(256), 0, st, blk, cursor, entries, s.L, s.nq, s.B, s.m, s.k, s.nb,
                          total);
       const int gs = (int)((total + kBmChunk - 1) / kBmChunk + nl);
       if (s.dI == 64)
-        hipLaunchKernelGGL((k_bm_scores<64>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off, scores,
+        HSA_LAUNCH((k_bm_scores<64>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off, scores,
                            s.L, s.nq, s.B, s.m, s.nb, nl);
       else
-        hipLaunchKernelGGL((k_bm_scores<128>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off,
+        HSA_LAUNCH((k_bm_scores<128>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off,
                            scores, s.L, s.nq, s.B, s.m, s.nb, nl);
       e = hipGetLastError();
     } else if (qw > 0) {
@@ -740,10 +740,10 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
     } else {
       dim3 grid(s.m, nq_total);
       if (s.dI == 64)
-        hipLaunchKernelGGL((k_token_scores<64>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
+        HSA_LAUNCH((k_token_scores<64>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
                            s.k, s.lens);
       else
-        hipLaunchKernelGGL((k_token_scores<128>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
+        HSA_LAUNCH((k_token_scores<128>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
                            s.k, s.lens);
       e = hipGetLastError();
     }

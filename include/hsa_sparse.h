@@ -394,6 +394,25 @@ hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape,
 typedef struct ihipEvent_t* hsa_sparse_event_t;
 hsa_sparse_status_t hsa_sparse_set_stage_events(hsa_sparse_event_t const* events, int n_events);
 
+/*
+ * Per-kernel timing (profiling aid).  After this call, kernel i (0-based,
+ * in launch order) of every entry-point call made by the calling thread
+ * carries start[i] and stop[i] in its dispatch, recorded when that kernel
+ * starts and ends (hipExtLaunchKernelGGL), so the stream runs no extra
+ * work for them; NULL entries and kernels past n_events - 1 record nothing.
+ * hsa_sparse_last_kernels() then names the kernels of the thread's last
+ * call, comma-separated, in launch order.  The events are the caller's
+ * hipEvent_t handles and must stay valid while such calls are made.
+ * n_events in [1, 32] with non-NULL arrays, or 0 with both NULL to stop.
+ */
+hsa_sparse_status_t hsa_sparse_set_kernel_events(hsa_sparse_event_t const* start,
+                                                 hsa_sparse_event_t const* stop,
+                                                 int n_events);
+
+/* Kernel names of the calling thread's last entry-point call while
+ * per-kernel timing is on ("" otherwise).  Valid until the next call. */
+const char* hsa_sparse_last_kernels(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -263,3 +263,15 @@ def test_per_head_validation(lib):
     assert lib.hsa_head_landmarks(ctypes.byref(t), None, None, 64, None, None) == 0  # past the last chunk
     assert lib.hsa_forward_heads(ctypes.byref(shape(**dict(base, batch=0))), None, 0, None, None, None, None, None,
                                  None, None, None, 0, None) == 0
+
+
+def test_kernel_event_validation(lib):
+    Ev = ctypes.c_void_p * 40
+    a, b = Ev(), Ev()
+    assert lib.hsa_sparse_set_kernel_events(a, b, 33) == 1      # at most 32 kernels
+    assert lib.hsa_sparse_set_kernel_events(a, None, 4) == 1
+    assert lib.hsa_sparse_set_kernel_events(None, None, 0) == 0  # off
+    assert lib.hsa_sparse_last_kernels() == b""
+    # NULL events are allowed: kernels are then named but not timed
+    assert lib.hsa_sparse_set_kernel_events(a, b, 4) == 0
+    assert lib.hsa_sparse_set_kernel_events(None, None, 0) == 0
