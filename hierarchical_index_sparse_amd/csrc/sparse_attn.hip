@@ -274,57 +274,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   }
 }
 
-// Log-sum-exp merge of the splits of one (query, head): 256 threads = 8
-// split groups x 32 float4 column groups; the groups meet in LDS.
+// Log-sum-exp merge of the splits of one (query, head), spread over CC
+// workgroups of 128 / CC output columns each: the partials come from other
+// XCDs' caches, so the merge is paced by how many loads the CUs keep in
+// flight, and with few (query, head) rows more CUs must take part.  256
+// threads = 8 * CC split groups x 32 / CC float4 column lanes; a group loads
+// 4 splits' partials per round, merges them against the group's own running
+// maximum, and the groups meet in LDS, rescaled to the overall maximum.
+template <int CC>
 __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, float* __restrict__ O,
                                                     float* __restrict__ lse, int Hq, int Hkv, int nsplit) {
-  __shared__ float red[8][129];
-  __shared__ float wmax[4];
-  const int qh = blockIdx.x;
+  constexpr int U = 4;                // splits per group and round
+  constexpr int LANES = 32 / CC;      // float4 lanes per group
+  constexpr int NG = 256 / LANES;     // split groups
+  constexpr int COLS = 128 / CC;      // output columns of this workgroup
+  __shared__ float red[NG][COLS + 1];
+  __shared__ float gmax[NG];
+  const int qh = blockIdx.x / CC;
+  const int chunk = blockIdx.x % CC;
   const int q = qh / Hq, h = qh % Hq;
   const int G = Hq / Hkv;
   const int g = h / G, head = h % G;
   const int tid = threadIdx.x;
   const float* base = part + ((size_t)(q * Hkv + g) * nsplit * 16 + head) * kPartStride;
   const size_t sstride = (size_t)16 * kPartStride;
+  const int sg = tid / LANES, dq = tid % LANES;
+  const int col = chunk * COLS + 4 * dq;
 
-  float M = -INFINITY;
-  for (int s = tid; s < nsplit; s += 256) M = fmaxf(M, base[s * sstride + 128]);
-  M = group_max_f<kWave>(M);
-  if (lane_id() == 0) wmax[tid / kWave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-
-  const int sg = tid / 32, dq = tid % 32;
+  float Mg = -INFINITY, Lt = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float Lt = 0.f;
-  if (M != -INFINITY) {
-    for (int s = sg; s < nsplit; s += 8) {
-      const float* p = base + s * sstride;
-      const float wgt = exp2f(p[128] - M);
-      const float4 v = *reinterpret_cast<const float4*>(p + 4 * dq);
-      acc.x += wgt * v.x;
-      acc.y += wgt * v.y;
-      acc.z += wgt * v.z;
-      acc.w += wgt * v.w;
-      Lt += wgt * p[129];
+  for (int s0 = sg; s0 < nsplit; s0 += NG * U) {
+    float4 v[U];
+    float mx[U], ls[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* p = base + (size_t)min(s0 + NG * u, nsplit - 1) * sstride;
+      mx[u] = p[128];
+      ls[u] = p[129];
+      v[u] = *reinterpret_cast<const float4*>(p + col);
+    }
+    float Mn = Mg;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + NG * u < nsplit) Mn = fmaxf(Mn, mx[u]);
+    if (Mn == -INFINITY) continue;  // no token in these splits
+    const float r = exp2f(Mg - Mn);  // 0 on the first round
+    acc.x *= r;
+    acc.y *= r;
+    acc.z *= r;
+    acc.w *= r;
+    Lt *= r;
+    Mg = Mn;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + NG * u >= nsplit) break;
+      const float wgt = exp2f(mx[u] - Mg);
+      acc.x += wgt * v[u].x;
+      acc.y += wgt * v[u].y;
+      acc.z += wgt * v[u].z;
+      acc.w += wgt * v[u].w;
+      Lt += wgt * ls[u];
     }
   }
   red[sg][4 * dq] = acc.x;
   red[sg][4 * dq + 1] = acc.y;
   red[sg][4 * dq + 2] = acc.z;
   red[sg][4 * dq + 3] = acc.w;
-  if (dq == 0) red[sg][128] = Lt;
+  if (dq == 0) {
+    red[sg][COLS] = Lt;
+    gmax[sg] = Mg;
+  }
   __syncthreads();
-  if (tid < 128) {
+  // groups past the splits hold nothing: only min(NG, nsplit) are read
+  const int ng = min(NG, nsplit);
+  if (tid < COLS) {
+    float M = -INFINITY;
+    for (int k = 0; k < ng; ++k) M = fmaxf(M, gmax[k]);
     float a = 0.f, l = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      a += red[k][tid];
-      l += red[k][128];
+    if (M != -INFINITY) {
+      for (int k = 0; k < ng; ++k) {
+        const float wk = exp2f(gmax[k] - M);  // 0 for a group without tokens
+        a += wk * red[k][tid];
+        l += wk * red[k][COLS];
+      }
     }
-    O[(size_t)qh * 128 + tid] = l > 0.f ? a / l : 0.f;
-    if (lse && tid == 0) lse[qh] = l > 0.f ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
+    O[(size_t)qh * 128 + chunk * COLS + tid] = l > 0.f ? a / l : 0.f;
+    if (lse && chunk == 0 && tid == 0) lse[qh] = l > 0.f ? (M + log2f(l)) * 0.69314718055994531f : -INFINITY;
   }
 }
 
@@ -369,8 +404,17 @@ hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* 
                      s.k, chunk, nsplit, scale_log2, n_items, s.lens);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  HSA_LAUNCH(k_attn_merge, dim3((unsigned)(nq_total * s.Hq)), dim3(256), 0, st, part, O, lse, s.Hq, s.Hkv,
-                     nsplit);
+  // about 1024 merge workgroups: few (query, head) rows get more column chunks
+  const long long rows = nq_total * s.Hq;
+  const dim3 mb(256);
+  if (rows >= 512)
+    HSA_LAUNCH(k_attn_merge<1>, dim3((unsigned)rows), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  else if (rows >= 256)
+    HSA_LAUNCH(k_attn_merge<2>, dim3((unsigned)(rows * 2)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  else if (rows >= 128)
+    HSA_LAUNCH(k_attn_merge<4>, dim3((unsigned)(rows * 4)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  else
+    HSA_LAUNCH(k_attn_merge<8>, dim3((unsigned)(rows * 8)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
   return hipGetLastError();
 }
 
