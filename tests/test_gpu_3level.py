@@ -170,7 +170,16 @@ def test_decode_3level_1m_sampled():
     w = WORKLOADS["decode_3level_1m"]
     inp = datagen.make_inputs(w)
     dev = pipeline.to_device(inp)
-    g = pipeline.to_host(pipeline.run_forward_3level(w, dev))
+    # bench.py's configuration: state built first, then the step from the
+    # newest block (its summary and its super-block's folded into the launch)
+    out = pipeline.alloc_outputs(w)
+    shape = _lib.shape_of(w)
+    _lib.hsa_block_summary(shape, dev["kI"], None, 0, out["S"])
+    _lib.hsa_super_summary(shape, w.group, out["S"], 0, out["S2"])
+    start = (w.seq_len - w.n_q) // w.block
+    out["S"][:, start:] = 0
+    out["S2"][:, start // w.group:] = 0
+    g = pipeline.to_host(pipeline.run_forward_3level(w, dev, out, summary_start_block=start))
     t = w.query_pos(0)
     c, C = t // w.block, t // (w.block * w.group)
     for b in range(w.batch):

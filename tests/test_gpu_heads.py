@@ -183,7 +183,13 @@ def test_head_decode_512k_sampled():
     w = WORKLOADS["head_decode_512k"]
     inp = datagen.make_inputs(w)
     dev = pipeline.to_device(inp)
-    g = pipeline.to_host(pipeline.run_forward_heads(w, dev))
+    # bench.py's configuration: landmarks built first, then the step from the
+    # newest chunk (its landmarks folded into the select launch)
+    out = pipeline.alloc_outputs(w)
+    _lib.hsa_head_landmarks(_lib.shape_of(w), dev["K"], dev["W"], 0, out["LK"])
+    start = (w.seq_len - w.n_q) // w.block
+    out["LK"][:, start:] = 0
+    g = pipeline.to_host(pipeline.run_forward_heads(w, dev, out, summary_start_block=start))
     t = w.query_pos(0)
     c = t // w.block
     for b in range(w.batch):
