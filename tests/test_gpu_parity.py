@@ -229,3 +229,22 @@ def test_full_size_workload(name):
     if w.needles:
         for b in range(w.batch):
             assert set(inp["needles"][b].tolist()) <= set(gpu["blk"][b, 0].tolist())
+
+
+@pytest.mark.parametrize("name,L,nq,dI,B,m,k", [
+    # the block select at its capacity: 32770 blocks, 32768 scored per query
+    ("max_block_select", 8 * 32770, 2, 64, 8, 64, 512),
+    # the token select at its capacity: 256 kept blocks of 128 (32768
+    # candidates), 8192 kept (the longest staged list)
+    ("max_token_select", 65536, 2, 128, 128, 256, 8192),
+])
+def test_maximum_select_sizes(name, L, nq, dI, B, m, k):
+    w = small(name, batch=2, seq_len=L, n_q=nq, d_index=dI, block=B, top_m=m, top_k=k, n_heads_q=2,
+              n_heads_kv=1)
+    inp = make_small(w, 3)
+    dev = pipeline.to_device(inp)
+    gpu = pipeline.to_host(pipeline.run_forward(w, dev))
+    S = oracle_summaries(inp, w)
+    check_summaries(gpu["S"], S)
+    check_list_invariants(gpu, w)
+    check_queries(gpu, inp, w, S, [(b, i) for b in range(w.batch) for i in range(nq)])
