@@ -545,9 +545,9 @@ def main():
         return None if t is None else t.data_ptr()
 
     if w.per_head:
-        fn, call_args = lib.hsa_forward_heads, (sref, ptr(dev.get("W")), start_block, ptr(dev["Q"]), ptr(dev["K"]),
-                                           ptr(dev["V"]), ptr(out["LK"]), None, ptr(out["O"]), ptr(out["lse"]),
-                                           ptr(ws), nbytes, stream)
+        fn, call_args = lib.hsa_forward_heads, (sref, None, ptr(dev.get("W")), start_block, ptr(dev["Q"]),
+                                                ptr(dev["K"]), ptr(dev["V"]), ptr(out["LK"]), None, ptr(out["O"]),
+                                                ptr(out["lse"]), ptr(ws), nbytes, stream)
     elif w.group:
         fn, call_args = lib.hsa_forward_3level, (sref, w.group, w.top_m2, ptr(dev["qI"]), ptr(dev["kI"]),
                                             ptr(dev.get("W")), start_block, ptr(out["S"]), ptr(out["S2"]),

@@ -79,7 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_forward_3level.argtypes = [S, I32, I32, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_head_landmarks.argtypes = [S, P, P, I32, P, P]
     lib.hsa_head_topm.argtypes = [S, P, P, P, P, SZ, P]
-    lib.hsa_forward_heads.argtypes = [S, P, I32, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_heads.argtypes = [S, P, P, I32, P, P, P, P, P, P, P, P, SZ, P]
     EV = ctypes.POINTER(ctypes.c_void_p)
     lib.hsa_sparse_set_kernel_events.argtypes = [EV, EV, ctypes.c_int]
     lib.hsa_sparse_last_kernels.argtypes = []
@@ -247,9 +247,10 @@ def hsa_head_topm(shape, Q, LK, blk, workspace=None, stream=None):
 
 
 def hsa_forward_heads(shape, W, summary_start_block, Q, K, V, LK, blk_out, O, lse=None, workspace=None,
-                      stream=None):
+                      stream=None, seq_lens=None):
     ws, nbytes = _workspace(shape, HSA_SPARSE_OP_FORWARD_HEADS, workspace, Q.device)
-    st = load().hsa_forward_heads(ctypes.byref(shape), _ptr(W, "W", _I8, True), int(summary_start_block),
+    st = load().hsa_forward_heads(ctypes.byref(shape), _ptr(seq_lens, "seq_lens", _I32, True),
+                                  _ptr(W, "W", _I8, True), int(summary_start_block),
                                   _ptr(Q, "Q", _BF16), _ptr(K, "K", _BF16), _ptr(V, "V", _BF16),
                                   _ptr(LK, "LK", _BF16), _ptr(blk_out, "blk_out", _I32, True), _ptr(O, "O", _F32),
                                   _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes, _stream(stream))

@@ -546,15 +546,19 @@ hsa_sparse_status_t hsa_head_topm(const hsa_sparse_shape_t* shape, const uint16_
   return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_head_topm");
 }
 
-hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape, const int8_t* landmark_W,
-                                      int32_t summary_start_block, const uint16_t* Q, const uint16_t* K,
-                                      const uint16_t* V, uint16_t* LK, int32_t* blk_out, float* O, float* lse,
-                                      void* workspace, size_t workspace_bytes, hsa_sparse_stream_t stream) {
+hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape, const int32_t* seq_lens,
+                                      const int8_t* landmark_W, int32_t summary_start_block, const uint16_t* Q,
+                                      const uint16_t* K, const uint16_t* V, uint16_t* LK, int32_t* blk_out,
+                                      float* O, float* lse, void* workspace, size_t workspace_bytes,
+                                      hsa_sparse_stream_t stream) {
   CallScope calls;
   hsa::Dims d;
   hsa_sparse_status_t st = check_shape(shape, d, kHeads | kHeadSel | kAttn);
   if (st != HSA_SPARSE_OK) return st;
   if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
+  if (seq_lens && d.nq != 1 && d.b != 0)
+    return fail(HSA_SPARSE_INVALID_ARG, "seq_lens needs n_q == 1 (got %d)", d.nq);
+  d.lens = seq_lens;
   if (d.nL > 1 && !landmark_W) return fail(HSA_SPARSE_INVALID_ARG, "n_landmarks > 1 needs landmark_W");
   if (empty(d)) return HSA_SPARSE_OK;
   if (!Q || !K || !V || !LK || !O) return fail(HSA_SPARSE_INVALID_ARG, "Q, K, V, LK or O is NULL");

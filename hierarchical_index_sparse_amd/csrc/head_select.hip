@@ -36,7 +36,8 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
   return __float_as_uint((float)__longlong_as_double((long long)u)) >> 16;  // exact: 8 significant bits
 }
 
-// The landmarks of chunk j of sequence b (all kv heads), computed by the
+// The landmarks of chunk j of sequence b (all kv heads; rows at or past the
+// sequence's length Lb count as zero), computed by the
 // calling waves (wave of nw): a K row (Hkv * 128 bf16) is Hkv groups of 16
 // lanes x 16 bytes; wave w takes groups w, w + nw, ...; lane = (row phase
 // p = lane / 16, 16-byte column chunk lane % 16) sums rows p, p + 4, ...
@@ -45,13 +46,13 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
 // not depend on this order.  No LDS.
 template <int NL>
 __device__ __forceinline__ void head_landmark_chunk(const uint16_t* __restrict__ K, const int8_t* __restrict__ W,
-                                                    uint16_t* __restrict__ LK, int L, int B, int nb, int Hkv, int j,
-                                                    int b, int wave, int nw) {
+                                                    uint16_t* __restrict__ LK, int L, int Lb, int B, int nb, int Hkv,
+                                                    int j, int b, int wave, int nw) {
   constexpr int U = 8;
   const int lane = lane_id();
   const int p = lane >> 4, cl = lane & 15;
   const int RW = Hkv * 128;
-  const int rows = min(B, L - j * B);  // rows of the chunk inside the sequence
+  const int rows = min(B, Lb - j * B);  // rows of the chunk inside the sequence (L is the row stride)
   for (int cg = wave; cg < Hkv; cg += nw) {
     const int col = (cg * 16 + cl) * 8;
     double acc[NL][8];
@@ -100,14 +101,16 @@ __device__ __forceinline__ void head_landmark_chunk(const uint16_t* __restrict__
   }
 }
 
-// Workgroup (x, b): the landmarks of chunk start + x of sequence b.
+// Workgroup (x, b): the landmarks of chunk start + x of sequence b; with
+// per-sequence lengths (one query each), of chunk (Lb - 1) / B + x.
 template <int NL>
 __global__ __launch_bounds__(256) void k_head_landmarks(const uint16_t* __restrict__ K, const int8_t* __restrict__ W,
                                                         uint16_t* __restrict__ LK, int L, int B, int nb, int Hkv,
-                                                        int start) {
-  const int j = start + (int)blockIdx.x;
-  if (j >= nb) return;
-  head_landmark_chunk<NL>(K, W, LK, L, B, nb, Hkv, j, blockIdx.y, threadIdx.x / kWave, 4);
+                                                        int start, const int32_t* __restrict__ lens) {
+  const int Lb = seq_len_of(lens, L, blockIdx.y);
+  const int j = (lens ? (Lb - 1) / B : start) + (int)blockIdx.x;
+  if (j >= nb || j * B >= Lb) return;  // uniform
+  head_landmark_chunk<NL>(K, W, LK, L, Lb, B, nb, Hkv, j, blockIdx.y, threadIdx.x / kWave, 4);
 }
 
 // Workgroup (x, y): 128 landmark rows (chunk j, landmark l: row j*NL + l) of
@@ -121,14 +124,16 @@ template <int NL>
 __global__ __launch_bounds__(256) void k_head_scores_mfma(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ LK,
                                                           float* __restrict__ scores, int L, int nq, int B, int nb,
-                                                          int m, int Hq, int Hkv, int ctiles) {
+                                                          int m, int Hq, int Hkv, int ctiles,
+                                                          const int32_t* __restrict__ lens) {
   constexpr int DI = 128, KS = DI / 32;
   const int QPG = Hq / Hkv;
   const int ncols = nq * QPG;
   const int bg = blockIdx.y / ctiles, ct = blockIdx.y % ctiles;
   const int b = bg / Hkv, g = bg % Hkv;
+  const int Lb = seq_len_of(lens, L, b);
   const int col0 = ct * 64;
-  const int c_last = query_pos(L, nq, (min(ncols, col0 + 64) - 1) / QPG) / B;
+  const int c_last = query_pos(Lb, nq, (min(ncols, col0 + 64) - 1) / QPG) / B;
   if (c_last + 1 <= m) return;  // no query of the tile needs scores
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -171,7 +176,7 @@ __global__ __launch_bounds__(256) void k_head_scores_mfma(const uint16_t* __rest
           const int col = col0 + 16 * mt + 4 * gq + e;
           if (col >= ncols) continue;
           const int i = col / QPG;
-          const int c = query_pos(L, nq, i) / B;
+          const int c = query_pos(Lb, nq, i) / B;
           if (c + 1 > m && j >= 1 && j < c)
             scores[(((size_t)b * nq + i) * Hq + g * QPG + col % QPG) * nb + j] = acc[e];
         }
@@ -196,20 +201,23 @@ template <int NW, int R>
 __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_head_select(
     const float* __restrict__ scores, int32_t* __restrict__ blk, int32_t* __restrict__ tok, int L, int nq, int B,
     int nb, int m, int Hq, int Hkv, int rows, int nfold_wg, const uint16_t* __restrict__ K,
-    const int8_t* __restrict__ W, uint16_t* __restrict__ LK_out, int NL, int fold_start, int nfold) {
+    const int8_t* __restrict__ W, uint16_t* __restrict__ LK_out, int NL, int fold_start, int nfold,
+    const int32_t* __restrict__ lens) {
   constexpr int QPB = NW == 1 ? 4 : 1;  // rows per workgroup
   constexpr int GT = NW * kWave;        // threads per row
   __shared__ SelectSmem<NW> lds[QPB];
   __shared__ int32_t list[QPB][kHeadListMax];
   const int wave = threadIdx.x / kWave;
   if ((int)blockIdx.x < nfold_wg) {  // folded landmarks (uniform)
-    const int j = fold_start + (int)blockIdx.x % nfold;
     const int bs = (int)blockIdx.x / nfold;
-    if (j >= nb) return;
+    const int Lb = seq_len_of(lens, L, bs);
+    // per-sequence lengths (one query each): the chunk of the sequence's query
+    const int j = (lens ? (Lb - 1) / B : fold_start) + (int)blockIdx.x % nfold;
+    if (j >= nb || j * B >= Lb) return;
     const int nw = blockDim.x / kWave;
-    if (NL == 1) head_landmark_chunk<1>(K, W, LK_out, L, B, nb, Hkv, j, bs, wave, nw);
-    else if (NL == 2) head_landmark_chunk<2>(K, W, LK_out, L, B, nb, Hkv, j, bs, wave, nw);
-    else head_landmark_chunk<4>(K, W, LK_out, L, B, nb, Hkv, j, bs, wave, nw);
+    if (NL == 1) head_landmark_chunk<1>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
+    else if (NL == 2) head_landmark_chunk<2>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
+    else head_landmark_chunk<4>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
     return;
   }
   const int wg = (int)blockIdx.x - nfold_wg;
@@ -220,7 +228,7 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_head_select(
   const int gtid = NW == 1 ? lane_id() : (int)threadIdx.x;
   const int qpg = Hq / Hkv;
   const int g = (q % Hq) / qpg;
-  const int t = query_pos(L, nq, (q / Hq) % nq);
+  const int t = query_pos(seq_len_of(lens, L, q / (Hq * nq)), nq, (q / Hq) % nq);
   const int c = t / B;
   int32_t* out = blk + (size_t)q * m;
   int32_t* tq = tok ? tok + (size_t)q * m * B : nullptr;
@@ -284,12 +292,13 @@ size_t head_scores_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq 
 
 hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t* W, int start, uint16_t* LK,
                                  hipStream_t st) {
-  if (s.b == 0 || start >= s.nb) return hipSuccess;
-  dim3 grid(s.nb - start, s.b);
+  if (s.b == 0 || (!s.lens && start >= s.nb)) return hipSuccess;
+  // per-sequence lengths: the chunks the new queries touch (one query: one)
+  dim3 grid(s.lens ? (s.nq + s.B - 1) / s.B : s.nb - start, s.b);
   switch (s.nL) {
-    case 1: HSA_LAUNCH((k_head_landmarks<1>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
-    case 2: HSA_LAUNCH((k_head_landmarks<2>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
-    case 4: HSA_LAUNCH((k_head_landmarks<4>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start); break;
+    case 1: HSA_LAUNCH((k_head_landmarks<1>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start, s.lens); break;
+    case 2: HSA_LAUNCH((k_head_landmarks<2>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start, s.lens); break;
+    case 4: HSA_LAUNCH((k_head_landmarks<4>), grid, dim3(256), 0, st, K, W, LK, s.L, s.B, s.nb, s.Hkv, start, s.lens); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -297,7 +306,9 @@ hipError_t launch_head_landmarks(const Dims& s, const uint16_t* K, const int8_t*
 
 bool head_topm_can_fold(const Dims& s, int start_block) {
   // the rebuilt chunks start at the last one, which no query scores (a
-  // query scores chunks below its own)
+  // query scores chunks below its own); with per-sequence lengths (one
+  // query each) the rebuilt chunk is each sequence's own
+  if (s.lens) return s.nq == 1;
   const int c_max = (s.L - 1) / s.B;
   return start_block >= c_max && start_block < s.nb;
 }
@@ -306,12 +317,12 @@ template <int NW, int R>
 static hipError_t launch_head_select_r(const Dims& s, const float* scores, int32_t* blk, int32_t* tok,
                                        const HeadFold* fold, hipStream_t st) {
   const int rows = s.b * s.nq * s.Hq;
-  const int nfold = fold ? s.nb - fold->start_block : 0;
+  const int nfold = fold ? (s.lens ? 1 : s.nb - fold->start_block) : 0;
   const int nfold_wg = s.b * nfold;
   dim3 grid(nfold_wg + (NW == 1 ? (rows + 3) / 4 : rows)), block(NW == 1 ? 256 : NW * 64);
   HSA_LAUNCH((k_head_select<NW, R>), grid, block, 0, st, scores, blk, tok, s.L, s.nq, s.B, s.nb, s.m, s.Hq,
                      s.Hkv, rows, nfold_wg, fold ? fold->K : nullptr, fold ? fold->W : nullptr,
-                     fold ? fold->LK : nullptr, s.nL, fold ? fold->start_block : s.nb, max(nfold, 1));
+                     fold ? fold->LK : nullptr, s.nL, fold ? fold->start_block : s.nb, max(nfold, 1), s.lens);
   return hipGetLastError();
 }
 
@@ -347,7 +358,7 @@ hipError_t launch_head_topm(const Dims& s, const uint16_t* Q, const uint16_t* LK
     dim3 grid((s.nb * s.nL + 127) / 128, s.b * s.Hkv * ctiles);
 #define HSA_HS(NL)                                                                                               \
   HSA_LAUNCH((k_head_scores_mfma<NL>), grid, dim3(256), 0, st, Q, LK, scores, s.L, s.nq, s.B, s.nb, s.m, \
-                     s.Hq, s.Hkv, ctiles)
+             s.Hq, s.Hkv, ctiles, s.lens)
     if (s.nL == 1) HSA_HS(1); else if (s.nL == 2) HSA_HS(2); else HSA_HS(4);
 #undef HSA_HS
     hipError_t e = hipGetLastError();
@@ -372,6 +383,7 @@ static Dims attn_view(const Dims& s) {
   v.Hkv = 1;
   v.L = s.L * s.Hkv;
   v.k = s.m * s.B;
+  v.lens = nullptr;  // the lists hold causal tokens only (as rows s * Hkv + g)
   return v;
 }
 

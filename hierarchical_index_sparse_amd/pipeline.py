@@ -88,12 +88,13 @@ def run_forward_3level(w: Workload, dev: dict, out: dict | None = None, keep_lis
 
 
 def run_forward_heads(w: Workload, dev: dict, out: dict | None = None, keep_lists: bool = True,
-                      workspace: torch.Tensor | None = None, summary_start_block: int = 0) -> dict:
+                      workspace: torch.Tensor | None = None, summary_start_block: int = 0,
+                      seq_lens: torch.Tensor | None = None) -> dict:
     """Per-head chunk selection and attention through hsa_forward_heads."""
     shape = _lib.shape_of(w)
     out = out or alloc_outputs(w, dev["Q"].device)
     _lib.hsa_forward_heads(shape, dev.get("W"), summary_start_block, dev["Q"], dev["K"], dev["V"], out["LK"],
-                           out["blk"] if keep_lists else None, out["O"], out["lse"], workspace)
+                           out["blk"] if keep_lists else None, out["O"], out["lse"], workspace, seq_lens=seq_lens)
     return out
 
 

@@ -358,6 +358,11 @@ hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape,
  *   top_m * block tokens per (query, head) plus scratch).  Stage events
  *   mark landmarks (1), selection (2) and attention (4); event 3 is
  *   recorded right after 2.
+ *   seq_lens: NULL, or a decode step over sequences of different lengths
+ *   as for hsa_decode_step: device int32 [batch], n_q must be 1, seq_len
+ *   is the capacity, the query of sequence b sits at L_b - 1 and this call
+ *   rebuilds the landmarks of chunk (L_b - 1) / block of every sequence
+ *   (summary_start_block is then not read).
  * Errors: as for the other entry points; nothing is launched on an error.
  */
 hsa_sparse_status_t hsa_head_landmarks(const hsa_sparse_shape_t* shape,
@@ -373,6 +378,7 @@ hsa_sparse_status_t hsa_head_topm(const hsa_sparse_shape_t* shape,
                                   hsa_sparse_stream_t stream);
 
 hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape,
+                                      const int32_t* seq_lens,
                                       const int8_t* landmark_W,
                                       int32_t summary_start_block,
                                       const uint16_t* Q, const uint16_t* K,

@@ -236,7 +236,8 @@ def test_three_level_validation(lib):
 
 def test_per_head_validation(lib):
     def fwd(s, ws=1 << 40, W=None, LK=FAKE):
-        return lib.hsa_forward_heads(ctypes.byref(s), W, 0, FAKE, FAKE, FAKE, LK, None, FAKE, None, FAKE, ws, None)
+        return lib.hsa_forward_heads(ctypes.byref(s), None, W, 0, FAKE, FAKE, FAKE, LK, None, FAKE, None, FAKE, ws,
+                                     None)
 
     base = dict(n_q=1, block=64, top_m=8, n_heads_q=8, n_heads_kv=2, d_index=0, top_k=0)
     assert fwd(shape(**dict(base, top_m=1))) == 1
@@ -261,8 +262,11 @@ def test_per_head_validation(lib):
     assert lib.hsa_head_landmarks(ctypes.byref(t), FAKE, None, -1, FAKE, None) == 1
     assert lib.hsa_head_landmarks(ctypes.byref(shape(**dict(base, n_landmarks=2))), FAKE, None, 0, FAKE, None) == 1
     assert lib.hsa_head_landmarks(ctypes.byref(t), None, None, 64, None, None) == 0  # past the last chunk
-    assert lib.hsa_forward_heads(ctypes.byref(shape(**dict(base, batch=0))), None, 0, None, None, None, None, None,
-                                 None, None, None, 0, None) == 0
+    assert lib.hsa_forward_heads(ctypes.byref(shape(**dict(base, batch=0))), None, None, 0, None, None, None, None,
+                                 None, None, None, None, 0, None) == 0
+    # per-sequence lengths take one query per sequence
+    assert lib.hsa_forward_heads(ctypes.byref(shape(**dict(base, n_q=2))), FAKE, None, 0, FAKE, FAKE, FAKE, FAKE,
+                                 None, FAKE, None, FAKE, 1 << 40, None) == 1
 
 
 def test_kernel_event_validation(lib):

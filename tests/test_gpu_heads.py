@@ -205,3 +205,43 @@ def test_head_decode_512k_sampled():
     sub = {"Q": inp["Q"][:1], "K": inp["K"][:1], "V": inp["V"][:1], "W": inp["W"]}
     check_heads(w.with_(batch=1), sub, {k: v[:1] for k, v in g.items()}, LK0[None], [(0, 0)], [(0, 0)], stats)
     print(f"head_decode_512k: {stats['equal']} of {stats['lists']} lists of sequence 0 equal to the oracle's")
+
+
+def _check_varlen_step(w, inp, g, lens, stats):
+    qpg = w.n_heads_q // w.n_heads_kv
+    for b, Lb in enumerate(lens):
+        t = Lb - 1
+        LK_b = orc.head_landmarks(inp["K"][b, :Lb], w.block, inp.get("W"))
+        assert np.array_equal(g["LK"][b, :LK_b.shape[0]], LK_b), f"landmarks differ: b={b} L_b={Lb}"
+        LKf = orc.bf16_to_f64(LK_b)
+        Qf = orc.bf16_to_f64(inp["Q"][b, 0])
+        for h in range(w.n_heads_q):
+            score, eps = exact_scores(Qf[h], LKf[:, :, h // qpg, :])
+            check_list(g["blk"][b, 0, h], t, w.block, w.top_m, score, eps, f"b={b} L_b={Lb} h={h}")
+            ref = orc.select_blocks(inp["Q"][b, 0, h], LK_b[:, :, h // qpg, :], t, w.block, w.top_m)
+            stats["lists"] += 1
+            stats["equal"] += int(np.array_equal(ref, g["blk"][b, 0, h]))
+        seq = {"Q": inp["Q"][b:b + 1], "K": inp["K"][b:b + 1, :Lb], "V": inp["V"][b:b + 1, :Lb]}
+        r = orc.forward_query_heads(seq, 0, 0, t, w.block, w.top_m, w.scale, LK_b, blk_override=g["blk"][b, 0])
+        assert np.abs(g["O"][b, 0].astype(np.float64) - r["O"]).max() <= ATOL, (b, Lb)
+        assert np.abs(g["lse"][b, 0].astype(np.float64) - r["lse"]).max() <= ATOL, (b, Lb)
+
+
+def test_per_head_decode_different_lengths():
+    # one decode step over sequences of different lengths (seq_lens, n_q = 1):
+    # each sequence against the oracle run on its own first L_b rows; then
+    # three steps appending a token to every sequence, carrying LK, across
+    # a chunk boundary
+    w = case("varlen_heads", 5, 6000, 1, 32, 4, 8, 16, 2)
+    inp = datagen.make_inputs(w)
+    dev = pipeline.to_device(inp)
+    out = pipeline.alloc_outputs(w)
+    _lib.hsa_head_landmarks(_lib.shape_of(w), dev["K"], dev["W"], 0, out["LK"])
+    stats = {"lists": 0, "equal": 0}
+    for lens in ([6000, 3001, 32 * 7, 32 * 8 + 1, 1], [5998, 32 * 40 - 2, 32 * 8 - 1, 9, 2]):
+        for step in range(3 if lens[0] == 5998 else 1):
+            cur = [L + step for L in lens]
+            lt = torch.tensor(cur, dtype=torch.int32, device="cuda")
+            g = pipeline.to_host(pipeline.run_forward_heads(w, dev, out, seq_lens=lt))
+            _check_varlen_step(w, inp, g, cur, stats)
+    print(f"varlen heads: {stats['equal']} of {stats['lists']} lists equal to the oracle's")
