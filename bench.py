@@ -549,7 +549,7 @@ def main():
                                                 ptr(dev["K"]), ptr(dev["V"]), ptr(out["LK"]), None, ptr(out["O"]),
                                                 ptr(out["lse"]), ptr(ws), nbytes, stream)
     elif w.group:
-        fn, call_args = lib.hsa_forward_3level, (sref, w.group, w.top_m2, ptr(dev["qI"]), ptr(dev["kI"]),
+        fn, call_args = lib.hsa_forward_3level, (sref, None, w.group, w.top_m2, ptr(dev["qI"]), ptr(dev["kI"]),
                                             ptr(dev.get("W")), start_block, ptr(out["S"]), ptr(out["S2"]),
                                             ptr(dev["Q"]), ptr(dev["K"]), ptr(dev["V"]), ptr(out["sup"]), None, None,
                                             ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes, stream)

@@ -76,7 +76,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_decode_step.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_super_summary.argtypes = [S, I32, P, I32, P, P]
     lib.hsa_block_topm_3level.argtypes = [S, I32, I32, P, P, P, P, P, P, SZ, P]
-    lib.hsa_forward_3level.argtypes = [S, I32, I32, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_3level.argtypes = [S, P, I32, I32, P, P, P, I32, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_head_landmarks.argtypes = [S, P, P, I32, P, P]
     lib.hsa_head_topm.argtypes = [S, P, P, P, P, SZ, P]
     lib.hsa_forward_heads.argtypes = [S, P, P, I32, P, P, P, P, P, P, P, P, SZ, P]
@@ -221,9 +221,10 @@ def hsa_block_topm_3level(shape, group, top_m2, qI, S, S2, sup, blk, workspace=N
 
 
 def hsa_forward_3level(shape, group, top_m2, qI, kI, W, summary_start_block, S, S2, Q, K, V, sup_out, blk_out,
-                       tok_out, O, lse=None, workspace=None, stream=None):
+                       tok_out, O, lse=None, workspace=None, stream=None, seq_lens=None):
     ws, nbytes = _workspace(shape, HSA_SPARSE_OP_FORWARD, workspace, Q.device)
-    st = load().hsa_forward_3level(ctypes.byref(shape), int(group), int(top_m2), _ptr(qI, "qI", _BF16),
+    st = load().hsa_forward_3level(ctypes.byref(shape), _ptr(seq_lens, "seq_lens", _I32, True), int(group),
+                                   int(top_m2), _ptr(qI, "qI", _BF16),
                                    _ptr(kI, "kI", _BF16), _ptr(W, "W", _I8, True), int(summary_start_block),
                                    _ptr(S, "S", _BF16), _ptr(S2, "S2", _BF16), _ptr(Q, "Q", _BF16),
                                    _ptr(K, "K", _BF16), _ptr(V, "V", _BF16), _ptr(sup_out, "sup_out", _I32),

@@ -498,8 +498,8 @@ hsa_sparse_status_t hsa_block_topm_3level(const hsa_sparse_shape_t* shape, int32
   return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_block_topm_3level");
 }
 
-hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape, int32_t group, int32_t top_m2,
-                                       const uint16_t* qI, const uint16_t* kI, const int8_t* landmark_W,
+hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape, const int32_t* seq_lens, int32_t group,
+                                       int32_t top_m2, const uint16_t* qI, const uint16_t* kI, const int8_t* landmark_W,
                                        int32_t summary_start_block, uint16_t* S, uint16_t* S2, const uint16_t* Q,
                                        const uint16_t* K, const uint16_t* V, int32_t* sup_out, int32_t* blk_out,
                                        int32_t* tok_out, float* O, float* lse, void* workspace,
@@ -511,6 +511,9 @@ hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape, int32_t 
   st = check_level3(group, top_m2, l3.lgG);
   if (st != HSA_SPARSE_OK) return st;
   if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
+  if (seq_lens && d.nq != 1 && d.b != 0)
+    return fail(HSA_SPARSE_INVALID_ARG, "seq_lens needs n_q == 1 (got %d)", d.nq);
+  d.lens = seq_lens;
   return forward_impl(d, "hsa_forward_3level", qI, kI, landmark_W, summary_start_block, S, Q, K, V, blk_out,
                       tok_out, O, lse, workspace, workspace_bytes, stream, &l3);
 }

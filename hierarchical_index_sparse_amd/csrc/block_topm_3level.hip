@@ -12,7 +12,9 @@
 //
 // k_super_summary: S2[J, l] = bf16_rne(sum_g S[J*G + g, l] / G), one thread
 // per 8 output elements, fp32 sums scaled by the exact power of two 1/G;
-// blocks past the end count as zero.
+// blocks past the sequence's last block count as zero.  With per-sequence
+// lengths only the super-block holding each sequence's last block is
+// rebuilt.
 // Level 1 reuses the block top-m launcher with block size B*G, nsb
 // super-blocks and m2 kept.
 // k_block_topm_l2: one workgroup per query gathers the summary rows of its
@@ -29,17 +31,26 @@ namespace hsa {
 template <int DI>
 __global__ __launch_bounds__(256) void k_super_summary(const uint16_t* __restrict__ S, uint16_t* __restrict__ S2,
                                                        int nb, int nsb, int NL, int lgG, int start_super,
-                                                       int n_items) {
+                                                       int n_items, const int32_t* __restrict__ lens, int L,
+                                                       int B) {
   constexpr int C8 = DI / 8;  // 16-byte chunks per summary row
   const int item = blockIdx.x * 256 + threadIdx.x;
   if (item >= n_items) return;
   const int per_super = NL * C8;
-  const int nJ = nsb - start_super;
+  const int nJ = lens ? 1 : nsb - start_super;
   const int rest = item % per_super;      // l * C8 + e8
-  const int J = start_super + (item / per_super) % nJ;
   const int b = item / (per_super * nJ);
+  int J, nb_b;  // super-block, blocks of the sequence
+  if (lens) {
+    const int Lb = seq_len_of(lens, L, b);
+    J = ((Lb - 1) / B) >> lgG;
+    nb_b = (Lb + B - 1) / B;
+  } else {
+    J = start_super + (item / per_super) % nJ;
+    nb_b = nb;
+  }
   const int G = 1 << lgG;
-  const int g_end = min(G, nb - (J << lgG));
+  const int g_end = min(G, nb_b - (J << lgG));
   const uint16_t* src = S + (((size_t)b * nb + ((size_t)J << lgG)) * NL * C8 + rest) * 8;
   const size_t stride = (size_t)NL * DI;  // one block's summary rows
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -82,7 +93,7 @@ __global__ __launch_bounds__(NW * 64) void k_block_topm_l2(const uint16_t* __res
                                                            const uint16_t* __restrict__ S,
                                                            const int32_t* __restrict__ sup,
                                                            int32_t* __restrict__ blk, int L, int nq, int B, int lgG,
-                                                           int nb, int m2, int m) {
+                                                           int nb, int m2, int m, const int32_t* __restrict__ lens) {
   constexpr int NT = NW * kWave;
   constexpr int LPR = DI / 8;     // lanes per summary row
   constexpr int RPI = NT / LPR;   // rows per round of the workgroup
@@ -93,7 +104,7 @@ __global__ __launch_bounds__(NW * 64) void k_block_topm_l2(const uint16_t* __res
   const int q = blockIdx.x;
   const int tid = threadIdx.x;
   const int b = q / nq;
-  const int t = query_pos(L, nq, q % nq);
+  const int t = query_pos(seq_len_of(lens, L, b), nq, q % nq);
   const int c = t / B;
   const int gmask = (1 << lgG) - 1;
   const int C = c >> lgG;
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(1024) void k_block_topm_3level_decode(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ S, const uint16_t* __restrict__ S2,
     int32_t* __restrict__ sup, int32_t* __restrict__ blk, int L, int nq, int B, int lgG, int nb, int nsb, int m2,
     int m, int nq_total, const uint16_t* __restrict__ kI, uint16_t* __restrict__ S_out,
-    uint16_t* __restrict__ S2_out, int sum_start, int nsum) {
+    uint16_t* __restrict__ S2_out, int sum_start, int nsum, const int32_t* __restrict__ lens) {
   constexpr int LPR = DI / 8;      // lanes per summary row
   constexpr int RPI = 1024 / LPR;  // rows per round of the workgroup
   constexpr int U = 8;             // rounds of loads in flight
@@ -195,14 +206,15 @@ __global__ __launch_bounds__(1024) void k_block_topm_3level_decode(
   if ((int)blockIdx.x >= nq_total) {  // folded summaries of a newest block (uniform)
     const int w = (int)blockIdx.x - nq_total;
     const int bs = w / nsum;
-    const int jb = sum_start + w % nsum;
+    const int Lb = seq_len_of(lens, L, bs);
+    const int jb = (lens ? (Lb - 1) / B : sum_start) + w % nsum;
     if (jb >= nb) return;
-    summarise_block<DI, 1, 1024>(kI, nullptr, S_out, L, L, B, nb, jb, bs, u.red, S2_out, lgG);
+    summarise_block<DI, 1, 1024>(kI, nullptr, S_out, L, Lb, B, nb, jb, bs, u.red, S2_out, lgG);
     return;
   }
   const int q = blockIdx.x;
   const int b = q / nq;
-  const int t = query_pos(L, nq, q % nq);
+  const int t = query_pos(seq_len_of(lens, L, b), nq, q % nq);
   const int c = t / B;
   const int C = c >> lgG;
   const int gmask = (1 << lgG) - 1;
@@ -305,16 +317,16 @@ __global__ __launch_bounds__(1024) void k_block_topm_3level_decode(
 hipError_t launch_super_summary(const Dims& s, int lgG, const uint16_t* S, int start_super, uint16_t* S2,
                                 hipStream_t st) {
   const int nsb = (s.nb + (1 << lgG) - 1) >> lgG;
-  if (s.b == 0 || start_super >= nsb) return hipSuccess;
-  const long long items = (long long)s.b * (nsb - start_super) * s.nL * (s.dI / 8);
+  if (s.b == 0 || (!s.lens && start_super >= nsb)) return hipSuccess;
+  const long long items = (long long)s.b * (s.lens ? 1 : nsb - start_super) * s.nL * (s.dI / 8);
   const int n_items = (int)items;
   dim3 grid((unsigned)((items + 255) / 256));
   if (s.dI == 64)
     HSA_LAUNCH((k_super_summary<64>), grid, dim3(256), 0, st, S, S2, s.nb, nsb, s.nL, lgG, start_super,
-                       n_items);
+                       n_items, s.lens, s.L, s.B);
   else
     HSA_LAUNCH((k_super_summary<128>), grid, dim3(256), 0, st, S, S2, s.nb, nsb, s.nL, lgG, start_super,
-                       n_items);
+                       n_items, s.lens, s.L, s.B);
   return hipGetLastError();
 }
 
@@ -324,7 +336,7 @@ static hipError_t launch_l2_r(const Dims& s, int lgG, int m2, const uint16_t* qI
   dim3 grid(s.b * s.nq), block(NW * 64);
 #define HSA_L2(DI, NL)                                                                                   \
   HSA_LAUNCH((k_block_topm_l2<DI, NL, NW, R>), grid, block, 0, st, qI, S, sup, blk, s.L, s.nq, s.B, \
-                     lgG, s.nb, m2, s.m)
+                     lgG, s.nb, m2, s.m, s.lens)
   if (s.dI == 64) {
     if (s.nL == 1) HSA_L2(64, 1); else if (s.nL == 2) HSA_L2(64, 2); else HSA_L2(64, 4);
   } else {
@@ -351,9 +363,12 @@ static bool use_fused3(const Dims& s, int lgG, int m2) {
 
 bool block_topm_3level_can_fold(const Dims& s, int lgG, int m2, int start_block) {
   // every query sits in the last block (so in the last super-block), the
-  // only blocks and super-blocks that are re-summarised
+  // only blocks and super-blocks that are re-summarised; with per-sequence
+  // lengths one query per sequence, whose block is rebuilt
+  if (!use_fused3(s, lgG, m2)) return false;
+  if (s.lens) return s.nq == 1;
   const int c_max = (s.L - 1) / s.B;
-  return use_fused3(s, lgG, m2) && start_block >= c_max && start_block < s.nb;
+  return start_block >= c_max && start_block < s.nb;
 }
 
 template <int DI, int R1, int R2>
@@ -362,11 +377,11 @@ static hipError_t launch_fused3_r(const Dims& s, int lgG, int m2, const uint16_t
                                   const SummaryFold* fold, uint16_t* S2_out) {
   const int nq_total = s.b * s.nq;
   const int nsb = (s.nb + (1 << lgG) - 1) >> lgG;
-  const int nsum = fold ? s.nb - fold->start_block : 0;
+  const int nsum = fold ? (s.lens ? 1 : s.nb - fold->start_block) : 0;
   dim3 grid(nq_total + s.b * nsum);
   HSA_LAUNCH((k_block_topm_3level_decode<DI, R1, R2>), grid, dim3(1024), 0, st, qI, S, S2, sup, blk, s.L,
                      s.nq, s.B, lgG, s.nb, nsb, m2, s.m, nq_total, fold ? fold->kI : nullptr,
-                     fold ? fold->S : nullptr, S2_out, fold ? fold->start_block : s.nb, max(nsum, 1));
+                     fold ? fold->S : nullptr, S2_out, fold ? fold->start_block : s.nb, max(nsum, 1), s.lens);
   return hipGetLastError();
 }
 

@@ -17,10 +17,11 @@ namespace hsa {
 // L is the row stride of kI per sequence, Lb the sequence's length (rows
 // at or past Lb count as zero).  With S2, the summary of the super-block of
 // 2^lgG blocks holding block j is rebuilt too: the mean of its blocks'
-// summaries (block j's fresh value, the others read from S; blocks past nb
-// count as zero), summed in block order in fp32 and rounded once, the same
-// arithmetic as the super-block summary kernel.  No other workgroup may be
-// writing that super-block's blocks in S.
+// summaries (block j's fresh value, the others read from S; blocks past the
+// sequence's last block, ceil(Lb / B) - 1, count as zero), summed in block
+// order in fp32 and rounded once, the same arithmetic as the super-block
+// summary kernel.  No other workgroup may be writing that super-block's
+// blocks in S.
 template <int DI, int NL, int NTH = 256>
 __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI, const int8_t* __restrict__ W,
                                                 uint16_t* __restrict__ S, int L, int Lb, int B, int nb, int j, int b,
@@ -71,7 +72,7 @@ __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI,
     const uint32_t own = f32_to_bf16_rne(total * inv_b);
     S[(((size_t)b * nb + j) * NL + l) * DI + d] = (uint16_t)own;
     if (S2) {
-      const int J = j >> lgG, g0 = J << lgG, g1 = min(nb, g0 + (1 << lgG));
+      const int J = j >> lgG, g0 = J << lgG, g1 = min((Lb + B - 1) / B, g0 + (1 << lgG));
       const int nsb = (nb + (1 << lgG) - 1) >> lgG;
       float sum = 0.f;
       for (int g = g0; g < g1; ++g) {

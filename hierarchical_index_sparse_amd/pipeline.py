@@ -76,14 +76,15 @@ def run_forward(w: Workload, dev: dict, out: dict | None = None, keep_lists: boo
 
 
 def run_forward_3level(w: Workload, dev: dict, out: dict | None = None, keep_lists: bool = True,
-                       workspace: torch.Tensor | None = None, summary_start_block: int = 0) -> dict:
+                       workspace: torch.Tensor | None = None, summary_start_block: int = 0,
+                       seq_lens: torch.Tensor | None = None) -> dict:
     """Steps 1-4 through hsa_forward_3level (super-blocks of w.group blocks)."""
     shape = _lib.shape_of(w)
     out = out or alloc_outputs(w, dev["qI"].device)
     _lib.hsa_forward_3level(shape, w.group, w.top_m2, dev["qI"], dev["kI"], dev.get("W"), summary_start_block,
                             out["S"], out["S2"], dev["Q"], dev["K"], dev["V"], out["sup"],
                             out["blk"] if keep_lists else None, out["tok"] if keep_lists else None, out["O"],
-                            out["lse"], workspace)
+                            out["lse"], workspace, seq_lens=seq_lens)
     return out
 
 

@@ -287,6 +287,13 @@ hsa_sparse_status_t hsa_flat_topk(const hsa_sparse_shape_t* shape,
  *   hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_FORWARD).  Stage events
  *   (hsa_sparse_set_stage_events) mark the same four steps, step 1 ending
  *   after the super-block summaries.
+ *   seq_lens: NULL, or a decode step over sequences of different lengths as
+ *   for hsa_decode_step: device int32 [batch], n_q must be 1, seq_len is
+ *   the capacity (the row stride of kI, K, V, S and S2), the query of
+ *   sequence b sits at L_b - 1, and this call rebuilds the summary of block
+ *   (L_b - 1) / block and of the super-block holding it, counting only the
+ *   sequence's own blocks (summary_start_block is then not read).  Lengths
+ *   are clamped to [1, seq_len].
  * Errors: as for the other entry points; nothing is launched on an error.
  */
 hsa_sparse_status_t hsa_super_summary(const hsa_sparse_shape_t* shape,
@@ -304,6 +311,7 @@ hsa_sparse_status_t hsa_block_topm_3level(const hsa_sparse_shape_t* shape,
                                           hsa_sparse_stream_t stream);
 
 hsa_sparse_status_t hsa_forward_3level(const hsa_sparse_shape_t* shape,
+                                       const int32_t* seq_lens,
                                        int32_t group, int32_t top_m2,
                                        const uint16_t* qI, const uint16_t* kI,
                                        const int8_t* landmark_W,

@@ -202,9 +202,9 @@ def test_decode_step_validation(lib):
 
 
 def test_three_level_validation(lib):
-    def fwd(s, group=16, m2=8, S2=FAKE, sup=FAKE, ws=1 << 40):
-        return lib.hsa_forward_3level(ctypes.byref(s), group, m2, FAKE, FAKE, None, 0, FAKE, S2, FAKE, FAKE, FAKE,
-                                      sup, None, None, FAKE, None, FAKE, ws, None)
+    def fwd(s, group=16, m2=8, S2=FAKE, sup=FAKE, ws=1 << 40, lens=None):
+        return lib.hsa_forward_3level(ctypes.byref(s), lens, group, m2, FAKE, FAKE, None, 0, FAKE, S2, FAKE, FAKE,
+                                      FAKE, sup, None, None, FAKE, None, FAKE, ws, None)
 
     def sel(s, group=16, m2=8, ws=1 << 40):
         return lib.hsa_block_topm_3level(ctypes.byref(s), group, m2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None)
@@ -218,6 +218,8 @@ def test_three_level_validation(lib):
     assert fwd(s, S2=None) == 1
     assert fwd(s, sup=None) == 1
     assert fwd(shape(head_dim=64)) == 2
+    assert fwd(s, lens=FAKE) == 1            # per-sequence lengths need one query per sequence
+    assert b"n_q == 1" in lib.hsa_sparse_last_error()
     need = lib.hsa_sparse_workspace_size(ctypes.byref(s), _lib.HSA_SPARSE_OP_FORWARD)
     assert fwd(s, ws=need - 1) == 3
     assert sel(s, group=3) == 2 and sel(s, m2=0) == 1

@@ -9,7 +9,8 @@ paths of the block top-m launcher (MFMA scores for many queries, the GEMV
 with landmarks), both level-2 workgroup shapes, the one-launch decode
 kernel of both levels (with and without the newest summaries folded in),
 super-blocks of one block (the two-level lists), every super-block kept,
-and the full decode_3level_1m shape on sampled sequences.
+the full decode_3level_1m shape on sampled sequences, and decode steps over
+sequences of different lengths (seq_lens) against the oracle per sequence.
 """
 import numpy as np
 import pytest
@@ -202,3 +203,48 @@ def test_decode_3level_1m_sampled():
         assert np.array_equal(g["tok"][b, 0], r["tok"]), b
         assert np.abs(g["O"][b, 0].astype(np.float64) - r["O"]).max() <= ATOL
         assert np.abs(g["lse"][b, 0].astype(np.float64) - r["lse"]).max() <= ATOL
+
+
+# (batch, capacity, d_index, B, n_L, G, m2, m, k, start lengths): the first
+# takes the one-launch decode kernel with the newest block and super-block
+# folded in, the second (landmarks) the block-summary and super-summary
+# launches, the level-1 block top-m and the level-2 kernel
+VARLEN_CASES = [
+    (5, 20000, 64, 16, 1, 8, 10, 20, 200, [20000, 9999, 16 * 8 * 3 - 1, 16 * 8 * 3 + 1, 1]),
+    (3, 9000, 128, 32, 4, 4, 5, 8, 150, [8998, 4096, 31]),
+]
+
+
+@pytest.mark.parametrize("batch,cap,dI,B,nL,G,m2,m,k,lens0", VARLEN_CASES, ids=["one_launch", "landmarks"])
+def test_decode_3level_different_lengths(batch, cap, dI, B, nL, G, m2, m, k, lens0):
+    # sequences of different lengths in one capacity-sized cache (seq_lens,
+    # n_q = 1); state built over the whole capacity first, so the summaries
+    # of every sequence's newest block and super-block are stale; then three
+    # steps appending one token to every sequence (crossing block and
+    # super-block boundaries) with the state carried between steps.  Each
+    # sequence is compared with the oracle run on its first L_b rows.
+    w = case("varlen3", batch, cap, 1, dI, B, nL, m, k, G, m2)
+    inp = make(w, 2)
+    dev = pipeline.to_device(inp)
+    out = pipeline.alloc_outputs(w)
+    shape = _lib.shape_of(w)
+    _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), 0, out["S"])
+    _lib.hsa_super_summary(shape, G, out["S"], 0, out["S2"])
+    for step in range(3):
+        lens = [min(L + step, cap) for L in lens0]
+        lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        g = pipeline.to_host(pipeline.run_forward_3level(w, dev, out, summary_start_block=0, seq_lens=lt))
+        for b, Lb in enumerate(lens):
+            t = Lb - 1
+            ctx = f"step {step} b={b} L_b={Lb}"
+            S_b = orc.block_summary(inp["kI"][b, :Lb], B, inp.get("W"))
+            S2_b = orc.super_summary(S_b, G)
+            assert np.array_equal(g["S"][b, :S_b.shape[0]], S_b), f"summaries differ: {ctx}"
+            assert np.array_equal(g["S2"][b, :S2_b.shape[0]], S2_b), f"super-block summaries differ: {ctx}"
+            r = orc.forward_query_3level(inp, b, 0, t, B, G, m2, m, k, w.scale, S_b, S2_b)
+            sup = orc.select_blocks(inp["qI"][b, 0], S2_b, t, B * G, m2)
+            assert np.array_equal(g["sup"][b, 0], sup), f"super-block list differs: {ctx}"
+            assert np.array_equal(g["blk"][b, 0], r["blk"]), f"block list differs: {ctx}"
+            assert np.array_equal(g["tok"][b, 0], r["tok"]), f"token list differs: {ctx}"
+            assert np.abs(g["O"][b, 0].astype(np.float64) - r["O"]).max() <= ATOL, ctx
+            assert np.abs(g["lse"][b, 0].astype(np.float64) - r["lse"]).max() <= ATOL, ctx
