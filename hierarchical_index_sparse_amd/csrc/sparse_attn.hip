@@ -22,7 +22,10 @@
 //     (two MFMAs), which keeps P's rounding error near 2^-17 instead of
 //     bf16's 2^-9.
 // Splits (decode) write unnormalised partial results with their running max
-// and sum; k_attn_merge combines them (log-sum-exp merge).
+// and sum; k_attn_merge combines them (log-sum-exp merge).  When the split
+// count is a multiple of 4, the 4 waves of a workgroup hold 4 consecutive
+// splits of one (query, kv head) and combine them in LDS first, so one
+// partial per workgroup reaches memory and the merge reads a quarter.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                                      float* __restrict__ O, float* __restrict__ lse,
                                                      float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
                                                      int chunk, int nsplit, float scale_log2, int n_items,
-                                                     const int32_t* __restrict__ lens) {
+                                                     const int32_t* __restrict__ lens, bool premerge) {
   __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * 2 * kStageBytes];
   const int wave = threadIdx.x / kWave;
   const int item = blockIdx.x * 4 + wave;
@@ -249,6 +252,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   }
 
   l_run = sum_x32(sum_x16(l_run));
+  if constexpr (SPLIT) {
+    if (premerge) {  // uniform over the grid; every wave of the workgroup is here
+      // this wave's partial into its own (no longer used) staging area, in
+      // the partial layout; then each thread combines 8 columns of one head
+      float* mine = reinterpret_cast<float*>(kst);
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        float* dst = mine + (4 * gq + i2) * kPartStride + 8 * jl;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dst[c] = o[c][i2];
+      }
+      if (gq == 0) {
+        mine[jl * kPartStride + 128] = m_run;
+        mine[jl * kPartStride + 129] = l_run;
+      }
+      __syncthreads();
+      const int h = threadIdx.x >> 4, d0 = 8 * (threadIdx.x & 15);
+      if (h < G) {
+        const float* src[4];
+        float mw[4], M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          src[w] = reinterpret_cast<const float*>(stage_lds + (size_t)w * 2 * kStageBytes) + h * kPartStride;
+          mw[w] = src[w][128];
+          M = fmaxf(M, mw[w]);
+        }
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, Ls = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float a = __builtin_amdgcn_exp2f(mw[w] - M);  // 0 for a split without tokens
+            Ls += a * src[w][129];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += a * src[w][d0 + e];
+          }
+        }
+        float* dst = part + ((size_t)blockIdx.x * 16 + h) * kPartStride;
+        *reinterpret_cast<f32x4*>(dst + d0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        *reinterpret_cast<f32x4*>(dst + d0 + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+        if (d0 == 0) {
+          dst[128] = M;
+          dst[129] = Ls;
+        }
+      }
+      return;
+    }
+  }
   // outputs: lane holds heads 4gq+i, dims 8 jl + c (c = output tile)
 #pragma unroll
   for (int i2 = 0; i2 < 4; ++i2) {
@@ -396,14 +446,18 @@ hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* 
   dim3 grid((n_items + 3) / 4), block(256);
   if (nsplit == 1) {
     HSA_LAUNCH((k_sparse_attn<false>), grid, block, 0, st, Q, K, V, tok, O, lse, nullptr, s.L, s.nq, s.Hq,
-                       s.Hkv, s.k, chunk, nsplit, scale_log2, n_items, s.lens);
+                       s.Hkv, s.k, chunk, nsplit, scale_log2, n_items, s.lens, false);
     return hipGetLastError();
   }
   float* part = static_cast<float*>(ws);
+  // 4 splits per workgroup combined in LDS: n_items is then a multiple of 4
+  // and every workgroup holds 4 splits of one (query, kv head)
+  const bool premerge = nsplit % 4 == 0;
   HSA_LAUNCH((k_sparse_attn<true>), grid, block, 0, st, Q, K, V, tok, O, lse, part, s.L, s.nq, s.Hq, s.Hkv,
-                     s.k, chunk, nsplit, scale_log2, n_items, s.lens);
+                     s.k, chunk, nsplit, scale_log2, n_items, s.lens, premerge);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (premerge) nsplit /= 4;
   // about 1024 merge workgroups: few (query, head) rows get more column chunks
   const long long rows = nq_total * s.Hq;
   const dim3 mb(256);
