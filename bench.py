@@ -153,7 +153,7 @@ KERNEL_STAGE = {
     "k_block_topm_decode": "block_topm", "k_block_topm_l2": "block_topm", "k_block_topm_3level_decode": "block_topm",
     "k_head_scores_mfma": "block_topm", "k_head_select": "block_topm",
     "k_token_scores": "token_topk", "k_token_scores_tiled": "token_topk", "k_bm_scores": "token_topk",
-    "k_token_select": "token_topk",
+    "k_token_select": "token_topk", "k_token_enum": "token_topk",
     "k_sparse_attn": "sparse_attn", "k_attn_merge": "sparse_attn",
 }
 

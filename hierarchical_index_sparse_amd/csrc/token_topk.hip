@@ -16,6 +16,11 @@
 // Kernel 2 (k_token_select): one workgroup per query; when n_valid <= k all
 // candidates are written, otherwise the exact select of select.hpp runs over
 // the slot scores.
+// When no query can have more than k candidates (k >= m * B, or a context
+// of at most k tokens), every list is its candidate enumeration and
+// k_token_enum writes it alone: 4 slots per thread, one 16-byte store,
+// workgroups spread over the list so that long lists of few queries do not
+// wait on one workgroup's chain of block-list loads.
 #include <algorithm>
 
 #include "common.hpp"
@@ -30,6 +35,33 @@ __device__ __forceinline__ void candidate_count(int t, int B, int m, int& c, int
   c = t / B;
   n_sel = (c + 1 <= m) ? c + 1 : m;
   n_valid = (n_sel - 1) * B + (t - c * B + 1);
+}
+
+// Workgroup (q, y) writes the 1024-slot chunks y, y + gridDim.y, ... of
+// query q's list.  B >= 8, so 4 consecutive slots from a multiple of 4 lie
+// in one block.
+__global__ __launch_bounds__(256) void k_token_enum(const int32_t* __restrict__ blk, int32_t* __restrict__ tok,
+                                                    int L, int nq, int B, int log2B, int m, int k,
+                                                    const int32_t* __restrict__ lens) {
+  const int q = blockIdx.x;
+  const int t = query_pos(seq_len_of(lens, L, q / nq), nq, q % nq);
+  int c, n_sel, n_valid;
+  candidate_count(t, B, m, c, n_sel, n_valid);
+  int32_t* out = tok + (size_t)q * k;
+  for (long long s0l = ((long long)blockIdx.y * 256 + threadIdx.x) * 4; s0l < k; s0l += (long long)gridDim.y * 1024) {
+    const int s0 = (int)s0l;
+    const int base = s0 < n_valid ? blk[(size_t)q * m + (s0 >> log2B)] << log2B : 0;
+    int v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = s0 + e < n_valid ? base + ((s0 + e) & (B - 1)) : -1;
+    if ((k & 3) == 0) {
+      *reinterpret_cast<i32x4*>(out + s0) = i32x4{v[0], v[1], v[2], v[3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (s0 + e < k) out[s0 + e] = v[e];
+    }
+  }
 }
 
 template <int DI>
@@ -748,8 +780,11 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
       e = hipGetLastError();
     }
     if (e != hipSuccess) return e;
-  } else {
-    n_max = 1;  // every query keeps all of its candidates
+  } else {  // every query keeps all of its candidates
+    const dim3 grid((unsigned)nq_total, (unsigned)std::min<long long>((s.k + 1023ll) / 1024, 4096));
+    HSA_LAUNCH(k_token_enum, grid, dim3(256), 0, st, blk, tok, s.L, s.nq, s.B, __builtin_ctz((unsigned)s.B), s.m,
+               s.k, s.lens);
+    return hipGetLastError();
   }
   if (nq_total >= 512 && n_max <= 4 * 64 * 64) {  // many queries: a 4-wave workgroup per query
     int r = 1;

@@ -37,6 +37,10 @@ SMALL_CASES = [
     (small("k1", batch=2, seq_len=4100, n_q=3, d_index=128, block=128, top_m=3, top_k=1,
            n_heads_q=2, n_heads_kv=1), 8),
     (small("keep_all", seq_len=64, n_q=64, d_index=64, block=8, top_m=100, top_k=1000), 2),
+    # k >= m * B: every list is its candidate enumeration (two 1024-slot
+    # chunks, k not a multiple of 4)
+    (small("enumerate_ragged", batch=2, seq_len=3000, n_q=5, d_index=64, block=16, top_m=70, top_k=1123,
+           n_heads_q=4, n_heads_kv=2), 2),
     (small("decode_wide_select", batch=2, seq_len=40000, n_q=2, d_index=64, block=16, top_m=300,
            top_k=1000, n_heads_q=16, n_heads_kv=1), 2),
     (small("prefill_r64_select", seq_len=20000, n_q=512, d_index=128, block=128, top_m=100,
