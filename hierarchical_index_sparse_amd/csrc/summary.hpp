@@ -39,23 +39,33 @@ __device__ __forceinline__ void summarise_block(const uint16_t* __restrict__ kI,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[l][e] = 0.f;
 
+  // every row load (and projection weight) of the thread is issued before
+  // any is used: a block is at most 128 rows, NIT rounds of RPI rows
+  constexpr int NIT = (128 + RPI - 1) / RPI;
   const size_t seq_base = (size_t)b * L;
-  for (int r = r0; r < B; r += RPI) {
-    const int s = j * B + r;
-    if (s >= Lb) break;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(kI + (seq_base + s) * DI + col8 * 8);
+  u32x4 v[NIT];
+  float wl[NL][NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int r = r0 + it * RPI;
+    const bool ok = r < B && j * B + r < Lb;
+    v[it] = u32x4{0u, 0u, 0u, 0u};
+    if (ok) v[it] = *reinterpret_cast<const u32x4*>(kI + (seq_base + j * B + r) * DI + col8 * 8);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) wl[l][it] = ok ? (W ? (float)W[l * B + r] : 1.f) : 0.f;
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
     float x[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      x[2 * e] = bf16_lo(v[e]);
-      x[2 * e + 1] = bf16_hi(v[e]);
+      x[2 * e] = bf16_lo(v[it][e]);
+      x[2 * e + 1] = bf16_hi(v[it][e]);
     }
 #pragma unroll
-    for (int l = 0; l < NL; ++l) {
-      const float w = W ? (float)W[l * B + r] : 1.f;
+    for (int l = 0; l < NL; ++l)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[l][e] += w * x[e];
-    }
+      for (int e = 0; e < 8; ++e) acc[l][e] += wl[l][it] * x[e];
   }
 #pragma unroll
   for (int l = 0; l < NL; ++l)
