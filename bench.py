@@ -687,7 +687,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in, fp32 accumulate",
+        "dtype": "bf16",
+        "accumulate": "fp32",
         "data": ("synthetic (seeded; N(0,1) bf16 Q/K/V, one planted needle chunk per sequence and kv head)"
                  if w.per_head else "synthetic (seeded; integer-valued bf16 indexer vectors, N(0,1) bf16 Q/K/V)"),
         "config": {"workload": w.name,
