@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
     const float v = sc[idx < n ? idx : 0];  // branch-free: all loads in flight together
     key[r] = idx < n ? score_key(v) : 0u;
   }
-  select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+  select_top<NW, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = 1 + idx;
   });
 }
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
     const int idx = tid * R + r;
     key[r] = idx < n ? score_key(sc[idx]) : 0u;
   }
-  select_top<16, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+  select_top<16, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = 1 + idx;
   });
 }

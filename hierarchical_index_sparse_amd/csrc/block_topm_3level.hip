@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void k_block_topm_l2(const uint16_t* __res
     const int idx = tid * R + r;
     key[r] = (idx >= 1 && idx <= n - 2) ? score_key(sc[idx]) : 0u;
   }
-  select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+  select_top<NW, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = (sq[idx >> lgG] << lgG) + (idx & gmask);
   });
 }
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(1024) void k_block_topm_3level_decode(
     const int idx = tid * R2 + r;
     key[r] = (idx >= 1 && idx <= n - 2) ? score_key(u.q.sc[idx]) : 0u;
   }
-  select_top<16, R2>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+  select_top<16, R2, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = (u.q.sl[idx >> lgG] << lgG) + (idx & gmask);
   });
 }

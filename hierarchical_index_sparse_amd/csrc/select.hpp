@@ -270,8 +270,11 @@ __device__ __forceinline__ uint32_t find_threshold(const uint32_t (&key)[R], int
 // Requires: 1 <= want < number of non-empty keys.  Every thread of the
 // group must call it (it synchronises the group).  emit(pos, idx, take, key) is
 // called for every key of the thread in index order; `take` says whether
-// the key is kept, and then pos (0 .. want-1) is its output slot.
-template <int NW, int R, typename Emit>
+// the key is kept, and then pos (0 .. want-1) is its output slot.  With
+// END_SYNC the group synchronises once more after emission (for callers
+// that read what emit wrote to LDS, or reuse the LDS); a caller whose
+// threads only write global memory after the select passes false.
+template <int NW, int R, bool END_SYNC = true, typename Emit>
 __device__ __forceinline__ void select_top(const uint32_t (&key)[R], int want, SelectSmem<NW>& sm, Emit&& emit) {
   const int wave = sel_wave<NW>();
   const int lane = lane_id();
@@ -317,7 +320,7 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[R], int want, S
     emit(pos, idx0 + r, tk != 0, key[r]);
     pos += tk;
   }
-  sel_sync<NW>();  // LDS may be reused by the caller
+  if constexpr (END_SYNC) sel_sync<NW>();  // LDS may be reused by the caller
 }
 
 }  // namespace hsa

@@ -546,8 +546,8 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
       out[slot] = slot < n_valid ? blq[slot / B] * B + slot % B : -1;
     return;
   }
-  for (int p = threadIdx.x; p < n_sel; p += NT) bl[p] = blk[(size_t)q * m + p];
-  __syncthreads();
+  // the slot scores do not depend on the block list: both loads in flight
+  // together, one round trip before the barrier
   const float* sc = scores + (size_t)q * m * B;  // 32-byte aligned: m * B is a multiple of 8
   const int idx0 = threadIdx.x * R;
   uint32_t key[R];
@@ -574,10 +574,12 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
       key[r] = idx < n_valid ? score_key(v) : 0u;
     }
   }
+  for (int p = threadIdx.x; p < n_sel; p += NT) bl[p] = blk[(size_t)q * m + p];
+  __syncthreads();
   const int bmask = B - 1;
   const int tbase = ONEBLK ? (bl[min(idx0 >> log2B, n_sel - 1)] << log2B) | (idx0 & bmask) : 0;
   const int dummy = k + lane_id();
-  select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) {
+  select_top<NW, R, STAGED>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) {
     const int v = ONEBLK ? tbase + (idx - idx0) : (bl[idx >> log2B] << log2B) | (idx & bmask);
     if constexpr (STAGED) stage[take ? pos : dummy] = v;
     else if (take) out[pos] = v;
@@ -658,6 +660,14 @@ static hipError_t launch_tsel_r(bool scoring, const Dims& s, const float* sc, co
   const size_t dyn = scoring ? tsel_lds_bytes(s.m, s.k) : 0;
   constexpr bool kMulti = R > 8;
   constexpr bool kLong = NW * 64 * R > kStageMax;
+  if constexpr (NW == 16) {
+    // few queries, latency-bound: kept entries go straight to memory, so the
+    // select needs no closing barrier and no staged copy
+    if (scoring && oneblk) {
+      launch_tsel_k<16, R, false, true>(s, dyn, log2B, sc, blk, tok, st);
+      return hipGetLastError();
+    }
+  }
   if (!scoring || (staged && oneblk)) {
     // (without scoring the variant does not matter: the keep-all path)
     launch_tsel_k<NW, R, true, true>(s, dyn, log2B, sc, blk, tok, st);
