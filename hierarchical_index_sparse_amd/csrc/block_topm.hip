@@ -172,7 +172,8 @@ template <int NW, int R>
 __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const float* __restrict__ scores,
                                                                           int32_t* __restrict__ blk, int L, int nq,
                                                                           int B, int nb, int m, int nq_total,
-                                                                          const int32_t* __restrict__ lens) {
+                                                                          const int32_t* __restrict__ lens,
+                                                                          bool vec) {
   constexpr int QPB = NW == 1 ? 4 : 1;  // queries per workgroup
   constexpr int GT = NW * kWave;        // threads per select group
   __shared__ SelectSmem<NW> lds[QPB];
@@ -196,8 +197,29 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
     out[m - 1] = c;
   }
   if (want == 0) return;
-  const float* sc = scores + (size_t)q * nb + 1;
   uint32_t key[R];
+  if constexpr (R >= 4) {
+    if (vec) {
+      // (uniform) 16-byte-aligned score rows: slot = block number, thread
+      // x loads blocks x*R .. x*R+R-1 with R/4 aligned 16-byte loads and
+      // keeps blocks 1 .. c-1 (scalar loads at a stride of R floats were
+      // the select's longest phase)
+      const float* sc = scores + (size_t)q * nb;
+#pragma unroll
+      for (int r = 0; r < R; r += 4) {
+        const int j0 = gtid * R + r;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (j0 < nb) v = *reinterpret_cast<const f32x4*>(sc + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[r + e] = (j0 + e >= 1 && j0 + e <= n) ? score_key(v[e]) : 0u;
+      }
+      select_top<NW, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+        if (take) out[1 + pos] = idx;
+      });
+      return;
+    }
+  }
+  const float* sc = scores + (size_t)q * nb + 1;  // slot = block number - 1
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int idx = gtid * R + r;
@@ -305,8 +327,12 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
 template <int NW, int R>
 static hipError_t launch_select_r(int nq_total, const float* scores, int32_t* blk, const Dims& s, hipStream_t st) {
   dim3 grid(NW == 1 ? (nq_total + 3) / 4 : nq_total), block(NW == 1 ? 256 : NW * 64);
+  // block-number slots need nb % 4 == 0 (aligned rows) and slots for blocks
+  // 0 .. c_max - 1 of the latest query
+  const int c_max = (s.L - 1) / s.B;
+  const bool vec = R >= 4 && s.nb % 4 == 0 && (long long)NW * kWave * R >= c_max;
   HSA_LAUNCH((k_block_select<NW, R>), grid, block, 0, st, scores, blk, s.L, s.nq, s.B, s.nb, s.m, nq_total,
-                     s.lens);
+                     s.lens, vec);
   return hipGetLastError();
 }
 

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_head_select(
     const float* __restrict__ scores, int32_t* __restrict__ blk, int32_t* __restrict__ tok, int L, int nq, int B,
     int nb, int m, int Hq, int Hkv, int rows, int nfold_wg, const uint16_t* __restrict__ K,
     const int8_t* __restrict__ W, uint16_t* __restrict__ LK_out, int NL, int fold_start, int nfold,
-    const int32_t* __restrict__ lens) {
+    const int32_t* __restrict__ lens, bool vec) {
   constexpr int QPB = NW == 1 ? 4 : 1;  // rows per workgroup
   constexpr int GT = NW * kWave;        // threads per row
   __shared__ SelectSmem<NW> lds[QPB];
@@ -250,21 +250,43 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_head_select(
     }
   }
   if (want > 0) {
-    const float* sc = scores + (size_t)q * nb + 1;
     uint32_t key[R];
+    int off = 1;  // chunk of select slot s: s + off
+    bool loaded = false;
+    if constexpr (R >= 4) {
+      if (vec) {  // (uniform) aligned rows: slot = chunk, R/4 16-byte loads per thread
+        const float* sc = scores + (size_t)q * nb;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int idx = gtid * R + r;
-      const float v = sc[idx < n ? idx : 0];  // branch-free: all loads in flight together
-      key[r] = idx < n ? score_key(v) : 0u;
+        for (int r = 0; r < R; r += 4) {
+          const int j0 = gtid * R + r;
+          f32x4 v = {0.f, 0.f, 0.f, 0.f};
+          if (j0 < nb) v = *reinterpret_cast<const f32x4*>(sc + j0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) key[r + e] = (j0 + e >= 1 && j0 + e <= n) ? score_key(v[e]) : 0u;
+        }
+        off = 0;
+        loaded = true;
+      }
     }
-    select_top<NW, R>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+    if (!loaded) {
+      const float* sc = scores + (size_t)q * nb + 1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int idx = gtid * R + r;
+        const float v = sc[idx < n ? idx : 0];  // branch-free: all loads in flight together
+        key[r] = idx < n ? score_key(v) : 0u;
+      }
+    }
+    // the group synchronises after the select anyway (below) before the
+    // staged list is read, so the select's own closing barrier is not needed
+    select_top<NW, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
       if (!take) return;
-      out[1 + pos] = 1 + idx;
+      const int chunk = idx + off;
+      out[1 + pos] = chunk;
       if (staged) {
-        lst[1 + pos] = 1 + idx;
+        lst[1 + pos] = chunk;
       } else if (tq) {  // lists too long for LDS: each kept chunk's tokens from its thread
-        for (int r = 0; r < B; ++r) tq[(size_t)(1 + pos) * B + r] = ((1 + idx) * B + r) * Hkv + g;
+        for (int r = 0; r < B; ++r) tq[(size_t)(1 + pos) * B + r] = (chunk * B + r) * Hkv + g;
       }
     });
   }
@@ -320,9 +342,13 @@ static hipError_t launch_head_select_r(const Dims& s, const float* scores, int32
   const int nfold = fold ? (s.lens ? 1 : s.nb - fold->start_block) : 0;
   const int nfold_wg = s.b * nfold;
   dim3 grid(nfold_wg + (NW == 1 ? (rows + 3) / 4 : rows)), block(NW == 1 ? 256 : NW * 64);
+  // chunk-number slots need nb % 4 == 0 (aligned rows) and slots for chunks
+  // 0 .. c_max - 1 of the latest query
+  const int c_max = (s.L - 1) / s.B;
+  const bool vec = R >= 4 && s.nb % 4 == 0 && (long long)NW * kWave * R >= c_max;
   HSA_LAUNCH((k_head_select<NW, R>), grid, block, 0, st, scores, blk, tok, s.L, s.nq, s.B, s.nb, s.m, s.Hq,
                      s.Hkv, rows, nfold_wg, fold ? fold->K : nullptr, fold ? fold->W : nullptr,
-                     fold ? fold->LK : nullptr, s.nL, fold ? fold->start_block : s.nb, max(nfold, 1), s.lens);
+                     fold ? fold->LK : nullptr, s.nL, fold ? fold->start_block : s.nb, max(nfold, 1), s.lens, vec);
   return hipGetLastError();
 }
 
