@@ -177,29 +177,29 @@ __global__ __launch_bounds__(NW * 64) void k_flat_merge(const uint2* __restrict_
   // candidates: lists first .. first+nl-1; every list but the last holds k
   const int cnt_last = cin[(size_t)q * nchunk + first + nl - 1];
   const int n = (nl - 1) * k + cnt_last;
-  const uint2* src = lin + ((size_t)q * nchunk + first) * k;
+  const uint2* src = lin + ((size_t)q * nchunk + first) * k;  // list j of the group starts at j * k
   const int idx0 = threadIdx.x * R;
+  // only the keys stay in registers (R of them, up to 32 with 16 waves);
+  // a kept key's token is read back from the list when it is emitted
   uint32_t key[R];
-  int tk[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int s = idx0 + r;
-    uint2 v = make_uint2(0u, 0u);
-    if (s < n) v = src[s];  // list j of the group starts at j * k
-    key[r] = v.x;
-    tk[r] = (int)v.y;
+    key[r] = s < n ? src[s].x : 0u;
   }
   if (final_list) {
     int32_t* out = tok + (size_t)q * k;
     if (n <= k) {  // every candidate is kept (in index order)
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        if (idx0 + r < k) out[idx0 + r] = idx0 + r < n ? tk[r] : -1;
+        if (idx0 + r < k) out[idx0 + r] = idx0 + r < n ? (int)src[idx0 + r].y : -1;
       for (int p = NT * R + threadIdx.x; p < k; p += NT) out[p] = -1;
       return;
     }
     const int dummy = k + lane_id();
-    select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) { stage[take ? pos : dummy] = tk[idx - idx0]; });
+    select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) {
+      stage[take ? pos : dummy] = take ? (int)src[idx].y : 0;
+    });
     for (int p = threadIdx.x; p < k; p += NT) out[p] = stage[p];
     return;
   }
@@ -207,12 +207,12 @@ __global__ __launch_bounds__(NW * 64) void k_flat_merge(const uint2* __restrict_
   if (n <= k) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (idx0 + r < n) dst[idx0 + r] = make_uint2(key[r], (unsigned)tk[r]);
+      if (idx0 + r < n) dst[idx0 + r] = src[idx0 + r];
     if (threadIdx.x == 0) cout[(size_t)q * nchunk + grp] = n;
     return;
   }
   select_top<NW, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t kv) {
-    if (take) dst[pos] = make_uint2(kv, (unsigned)tk[idx - idx0]);
+    if (take) dst[pos] = make_uint2(kv, src[idx].y);
   });
   if (threadIdx.x == 0) cout[(size_t)q * nchunk + grp] = k;
 }

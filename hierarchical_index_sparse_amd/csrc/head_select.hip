@@ -41,14 +41,15 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double x) {
 // calling waves (wave of nw): a K row (Hkv * 128 bf16) is Hkv groups of 16
 // lanes x 16 bytes; wave w takes groups w, w + nw, ...; lane = (row phase
 // p = lane / 16, 16-byte column chunk lane % 16) sums rows p, p + 4, ...
-// with 8 rows of loads in flight, in fp64; the four row phases meet by lane
-// shuffles.  fp64 sums of bf16 values are exact here, so the result does
-// not depend on this order.  No LDS.
-template <int NL>
+// with 4 U rows of loads in flight, in fp64; the four row phases meet by
+// lane shuffles.  fp64 sums of bf16 values are exact here, so the result
+// does not depend on this order.  No LDS.  (U = 2 where the caller runs
+// 1024-thread workgroups, whose 128 registers per lane would otherwise
+// spill with four landmarks.)
+template <int NL, int U = 8>
 __device__ __forceinline__ void head_landmark_chunk(const uint16_t* __restrict__ K, const int8_t* __restrict__ W,
                                                     uint16_t* __restrict__ LK, int L, int Lb, int B, int nb, int Hkv,
                                                     int j, int b, int wave, int nw) {
-  constexpr int U = 8;
   const int lane = lane_id();
   const int p = lane >> 4, cl = lane & 15;
   const int RW = Hkv * 128;
@@ -215,9 +216,9 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_head_select(
     const int j = (lens ? (Lb - 1) / B : fold_start) + (int)blockIdx.x % nfold;
     if (j >= nb || j * B >= Lb) return;
     const int nw = blockDim.x / kWave;
-    if (NL == 1) head_landmark_chunk<1>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
-    else if (NL == 2) head_landmark_chunk<2>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
-    else head_landmark_chunk<4>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
+    if (NL == 1) head_landmark_chunk<1, 2>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
+    else if (NL == 2) head_landmark_chunk<2, 2>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
+    else head_landmark_chunk<4, 2>(K, W, LK_out, L, Lb, B, nb, Hkv, j, bs, wave, nw);
     return;
   }
   const int wg = (int)blockIdx.x - nfold_wg;
