@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import os
 import sys
@@ -475,6 +476,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill_64k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-sample", type=int, default=1024, help="queries the CPU oracle is timed on")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="run the workload at this batch instead of its own (a batch study: the line then says "
+                         "batch_override; the workload's own batch is the measured configuration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flat", action="store_true",
                     help="skip timing the flat indexer (every causal token scored) on the same inputs")
@@ -490,6 +494,8 @@ def main():
         sys.exit(2)
 
     w = WORKLOADS[args.workload]
+    if args.batch > 0:
+        w = dataclasses.replace(w, batch=args.batch)
     inp = datagen.make_inputs(w)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_sample)
 
@@ -691,7 +697,7 @@ def main():
         "accumulate": "fp32",
         "data": ("synthetic (seeded; N(0,1) bf16 Q/K/V, one planted needle chunk per sequence and kv head)"
                  if w.per_head else "synthetic (seeded; integer-valued bf16 indexer vectors, N(0,1) bf16 Q/K/V)"),
-        "config": {"workload": w.name,
+        "config": {"workload": w.name, "batch_override": args.batch > 0,
                    "summary_start_block": start_block if lens is None else "each sequence's last block",
                    "seq_lens": None if lens is None else f"uniform in [{w.varlen_min}, {w.seq_len}], "
                                                          f"mean {float(np.mean(lens)):.0f} (seeded)",
