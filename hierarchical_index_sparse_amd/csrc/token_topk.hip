@@ -8,7 +8,11 @@
 // blocks other than the query's own block c are full and precede c, and c
 // is the last valid list entry, so the valid slots are exactly the prefix
 // [0, n_valid) with n_valid = (n_sel - 1) * B + (t - c * B + 1), and slot
-// order is token order.
+// order is token order.  A list holds n_sel = min(c + 1, m) blocks when it
+// comes from the two-level selection; the three-level one can keep fewer
+// (its candidates are the blocks of the kept super-blocks), padded with -1.
+// The scorers skip -1 entries and the select and the enumeration take n_sel
+// from the list itself; min(c + 1, m) is only an upper bound.
 //
 // Kernel 1 (k_token_scores): one workgroup per (query, list entry) streams
 // that block's kI rows (d_index/8 lanes per row, 16-byte loads) and writes
@@ -50,10 +54,16 @@ __global__ __launch_bounds__(256) void k_token_enum(const int32_t* __restrict__ 
   int32_t* out = tok + (size_t)q * k;
   for (long long s0l = ((long long)blockIdx.y * 256 + threadIdx.x) * 4; s0l < k; s0l += (long long)gridDim.y * 1024) {
     const int s0 = (int)s0l;
-    const int base = s0 < n_valid ? blk[(size_t)q * m + (s0 >> log2B)] << log2B : 0;
+    // a slot is a token iff its list entry is a block and the token is causal
+    // (only the last kept block, c, is cut by t); -1 entries and what follows
+    // them come after every valid slot
+    const int j = s0 < n_valid ? blk[(size_t)q * m + (s0 >> log2B)] : -1;
     int v[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = s0 + e < n_valid ? base + ((s0 + e) & (B - 1)) : -1;
+    for (int e = 0; e < 4; ++e) {
+      const int tk = (j << log2B) + ((s0 + e) & (B - 1));
+      v[e] = (j >= 0 && s0 + e < n_valid && tk <= t) ? tk : -1;
+    }
     if ((k & 3) == 0) {
       *reinterpret_cast<i32x4*>(out + s0) = i32x4{v[0], v[1], v[2], v[3]};
     } else {
@@ -81,6 +91,7 @@ __global__ __launch_bounds__(256) void k_token_scores(const uint16_t* __restrict
   candidate_count(t, B, m, c, n_sel, n_valid);
   if (n_valid <= k || p >= n_sel) return;
   const int j = blk[(size_t)q * m + p];
+  if (j < 0) return;  // a shorter (three-level) list
 
   const int tid = threadIdx.x;
   const int col8 = tid % LPR;
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_e
     candidate_count(query_pos(L, nq, i0 + qq), B, m, c, n_sel, n_valid);
     if (n_valid > k && p < n_sel) {
       const int j = blk[(qrow0 + qq) * m + p];
-      atomicOr(reinterpret_cast<unsigned long long*>(&bitmap[j * QW + qq / 64]), 1ull << (qq % 64));
+      if (j >= 0) atomicOr(reinterpret_cast<unsigned long long*>(&bitmap[j * QW + qq / 64]), 1ull << (qq % 64));
     }
   }
   __syncthreads();
@@ -282,8 +293,8 @@ __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_e
     const int qq = x / m, p = x % m;
     int c, n_sel, n_valid;
     candidate_count(query_pos(L, nq, i0 + qq), B, m, c, n_sel, n_valid);
-    if (n_valid > k && p < n_sel) {
-      const int j = blk[(qrow0 + qq) * m + p];
+    const int j = (n_valid > k && p < n_sel) ? blk[(qrow0 + qq) * m + p] : -1;
+    if (j >= 0) {
       int rank = 0;
 #pragma unroll
       for (int w = 0; w < QW; ++w) {
@@ -396,7 +407,9 @@ __device__ __forceinline__ bool bm_entry(const int32_t* __restrict__ blk, long l
   int c, n_sel, n_valid;
   candidate_count(query_pos(L, nq, q % nq), B, m, c, n_sel, n_valid);
   if (n_valid <= k || p >= n_sel) return false;
-  bj = (q / nq) * nb + blk[e];
+  const int j = blk[e];
+  if (j < 0) return false;  // a shorter (three-level) list
+  bj = (q / nq) * nb + j;
   return true;
 }
 
@@ -538,31 +551,37 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   const int i = q % nq;
   const int t = query_pos(seq_len_of(lens, L, q / nq), nq, i);
   int c, n_sel, n_valid;
-  candidate_count(t, B, m, c, n_sel, n_valid);
+  candidate_count(t, B, m, c, n_sel, n_valid);  // upper bounds: the list may be shorter
   int32_t* out = tok + (size_t)q * k;
+  const int32_t* blq = blk + (size_t)q * m;
   if (n_valid <= k) {
-    const int32_t* blq = blk + (size_t)q * m;
-    for (int slot = threadIdx.x; slot < k; slot += NT)
-      out[slot] = slot < n_valid ? blq[slot / B] * B + slot % B : -1;
+    // keep all: a slot is a token iff its entry is a block and the token is
+    // causal; the invalid slots all follow the valid ones
+    for (int slot = threadIdx.x; slot < k; slot += NT) {
+      const int j = slot < n_valid ? blq[slot >> log2B] : -1;
+      const int tk = (j << log2B) + (slot & (B - 1));
+      out[slot] = (j >= 0 && slot < n_valid && tk <= t) ? tk : -1;
+    }
     return;
   }
   // the slot scores do not depend on the block list: both loads in flight
-  // together, one round trip before the barrier
+  // together, one round trip before the barrier (slots past the list's
+  // real length are read but masked below)
   const float* sc = scores + (size_t)q * m * B;  // 32-byte aligned: m * B is a multiple of 8
   const int idx0 = threadIdx.x * R;
-  uint32_t key[R];
+  float v[R];
   if constexpr (R >= 4) {
 #pragma unroll
     for (int r = 0; r < R; r += 4) {
       if (idx0 + r + 3 < n_valid) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[r + e] = score_key(v[e]);
+        for (int e = 0; e < 4; ++e) v[r + e] = x[e];
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int idx = idx0 + r + e;
-          key[r + e] = idx < n_valid ? score_key(sc[idx]) : 0u;
+          v[r + e] = idx < n_valid ? sc[idx] : 0.f;
         }
       }
     }
@@ -570,12 +589,32 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = idx0 + r;
-      const float v = sc[idx < n_valid ? idx : 0];
-      key[r] = idx < n_valid ? score_key(v) : 0u;
+      v[r] = sc[idx < n_valid ? idx : 0];
     }
   }
-  for (int p = threadIdx.x; p < n_sel; p += NT) bl[p] = blk[(size_t)q * m + p];
+  for (int p = threadIdx.x; p < n_sel; p += NT) bl[p] = blq[p];
   __syncthreads();
+  // the list's length: its entries are a valid prefix, then -1
+  if (bl[n_sel - 1] < 0) {  // (uniform) shorter than min(c + 1, m)
+    int lo = 0, hi = n_sel - 1;  // bl[lo] is valid, bl[hi] is not
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (bl[mid] >= 0) lo = mid;
+      else hi = mid;
+    }
+    n_sel = lo + 1;
+    n_valid = (n_sel - 1) * B + (t - c * B + 1);
+    if (n_valid <= k) {
+      for (int slot = threadIdx.x; slot < k; slot += NT) {
+        const int j = slot < n_valid ? bl[slot >> log2B] : -1;
+        out[slot] = slot < n_valid ? (j << log2B) + (slot & (B - 1)) : -1;
+      }
+      return;
+    }
+  }
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) key[r] = idx0 + r < n_valid ? score_key(v[r]) : 0u;
   const int bmask = B - 1;
   const int tbase = ONEBLK ? (bl[min(idx0 >> log2B, n_sel - 1)] << log2B) | (idx0 & bmask) : 0;
   const int dummy = k + lane_id();

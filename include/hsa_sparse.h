@@ -140,7 +140,11 @@ hsa_sparse_status_t hsa_block_topm(const hsa_sparse_shape_t* shape,
 /*
  * Step 3, token scores and top-k inside the kept blocks (HISA page, step
  * two).
- *   qI, kI  as above; blk [batch, n_q, top_m] from step 2.
+ *   qI, kI  as above; blk [batch, n_q, top_m] from step 2
+ *           (hsa_block_topm or hsa_block_topm_3level): per query an
+ *           ascending list of blocks <= c = t / block whose last entry is c,
+ *           -1 padded; it may hold fewer than min(c + 1, top_m) blocks (the
+ *           three-level selection can keep fewer).
  *   tok     [batch, n_q, top_k] int32 output: candidates are the tokens
  *           s <= t of the kept blocks; all of them if at most top_k, else
  *           the best top_k by qI . kI[s]; ascending, -1 padded.

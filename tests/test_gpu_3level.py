@@ -42,6 +42,12 @@ CASES = [
     # one-launch decode path at its widest: 1998 level-1 keys (R1 = 2) and
     # 4800 level-2 slots (R2 = 8)
     (case("one_launch_r2_r8", 2, 128000, 3, 64, 8, 1, 300, 400, 8, 600), 2),
+    # fewer level-2 candidates than m (2 super-blocks of 8 blocks: at most 16
+    # blocks for m = 31): the lists are shorter than min(c + 1, m) and the
+    # token stage (block-major scoring here) must take their length from them
+    (case("fewer_candidates_than_m", 2, 10100, 118, 128, 32, 1, 31, 209, 8, 2), 2),
+    (case("fewer_candidates_decode", 3, 20000, 1, 64, 16, 1, 40, 100, 4, 3), 2),
+    (case("fewer_candidates_keep_all", 1, 9000, 50, 64, 16, 1, 60, 960, 8, 2), 2),
 ]
 
 
