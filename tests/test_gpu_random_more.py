@@ -1,0 +1,132 @@
+"""Seeded random sweeps of the decode step over sequences of different
+lengths, of hsa_forward with a later summary_start_block (stale state for
+the newest blocks), and of the flat indexer, each against the oracle or the
+full recomputation.  Parameters are drawn from fixed seeds; the test ids
+name them.
+"""
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_index_sparse_amd import _lib, datagen, pipeline
+from hierarchical_index_sparse_amd.workloads import Workload
+from oracle import hisa_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def _dims(rng, L_max):
+    B = int(rng.choice([8, 16, 32, 64, 128]))
+    L = int(rng.integers(1, L_max + 1))
+    dI = int(rng.choice([64, 128]))
+    nL = int(rng.choice([1, 1, 2, 4]))
+    m = int(rng.integers(2, 41))
+    k = m * B + int(rng.integers(0, 30)) if rng.random() < 0.15 else int(rng.integers(1, min(m * B, 700) + 1))
+    if k < m * B and m * B > 32768:
+        m = 32768 // B
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8, 16]))
+    vr = int(rng.choice([1, 2, 3, 8]))
+    return B, L, dI, nL, m, k, Hq, Hkv, vr
+
+
+# ------------------------------------------------------- decode, per-sequence lengths
+
+def draw_decode(idx):
+    rng = np.random.default_rng(20000 + idx)
+    B, cap, dI, nL, m, k, Hq, Hkv, vr = _dims(rng, 12000)
+    batch = int(rng.integers(1, 7))
+    w = Workload(name=f"rd_{idx}", batch=batch, seq_len=cap, n_q=1, d_index=dI, block=B, top_m=m, top_k=k,
+                 n_heads_q=Hq, n_heads_kv=Hkv, n_landmarks=nL)
+    edges = [cap, 1, B, B + 1, m * B, m * B + 1]
+    lens = [int(min(cap, max(1, edges[j] if rng.random() < 0.3 else rng.integers(1, cap + 1))))
+            for j in rng.integers(0, len(edges), batch)]
+    return w, vr, lens
+
+
+DECODE = [draw_decode(i) for i in range(40)]
+
+
+@pytest.mark.parametrize("w,vr,lens", DECODE, ids=[f"{c[0].name}-b{c[0].batch}-cap{c[0].seq_len}-d{c[0].d_index}"
+                                                   f"-B{c[0].block}-nL{c[0].n_landmarks}-m{c[0].top_m}-k{c[0].top_k}"
+                                                   for c in DECODE])
+def test_random_decode_step(w, vr, lens):
+    from test_gpu_varlen import check_step, run_step
+    inp = datagen.make_inputs(w, q_range=vr, centre_range=max(1, vr // 2), noise_range=max(1, vr // 2))
+    dev = pipeline.to_device(inp)
+    out = pipeline.alloc_outputs(w)
+    _lib.hsa_block_summary(_lib.shape_of(w), dev["kI"], dev.get("W"), 0, out["S"])
+    for step in range(2):  # a second step appends a token to every sequence (S carried)
+        cur = [min(w.seq_len, L + step) for L in lens]
+        check_step(w, inp, run_step(w, dev, out, cur), cur)
+
+
+# ------------------------------------------------------- incremental summaries
+
+def draw_incremental(idx):
+    rng = np.random.default_rng(30000 + idx)
+    B, L, dI, nL, m, k, Hq, Hkv, vr = _dims(rng, 8000)
+    nq = int(rng.integers(1, min(L, 400) + 1))
+    batch = int(rng.integers(1, 3))
+    w = Workload(name=f"ri_{idx}", batch=batch, seq_len=L, n_q=nq, d_index=dI, block=B, top_m=m, top_k=k,
+                 n_heads_q=Hq, n_heads_kv=Hkv, n_landmarks=nL)
+    start = int(rng.integers(0, (L - nq) // B + 1))
+    return w, vr, start
+
+
+INCREMENTAL = [draw_incremental(i) for i in range(30)]
+
+
+@pytest.mark.parametrize("w,vr,start", INCREMENTAL,
+                         ids=[f"{c[0].name}-L{c[0].seq_len}-q{c[0].n_q}-B{c[0].block}-nL{c[0].n_landmarks}-s{c[2]}"
+                              for c in INCREMENTAL])
+def test_random_incremental_summaries(w, vr, start):
+    # summaries of blocks before `start` are state; the call rebuilds the rest:
+    # every output equals a forward that builds all summaries
+    inp = datagen.make_inputs(w, q_range=vr, centre_range=max(1, vr // 2), noise_range=max(1, vr // 2))
+    dev = pipeline.to_device(inp)
+    full = pipeline.to_host(pipeline.run_forward(w, dev))
+    out = pipeline.alloc_outputs(w)
+    _lib.hsa_block_summary(_lib.shape_of(w), dev["kI"], dev.get("W"), 0, out["S"])
+    out["S"][:, start:] = 0
+    inc = pipeline.to_host(pipeline.run_forward(w, dev, out, summary_start_block=start))
+    for key in ("S", "blk", "tok", "O", "lse"):
+        assert np.array_equal(inc[key], full[key], equal_nan=True), key
+
+
+# ------------------------------------------------------- flat indexer
+
+def draw_flat(idx):
+    rng = np.random.default_rng(40000 + idx)
+    L = int(rng.integers(1, 90001))
+    nq = int(rng.integers(1, 4)) if rng.random() < 0.5 else int(rng.integers(1, min(L, 300) + 1))
+    k = int(rng.integers(1, 8193)) if rng.random() < 0.85 else L + int(rng.integers(0, 50))
+    batch = int(rng.integers(1, 3)) if L * nq < 3_000_000 else 1
+    dI = int(rng.choice([64, 128]))
+    vr = int(rng.choice([1, 2, 8]))
+    w = Workload(name=f"rf_{idx}", batch=batch, seq_len=L, n_q=nq, d_index=dI, block=128, top_m=2, top_k=k,
+                 n_heads_q=1, n_heads_kv=1, n_landmarks=1)
+    return w, vr
+
+
+FLAT = [draw_flat(i) for i in range(30)]
+
+
+@pytest.mark.parametrize("w,vr", FLAT, ids=[f"{c[0].name}-b{c[0].batch}-L{c[0].seq_len}-q{c[0].n_q}"
+                                            f"-d{c[0].d_index}-k{c[0].top_k}" for c in FLAT])
+def test_random_flat_topk(w, vr):
+    inp = datagen.make_inputs(w, attention=False, q_range=vr, centre_range=max(1, vr // 2),
+                              noise_range=max(1, vr // 2))
+    dev = pipeline.to_device({"qI": inp["qI"], "kI": inp["kI"]})
+    tok = torch.full((w.batch, w.n_q, w.top_k), -7, dtype=torch.int32, device="cuda")
+    _lib.hsa_flat_topk(_lib.shape_of(w), dev["qI"], dev["kI"], tok)
+    torch.cuda.synchronize()
+    tok = tok.cpu().numpy()
+    rng = np.random.default_rng(6)
+    pairs = [(b, i) for b in range(w.batch) for i in range(w.n_q)]
+    if len(pairs) > 12:
+        pairs = sorted(set([pairs[j] for j in rng.choice(len(pairs), 10, replace=False)] +
+                           [(b, w.n_q - 1) for b in range(w.batch)]))
+    for b, i in pairs:
+        t = w.seq_len - w.n_q + i
+        assert np.array_equal(tok[b, i], orc.flat_topk(inp["qI"][b, i], inp["kI"][b], t, w.top_k)), (b, i, t)
