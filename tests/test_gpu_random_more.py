@@ -130,3 +130,89 @@ def test_random_flat_topk(w, vr):
     for b, i in pairs:
         t = w.seq_len - w.n_q + i
         assert np.array_equal(tok[b, i], orc.flat_topk(inp["qI"][b, i], inp["kI"][b], t, w.top_k)), (b, i, t)
+
+
+# ------------------------------------------------------- per-head and three-level decode, different lengths
+
+def draw_heads_varlen(idx):
+    rng = np.random.default_rng(50000 + idx)
+    B = int(rng.choice([8, 16, 32, 64, 128]))
+    cap = int(rng.integers(1, 12001))
+    nL = int(rng.choice([1, 2, 4]))
+    m = int(rng.integers(2, 30))
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 4, 8]))
+    batch = int(rng.integers(1, 5))
+    w = Workload(name=f"rhv_{idx}", batch=batch, seq_len=cap, n_q=1, d_index=128, block=B, top_m=m, top_k=m * B,
+                 n_heads_q=Hq, n_heads_kv=Hkv, n_landmarks=nL, per_head=True)
+    lens = [int(x) for x in rng.integers(1, cap + 1, batch)]
+    return w, lens
+
+
+HEADS_VARLEN = [draw_heads_varlen(i) for i in range(20)]
+
+
+@pytest.mark.parametrize("w,lens", HEADS_VARLEN, ids=[f"{c[0].name}-b{c[0].batch}-cap{c[0].seq_len}-B{c[0].block}"
+                                                      f"-nL{c[0].n_landmarks}-m{c[0].top_m}" for c in HEADS_VARLEN])
+def test_random_heads_decode_step(w, lens):
+    from test_gpu_heads import _check_varlen_step
+    inp = datagen.make_inputs(w)
+    dev = pipeline.to_device(inp)
+    out = pipeline.alloc_outputs(w)
+    _lib.hsa_head_landmarks(_lib.shape_of(w), dev["K"], dev.get("W"), 0, out["LK"])
+    stats = {"lists": 0, "equal": 0}
+    for step in range(2):
+        cur = [min(w.seq_len, L + step) for L in lens]
+        lt = torch.tensor(cur, dtype=torch.int32, device="cuda")
+        g = pipeline.to_host(pipeline.run_forward_heads(w, dev, out, seq_lens=lt))
+        _check_varlen_step(w, inp, g, cur, stats)
+
+
+def draw_3level_varlen(idx):
+    rng = np.random.default_rng(60000 + idx)
+    B = int(rng.choice([8, 16, 32, 64]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    cap = int(rng.integers(1, 30001))
+    nL = int(rng.choice([1, 1, 2, 4]))
+    m2 = int(rng.integers(2, min(8192 // G, 40) + 1))
+    m = int(rng.integers(2, 50))
+    k = m * B if rng.random() < 0.15 else int(rng.integers(1, min(m * B, 500) + 1))
+    if m * B > 32768:
+        m = 32768 // B
+    batch = int(rng.integers(1, 5))
+    w = Workload(name=f"r3v_{idx}", batch=batch, seq_len=cap, n_q=1, d_index=int(rng.choice([64, 128])), block=B,
+                 top_m=m, top_k=k, n_heads_q=4, n_heads_kv=1, n_landmarks=nL, group=G, top_m2=m2)
+    lens = [int(x) for x in rng.integers(1, cap + 1, batch)]
+    return w, lens
+
+
+THREE_VARLEN = [draw_3level_varlen(i) for i in range(20)]
+
+
+@pytest.mark.parametrize("w,lens", THREE_VARLEN, ids=[f"{c[0].name}-b{c[0].batch}-cap{c[0].seq_len}-B{c[0].block}"
+                                                      f"-G{c[0].group}-m2{c[0].top_m2}-m{c[0].top_m}"
+                                                      f"-nL{c[0].n_landmarks}" for c in THREE_VARLEN])
+def test_random_three_level_decode_step(w, lens):
+    from parity import ATOL
+    inp = datagen.make_inputs(w, q_range=2, centre_range=1, noise_range=1)
+    dev = pipeline.to_device(inp)
+    out = pipeline.alloc_outputs(w)
+    shape = _lib.shape_of(w)
+    _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), 0, out["S"])
+    _lib.hsa_super_summary(shape, w.group, out["S"], 0, out["S2"])
+    B, G = w.block, w.group
+    for step in range(2):
+        cur = [min(w.seq_len, L + step) for L in lens]
+        lt = torch.tensor(cur, dtype=torch.int32, device="cuda")
+        g = pipeline.to_host(pipeline.run_forward_3level(w, dev, out, seq_lens=lt))
+        for b, Lb in enumerate(cur):
+            t = Lb - 1
+            ctx = f"{w.name} step {step} b={b} L_b={Lb}"
+            S_b = orc.block_summary(inp["kI"][b, :Lb], B, inp.get("W"))
+            S2_b = orc.super_summary(S_b, G)
+            assert np.array_equal(g["S"][b, :S_b.shape[0]], S_b), f"summaries differ: {ctx}"
+            assert np.array_equal(g["S2"][b, :S2_b.shape[0]], S2_b), f"super-block summaries differ: {ctx}"
+            r = orc.forward_query_3level(inp, b, 0, t, B, G, w.top_m2, w.top_m, w.top_k, w.scale, S_b, S2_b)
+            assert np.array_equal(g["blk"][b, 0], r["blk"]), f"block list differs: {ctx}"
+            assert np.array_equal(g["tok"][b, 0], r["tok"]), f"token list differs: {ctx}"
+            assert np.abs(g["O"][b, 0].astype(np.float64) - r["O"]).max() <= ATOL, ctx
