@@ -488,8 +488,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sequences or queries would shard with no exchange; see the design notes)",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(decode sequences and prefill queries would shard across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
