@@ -254,3 +254,35 @@ def test_decode_3level_different_lengths(batch, cap, dI, B, nL, G, m2, m, k, len
             assert np.array_equal(g["tok"][b, 0], r["tok"]), f"token list differs: {ctx}"
             assert np.abs(g["O"][b, 0].astype(np.float64) - r["O"]).max() <= ATOL, ctx
             assert np.abs(g["lse"][b, 0].astype(np.float64) - r["lse"]).max() <= ATOL, ctx
+
+
+def test_standalone_token_topk_on_three_level_lists():
+    # hsa_block_topm_3level's lists (shorter than min(c + 1, m) here: two
+    # super-blocks of 4 blocks for m = 20) through the standalone
+    # hsa_token_topk and hsa_sparse_attn, against the oracle
+    w = case("standalone_short_lists", 2, 6000, 40, 64, 16, 1, 20, 90, 4, 2)
+    inp = make(w, 2)
+    dev = pipeline.to_device(inp)
+    shape = _lib.shape_of(w)
+    st = pipeline.alloc_outputs(w)
+    _lib.hsa_block_summary(shape, dev["kI"], None, 0, st["S"])
+    _lib.hsa_super_summary(shape, w.group, st["S"], 0, st["S2"])
+    _lib.hsa_block_topm_3level(shape, w.group, w.top_m2, dev["qI"], st["S"], st["S2"], st["sup"], st["blk"])
+    _lib.hsa_token_topk(shape, dev["qI"], dev["kI"], st["blk"], st["tok"])
+    _lib.hsa_sparse_attn(shape, dev["Q"], dev["K"], dev["V"], st["tok"], st["O"], st["lse"])
+    torch.cuda.synchronize()
+    g = pipeline.to_host(st)
+    S = oracle_summaries(inp, w)
+    S2 = np.stack([orc.super_summary(S[b], w.group) for b in range(w.batch)])
+    short = 0
+    for b in range(w.batch):
+        for i in range(w.n_q):
+            t = w.query_pos(i)
+            r = orc.forward_query_3level(inp, b, i, t, w.block, w.group, w.top_m2, w.top_m, w.top_k, w.scale, S[b],
+                                         S2[b])
+            ctx = f"b={b} i={i} t={t}"
+            assert np.array_equal(g["blk"][b, i], r["blk"]), ctx
+            assert np.array_equal(g["tok"][b, i], r["tok"]), ctx
+            assert np.abs(g["O"][b, i].astype(np.float64) - r["O"]).max() <= ATOL, ctx
+            short += int((r["blk"] >= 0).sum() < min(t // w.block + 1, w.top_m))
+    assert short > 0  # the case does exercise lists shorter than min(c + 1, m)
