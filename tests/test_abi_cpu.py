@@ -281,3 +281,23 @@ def test_kernel_event_validation(lib):
     # NULL events are allowed: kernels are then named but not timed
     assert lib.hsa_sparse_set_kernel_events(a, b, 4) == 0
     assert lib.hsa_sparse_set_kernel_events(None, None, 0) == 0
+
+
+def test_header_is_a_c_abi(tmp_path):
+    # a pedantic C99 translation unit includes the header alone, takes the
+    # address of every declared entry point and links against the library
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "abi.c"
+    src.write_text('#include "hsa_sparse.h"\n#include <stdio.h>\ntypedef void (*fn_t)(void);\n'
+                   "int main(void) {\n  fn_t fns[] = {\n" + ",\n".join(f"    (fn_t)&{n}" for n in names) +
+                   '\n  };\n  printf("%d\\n", (int)(sizeof(fns) / sizeof(fns[0])));\n  return 0;\n}\n')
+    lib_dir = os.path.dirname(_lib.LIB_PATH)
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-I", os.path.dirname(HEADER), str(src),
+                        "-L", lib_dir, "-lhsa_sparse", "-Wl,--allow-shlib-undefined", "-o", str(tmp_path / "abi")],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
