@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
 
 #include "hsa_sparse.h"
@@ -70,6 +71,8 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
     if (s->top_k < 1) return fail(HSA_SPARSE_INVALID_ARG, "top_k must be >= 1");
     if (s->d_index != 64 && s->d_index != 128)
       return fail(HSA_SPARSE_UNSUPPORTED, "d_index must be 64 or 128 (got %d)", s->d_index);
+    // token positions and the padded score-row length are 32-bit integers
+    if (s->seq_len > (1 << 30)) return fail(HSA_SPARSE_UNSUPPORTED, "flat top-k needs seq_len <= 2^30");
   }
   if (need_index) {
     if (s->d_index != 64 && s->d_index != 128)
@@ -242,7 +245,12 @@ hsa_sparse_status_t hsa_sparse_set_kernel_events(hsa_sparse_event_t const* start
 const char* hsa_sparse_last_kernels(void) { return g_kernel_names.c_str(); }
 
 const char* hsa_sparse_strerror(hsa_sparse_status_t status) {
-  switch (status) {
+  // a C caller may pass any int; read the bits as one, since a value
+  // outside the enumerators' range is not a valid C++ enum value
+  static_assert(sizeof(status) == sizeof(int), "C enum is int-sized");
+  int code;
+  std::memcpy(&code, &status, sizeof code);
+  switch (code) {
     case HSA_SPARSE_OK: return "success";
     case HSA_SPARSE_INVALID_ARG: return "invalid argument";
     case HSA_SPARSE_UNSUPPORTED: return "unsupported shape";

@@ -219,8 +219,9 @@ __global__ __launch_bounds__(NW * 64) void k_flat_merge(const uint2* __restrict_
 
 // ----------------------------------------------------------------- host side
 
-static int flat_nchunk(const Dims& s) { return (s.L + kFlatChunk - 1) / kFlatChunk; }
-static int flat_lp(const Dims& s) { return (s.L + 3) & ~3; }
+// seq_len <= 2^30 (checked by the caller), so both fit in an int
+static int flat_nchunk(const Dims& s) { return (int)(((long long)s.L + kFlatChunk - 1) / kFlatChunk); }
+static int flat_lp(const Dims& s) { return (int)(((long long)s.L + 3) & ~3ll); }
 static bool flat_needs_lists(const Dims& s) { return s.k < s.L && flat_nchunk(s) > 1; }
 
 bool flat_topk_supported(const Dims& s) {

@@ -240,8 +240,9 @@ hsa_sparse_status_t hsa_decode_step(const hsa_sparse_shape_t* shape,
  *   workspace  >= hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_FLAT_TOPK):
  *           every causal score in fp32 ([batch * n_q, seq_len] rounded up to
  *           a multiple of 4 per row) plus the chunk winners' lists when
- *           seq_len > 32768.
- * Supported: d_index in {64, 128}; top_k <= 8192 when top_k < seq_len.
+ *           top_k < seq_len and seq_len > 8192.
+ * Supported: d_index in {64, 128}; seq_len <= 2^30; top_k <= 8192 when
+ *           top_k < seq_len.
  * Errors: as for the other entry points; nothing is launched on an error.
  */
 hsa_sparse_status_t hsa_flat_topk(const hsa_sparse_shape_t* shape,
