@@ -394,3 +394,19 @@ def test_datagen_deterministic_and_shaped():
     assert spread.max() <= 8
     c = datagen.make_inputs(w.with_(seed=1))
     assert not np.array_equal(a["kI"], c["kI"])
+
+
+def test_datagen_matches_stored_hashes():
+    # every generated tensor of every named workload (shrunk) hashes as when
+    # tests/golden/datagen_sha256.txt was written: inputs are the same on
+    # every machine and across library versions
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "make_datagen_hashes.py")
+    spec = importlib.util.spec_from_file_location("make_datagen_hashes", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    stored = [ln.rstrip("\n") for ln in open(mod.OUT) if not ln.startswith("#")]
+    fresh = list(mod.lines())
+    assert [ln.rsplit(" ", 1)[0] for ln in fresh] == [ln.rsplit(" ", 1)[0] for ln in stored]
+    changed = [a for a, b in zip(fresh, stored) if a != b]
+    assert not changed, f"generated inputs changed: {changed[:5]}"
