@@ -415,12 +415,14 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
 
 // Split plan: enough waves to fill the chip when there are few queries.
 static void split_plan(const Dims& s, int& nsplit, int& chunk) {
-  // at least 2 tiles (64 entries) per split, at most 256 splits (the merge
-  // reads every split's partial); at most ~2048 waves in total
+  // at least 2 tiles (64 entries) per split (one-tile splits spend more on
+  // each wave's start than they gain in waves), at most 1024 splits (the
+  // merge reads a quarter of them after the in-workgroup pre-merge); at
+  // most ~2048 waves in total
   const long long items = (long long)s.b * s.nq * s.Hkv;
   const int tiles = (s.k + 31) / 32;
   long long want = (items <= 0 || items >= 2048) ? 1 : (2048 + items - 1) / items;
-  const long long cap = min((tiles + 1) / 2, 256);
+  const long long cap = min((tiles + 1) / 2, 1024);
   if (want > cap) want = cap;
   if (want < 1) want = 1;
   const int tiles_per = (int)((tiles + want - 1) / want);
