@@ -122,6 +122,9 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
   }
   const long long nq_total = (long long)s->batch * s->n_q;
   if (nq_total > (1ll << 30)) return fail(HSA_SPARSE_UNSUPPORTED, "batch * n_q too large");
+  // attention numbers its (query, head) rows with 32-bit integers
+  if (need_attn && nq_total * s->n_heads_q > (1ll << 30))
+    return fail(HSA_SPARSE_UNSUPPORTED, "batch * n_q * n_heads_q too large");
   d.b = s->batch;
   d.L = s->seq_len;
   d.nq = s->n_q;

@@ -39,9 +39,10 @@
  * two in [8, 128]; n_landmarks in {1, 2, 4}; n_heads_kv divides n_heads_q
  * with at most 16 query heads per kv head; top_m >= 2; top_k >= 1;
  * ceil(seq_len / block) - 2 <= 32768; top_m * block <= 32768 unless
- * top_k >= top_m * block (then no token scoring is needed); for attention,
- * seq_len * n_heads_kv * 256 < 2^31 (a kv row's byte offset in its
- * sequence is a 31-bit integer).
+ * top_k >= top_m * block (then no token scoring is needed);
+ * batch * n_q <= 2^30; for attention, seq_len * n_heads_kv * 256 < 2^31
+ * (a kv row's byte offset in its sequence is a 31-bit integer) and
+ * batch * n_q * n_heads_q <= 2^30.
  */
 #ifndef HSA_SPARSE_H
 #define HSA_SPARSE_H

@@ -82,6 +82,8 @@ static void shape_checks(void) {
   s = base(); s.scale = 0.0f / 0.0f; EXPECT(forward(&s, FAKE_U16, BIG_WS), HSA_SPARSE_INVALID_ARG);
   s = base(); s.seq_len = INT_MAX; s.n_q = 1; EXPECT(forward(&s, FAKE_U16, BIG_WS), HSA_SPARSE_UNSUPPORTED);
   s = base(); s.top_m = INT_MAX; s.top_k = 1; EXPECT(forward(&s, FAKE_U16, BIG_WS), HSA_SPARSE_UNSUPPORTED);
+  s = base(); s.batch = 1 << 20; s.n_q = 1 << 10; s.seq_len = 1 << 10; /* 2^34 (query, head) rows */
+  EXPECT(forward(&s, FAKE_U16, BIG_WS), HSA_SPARSE_UNSUPPORTED);
   s = base(); EXPECT(forward(&s, NULL, BIG_WS), HSA_SPARSE_INVALID_ARG);
   s = base(); EXPECT(forward(&s, FAKE_U16, 1), HSA_SPARSE_WORKSPACE_TOO_SMALL);
   s = base(); s.batch = 0; EXPECT(forward(&s, NULL, 0), HSA_SPARSE_OK);
