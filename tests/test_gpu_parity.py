@@ -252,3 +252,24 @@ def test_maximum_select_sizes(name, L, nq, dI, B, m, k):
     check_summaries(gpu["S"], S)
     check_list_invariants(gpu, w)
     check_queries(gpu, inp, w, S, [(b, i) for b in range(w.batch) for i in range(nq)])
+
+
+@pytest.mark.parametrize("name,L,m,k", [
+    # 375 splits of 2 tiles: more than 256, not a multiple of 4, so every
+    # split's partial goes to the merge
+    ("splits_375_unmerged", 40000, 200, 24000),
+    # 512 splits (the most a 32768-entry list gets), pre-merged 4 to a
+    # workgroup: 128 partials per row reach the merge
+    ("splits_512_premerged", 50000, 256, 32768),
+])
+def test_one_query_with_a_long_list(name, L, m, k):
+    # one query and one kv head: the split plan's cap, not the wave target,
+    # sets the split count
+    w = small(name, batch=1, seq_len=L, n_q=1, d_index=128, block=128, top_m=m, top_k=k, n_heads_q=16,
+              n_heads_kv=1)
+    inp = make_small(w, 3)
+    gpu = pipeline.to_host(pipeline.run_forward(w, pipeline.to_device(inp)))
+    S = oracle_summaries(inp, w)
+    check_summaries(gpu["S"], S)
+    check_list_invariants(gpu, w)
+    check_queries(gpu, inp, w, S, [(0, 0)])
