@@ -300,7 +300,10 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
     wall = time.perf_counter() - t0
     _ORC_STATE.clear()
     # the summaries are built once per sequence: charge them in full
+    # (they are handed on to parity_check under the underscore keys)
     return {
+        "_S": S,
+        "_S2": S2,
         "value": done / (wall + t_summary),
         "unit": "queries/s",
         "cores": cores,
@@ -311,6 +314,31 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
                   f"built once ({t_summary:.2f} s); "
                   f"{wall:.1f} s wall on {cores} worker processes",
     }
+
+
+def parity_check(w: Workload, inp: dict, S, S2, gpu: dict, pairs) -> dict:
+    """The oracle against the GPU outputs of the benchmarked configuration on
+    the sampled (sequence, query) pairs: index sets bit for bit, O and lse
+    within the 2e-3 max-abs bound.  gpu[key][n] holds pair n's row."""
+    from oracle import hisa_oracle as orc
+    lens = inp.get("seq_lens")
+    exact, err_o, err_l = True, 0.0, 0.0
+    for n, (b, i) in enumerate(pairs):
+        t = w.query_pos(i) if lens is None else int(lens[b]) - 1
+        if w.group:
+            r = orc.forward_query_3level(inp, b, i, t, w.block, w.group, w.top_m2, w.top_m, w.top_k, w.scale, S[b],
+                                         S2[b])
+        else:
+            r = orc.forward_query(inp, b, i, t, w.block, w.top_m, w.top_k, w.scale, S_bits=S[b])
+        exact = exact and bool(np.array_equal(gpu["blk"][n], r["blk"]) and np.array_equal(gpu["tok"][n], r["tok"]))
+        err_o = max(err_o, float(np.abs(gpu["O"][n].astype(np.float64) - r["O"]).max()))
+        err_l = max(err_l, float(np.abs(gpu["lse"][n].astype(np.float64) - r["lse"]).max()))
+    return {"queries": len(pairs), "index_sets_exact": exact, "max_abs_err_O": err_o, "max_abs_err_lse": err_l,
+            "tolerance": PARITY_ATOL, "pass": exact and err_o <= PARITY_ATOL and err_l <= PARITY_ATOL}
+
+
+PARITY_ATOL = 2e-3
+PARITY_SAMPLE = 16
 
 
 # ------------------------------------------------------------- HIP events
@@ -498,6 +526,7 @@ def main():
         w = dataclasses.replace(w, batch=args.batch)
     inp = datagen.make_inputs(w)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_sample)
+    ora_S, ora_S2 = (None, None) if cpu is None else (cpu.pop("_S"), cpu.pop("_S2"))
 
     import torch
 
@@ -648,6 +677,37 @@ def main():
         hip.destroy(a)
         hip.destroy(b)
 
+    # Parity of the benchmarked configuration: one more call writes the index
+    # lists too; its O must equal the timed steps' bit for bit, and a sample
+    # of queries is checked against the oracle (which ran before the GPU was
+    # touched, for the CPU baseline).  Per-head lists rank float scores and
+    # are checked with an fp32 bound in the tests instead.
+    parity = None
+    if ora_S is not None and not w.per_head:
+        chk = pipeline.alloc_outputs(w)
+        if w.group:
+            _lib.hsa_forward_3level(shape, w.group, w.top_m2, dev["qI"], dev["kI"], dev.get("W"), start_block,
+                                    out["S"], out["S2"], dev["Q"], dev["K"], dev["V"], chk["sup"], chk["blk"],
+                                    chk["tok"], chk["O"], chk["lse"], ws)
+        elif lens is None:
+            _lib.hsa_forward(shape, dev["qI"], dev["kI"], dev.get("W"), start_block, out["S"], dev["Q"], dev["K"],
+                             dev["V"], chk["blk"], chk["tok"], chk["O"], chk["lse"], ws)
+        else:
+            _lib.hsa_decode_step(shape, dev["seq_lens"], dev["qI"], dev["kI"], dev.get("W"), out["S"], dev["Q"],
+                                 dev["K"], dev["V"], chk["blk"], chk["tok"], chk["O"], chk["lse"], ws)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(chk["O"], out["O"]) and torch.equal(chk["lse"], out["lse"]))
+        total = w.batch * w.n_q
+        flat_ids = np.unique(np.linspace(0, total - 1, min(PARITY_SAMPLE, total)).round().astype(np.int64))
+        pairs = [(int(x // w.n_q), int(x % w.n_q)) for x in flat_ids]
+        bs = torch.tensor([p[0] for p in pairs], device="cuda")
+        qs = torch.tensor([p[1] for p in pairs], device="cuda")
+        rows = {key: chk[key][bs, qs].cpu().numpy() for key in ("blk", "tok", "O", "lse")}
+        del chk
+        parity = parity_check(w, inp, ora_S, ora_S2, rows, pairs)
+        parity["timed_outputs_identical"] = same
+        parity["pass"] = parity["pass"] and same
+
     # the flat indexer takes one length for the batch
     flat = None if (args.no_flat or lens is not None or w.group or w.per_head) else flat_comparison(
         w, dev, shape, stage_ms, args.steps, hip)
@@ -717,6 +777,7 @@ def main():
         **({"three_level_vs_two_level": two} if w.group else {}),
         **({"per_head_vs_dense_attention": dense} if w.per_head else {}),
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(res), flush=True)
 

@@ -100,3 +100,24 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_parity_check_flags_differences():
+    w = Workload(name="p", batch=2, seq_len=700, n_q=5, d_index=16, block=16, top_m=4, top_k=30, n_heads_q=4,
+                 n_heads_kv=2)
+    inp = datagen.make_inputs(w)
+    S = [orc.block_summary(inp["kI"][b], w.block) for b in range(w.batch)]
+    pairs = [(0, 0), (1, 4)]
+    rows = {key: [] for key in ("blk", "tok", "O", "lse")}
+    for b, i in pairs:
+        r = orc.forward_query(inp, b, i, w.query_pos(i), w.block, w.top_m, w.top_k, w.scale, S_bits=S[b])
+        for key in rows:
+            rows[key].append(np.asarray(r[key], dtype=np.float32 if key in ("O", "lse") else np.int32))
+    rows = {key: np.stack(v) for key, v in rows.items()}
+    good = bench.parity_check(w, inp, S, None, rows, pairs)
+    assert good["pass"] and good["index_sets_exact"] and good["max_abs_err_O"] < 1e-6
+    bad = dict(rows, tok=rows["tok"].copy())
+    bad["tok"][1, 0] += 1
+    assert not bench.parity_check(w, inp, S, None, bad, pairs)["index_sets_exact"]
+    off = bench.parity_check(w, inp, S, None, dict(rows, O=rows["O"] + 3e-3), pairs)
+    assert off["index_sets_exact"] and not off["pass"]
