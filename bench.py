@@ -151,6 +151,7 @@ def algorithmic_work(w: Workload, lens=None) -> dict:
 KERNEL_STAGE = {
     "k_block_summary": "block_summary", "k_super_summary": "block_summary", "k_head_landmarks": "block_summary",
     "k_block_scores": "block_topm", "k_block_scores_mfma": "block_topm", "k_block_select": "block_topm",
+    "k_block_scores_max": "block_topm",
     "k_block_topm_decode": "block_topm", "k_block_topm_l2": "block_topm", "k_block_topm_3level_decode": "block_topm",
     "k_head_scores_mfma": "block_topm", "k_head_select": "block_topm",
     "k_token_scores": "token_topk", "k_token_scores_tiled": "token_topk", "k_bm_scores": "token_topk",
@@ -185,19 +186,34 @@ def kernel_work(w: Workload, kernel: str, lens=None) -> dict:
             sb, st, kept = per_query_counts(w, np.asarray(lens, dtype=np.int64) - 1)
         sb, st = float(sb.sum()), float(st.sum())
         nqt = b * nq
-        if kernel == "k_block_scores_mfma":
-            return {"bytes": sb * 4, "flops": 2.0 * dI * nL * sb, "bound": "mfma"}
+        if kernel in ("k_block_scores_mfma", "k_block_scores_max"):
+            out = 4.0 * nqt if kernel == "k_block_scores_max" else sb * 4
+            return {"bytes": out, "flops": 2.0 * dI * nL * sb, "bound": "mfma"}
         if kernel == "k_block_scores":
             return {"bytes": nqt * dI * 2 + sb * nL * dI * 2 + sb * 4, "flops": 2.0 * dI * nL * sb, "bound": "hbm"}
         if kernel == "k_block_select":
             return {"bytes": sb * 4 + nqt * w.top_m * 4, "flops": 0.0, "bound": "hbm"}
         if kernel in ("k_token_scores", "k_token_scores_tiled", "k_bm_scores"):
-            return {"bytes": nqt * dI * 2 + st * dI * 2 + st * 4, "flops": 2.0 * dI * st, "bound": "hbm"}
+            # prefill scorers contract a tile of queries against kI rows that
+            # many queries share (served from LDS, L2 and the MALL): MFMA roof
+            bound = "hbm" if kernel == "k_token_scores" else "mfma"
+            return {"bytes": nqt * dI * 2 + st * dI * 2 + st * 4, "flops": 2.0 * dI * st, "bound": bound}
         if kernel == "k_token_select":
             return {"bytes": st * 4 + nqt * w.top_k * 4, "flops": 0.0, "bound": "hbm"}
     if stage is None:
         return {"bytes": 0.0, "flops": 0.0, "bound": "hbm"}
-    return {"bytes": work[stage]["bytes"], "flops": work[stage]["flops"], "bound": "hbm"}
+    # prefill attention gathers K/V rows that many queries share (a working
+    # set far smaller than the bytes gathered, served from L2 and the MALL):
+    # its roof is the bf16 MFMA rate of S = q K^T and O = P V; decode
+    # attention streams each sequence's rows once: HBM
+    bound = "mfma" if kernel == "k_sparse_attn" and regime(w) == "prefill" else "hbm"
+    return {"bytes": work[stage]["bytes"], "flops": work[stage]["flops"], "bound": bound}
+
+
+def regime(w: Workload) -> str:
+    """"decode": one query per sequence, every byte of a step read once;
+    "prefill": many queries per sequence re-reading shared rows."""
+    return "decode" if w.n_q == 1 else "prefill"
 
 
 # ----------------------------------------------------- hardware traffic
@@ -220,10 +236,12 @@ def kernel_source_hash(kernel: str) -> str:
 
 
 def recorded_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE record
-    (profiles/<workload>_traffic.txt), each scaled by what the same counter
-    read for a device copy of known size; None if there is no record for
-    this kernel or its sources changed since it was taken."""
+    """Memory-fabric bytes per launch from the committed FETCH_SIZE /
+    WRITE_SIZE record (profiles/<workload>_traffic.txt), each scaled by what
+    the same counter read for a device copy of known size; None if there is
+    no record for this kernel or its sources changed since it was taken.
+    These counters count the bytes between the L2 caches and the fabric, so
+    reads served by the MALL are included: an upper bound on DRAM bytes."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -272,6 +290,17 @@ def _oracle_one(args):
     return 1
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
     """Time the CPU oracle on an evenly spaced sample of the workload's queries."""
     import multiprocessing as mp
@@ -307,6 +336,7 @@ def cpu_baseline(w: Workload, inp: dict, sample: int) -> dict:
         "value": done / (wall + t_summary),
         "unit": "queries/s",
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{done} of {total} queries, evenly spaced over the batch and positions; "
                   f"{'landmarks' if w.per_head else 'block summaries'}"
@@ -497,37 +527,113 @@ def dense_comparison(w: Workload, dev: dict, steps: int, hip, step_ms: float) ->
 # ------------------------------------------------------------------- main
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill_64k", choices=sorted(WORKLOADS))
-    ap.add_argument("--cpu-sample", type=int, default=1024, help="queries the CPU oracle is timed on")
-    ap.add_argument("--batch", type=int, default=0,
-                    help="run the workload at this batch instead of its own (a batch study: the line then says "
-                         "batch_override; the workload's own batch is the measured configuration)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flat", action="store_true",
-                    help="skip timing the flat indexer (every causal token scored) on the same inputs")
-    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
-                    help="first run one device-to-device copy of this many MiB (a kernel of known "
-                         "traffic, to scale hardware byte counters against)")
-    args = ap.parse_args()
+# the SURVEY configurations reported beside the headline workload
+CONFIG_WORKLOADS = ("decode_128k", "chunked_prefill_512k", "decode_512k", "landmark_decode_1m")
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
-              "(decode sequences and prefill queries would shard across GPUs with no exchange)",
-              file=sys.stderr)
-        sys.exit(2)
 
-    w = WORKLOADS[args.workload]
-    if args.batch > 0:
-        w = dataclasses.replace(w, batch=args.batch)
-    inp = datagen.make_inputs(w)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_sample)
-    ora_S, ora_S2 = (None, None) if cpu is None else (cpu.pop("_S"), cpu.pop("_S2"))
+def measured_peaks(hip) -> dict:
+    """What this GPU reaches on a plain device copy (torch's copy kernel,
+    1 GiB read + 1 GiB written) and on a large bf16 GEMM (torch.matmul,
+    8192^3, hipBLASLt), best of several runs each: the measured ceilings the
+    vendor peaks are set against."""
+    import torch
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
 
+    def best_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = hip.create(), hip.create()
+            hip.record(a, stream)
+            fn()
+            hip.record(b, stream)
+            times.append(hip.elapsed_ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        return min(times)
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = best_ms(lambda: dst.copy_(src), 10)
+    out["copy_GBs"] = 2.0 * n / (ms / 1000.0) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((m, m), device="cuda", dtype=torch.bfloat16)
+    c = torch.empty((m, m), device="cuda", dtype=torch.bfloat16)
+    ms = best_ms(lambda: torch.matmul(a, b, out=c), 10)
+    out["bf16_gemm_TFLOPs"] = 2.0 * m ** 3 / (ms / 1000.0) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    out["vendor_hbm_GBs"] = HBM_PEAK_GBS
+    out["vendor_bf16_mfma_TFLOPs"] = MFMA_BF16_PEAK_TFLOPS
+    out["note"] = ("copy: 1 GiB device-to-device copy (2 GiB moved), best of 10; gemm: 8192^3 bf16 torch.matmul, "
+                   "best of 10")
+    return out
+
+
+def roofline_entry(w: Workload, kernel: str, kernel_ms: float, lens, peaks: dict | None) -> dict:
+    """The roofline of one kernel: algorithmic work per launch over its
+    average duration, against the roof its regime is bound by (bf16 MFMA
+    for the contractions over shared, cache-resident operands; HBM for
+    kernels that stream their bytes once)."""
+    kw = kernel_work(w, kernel, lens)
+    sec = kernel_ms / 1000.0
+    if kw["bound"] == "mfma":
+        achieved = kw["flops"] / sec / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS}
+        if peaks:
+            roof["frac_of_measured_gemm"] = achieved / peaks["bf16_gemm_TFLOPs"]
+        if kw["bytes"]:
+            roof["gather_rate_GBs"] = kw["bytes"] / sec / 1e9
+            roof["gather_note"] = ("algorithmic bytes gathered per second; rows shared by many queries are served "
+                                   "from LDS, L2 and the MALL, so this is a rate, not a fraction of HBM")
+        roof["algorithmic_per_launch"] = kw["flops"]
+    else:
+        achieved = kw["bytes"] / sec / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+        if peaks:
+            roof["frac_of_measured_copy"] = achieved / peaks["copy_GBs"]
+        roof["algorithmic_per_launch"] = kw["bytes"]
+    roof["traffic"] = recorded_traffic(w.name, kernel)
+    roof["traffic_note"] = ("FETCH_SIZE and WRITE_SIZE per launch, scaled by a copy of known size: bytes between "
+                            "L2 and the memory fabric, MALL hits included (an upper bound on DRAM bytes)")
+    roof["kernel"] = kernel
+    roof["stage"] = KERNEL_STAGE.get(kernel)
+    roof["kernel_ms_timed"] = kernel_ms
+    return roof
+
+
+def stage_rates(w: Workload, work: dict, stage_ms: dict) -> dict:
+    """Per stage: time, algorithmic bytes and flops per second, and the
+    fraction of a roof only where it is one: HBM for stages that stream
+    their bytes once (decode, and the block summaries), bf16 MFMA for the
+    stages with MFMA contractions.  Prefill stages gather rows that many
+    queries share, so their byte rates are rates only."""
+    out = {}
+    for n in STAGES:
+        sec = stage_ms[n] / 1000.0
+        gbs = work[n]["bytes"] / sec / 1e9 if sec > 0 else 0.0
+        tfs = work[n]["flops"] / sec / 1e12 if sec > 0 else 0.0
+        e = {"ms": stage_ms[n], "algorithmic_GBs": gbs}
+        streams = regime(w) == "decode" or n == "block_summary"
+        e["hbm_frac"] = gbs / HBM_PEAK_GBS if streams and gbs <= HBM_PEAK_GBS else None
+        if work[n]["flops"]:
+            e["TFLOPs"] = tfs
+            e["mfma_frac"] = tfs / MFMA_BF16_PEAK_TFLOPS
+        out[n] = e
+    return out
+
+
+def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=True) -> dict:
+    """Time K steps of the workload's whole path (after W warmup steps) and
+    the breakdowns around them; check the benchmarked configuration's
+    outputs against the oracle when `ora` (its summaries) is given."""
     import torch
 
     from hierarchical_index_sparse_amd import _lib, pipeline
@@ -585,25 +691,25 @@ def main():
                                                 ptr(out["lse"]), ptr(ws), nbytes, stream)
     elif w.group:
         fn, call_args = lib.hsa_forward_3level, (sref, None, w.group, w.top_m2, ptr(dev["qI"]), ptr(dev["kI"]),
-                                            ptr(dev.get("W")), start_block, ptr(out["S"]), ptr(out["S2"]),
-                                            ptr(dev["Q"]), ptr(dev["K"]), ptr(dev["V"]), ptr(out["sup"]), None, None,
-                                            ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes, stream)
+                                                 ptr(dev.get("W")), start_block, ptr(out["S"]), ptr(out["S2"]),
+                                                 ptr(dev["Q"]), ptr(dev["K"]), ptr(dev["V"]), ptr(out["sup"]), None,
+                                                 None, ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes, stream)
     elif lens is None:
         fn, call_args = lib.hsa_forward, (sref, ptr(dev["qI"]), ptr(dev["kI"]), ptr(dev.get("W")), start_block,
-                                     ptr(out["S"]), ptr(dev["Q"]), ptr(dev["K"]), ptr(dev["V"]), None, None,
-                                     ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes, stream)
+                                          ptr(out["S"]), ptr(dev["Q"]), ptr(dev["K"]), ptr(dev["V"]), None, None,
+                                          ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes, stream)
     else:
         fn, call_args = lib.hsa_decode_step, (sref, ptr(dev["seq_lens"]), ptr(dev["qI"]), ptr(dev["kI"]),
-                                         ptr(dev.get("W")), ptr(out["S"]), ptr(dev["Q"]), ptr(dev["K"]),
-                                         ptr(dev["V"]), None, None, ptr(out["O"]), ptr(out["lse"]), ptr(ws), nbytes,
-                                         stream)
+                                              ptr(dev.get("W")), ptr(out["S"]), ptr(dev["Q"]), ptr(dev["K"]),
+                                              ptr(dev["V"]), None, None, ptr(out["O"]), ptr(out["lse"]), ptr(ws),
+                                              nbytes, stream)
 
     def step():
         st = fn(*call_args)
         if st != 0:
             raise _lib.HsaSparseError(st, fn.__name__, lib.hsa_sparse_last_error().decode())
 
-    if args.calibrate_copy_mib:
+    if args.calibrate_copy_mib and headline:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -616,10 +722,9 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    hip = HipEvents()
     # Stage breakdown (untimed): all five stage boundaries recorded.  Every
     # recorded event costs the stream a few microseconds, so the timed region
-    # below records only the two around the dominant stage.
+    # below records none of them.
     n_prof = max(3, min(args.steps, 10))
     events = [[hip.create() for _ in range(5)] for _ in range(n_prof)]
     for s in range(n_prof):
@@ -679,11 +784,11 @@ def main():
 
     # Parity of the benchmarked configuration: one more call writes the index
     # lists too; its O must equal the timed steps' bit for bit, and a sample
-    # of queries is checked against the oracle (which ran before the GPU was
-    # touched, for the CPU baseline).  Per-head lists rank float scores and
-    # are checked with an fp32 bound in the tests instead.
+    # of queries is checked against the oracle.  Per-head lists rank float
+    # scores and are checked with an fp32 bound in the tests instead.
     parity = None
-    if ora_S is not None and not w.per_head:
+    if ora is not None and not w.per_head:
+        ora_S, ora_S2 = ora
         chk = pipeline.alloc_outputs(w)
         if w.group:
             _lib.hsa_forward_3level(shape, w.group, w.top_m2, dev["qI"], dev["kI"], dev.get("W"), start_block,
@@ -708,48 +813,140 @@ def main():
         parity["timed_outputs_identical"] = same
         parity["pass"] = parity["pass"] and same
 
-    # the flat indexer takes one length for the batch
-    flat = None if (args.no_flat or lens is not None or w.group or w.per_head) else flat_comparison(
-        w, dev, shape, stage_ms, args.steps, hip)
-    two = None
-    if w.group:
-        blk3 = pipeline.alloc_outputs(w)["blk"]
-        _lib.hsa_block_topm_3level(shape, w.group, w.top_m2, dev["qI"], out["S"], out["S2"], out["sup"], blk3)
-        torch.cuda.synchronize()
-        two = two_level_comparison(w, dev, shape, stage_ms, blk3.cpu().numpy(), args.steps, hip)
-    dense = dense_comparison(w, dev, args.steps, hip, gpu_step_ms) if w.per_head else None
+    extras = {}
+    if headline:
+        # the flat indexer takes one length for the batch
+        if not (args.no_flat or lens is not None or w.group or w.per_head):
+            extras["indexer_vs_flat"] = flat_comparison(w, dev, shape, stage_ms, args.steps, hip)
+        if w.group:
+            blk3 = pipeline.alloc_outputs(w)["blk"]
+            _lib.hsa_block_topm_3level(shape, w.group, w.top_m2, dev["qI"], out["S"], out["S2"], out["sup"], blk3)
+            torch.cuda.synchronize()
+            extras["three_level_vs_two_level"] = two_level_comparison(w, dev, shape, stage_ms, blk3.cpu().numpy(),
+                                                                      args.steps, hip)
+        if w.per_head:
+            extras["per_head_vs_dense_attention"] = dense_comparison(w, dev, args.steps, hip, gpu_step_ms)
+    del dev, out, ws
+    torch.cuda.empty_cache()
 
     ms_per_step = (t1 - t0) * 1000.0 / args.steps
     queries = w.batch * w.n_q
-    value = queries / (ms_per_step / 1000.0)
-
     work = algorithmic_work(w, lens)
-    kw = kernel_work(w, dom, lens)
-    dom_s = dom_ms / 1000.0
-    # only the MFMA block scorer is measured against the bf16 MFMA roof;
-    # every other kernel streams its operands and is measured against HBM
-    if kw["bound"] == "mfma":
-        achieved = kw["flops"] / dom_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    step_bytes = sum(work[n]["bytes"] for n in STAGES)
+    step_flops = sum(work[n]["flops"] for n in STAGES)
+    step_sec = ms_per_step / 1000.0
+    step = {"algorithmic_GB": step_bytes / 1e9, "algorithmic_TFLOP": step_flops / 1e12}
+    if regime(w) == "decode":
+        # every byte of a decode step is read once: the whole step against HBM
+        step["hbm_frac"] = step_bytes / step_sec / 1e9 / HBM_PEAK_GBS
     else:
-        achieved = kw["bytes"] / dom_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    roof["traffic"] = recorded_traffic(w.name, dom)
-    roof["kernel"] = dom
-    roof["stage"] = KERNEL_STAGE.get(dom)
-    roof["kernel_ms_timed"] = dom_ms
-    roof["algorithmic_per_launch"] = kw["flops"] if kw["bound"] == "mfma" else kw["bytes"]
+        step["mfma_frac"] = step_flops / step_sec / 1e12 / MFMA_BF16_PEAK_TFLOPS
+    return {
+        "value": queries / step_sec,
+        "ms_per_step": ms_per_step,
+        "stage_ms": stage_ms,
+        "kernel_us": [[n, round(u, 2)] for n, u in zip(names, kernel_us)],
+        "gpu_step_ms_all_stage_events": gpu_step_ms,
+        "stage_rates": stage_rates(w, work, stage_ms),
+        "step_roofline": step,
+        "roofline": roofline_entry(w, dom, dom_ms, lens, peaks),
+        "parity": parity,
+        **extras,
+    }
+
+
+def config_of(w: Workload, args, lens) -> dict:
+    return {"workload": w.name, "batch_override": args.batch > 0,
+            "summary_start_block": (w.seq_len - w.n_q) // w.block if lens is None else "each sequence's last block",
+            "seq_lens": None if lens is None else f"uniform in [{w.varlen_min}, {w.seq_len}], "
+                                                  f"mean {float(np.mean(lens)):.0f} (seeded)",
+            "batch": w.batch, "seq_len": w.seq_len, "n_q": w.n_q,
+            "d_index": w.d_index, "block": w.block, "top_m": w.top_m, "top_k": w.top_k,
+            "heads_q": w.n_heads_q, "heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
+            "n_landmarks": w.n_landmarks,
+            **({"group": w.group, "top_m2": w.top_m2} if w.group else {}),
+            **({"selection": "per query head from Q and landmarks of K"} if w.per_head else {}),
+            "parallelism": "single GPU"}
+
+
+def oracle_state(w: Workload, inp: dict):
+    """The oracle's summaries (and super-block summaries) of every sequence,
+    for the parity check of a configuration (single process)."""
+    from oracle import hisa_oracle as orc
+    if w.per_head:
+        return None
+    lens = inp.get("seq_lens")
+    S = [orc.block_summary(inp["kI"][b] if lens is None else inp["kI"][b, :int(lens[b])], w.block, inp.get("W"))
+         for b in range(w.batch)]
+    return S, ([orc.super_summary(x, w.group) for x in S] if w.group else None)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_64k", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-sample", type=int, default=1024, help="queries the CPU oracle is timed on")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="run the workload at this batch instead of its own (a batch study: the line then says "
+                         "batch_override; the workload's own batch is the measured configuration)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flat", action="store_true",
+                    help="skip timing the flat indexer (every causal token scored) on the same inputs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the headline workload (default: also the other SURVEY configurations, "
+                         "reported under 'configs')")
+    ap.add_argument("--no-peaks", action="store_true", help="skip measuring copy bandwidth and GEMM rate")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a kernel of known "
+                         "traffic, to scale hardware byte counters against)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(decode sequences and prefill queries would shard across GPUs with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    if args.batch > 0:
+        w = dataclasses.replace(w, batch=args.batch)
+    inp = datagen.make_inputs(w)
+    # the oracle is timed in forked worker processes: before the GPU is touched
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_sample)
+    ora = None if cpu is None else (cpu.pop("_S"), cpu.pop("_S2"))
+
+    import torch  # noqa: F401
+    hip = HipEvents()
+    peaks = None if args.no_peaks else measured_peaks(hip)
+    head = measure(w, inp, args, hip, peaks, ora, headline=True)
+    lens = inp.get("seq_lens")
+    del inp
+
+    configs = None
+    explicit = any(a == "--workload" or a.startswith("--workload=") for a in sys.argv[1:])
+    if not (args.no_configs or explicit or args.batch):
+        configs = {}
+        for name in CONFIG_WORKLOADS:
+            wc = WORKLOADS[name]
+            cinp = datagen.make_inputs(wc)
+            r = measure(wc, cinp, args, hip, peaks, oracle_state(wc, cinp), headline=False)
+            del cinp
+            configs[name] = {"value": r["value"], "unit": "queries/s", "ms_per_step": r["ms_per_step"],
+                             "stage_ms": r["stage_ms"], "kernel_us": r["kernel_us"],
+                             "stage_rates": r["stage_rates"], "step_roofline": r["step_roofline"],
+                             "roofline": r["roofline"], "parity": r["parity"],
+                             "config": config_of(wc, args, None)}
 
     res = {
         "metric": "queries/sec end-to-end (index+attn)",
-        "value": value,
+        "value": head["value"],
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -757,27 +954,11 @@ def main():
         "accumulate": "fp32",
         "data": ("synthetic (seeded; N(0,1) bf16 Q/K/V, one planted needle chunk per sequence and kv head)"
                  if w.per_head else "synthetic (seeded; integer-valued bf16 indexer vectors, N(0,1) bf16 Q/K/V)"),
-        "config": {"workload": w.name, "batch_override": args.batch > 0,
-                   "summary_start_block": start_block if lens is None else "each sequence's last block",
-                   "seq_lens": None if lens is None else f"uniform in [{w.varlen_min}, {w.seq_len}], "
-                                                         f"mean {float(np.mean(lens)):.0f} (seeded)",
-                   "batch": w.batch, "seq_len": w.seq_len, "n_q": w.n_q,
-                   "d_index": w.d_index, "block": w.block, "top_m": w.top_m, "top_k": w.top_k,
-                   "heads_q": w.n_heads_q, "heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
-                   "n_landmarks": w.n_landmarks,
-                   **({"group": w.group, "top_m2": w.top_m2} if w.group else {}),
-                   **({"selection": "per query head from Q and landmarks of K"} if w.per_head else {}),
-                   "parallelism": "single GPU"},
-        "stage_ms": stage_ms,
-        "kernel_us": [[n, round(u, 2)] for n, u in zip(names, kernel_us)],
-        "gpu_step_ms_all_stage_events": gpu_step_ms,
-        "stage_hbm_frac": {n: work[n]["bytes"] / (stage_ms[n] / 1000.0) / 1e9 / HBM_PEAK_GBS for n in STAGES},
-        "roofline": roof,
-        "indexer_vs_flat": flat,
-        **({"three_level_vs_two_level": two} if w.group else {}),
-        **({"per_head_vs_dense_attention": dense} if w.per_head else {}),
+        "config": config_of(w, args, lens),
+        **{k: v for k, v in head.items() if k not in ("value", "ms_per_step")},
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
-        "parity": parity,
+        "configs": configs,
     }
     print(json.dumps(res), flush=True)
 

@@ -347,7 +347,9 @@ def forward_query(seq: dict, b: int, i: int, t: int, block: int, m: int, k: int,
 
 
 def scored_items(t: int, block: int, m: int, k: int) -> int:
-    """How many summaries plus tokens the oracle scores for the query at t."""
+    """How many block summaries plus tokens the oracle ranks (scores and compares
+    in a top selection) for the query at t; forced blocks and the candidates
+    of a list that keeps all of them are not ranked."""
     c = t // block
     n_blocks = 0 if c + 1 <= m else c - 1
     cand = (t + 1) if c + 1 <= m else (m - 1) * block + (t - c * block + 1)

@@ -76,16 +76,3 @@ def check_list_invariants(gpu: dict, w, chunk: int = 256):
                 tb = tok[b, r][tv[b, r]] // B
                 pos = np.searchsorted(bl, tb)
                 assert np.all(pos < bl.size) and np.array_equal(bl[np.minimum(pos, bl.size - 1)], tb)
-
-
-def sample_queries(w, n_random: int = 24, seed: int = 0):
-    nq = w.n_q
-    picks = {0, nq - 1}
-    for v in (w.block - 1, w.block, w.top_m * w.block - 1, w.top_m * w.block, w.top_k - 1, w.top_k,
-              w.top_k + 1, (w.top_m + 1) * w.block):
-        i = v - (w.seq_len - nq)
-        if 0 <= i < nq:
-            picks.add(i)
-    rng = np.random.default_rng(seed)
-    picks.update(int(x) for x in rng.integers(0, nq, size=min(n_random, nq)))
-    return [(b, i) for b in range(w.batch) for i in sorted(picks)]

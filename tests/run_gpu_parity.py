@@ -17,11 +17,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(HERE))
 sys.path.insert(0, HERE)
 
-import torch  # noqa: E402
-
-torch.zeros(1, device="cuda")
-torch.cuda.synchronize()
-
 import importlib  # noqa: E402
 import glob  # noqa: E402
 
@@ -42,6 +37,7 @@ def cases():
         names, vals = marks[0].args[0], marks[0].args[1]
         names = [n.strip() for n in names.split(",")] if isinstance(names, str) else list(names)
         for v in vals:
+            v = getattr(v, "values", v)  # pytest.param(...) carries its values
             v = v if len(names) > 1 else (v,)
             kw = dict(zip(names, v))
             label = getattr(v[0], "name", None) or "-".join(str(x) for x in v)
@@ -51,9 +47,17 @@ def cases():
 
 
 def main(only):
-    for name, fn in cases():
-        if only and not any(o in name for o in only):
-            continue
+    selected = [(name, fn) for name, fn in cases() if not only or any(o in name for o in only)]
+    # the oracle's all-query results are computed in forked processes, which
+    # must happen before this process initialises the GPU
+    import oracle_cache
+    need = [w for w in oracle_cache.ALL_QUERY_WORKLOADS
+            if any(n.startswith("test_full_size_prefill_every_query") and w in n for n, _ in selected)]
+    oracle_cache.precompute(need)
+    import torch
+    torch.zeros(1, device="cuda")
+    torch.cuda.synchronize()
+    for name, fn in selected:
         print(f"RUN  {name}", flush=True)
         t = time.time()
         try:

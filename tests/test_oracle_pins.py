@@ -286,6 +286,53 @@ def test_work_count_bound():
             assert n <= -(-(t + 1) // B) + m * B
 
 
+def test_scored_items_counts_what_the_selects_rank(monkeypatch):
+    # scored_items is a closed form: check it against what select_blocks and
+    # select_tokens actually rank (the sizes they hand to top_by_score) on
+    # small random inputs, over every query position of several shapes, so an
+    # off-by-one block or token in the formula fails
+    sizes = []
+    real = orc.top_by_score
+
+    def counting(scores, ids, count):
+        sizes.append(len(scores))
+        return real(scores, ids, count)
+
+    monkeypatch.setattr(orc, "top_by_score", counting)
+    rng = np.random.default_rng(11)
+    for B, m, k, L in [(8, 2, 5, 100), (8, 3, 20, 150), (16, 4, 40, 300), (4, 6, 7, 97), (16, 5, 100, 333)]:
+        d = 4
+        kI = rng.integers(-2, 3, size=(L, d))
+        kb = bits_of_ints(kI)
+        S = orc.block_summary(kb, B)
+        for t in range(L):
+            qb = bits_of_ints(rng.integers(-2, 3, size=d))
+            sizes.clear()
+            blk = orc.select_blocks(qb, S, t, B, m)
+            orc.select_tokens(qb, kb, blk, t, B, k)
+            assert sum(sizes) == orc.scored_items(t, B, m, k), (B, m, k, t, sizes)
+
+
+def test_prefill_64k_work_totals():
+    # the algorithmic totals the roofline figures of the 64K prefill rest on
+    # (L = n_q = 65536, B = 128, m = 64, k = 2048): summed over every query
+    # from the oracle's own candidate enumeration and its scored_items
+    B, m, k, L = 128, 64, 2048, 65536
+    cand_total = kept_total = scored_total = 0
+    for t in range(L):
+        c = t // B
+        blk = np.arange(c + 1) if c + 1 <= m else np.concatenate([np.arange(m - 1), [c]])
+        n = orc.candidate_tokens(blk, t, B).size
+        cand_total += n
+        kept_total += min(n, k)
+        scored_total += orc.scored_items(t, B, m, k)
+    assert kept_total == 132_121_600           # kept (query, token) pairs
+    assert cand_total == 499_679_232           # candidate tokens (499.7 M)
+    # scored = causal blocks beyond the forced ones + candidates of the
+    # queries with more than k of them
+    assert scored_total == 16_429_056 + 497_581_056
+
+
 # ------------------------------------------------------------ attention ---
 
 
