@@ -630,6 +630,10 @@ def stage_rates(w: Workload, work: dict, stage_ms: dict) -> dict:
     return out
 
 
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=True) -> dict:
     """Time K steps of the workload's whole path (after W warmup steps) and
     the breakdowns around them; check the benchmarked configuration's
@@ -912,6 +916,7 @@ def main():
     w = WORKLOADS[args.workload]
     if args.batch > 0:
         w = dataclasses.replace(w, batch=args.batch)
+    progress(f"inputs of {w.name}")
     inp = datagen.make_inputs(w)
     # the oracle is timed in forked worker processes: before the GPU is touched
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_sample)
@@ -919,7 +924,9 @@ def main():
 
     import torch  # noqa: F401
     hip = HipEvents()
+    progress("measured peaks")
     peaks = None if args.no_peaks else measured_peaks(hip)
+    progress(f"measuring {w.name}")
     head = measure(w, inp, args, hip, peaks, ora, headline=True)
     lens = inp.get("seq_lens")
     del inp
@@ -930,7 +937,9 @@ def main():
         configs = {}
         for name in CONFIG_WORKLOADS:
             wc = WORKLOADS[name]
+            progress(f"inputs of {name}")
             cinp = datagen.make_inputs(wc)
+            progress(f"measuring {name}")
             r = measure(wc, cinp, args, hip, peaks, oracle_state(wc, cinp), headline=False)
             del cinp
             configs[name] = {"value": r["value"], "unit": "queries/s", "ms_per_step": r["ms_per_step"],

@@ -27,8 +27,14 @@ def pytest_collection_modifyitems(config, items):
         return
     names = sorted({m.args[0] for item in items for m in item.iter_markers("oracle_all")})
     if names:
+        import contextlib
+
         import oracle_cache
-        oracle_cache.precompute(names, log=lambda s: print(s, flush=True))
+        # progress lines reach the terminal even though output is captured
+        capman = config.pluginmanager.getplugin("capturemanager")
+        quiet = capman.global_and_fixture_disabled() if capman else contextlib.nullcontext()
+        with quiet:
+            oracle_cache.precompute(names, log=lambda s: print(s, flush=True))
     if any(item.get_closest_marker("gpu") for item in items):
         import torch
         if torch.cuda.is_available():

@@ -77,8 +77,13 @@ def precompute(names=ALL_QUERY_WORKLOADS, log=print) -> None:
         _state.update(w=w, inp=inp, S=S, res=res)
         step = 64
         chunks = [(i, min(nq, i + step)) for i in range(0, nq, step)]
+        n, last = 0, time.perf_counter()
         with mp.get_context("fork").Pool(workers(), initializer=_worker_init) as pool:
-            n = sum(pool.imap_unordered(_run_chunk, chunks))
+            for done in pool.imap_unordered(_run_chunk, chunks):
+                n += done
+                if time.perf_counter() - last > 20.0:  # progress for long runs
+                    last = time.perf_counter()
+                    log(f"[oracle_cache] {name}: {n} of {nq} queries")
         _state.clear()
         assert n == nq
         _done[name] = (w, inp, S, res)
