@@ -818,6 +818,9 @@ def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=Tr
         parity["pass"] = parity["pass"] and same
 
     extras = {}
+    if regime(w) == "prefill" and not (w.per_head or w.group or lens is not None):
+        extras["block_score_mfma"] = block_score_mfma(w, dev, out["S"], hip, args.steps, peaks,
+                                                      stage_ms["block_topm"])
     if headline:
         # the flat indexer takes one length for the batch
         if not (args.no_flat or lens is not None or w.group or w.per_head):
@@ -857,6 +860,48 @@ def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=Tr
         "parity": parity,
         **extras,
     }
+
+
+def block_score_mfma(w: Workload, dev: dict, S, hip, steps: int, peaks: dict | None, stage_ms: float) -> dict:
+    """The block-score contraction on its own: hsa_block_score_max runs the
+    MFMA tiling of step 2 with each query's maximum formed on chip (4 bytes
+    per query leave it), so its kernel time is the contraction's.  Measured
+    against the bf16 MFMA peak with the algorithmic causal flops (scored
+    blocks x landmark rows x 2 d_index)."""
+    import torch
+
+    from hierarchical_index_sparse_amd import _lib
+    shape = _lib.shape_of(w)
+    out = torch.empty((w.batch, w.n_q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, _lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_BLOCK_SCORE_MAX)),
+                     dtype=torch.uint8, device="cuda")
+    _lib.hsa_block_score_max(shape, dev["qI"], S, out, ws)
+    torch.cuda.synchronize()
+    n = max(5, min(steps, 20))
+    ev = [(hip.create(), hip.create()) for _ in range(n)]
+    names = None
+    for a, b in ev:
+        _lib.hsa_sparse_set_kernel_events([a], [b])
+        _lib.hsa_block_score_max(shape, dev["qI"], S, out, ws)
+        names = _lib.hsa_sparse_last_kernels()
+    torch.cuda.synchronize()
+    _lib.hsa_sparse_set_kernel_events(None, None)
+    us = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev])) * 1000.0
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    del out, ws
+    sb, _, _ = per_query_counts(w)
+    flops = 2.0 * w.d_index * w.n_landmarks * float(sb.sum()) * w.batch
+    tfs = flops / (us / 1e6) / 1e12
+    res = {"kernel": names[0], "kernel_us": us, "algorithmic_GFLOP": flops / 1e9, "achieved_TFLOPs": tfs,
+           "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tfs / MFMA_BF16_PEAK_TFLOPS,
+           "block_topm_stage_ms": stage_ms,
+           "note": "score-only build of the block-score MFMA tiling (per-query maximum on chip, 4 B per query "
+                   "written); the block_topm stage (scores written, then the exact top-m select) for comparison"}
+    if peaks:
+        res["frac_of_measured_gemm"] = tfs / peaks["bf16_gemm_TFLOPs"]
+    return res
 
 
 def config_of(w: Workload, args, lens) -> dict:
@@ -946,6 +991,7 @@ def main():
                              "stage_ms": r["stage_ms"], "kernel_us": r["kernel_us"],
                              "stage_rates": r["stage_rates"], "step_roofline": r["step_roofline"],
                              "roofline": r["roofline"], "parity": r["parity"],
+                             **({"block_score_mfma": r["block_score_mfma"]} if "block_score_mfma" in r else {}),
                              "config": config_of(wc, args, None)}
 
     res = {

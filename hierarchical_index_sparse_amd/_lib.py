@@ -24,6 +24,7 @@ HSA_SPARSE_OP_FORWARD = 4
 HSA_SPARSE_OP_FLAT_TOPK = 5
 HSA_SPARSE_OP_HEAD_TOPM = 6
 HSA_SPARSE_OP_FORWARD_HEADS = 7
+HSA_SPARSE_OP_BLOCK_SCORE_MAX = 8
 
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "HIP_ERROR"}
 
@@ -31,7 +32,7 @@ EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_
            "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
            "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_super_summary",
            "hsa_block_topm_3level", "hsa_forward_3level", "hsa_head_landmarks", "hsa_head_topm",
-           "hsa_forward_heads", "hsa_sparse_set_kernel_events", "hsa_sparse_last_kernels")
+           "hsa_forward_heads", "hsa_sparse_set_kernel_events", "hsa_sparse_last_kernels", "hsa_block_score_max")
 
 
 class HsaSparseShape(ctypes.Structure):
@@ -68,6 +69,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_sparse_last_error.restype = ctypes.c_char_p
     lib.hsa_block_summary.argtypes = [S, P, P, I32, P, P]
     lib.hsa_block_topm.argtypes = [S, P, P, P, P, SZ, P]
+    lib.hsa_block_score_max.argtypes = [S, P, P, P, P, SZ, P]
     lib.hsa_token_topk.argtypes = [S, P, P, P, P, P, SZ, P]
     lib.hsa_sparse_attn.argtypes = [S, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward.argtypes = [S, P, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -85,7 +87,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_sparse_last_kernels.argtypes = []
     lib.hsa_sparse_last_kernels.restype = ctypes.c_char_p
     for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
-                 "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step"):
+                 "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_block_score_max"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -204,6 +206,13 @@ def hsa_forward(shape, qI, kI, W, summary_start_block, S, Q, K, V, blk_out, tok_
                             _ptr(O, "O", _F32), _ptr(lse, "lse", _F32, True), ws.data_ptr(), nbytes,
                             _stream(stream))
     _check(st, "hsa_forward")
+
+
+def hsa_block_score_max(shape, qI, S, out, workspace=None, stream=None):
+    ws, nbytes = _workspace(shape, HSA_SPARSE_OP_BLOCK_SCORE_MAX, workspace, qI.device)
+    st = load().hsa_block_score_max(ctypes.byref(shape), _ptr(qI, "qI", _BF16), _ptr(S, "S", _BF16),
+                                    _ptr(out, "out", _F32), ws.data_ptr(), nbytes, _stream(stream))
+    _check(st, "hsa_block_score_max")
 
 
 def hsa_super_summary(shape, group, S, start_super, S2, stream=None):

@@ -147,6 +147,7 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
 
 bool empty(const hsa::Dims& d) { return d.b == 0 || d.nq == 0; }
 
+
 // Super-block level of the three-level selection.
 struct Level3 {
   int lgG, m2;
@@ -297,6 +298,8 @@ size_t hsa_sparse_workspace_size(const hsa_sparse_shape_t* shape, int op) {
       return check_shape(shape, d, kFlat) == HSA_SPARSE_OK ? hsa::flat_topk_ws_bytes(d) : 0;
     case HSA_SPARSE_OP_HEAD_TOPM:
       return check_shape(shape, d, kHeads | kHeadSel) == HSA_SPARSE_OK ? hsa::head_scores_ws_bytes(d) : 0;
+    case HSA_SPARSE_OP_BLOCK_SCORE_MAX:
+      return check_shape(shape, d, kSelect | kSummary) == HSA_SPARSE_OK ? hsa::block_score_max_ws_bytes(d) : 0;
     case HSA_SPARSE_OP_FORWARD_HEADS:
       return check_shape(shape, d, kHeads | kHeadSel | kAttn) == HSA_SPARSE_OK ? heads_layout(d).total : 0;
     default: return 0;
@@ -331,6 +334,22 @@ hsa_sparse_status_t hsa_block_topm(const hsa_sparse_shape_t* shape, const uint16
     return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "block_topm needs %zu workspace bytes", need);
   hipError_t e = hsa::launch_block_topm(d, qI, S, blk, workspace, stream);
   return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_block_topm");
+}
+
+hsa_sparse_status_t hsa_block_score_max(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* S,
+                                        float* out, void* workspace, size_t workspace_bytes,
+                                        hsa_sparse_stream_t stream) {
+  CallScope calls;
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSelect | kSummary);
+  if (st != HSA_SPARSE_OK) return st;
+  if (empty(d)) return HSA_SPARSE_OK;
+  if (!qI || !S || !out) return fail(HSA_SPARSE_INVALID_ARG, "qI, S or out is NULL");
+  const size_t need = hsa::block_score_max_ws_bytes(d);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "block_score_max needs %zu workspace bytes", need);
+  hipError_t e = hsa::launch_block_score_max(d, qI, S, out, workspace, stream);
+  return e == hipSuccess ? HSA_SPARSE_OK : hip_fail(e, "hsa_block_score_max");
 }
 
 hsa_sparse_status_t hsa_token_topk(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,

@@ -14,6 +14,8 @@
 // registers and reduces across the row's lanes with xor shuffles.
 // Kernel 2 (k_block_select): one workgroup per query runs the exact
 // register-resident select of select.hpp over those scores.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -168,6 +170,128 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
   }
 }
 
+// Score-only build of the MFMA block-score tiling (a measurement aid, the
+// contraction of k_block_scores_mfma without the selection): one workgroup
+// takes 64 consecutive queries, holds their indexer vectors as MFMA A
+// operands in registers, and walks its chunk of 128-row summary tiles (wave
+// w: rows 32w .. 32w+31 of each tile, the next tile's rows loaded while the
+// current one is multiplied).  Instead of writing every score it keeps,
+// per query, the maximum over the scored blocks 1 .. c-1 (all landmark
+// rows of a block count, so the landmark maximum is part of it), reduced
+// over lanes and waves on chip: one float per (query, chunk) leaves the
+// chip.  -inf marks a query with no scored block in the chunk.
+template <int DI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_block_scores_max(
+    const uint16_t* __restrict__ qI, const uint16_t* __restrict__ S, float* __restrict__ out, int L, int nq, int B,
+    int nb, int NL, int m, int qtiles_per_seq, int tiles_per_chunk, int nchunks) {
+  constexpr int KS = DI / 32;
+  __shared__ float red[4][64];
+  const int b = blockIdx.y / qtiles_per_seq;
+  const int i0 = (blockIdx.y % qtiles_per_seq) * 64;
+  const int chunk = blockIdx.x;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int jl = lane & 15, gq = lane >> 4;
+  const int nrows = nb * NL;
+  const int i_last = min(nq, i0 + 64) - 1;
+  const int c_last = query_pos(L, nq, i_last) / B;
+  // rows that any query of the tile scores: blocks 1 .. c_last - 1
+  const int tile_lo = chunk * tiles_per_chunk;
+  const int tile_hi = min((c_last * NL + 127) / 128, (chunk + 1) * tiles_per_chunk);  // exclusive
+
+  // per-lane limits: the lane's accumulator rows hold queries 16 mt + 4 gq + e
+  int row_hi[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + 16 * mt + 4 * gq + e;
+      const int c = i < nq ? query_pos(L, nq, i) / B : 0;
+      row_hi[mt][e] = c + 1 > m ? c * NL : 0;  // scored rows: NL <= row < c * NL
+    }
+  float mx[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mx[mt][e] = -INFINITY;
+
+  if (c_last + 1 > m && tile_lo < tile_hi) {
+    u32x4 a[4][KS];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int qa = min(i0 + 16 * mt + jl, nq - 1);
+      const uint16_t* qsrc = qI + ((size_t)b * nq + qa) * DI + 8 * gq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[mt][ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
+    }
+    const uint16_t* Sb = S + (size_t)b * nrows * DI + 8 * gq;
+    auto load_tile = [&](int tile, u32x4 (&bs)[2][KS]) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = min(tile * 128 + wave * 32 + 16 * nt + jl, nrows - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bs[nt][ks] = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + 32 * ks);
+      }
+    };
+    auto compute = [&](int tile, const u32x4 (&bs)[2][KS]) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = tile * 128 + wave * 32 + 16 * nt + jl;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][ks]),
+                                                          __builtin_bit_cast(bf16x8, bs[nt][ks]), acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (row >= NL && row < row_hi[mt][e]) mx[mt][e] = fmaxf(mx[mt][e], acc[e]);
+        }
+      }
+    };
+    // two row buffers in turn: the next tile's loads are always in flight
+    // (clamped to the last tile, so they are unconditional) while the
+    // current one is multiplied
+    u32x4 b0[2][KS], b1[2][KS];
+    load_tile(tile_lo, b0);
+    for (int tile = tile_lo; tile < tile_hi; tile += 2) {
+      load_tile(min(tile + 1, tile_hi - 1), b1);
+      compute(tile, b0);
+      if (tile + 1 >= tile_hi) break;
+      load_tile(min(tile + 2, tile_hi - 1), b0);
+      compute(tile + 1, b1);
+    }
+  }
+  // max over the 16 rows a lane group holds (lanes jl), then over the waves
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = group_max_f<16>(mx[mt][e]);
+      if (jl == 0) red[wave][16 * mt + 4 * gq + e] = v;
+    }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int i = i0 + threadIdx.x;
+    if (i < nq) {
+      const float v = fmaxf(fmaxf(red[0][threadIdx.x], red[1][threadIdx.x]),
+                            fmaxf(red[2][threadIdx.x], red[3][threadIdx.x]));
+      out[((size_t)b * nq + i) * nchunks + chunk] = v;
+    }
+  }
+}
+
+// The per-chunk maxima of k_block_scores_max reduced to one per query.
+__global__ __launch_bounds__(256) void k_block_max_reduce(const float* __restrict__ part, float* __restrict__ out,
+                                                          int nq_total, int nchunks) {
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  if (q >= nq_total) return;
+  float v = -INFINITY;
+  for (int c = 0; c < nchunks; ++c) v = fmaxf(v, part[(size_t)q * nchunks + c]);
+  out[q] = v;
+}
+
 template <int NW, int R>
 __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const float* __restrict__ scores,
                                                                           int32_t* __restrict__ blk, int L, int nq,
@@ -240,7 +364,7 @@ __global__ __launch_bounds__(NW == 1 ? 256 : NW * 64) void k_block_select(const 
 // newest blocks when the host folds that in (as for k_block_scores).
 constexpr int kFusedMaxBlocks = 2048;
 
-template <int DI, int R>
+template <int DI, int R, int NWS>
 __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __restrict__ qI,
                                                             const uint16_t* __restrict__ S, int32_t* __restrict__ blk,
                                                             int L, int nq, int B, int nb, int m, int nq_total,
@@ -250,8 +374,8 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
   constexpr int LPR = DI / 8;      // lanes per summary row
   constexpr int RPI = 1024 / LPR;  // rows per round of the workgroup
   constexpr int U = 8;             // rounds of loads in flight
-  __shared__ float sc[kFusedMaxBlocks];
-  __shared__ SelectSmem<16> sm;
+  __shared__ __attribute__((aligned(16))) float sc[kFusedMaxBlocks];
+  __shared__ SelectSmem<NWS> sm;
   __shared__ float red[1][1024 / LPR][DI];
   if ((int)blockIdx.x >= nq_total) {  // folded summary of a newest block (uniform)
     const int w = (int)blockIdx.x - nq_total;
@@ -313,13 +437,25 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
     }
   }
   __syncthreads();
+  // the select: 16 waves (R keys per thread) or one wave (R keys per lane,
+  // no workgroup barriers)
+  if (NWS == 1 && tid >= kWave) return;
   uint32_t key[R];
+  if constexpr (R >= 4) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int idx = tid * R + r;
-    key[r] = idx < n ? score_key(sc[idx]) : 0u;
+    for (int r = 0; r < R; r += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sc + tid * R + r);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[r + e] = tid * R + r + e < n ? score_key(v[e]) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = tid * R + r;
+      key[r] = idx < n ? score_key(sc[idx]) : 0u;
+    }
   }
-  select_top<16, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+  select_top<NWS, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = 1 + idx;
   });
 }
@@ -353,6 +489,43 @@ static hipError_t launch_select(int R, int nq_total, const float* scores, int32_
 }
 
 size_t block_topm_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq * s.nb * sizeof(float)); }
+
+// Chunks of 128-row summary tiles per query tile of k_block_scores_max: about
+// 1024 workgroups in all when there are few query tiles.
+static void score_max_plan(const Dims& s, int& tiles_per_chunk, int& nchunks) {
+  const int qtiles = std::max(1, s.b * ((s.nq + 63) / 64));
+  const int ntiles = std::max(1, (s.nb * s.nL + 127) / 128);
+  const int want = std::max(1, std::min(ntiles, (1024 + qtiles - 1) / qtiles));
+  tiles_per_chunk = (ntiles + want - 1) / want;
+  nchunks = (ntiles + tiles_per_chunk - 1) / tiles_per_chunk;
+}
+
+size_t block_score_max_ws_bytes(const Dims& s) {
+  int tpc, nchunks;
+  score_max_plan(s, tpc, nchunks);
+  return nchunks > 1 ? align_up((size_t)s.b * s.nq * nchunks * sizeof(float)) : 0;
+}
+
+hipError_t launch_block_score_max(const Dims& s, const uint16_t* qI, const uint16_t* S, float* out, void* ws,
+                                  hipStream_t st) {
+  const int nq_total = s.b * s.nq;
+  if (nq_total == 0) return hipSuccess;
+  int tpc, nchunks;
+  score_max_plan(s, tpc, nchunks);
+  const int qtiles = (s.nq + 63) / 64;
+  float* dst = nchunks > 1 ? static_cast<float*>(ws) : out;
+  const dim3 grid(nchunks, qtiles * s.b);
+  if (s.dI == 64)
+    HSA_LAUNCH((k_block_scores_max<64>), grid, dim3(256), 0, st, qI, S, dst, s.L, s.nq, s.B, s.nb, s.nL, s.m, qtiles,
+               tpc, nchunks);
+  else
+    HSA_LAUNCH((k_block_scores_max<128>), grid, dim3(256), 0, st, qI, S, dst, s.L, s.nq, s.B, s.nb, s.nL, s.m,
+               qtiles, tpc, nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nchunks == 1) return e;
+  HSA_LAUNCH(k_block_max_reduce, dim3((nq_total + 255) / 256), dim3(256), 0, st, dst, out, nq_total, nchunks);
+  return hipGetLastError();
+}
 
 static int pick_r(int n, int nw) {
   int r = 1;
@@ -400,12 +573,12 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
     const int start = fold ? fold->start_block : s.nb;
     const int ns = max(nsum, 1);
 #define HSA_FD(DI, RR)                                                                                             \
-  HSA_LAUNCH((k_block_topm_decode<DI, RR>), grid, dim3(1024), 0, st, qI, S, blk, s.L, s.nq, s.B, s.nb, s.m, \
+  HSA_LAUNCH((k_block_topm_decode<DI, RR, 1>), grid, dim3(1024), 0, st, qI, S, blk, s.L, s.nq, s.B, s.nb, s.m, \
                      nq_total, kI, S_out, start, ns, s.lens)
     if (s.dI == 64) {
-      if (n_max <= 1024) HSA_FD(64, 1); else HSA_FD(64, 2);
+      if (n_max <= 1024) HSA_FD(64, 16); else HSA_FD(64, 32);
     } else {
-      if (n_max <= 1024) HSA_FD(128, 1); else HSA_FD(128, 2);
+      if (n_max <= 1024) HSA_FD(128, 16); else HSA_FD(128, 32);
     }
 #undef HSA_FD
     return hipGetLastError();

@@ -58,6 +58,14 @@ bool block_topm_can_fold(const Dims& s, int start_block);
 hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* S, int32_t* blk,
                              void* ws, hipStream_t st, const SummaryFold* fold = nullptr);
 
+// step 2's block-score contraction without the selection (a measurement
+// aid): out[q] = the highest score over query q's scored blocks 1..c-1
+// (-inf when it scores none), in one MFMA launch that writes 4 bytes per
+// query (per summary-tile chunk when there are few queries, then reduced).
+size_t block_score_max_ws_bytes(const Dims& s);
+hipError_t launch_block_score_max(const Dims& s, const uint16_t* qI, const uint16_t* S, float* out, void* ws,
+                                  hipStream_t st);
+
 // step 2 through super-blocks of 2^lgG blocks: S2 summaries of the
 // super-blocks from start_super on, then level 1 (top-m2 super-blocks into
 // sup [b*nq, m2]) and level 2 (top-m blocks among theirs into blk)

@@ -88,7 +88,8 @@ enum {
   HSA_SPARSE_OP_FORWARD = 4,
   HSA_SPARSE_OP_FLAT_TOPK = 5,
   HSA_SPARSE_OP_HEAD_TOPM = 6,
-  HSA_SPARSE_OP_FORWARD_HEADS = 7
+  HSA_SPARSE_OP_FORWARD_HEADS = 7,
+  HSA_SPARSE_OP_BLOCK_SCORE_MAX = 8
 };
 
 /* Bytes of device workspace the operation `op` needs for `shape`
@@ -137,6 +138,25 @@ hsa_sparse_status_t hsa_block_topm(const hsa_sparse_shape_t* shape,
                                    int32_t* blk, void* workspace,
                                    size_t workspace_bytes,
                                    hsa_sparse_stream_t stream);
+
+/*
+ * The block-score contraction of step 2 without its selection, for
+ * measuring the contraction on its own (HISA page, complexity: the block
+ * scores are the L^2/B term of O(L^2/B + L*m*B)).
+ *   out  [batch, n_q] fp32: for the query at t with c = t / block and
+ *        c + 1 > top_m, max over blocks 1..c-1 of score_j (the best score
+ *        hsa_block_topm ranks); -inf when c + 1 <= top_m (nothing scored).
+ *   workspace  >= hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_BLOCK_SCORE_MAX).
+ * Scores run on the same bf16 MFMA tiling as hsa_block_topm's for many
+ * queries, but each query's maximum is formed on chip, so one float per
+ * query (per chunk of summary tiles, when there are few queries) is written.
+ * Errors: as for hsa_block_topm.
+ */
+hsa_sparse_status_t hsa_block_score_max(const hsa_sparse_shape_t* shape,
+                                        const uint16_t* qI, const uint16_t* S,
+                                        float* out, void* workspace,
+                                        size_t workspace_bytes,
+                                        hsa_sparse_stream_t stream);
 
 /*
  * Step 3, token scores and top-k inside the kept blocks (HISA page, step

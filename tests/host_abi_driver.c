@@ -99,6 +99,12 @@ static void stage_checks(void) {
 
   EXPECT(hsa_block_topm(&s, NULL, FAKE_U16, FAKE_I32, FAKE_WS, BIG_WS, NULL), HSA_SPARSE_INVALID_ARG);
   EXPECT(hsa_block_topm(&s, FAKE_U16, FAKE_U16, FAKE_I32, FAKE_WS, 0, NULL), HSA_SPARSE_WORKSPACE_TOO_SMALL);
+  EXPECT(hsa_block_score_max(&s, NULL, FAKE_U16, FAKE_F32, FAKE_WS, BIG_WS, NULL), HSA_SPARSE_INVALID_ARG);
+  {
+    hsa_sparse_shape_t c = s;  /* few queries, many summary tiles: per-chunk maxima in the workspace */
+    c.seq_len = 1 << 20; c.n_q = 64; c.block = 64;
+    EXPECT(hsa_block_score_max(&c, FAKE_U16, FAKE_U16, FAKE_F32, FAKE_WS, 0, NULL), HSA_SPARSE_WORKSPACE_TOO_SMALL);
+  }
   EXPECT(hsa_token_topk(&s, FAKE_U16, FAKE_U16, NULL, FAKE_I32, FAKE_WS, BIG_WS, NULL), HSA_SPARSE_INVALID_ARG);
   EXPECT(hsa_sparse_attn(&s, FAKE_U16, FAKE_U16, FAKE_U16, FAKE_I32, NULL, NULL, FAKE_WS, BIG_WS, NULL),
          HSA_SPARSE_INVALID_ARG);

@@ -121,3 +121,24 @@ def test_parity_check_flags_differences():
     assert not bench.parity_check(w, inp, S, None, bad, pairs)["index_sets_exact"]
     off = bench.parity_check(w, inp, S, None, dict(rows, O=rows["O"] + 3e-3), pairs)
     assert off["index_sets_exact"] and not off["pass"]
+
+
+def test_rooflines_are_fractions():
+    # no HBM fraction above 1 is printed: prefill stages (rows shared by many
+    # queries) report rates only, and the prefill attention and scorers are
+    # measured against the bf16 MFMA roof with the method's flops
+    w = WORKLOADS["prefill_64k"]
+    work = bench.algorithmic_work(w)
+    rates = bench.stage_rates(w, work, {"block_summary": 0.008, "block_topm": 0.12, "token_topk": 1.45,
+                                        "sparse_attn": 5.5})
+    for name, r in rates.items():
+        assert r["hbm_frac"] is None or r["hbm_frac"] <= 1.0, name
+        assert r.get("mfma_frac", 0.0) <= 1.0, name
+    assert rates["sparse_attn"]["hbm_frac"] is None
+    roof = bench.roofline_entry(w, "k_sparse_attn", 5.5, None, None)
+    assert roof["bound"] == "mfma" and 0 < roof["frac"] < 1
+    assert roof["achieved"] == pytest.approx(4.0 * 128 * 16 * 132_121_600 / 5.5e-3 / 1e12)
+    # decode streams its rows once: HBM roof
+    wd = WORKLOADS["decode_128k"]
+    assert bench.roofline_entry(wd, "k_sparse_attn", 0.0097, None, None)["bound"] == "hbm"
+    assert bench.kernel_work(w, "k_block_scores_max")["bytes"] == 4.0 * w.n_q
