@@ -170,42 +170,54 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
   }
 }
 
-// Score-only build of the MFMA block-score tiling (a measurement aid, the
-// contraction of k_block_scores_mfma without the selection): one workgroup
-// takes 64 consecutive queries, holds their indexer vectors as MFMA A
-// operands in registers, and walks its chunk of 128-row summary tiles (wave
-// w: rows 32w .. 32w+31 of each tile, the next tile's rows loaded while the
-// current one is multiplied).  Instead of writing every score it keeps,
-// per query, the maximum over the scored blocks 1 .. c-1 (all landmark
-// rows of a block count, so the landmark maximum is part of it), reduced
-// over lanes and waves on chip: one float per (query, chunk) leaves the
-// chip.  -inf marks a query with no scored block in the chunk.
+// Score-only build of the block-score contraction (a measurement aid: the
+// scores of k_block_scores_mfma without the selection), tiled for the
+// matrix cores.  One workgroup takes 256 consecutive queries (wave w holds
+// queries 64w .. 64w+63 as MFMA A operands in registers) and walks its
+// chunk of 128-row summary tiles; each tile is loaded once per workgroup
+// into LDS (padded rows, double-buffered: the next tile's rows are in
+// flight in registers while the current one is multiplied) and read by all
+// four waves as B operands, so every summary row fetched from L2 feeds 256
+// queries.  Instead of writing every score it keeps, per query, the maximum
+// over the scored blocks 1 .. c-1 (all landmark rows of a block count, so
+// the landmark maximum is part of it), reduced over lanes on chip: one
+// float per (query, chunk) leaves the chip.  -inf marks a query with no
+// scored block in the chunk.
+constexpr int kMaxQT = 256;   // queries per workgroup
+constexpr int kMaxRT = 128;   // summary rows per tile
+
 template <int DI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_block_scores_max(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ S, float* __restrict__ out, int L, int nq, int B,
     int nb, int NL, int m, int qtiles_per_seq, int tiles_per_chunk, int nchunks) {
   constexpr int KS = DI / 32;
-  __shared__ float red[4][64];
+  constexpr int LPR = DI / 8;              // 16-byte lanes per summary row
+  constexpr int RPP = 256 / LPR;           // rows per load pass of the workgroup
+  constexpr int NP = kMaxRT / RPP;         // load passes per tile
+  constexpr int PITCH = DI + 8;            // LDS row pitch (bf16): 16-byte reads conflict-free
+  __shared__ __attribute__((aligned(16))) uint16_t bt[2][kMaxRT * PITCH];
   const int b = blockIdx.y / qtiles_per_seq;
-  const int i0 = (blockIdx.y % qtiles_per_seq) * 64;
+  const int i0 = (blockIdx.y % qtiles_per_seq) * kMaxQT;
   const int chunk = blockIdx.x;
-  const int wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
   const int lane = lane_id();
   const int jl = lane & 15, gq = lane >> 4;
   const int nrows = nb * NL;
-  const int i_last = min(nq, i0 + 64) - 1;
+  const int i_last = min(nq, i0 + kMaxQT) - 1;
   const int c_last = query_pos(L, nq, i_last) / B;
-  // rows that any query of the tile scores: blocks 1 .. c_last - 1
+  // rows any query of the tile scores: blocks 1 .. c_last - 1
   const int tile_lo = chunk * tiles_per_chunk;
-  const int tile_hi = min((c_last * NL + 127) / 128, (chunk + 1) * tiles_per_chunk);  // exclusive
+  const int tile_hi = min((c_last * NL + kMaxRT - 1) / kMaxRT, (chunk + 1) * tiles_per_chunk);  // exclusive
 
-  // per-lane limits: the lane's accumulator rows hold queries 16 mt + 4 gq + e
+  // the lane's accumulator entries hold queries qw + 16 mt + 4 gq + e
+  const int qw = i0 + 64 * wave;
   int row_hi[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = i0 + 16 * mt + 4 * gq + e;
+      const int i = qw + 16 * mt + 4 * gq + e;
       const int c = i < nq ? query_pos(L, nq, i) / B : 0;
       row_hi[mt][e] = c + 1 > m ? c * NL : 0;  // scored rows: NL <= row < c * NL
     }
@@ -215,71 +227,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int e = 0; e < 4; ++e) mx[mt][e] = -INFINITY;
 
-  if (c_last + 1 > m && tile_lo < tile_hi) {
+  if (c_last + 1 > m && tile_lo < tile_hi) {  // uniform over the workgroup
     u32x4 a[4][KS];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int qa = min(i0 + 16 * mt + jl, nq - 1);
+      const int qa = min(qw + 16 * mt + jl, nq - 1);
       const uint16_t* qsrc = qI + ((size_t)b * nq + qa) * DI + 8 * gq;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) a[mt][ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
     }
-    const uint16_t* Sb = S + (size_t)b * nrows * DI + 8 * gq;
-    auto load_tile = [&](int tile, u32x4 (&bs)[2][KS]) {
+    const uint16_t* Sb = S + (size_t)b * nrows * DI;
+    const int lr = tid / LPR, lc = 8 * (tid % LPR);  // this thread's row in a pass, first column
+    u32x4 st[NP];
+    auto load_tile = [&](int tile) {  // global -> registers
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int row = min(tile * 128 + wave * 32 + 16 * nt + jl, nrows - 1);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bs[nt][ks] = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + 32 * ks);
+      for (int p = 0; p < NP; ++p) {
+        const int row = min(tile * kMaxRT + p * RPP + lr, nrows - 1);
+        st[p] = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + lc);
       }
     };
-    auto compute = [&](int tile, const u32x4 (&bs)[2][KS]) {
+    auto stage_tile = [&](int buf) {  // registers -> LDS
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int row = tile * 128 + wave * 32 + 16 * nt + jl;
+      for (int p = 0; p < NP; ++p)
+        *reinterpret_cast<u32x4*>(&bt[buf][(p * RPP + lr) * PITCH + lc]) = st[p];
+    };
+    load_tile(tile_lo);
+    stage_tile(0);
+    __syncthreads();
+    int buf = 0;
+    for (int tile = tile_lo; tile < tile_hi; ++tile) {
+      const bool more = tile + 1 < tile_hi;  // uniform
+      if (more) load_tile(tile + 1);
+      const uint16_t* bb = bt[buf];
+#pragma unroll 2
+      for (int nt = 0; nt < kMaxRT / 16; ++nt) {
+        const int row = tile * kMaxRT + 16 * nt + jl;
+        u32x4 bs[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          bs[ks] = *reinterpret_cast<const u32x4*>(bb + (16 * nt + jl) * PITCH + 8 * gq + 32 * ks);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][ks]),
-                                                          __builtin_bit_cast(bf16x8, bs[nt][ks]), acc, 0, 0, 0);
+                                                          __builtin_bit_cast(bf16x8, bs[ks]), acc, 0, 0, 0);
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (row >= NL && row < row_hi[mt][e]) mx[mt][e] = fmaxf(mx[mt][e], acc[e]);
         }
       }
-    };
-    // two row buffers in turn: the next tile's loads are always in flight
-    // (clamped to the last tile, so they are unconditional) while the
-    // current one is multiplied
-    u32x4 b0[2][KS], b1[2][KS];
-    load_tile(tile_lo, b0);
-    for (int tile = tile_lo; tile < tile_hi; tile += 2) {
-      load_tile(min(tile + 1, tile_hi - 1), b1);
-      compute(tile, b0);
-      if (tile + 1 >= tile_hi) break;
-      load_tile(min(tile + 2, tile_hi - 1), b0);
-      compute(tile + 1, b1);
+      if (more) {
+        stage_tile(buf ^ 1);  // the other buffer: last read two tiles ago, before the barrier below
+        __syncthreads();
+        buf ^= 1;
+      }
     }
   }
-  // max over the 16 rows a lane group holds (lanes jl), then over the waves
+  // max over the 16 rows (lanes jl) of each accumulator entry
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float v = group_max_f<16>(mx[mt][e]);
-      if (jl == 0) red[wave][16 * mt + 4 * gq + e] = v;
+      const int i = qw + 16 * mt + 4 * gq + e;
+      if (jl == 0 && i < nq) out[((size_t)b * nq + i) * nchunks + chunk] = v;
     }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int i = i0 + threadIdx.x;
-    if (i < nq) {
-      const float v = fmaxf(fmaxf(red[0][threadIdx.x], red[1][threadIdx.x]),
-                            fmaxf(red[2][threadIdx.x], red[3][threadIdx.x]));
-      out[((size_t)b * nq + i) * nchunks + chunk] = v;
-    }
-  }
 }
 
 // The per-chunk maxima of k_block_scores_max reduced to one per query.
@@ -490,11 +504,11 @@ static hipError_t launch_select(int R, int nq_total, const float* scores, int32_
 
 size_t block_topm_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq * s.nb * sizeof(float)); }
 
-// Chunks of 128-row summary tiles per query tile of k_block_scores_max: about
+// Chunks of 128-row summary tiles per 256-query tile of k_block_scores_max: about
 // 1024 workgroups in all when there are few query tiles.
 static void score_max_plan(const Dims& s, int& tiles_per_chunk, int& nchunks) {
-  const int qtiles = std::max(1, s.b * ((s.nq + 63) / 64));
-  const int ntiles = std::max(1, (s.nb * s.nL + 127) / 128);
+  const int qtiles = std::max(1, s.b * ((s.nq + kMaxQT - 1) / kMaxQT));
+  const int ntiles = std::max(1, (s.nb * s.nL + kMaxRT - 1) / kMaxRT);
   const int want = std::max(1, std::min(ntiles, (1024 + qtiles - 1) / qtiles));
   tiles_per_chunk = (ntiles + want - 1) / want;
   nchunks = (ntiles + tiles_per_chunk - 1) / tiles_per_chunk;
@@ -512,7 +526,7 @@ hipError_t launch_block_score_max(const Dims& s, const uint16_t* qI, const uint1
   if (nq_total == 0) return hipSuccess;
   int tpc, nchunks;
   score_max_plan(s, tpc, nchunks);
-  const int qtiles = (s.nq + 63) / 64;
+  const int qtiles = (s.nq + kMaxQT - 1) / kMaxQT;
   float* dst = nchunks > 1 ? static_cast<float*>(ws) : out;
   const dim3 grid(nchunks, qtiles * s.b);
   if (s.dI == 64)
