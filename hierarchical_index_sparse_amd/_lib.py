@@ -32,7 +32,11 @@ EXPORTS = ("hsa_sparse_workspace_size", "hsa_sparse_strerror", "hsa_sparse_last_
            "hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
            "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_super_summary",
            "hsa_block_topm_3level", "hsa_forward_3level", "hsa_head_landmarks", "hsa_head_topm",
-           "hsa_forward_heads", "hsa_sparse_set_kernel_events", "hsa_sparse_last_kernels", "hsa_block_score_max")
+           "hsa_forward_heads", "hsa_sparse_set_kernel_events", "hsa_sparse_last_kernels", "hsa_forward_noalloc",
+           "hsa_block_score_max")
+
+# bytes of the device array hsa_forward_noalloc uses as its scratch
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 class HsaSparseShape(ctypes.Structure):
@@ -73,6 +77,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_token_topk.argtypes = [S, P, P, P, P, P, SZ, P]
     lib.hsa_sparse_attn.argtypes = [S, P, P, P, P, P, P, P, SZ, P]
     lib.hsa_forward.argtypes = [S, P, P, P, I32, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.hsa_forward_noalloc.argtypes = [S, P, P, P, I32, P, P, P, P, P, P, P, P, P]
     lib.hsa_sparse_set_stage_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.hsa_flat_topk.argtypes = [S, P, P, P, P, SZ, P]
     lib.hsa_decode_step.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -87,7 +92,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.hsa_sparse_last_kernels.argtypes = []
     lib.hsa_sparse_last_kernels.restype = ctypes.c_char_p
     for name in ("hsa_block_summary", "hsa_block_topm", "hsa_token_topk", "hsa_sparse_attn", "hsa_forward",
-                 "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_block_score_max"):
+                 "hsa_sparse_set_stage_events", "hsa_flat_topk", "hsa_decode_step", "hsa_forward_noalloc",
+                 "hsa_block_score_max"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -213,6 +219,16 @@ def hsa_block_score_max(shape, qI, S, out, workspace=None, stream=None):
     st = load().hsa_block_score_max(ctypes.byref(shape), _ptr(qI, "qI", _BF16), _ptr(S, "S", _BF16),
                                     _ptr(out, "out", _F32), ws.data_ptr(), nbytes, _stream(stream))
     _check(st, "hsa_block_score_max")
+
+
+def hsa_forward_noalloc(shape, qI, kI, W, summary_start_block, S, Q, K, V, blk_out, tok_out, O, lse=None,
+                        stream=None):
+    st = load().hsa_forward_noalloc(ctypes.byref(shape), _ptr(qI, "qI", _BF16), _ptr(kI, "kI", _BF16),
+                                    _ptr(W, "W", _I8, True), int(summary_start_block), _ptr(S, "S", _BF16),
+                                    _ptr(Q, "Q", _BF16), _ptr(K, "K", _BF16), _ptr(V, "V", _BF16),
+                                    _ptr(blk_out, "blk_out", _I32, True), _ptr(tok_out, "tok_out", _I32, True),
+                                    _ptr(O, "O", _F32), _ptr(lse, "lse", _F32, True), _stream(stream))
+    _check(st, "hsa_forward_noalloc")
 
 
 def hsa_super_summary(shape, group, S, start_super, S2, stream=None):

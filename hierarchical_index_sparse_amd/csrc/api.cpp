@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "hsa_sparse.h"
@@ -147,6 +148,41 @@ hsa_sparse_status_t check_shape(const hsa_sparse_shape_t* s, hsa::Dims& d, unsig
 
 bool empty(const hsa::Dims& d) { return d.b == 0 || d.nq == 0; }
 
+// Scratch of hsa_forward_noalloc: a fixed-size device array in the code
+// object, so that call allocates nothing.  Every GPU the library runs on
+// holds its own copy until the process ends.  Its host-side name is not a
+// device address: host code uses only the per-device address that
+// hipGetSymbolAddress returns (kept in g_scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[HSA_SPARSE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // guarded by g_scratch_mu
+
+// The device address of `scratch` on the stream's device, looked up once
+// per device with that device current.
+hsa_sparse_status_t static_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HSA_SPARSE_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (back != hipSuccess) return hip_fail(back, "hipSetDevice");
+    if (!p) return fail(HSA_SPARSE_HIP_ERROR, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSA_SPARSE_OK;
+}
 
 // Super-block level of the three-level selection.
 struct Level3 {
@@ -474,6 +510,26 @@ hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape, const uint16_t*
   if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
   return forward_impl(d, "hsa_forward", qI, kI, landmark_W, summary_start_block, S, Q, K, V, blk_out, tok_out, O,
                       lse, workspace, workspace_bytes, stream);
+}
+
+hsa_sparse_status_t hsa_forward_noalloc(const hsa_sparse_shape_t* shape, const uint16_t* qI, const uint16_t* kI,
+                                        const int8_t* landmark_W, int32_t summary_start_block, uint16_t* S,
+                                        const uint16_t* Q, const uint16_t* K, const uint16_t* V, int32_t* blk_out,
+                                        int32_t* tok_out, float* O, float* lse, hsa_sparse_stream_t stream) {
+  hsa::Dims d;
+  hsa_sparse_status_t st = check_shape(shape, d, kSummary | kSelect | kAttn);
+  if (st != HSA_SPARSE_OK) return st;
+  if (summary_start_block < 0) return fail(HSA_SPARSE_INVALID_ARG, "summary_start_block < 0");
+  const size_t need = forward_layout(d).total;
+  if (need > (size_t)HSA_SPARSE_NOALLOC_SCRATCH_BYTES)
+    return fail(HSA_SPARSE_WORKSPACE_TOO_SMALL, "hsa_forward_noalloc: this shape needs %zu scratch bytes, "
+                "more than the %zu of the static scratch", need, (size_t)HSA_SPARSE_NOALLOC_SCRATCH_BYTES);
+  if (empty(d)) return HSA_SPARSE_OK;
+  void* ws = nullptr;
+  st = static_scratch(stream, &ws);
+  if (st != HSA_SPARSE_OK) return st;
+  return forward_impl(d, "hsa_forward_noalloc", qI, kI, landmark_W, summary_start_block, S, Q, K, V, blk_out,
+                      tok_out, O, lse, ws, (size_t)HSA_SPARSE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 hsa_sparse_status_t hsa_decode_step(const hsa_sparse_shape_t* shape, const int32_t* seq_lens, const uint16_t* qI,

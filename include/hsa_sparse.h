@@ -30,7 +30,9 @@
  *   - Calls are asynchronous on `stream` (NULL = the default stream) and
  *     never synchronise the host; results are valid once the stream has
  *     reached them.  The library allocates no device memory: scratch space
- *     is the caller's `workspace`, sized by hsa_sparse_workspace_size().
+ *     is the caller's `workspace`, sized by hsa_sparse_workspace_size()
+ *     (hsa_forward_noalloc uses a fixed device array of the library
+ *     instead).
  *   - Arguments are validated before anything is launched.  On an error
  *     nothing is written and nothing is enqueued.  hsa_sparse_last_error()
  *     returns a message for the calling thread's last failure.
@@ -215,6 +217,34 @@ hsa_sparse_status_t hsa_forward(const hsa_sparse_shape_t* shape,
                                 int32_t* tok_out, float* O, float* lse,
                                 void* workspace, size_t workspace_bytes,
                                 hsa_sparse_stream_t stream);
+
+/*
+ * hsa_forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Arguments, results and errors are those of
+ * hsa_forward.  Its scratch is a device array inside the library of
+ * HSA_SPARSE_NOALLOC_SCRATCH_BYTES bytes, of which every GPU the library
+ * runs on holds one copy until the process ends; its address on the
+ * stream's device is looked up on the first call there.  The call makes no
+ * allocation of its own.
+ *   - A shape whose hsa_sparse_workspace_size(shape, HSA_SPARSE_OP_FORWARD)
+ *     exceeds HSA_SPARSE_NOALLOC_SCRATCH_BYTES is rejected with
+ *     HSA_SPARSE_WORKSPACE_TOO_SMALL before anything is enqueued.
+ *   - Every call on one GPU shares that GPU's scratch: calls whose work
+ *     overlaps on the GPU (on different streams, or from several threads
+ *     without ordering) race and give wrong results.  Calls in one stream's
+ *     order are safe; the scratch keeps the last call's contents, and no
+ *     call relies on them.
+ */
+#define HSA_SPARSE_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+hsa_sparse_status_t hsa_forward_noalloc(const hsa_sparse_shape_t* shape,
+                                        const uint16_t* qI, const uint16_t* kI,
+                                        const int8_t* landmark_W,
+                                        int32_t summary_start_block, uint16_t* S,
+                                        const uint16_t* Q, const uint16_t* K,
+                                        const uint16_t* V, int32_t* blk_out,
+                                        int32_t* tok_out, float* O, float* lse,
+                                        hsa_sparse_stream_t stream);
 
 /*
  * One decode step over a batch of sequences of different lengths (HISA

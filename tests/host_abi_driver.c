@@ -63,6 +63,25 @@ static hsa_sparse_status_t forward(const hsa_sparse_shape_t* s, const uint16_t* 
                      NULL, FAKE_WS, ws, NULL);
 }
 
+/* hsa_forward_noalloc: shapes whose scratch exceeds the static array are
+   rejected before anything else happens (no HIP call) */
+static void noalloc_checks(void) {
+  hsa_sparse_shape_t s = base();
+  s.seq_len = 65536; s.n_q = 65536; s.block = 128; s.top_m = 64; s.top_k = 2048;
+  s.n_heads_q = 16; s.n_heads_kv = 1;
+  EXPECT(hsa_forward_noalloc(&s, FAKE_U16, FAKE_U16, NULL, 0, FAKE_OUT16, FAKE_U16, FAKE_U16, FAKE_U16, NULL, NULL,
+                             FAKE_F32, NULL, NULL), HSA_SPARSE_WORKSPACE_TOO_SMALL);
+  s = base(); s.top_m = 1;
+  EXPECT(hsa_forward_noalloc(&s, FAKE_U16, FAKE_U16, NULL, 0, FAKE_OUT16, FAKE_U16, FAKE_U16, FAKE_U16, NULL, NULL,
+                             FAKE_F32, NULL, NULL), HSA_SPARSE_INVALID_ARG);
+  s = base();
+  EXPECT(hsa_forward_noalloc(&s, FAKE_U16, FAKE_U16, NULL, -1, FAKE_OUT16, FAKE_U16, FAKE_U16, FAKE_U16, NULL, NULL,
+                             FAKE_F32, NULL, NULL), HSA_SPARSE_INVALID_ARG);
+  s = base(); s.batch = 0;
+  EXPECT(hsa_forward_noalloc(&s, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL),
+         HSA_SPARSE_OK);
+}
+
 static void shape_checks(void) {
   hsa_sparse_shape_t s;
   EXPECT(forward(NULL, FAKE_U16, BIG_WS), HSA_SPARSE_INVALID_ARG);
@@ -220,6 +239,7 @@ int main(void) {
   shape_checks();
   stage_checks();
   workspace_sizes();
+  noalloc_checks();
   misc();
   if (n_fail) {
     printf("%d of %d checks failed\n", n_fail, n_checks);
