@@ -143,13 +143,18 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
     u32x4 a[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
+    // both row tiles' accumulators advance together over ks (two
+    // independent MFMA chains in flight)
+    f32x4 accs[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        accs[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
+                                                           __builtin_bit_cast(bf16x8, bs[nt][ks]), accs[nt], 0, 0, 0);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
-                                                      __builtin_bit_cast(bf16x8, bs[nt][ks]), acc, 0, 0, 0);
+      f32x4 acc = accs[nt];
       // lane: queries 16mt + 4gq + e, summary row row0 + 16nt + jl
       if constexpr (NL > 1) {
 #pragma unroll
@@ -197,7 +202,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int PITCH = DI + 8;            // LDS row pitch (bf16): 16-byte reads conflict-free
   __shared__ __attribute__((aligned(16))) uint16_t bt[2][kMaxRT * PITCH];
   const int b = blockIdx.y / qtiles_per_seq;
-  const int i0 = (blockIdx.y % qtiles_per_seq) * kMaxQT;
+  // the latest query tiles (the most causal tiles) are dispatched first
+  const int i0 = (qtiles_per_seq - 1 - (int)(blockIdx.y % qtiles_per_seq)) * kMaxQT;
   const int chunk = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -266,17 +272,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
           bs[ks] = *reinterpret_cast<const u32x4*>(bb + (16 * nt + jl) * PITCH + 8 * gq + 32 * ks);
+        // the 4 query tiles' accumulators advance together over ks: four
+        // independent MFMA chains in flight instead of one at a time
+        f32x4 acc[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][ks]),
-                                                          __builtin_bit_cast(bf16x8, bs[ks]), acc, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][ks]),
+                                                              __builtin_bit_cast(bf16x8, bs[ks]), acc[mt], 0, 0, 0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (row >= NL && row < row_hi[mt][e]) mx[mt][e] = fmaxf(mx[mt][e], acc[e]);
-        }
+            if (row >= NL && row < row_hi[mt][e]) mx[mt][e] = fmaxf(mx[mt][e], acc[mt][e]);
       }
       if (more) {
         stage_tile(buf ^ 1);  // the other buffer: last read two tiles ago, before the barrier below
@@ -504,12 +515,15 @@ static hipError_t launch_select(int R, int nq_total, const float* scores, int32_
 
 size_t block_topm_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq * s.nb * sizeof(float)); }
 
-// Chunks of 128-row summary tiles per 256-query tile of k_block_scores_max: about
-// 1024 workgroups in all when there are few query tiles.
+// Chunks of 128-row summary tiles per 256-query tile of k_block_scores_max.
+// A workgroup loads its queries' indexer vectors (64 KB) once for all the
+// tiles of its chunk, so the tiles are split into chunks only as far as
+// needed to give about two workgroups per CU (512), the most the LDS holds,
+// so that causal tiles of very different lengths still spread over the chip.
 static void score_max_plan(const Dims& s, int& tiles_per_chunk, int& nchunks) {
   const int qtiles = std::max(1, s.b * ((s.nq + kMaxQT - 1) / kMaxQT));
   const int ntiles = std::max(1, (s.nb * s.nL + kMaxRT - 1) / kMaxRT);
-  const int want = std::max(1, std::min(ntiles, (1024 + qtiles - 1) / qtiles));
+  const int want = std::max(1, std::min(ntiles, (512 + qtiles - 1) / qtiles));
   tiles_per_chunk = (ntiles + want - 1) / want;
   nchunks = (ntiles + tiles_per_chunk - 1) / tiles_per_chunk;
 }

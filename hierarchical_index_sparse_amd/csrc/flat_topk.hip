@@ -15,7 +15,10 @@
 // 16-byte store.  Tiles after the tile's last query are skipped.  Bound by
 // the score writes (4 bytes per causal pair).
 //
-// Kernel 2 (k_flat_chunk_select): the t+1 candidates of a query are cut into
+// Kernel 2, contexts of at most 65536 tokens (k_flat_row_select): one
+// 16-wave workgroup per query selects from its whole score row held in
+// registers (up to 64 keys per thread), in one pass over the row.
+// Longer contexts (k_flat_chunk_select): the t+1 candidates of a query are cut into
 // chunks of kFlatChunk tokens (what one 4-wave select holds in registers);
 // each chunk keeps its own top-min(k, n) with the exact select of
 // select.hpp.  A query with a single chunk writes its list directly.
@@ -25,6 +28,8 @@
 // top-k under (score desc, index asc) is contained in the union of the
 // chunks' top-k under the same order, and every level keeps the lists in
 // ascending index order, so ties resolve exactly as in one select.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -73,21 +78,84 @@ __global__ __launch_bounds__(256) void k_flat_scores(const uint16_t* __restrict_
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
     }
+    // the 8 (query tile, key tile) accumulators advance together over ks:
+    // eight independent MFMA chains in flight
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc[mt][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          acc[mt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kt][ks]),
+                                                                __builtin_bit_cast(bf16x8, qb[mt][ks]), acc[mt][kt],
+                                                                0, 0, 0);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       float* dst = scores + ((size_t)b * nq + i0 + 16 * mt + jl) * Lp;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kt][ks]),
-                                                        __builtin_bit_cast(bf16x8, qb[mt][ks]), acc, 0, 0, 0);
         // lane: tokens s0 .. s0+3 of query i0 + 16mt + jl
         const int s0 = key0 + 16 * kt + 4 * gq;
-        if (s0 <= tq[mt]) *reinterpret_cast<f32x4*>(dst + s0) = acc;
+        if (s0 <= tq[mt]) *reinterpret_cast<f32x4*>(dst + s0) = acc[mt][kt];
       }
     }
+  }
+}
+
+// Rows of at most kFlatRowMax candidates (contexts up to 64K tokens): one
+// 16-wave workgroup per query holds the whole score row in registers
+// (R keys per thread) and runs the exact select of select.hpp once, with
+// the kept tokens staged in LDS and written in coalesced stores.  The row
+// is read from memory once and nothing is merged.  Queries are launched in
+// groups of similar row length (R = the smallest power of two with
+// 1024 R >= t + 1), so short rows do not pay for the longest.
+constexpr int kFlatRowMax = 16 * 64 * 64;
+
+template <int R>
+__global__ __launch_bounds__(1024) void k_flat_row_select(const float* __restrict__ scores, int32_t* __restrict__ tok,
+                                                          int L, int nq, int Lp, int k, int i_lo) {
+  constexpr int NT = 1024;
+  __shared__ SelectSmem<16> lds;
+  extern __shared__ int stage[];  // k + 64 ints
+  const int i = i_lo + (int)blockIdx.x;
+  const size_t q = (size_t)blockIdx.y * nq + i;
+  const int n = query_pos(L, nq, i) + 1;  // candidates: tokens 0 .. t
+  int32_t* out = tok + q * k;
+  if (n <= k) {  // every causal token is kept
+    for (int s = threadIdx.x; s < k; s += NT) out[s] = s < n ? s : -1;
+    return;
+  }
+  const float* sc = scores + q * Lp;
+  const int idx0 = threadIdx.x * R;
+  uint32_t key[R];
+  if constexpr (R >= 4) {
+#pragma unroll
+    for (int r = 0; r < R; r += 4) {
+      if (idx0 + r + 3 < n) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[r + e] = score_key(v[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[r + e] = idx0 + r + e < n ? score_key(sc[idx0 + r + e]) : 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) key[r] = idx0 + r < n ? score_key(sc[idx0 + r]) : 0u;
+  }
+  const int dummy = k + lane_id();
+  select_top<16, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) { stage[take ? pos : dummy] = idx; });
+  if ((k & 3) == 0) {
+    for (int p = threadIdx.x * 4; p < k; p += NT * 4)
+      *reinterpret_cast<i32x4*>(out + p) = *reinterpret_cast<const i32x4*>(stage + p);
+  } else {
+    for (int p = threadIdx.x; p < k; p += NT) out[p] = stage[p];
   }
 }
 
@@ -222,7 +290,8 @@ __global__ __launch_bounds__(NW * 64) void k_flat_merge(const uint2* __restrict_
 // seq_len <= 2^30 (checked by the caller), so both fit in an int
 static int flat_nchunk(const Dims& s) { return (int)(((long long)s.L + kFlatChunk - 1) / kFlatChunk); }
 static int flat_lp(const Dims& s) { return (int)(((long long)s.L + 3) & ~3ll); }
-static bool flat_needs_lists(const Dims& s) { return s.k < s.L && flat_nchunk(s) > 1; }
+static bool flat_row_select(const Dims& s) { return s.k < s.L && s.L <= kFlatRowMax; }
+static bool flat_needs_lists(const Dims& s) { return s.k < s.L && !flat_row_select(s) && flat_nchunk(s) > 1; }
 
 bool flat_topk_supported(const Dims& s) {
   if (s.k >= s.L) return true;  // everything is kept: no select
@@ -280,6 +349,27 @@ hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* k
   }
   // staged final lists: k + 64 ints (k <= kFlatStageMax when a select runs)
   const size_t dyn = s.k < s.L ? sizeof(int) * ((size_t)s.k + kWave) : 0;
+  if (flat_row_select(s)) {
+    // one launch per row-length group: queries i with 512 R < t + 1 <= 1024 R
+    const int base = s.L - s.nq;  // t = base + i
+    for (int R = 1; R <= 64; R <<= 1) {
+      const int i_lo = R == 1 ? 0 : std::max(0, 512 * R - base);
+      const int i_hi = std::min(s.nq, 1024 * R - base);
+      if (i_lo >= i_hi) continue;
+      const dim3 grid(i_hi - i_lo, s.b);
+#define HSA_FR(RR)                                                                                         \
+  case RR:                                                                                                 \
+    HSA_LAUNCH((k_flat_row_select<RR>), grid, dim3(1024), dyn, st, scores, tok, s.L, s.nq, Lp, s.k, i_lo); \
+    break;
+      switch (R) {
+        HSA_FR(1) HSA_FR(2) HSA_FR(4) HSA_FR(8) HSA_FR(16) HSA_FR(32) HSA_FR(64)
+      }
+#undef HSA_FR
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   HSA_LAUNCH((k_flat_chunk_select<4, 32>), dim3(nq_total, s.k < s.L ? nchunk : 1), dim3(256), dyn, st,
                      scores, lists[0], counts[0], tok, s.L, s.nq, Lp, s.k, nchunk);
   hipError_t e = hipGetLastError();

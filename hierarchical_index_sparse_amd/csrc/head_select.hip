@@ -158,13 +158,18 @@ __global__ __launch_bounds__(256) void k_head_scores_mfma(const uint16_t* __rest
     u32x4 a[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
+    // both row tiles' accumulators advance together over ks (two
+    // independent MFMA chains in flight)
+    f32x4 accs[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+        accs[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
+                                                           __builtin_bit_cast(bf16x8, bs[nt][ks]), accs[nt], 0, 0, 0);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
-                                                      __builtin_bit_cast(bf16x8, bs[nt][ks]), acc, 0, 0, 0);
+      f32x4 acc = accs[nt];
       if constexpr (NL > 1) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] = group_max_f<NL>(acc[e]);

@@ -512,17 +512,29 @@ __global__ __launch_bounds__(256) void k_bm_scores(const uint16_t* __restrict__ 
   }
   float* dst = scores + (size_t)ent.x * m * B + (size_t)ent.y * B + 4 * gq;
   const uint16_t* kb = kI + (size_t)b * L * DI;
-  for (int r0 = 0; r0 < B; r0 += 16) {
-    const int row = min(j * B + r0 + jl, L - 1);
-    u32x4 a[KS];
+  // two 16-row tiles at a time (B >= 16 here, a multiple of 16): their
+  // accumulators advance together over ks, two independent MFMA chains
+  for (int r0 = 0; r0 < B; r0 += 32) {
+    const bool two = r0 + 16 < B;  // uniform
+    u32x4 a[2][KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * DI + 8 * gq + 32 * ks);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+      const int row = min(j * B + r0 + 16 * h + jl, L - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        a[h][ks] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * DI + 8 * gq + 32 * ks);
+    }
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
-                                                    __builtin_bit_cast(bf16x8, qb[ks]), acc, 0, 0, 0);
-    if (live) *reinterpret_cast<f32x4*>(dst + r0) = acc;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[h][ks]),
+                                                         __builtin_bit_cast(bf16x8, qb[ks]), acc[h], 0, 0, 0);
+    if (live) {
+      *reinterpret_cast<f32x4*>(dst + r0) = acc[0];
+      if (two) *reinterpret_cast<f32x4*>(dst + r0 + 16) = acc[1];
+    }
   }
 }
 

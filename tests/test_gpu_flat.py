@@ -51,6 +51,10 @@ CASES = [
     ("three_levels_wide", 1, 5 * 32768 + 11, 2, 64, 8192, 2),  # 21 chunks, 16-wave merges of 4
     ("two_levels", 2, 70000, 3, 128, 2048, 1),                 # 9 chunks, 4-wave merges of 4
     ("wide_merge", 1, 70000, 2, 64, 4096, 2),                  # 9 chunks, 16-wave merges of 8
+    # contexts up to 65536: one whole-row select per query, launched in
+    # groups of row length (1024 R keys, R = 1 .. 64); heavy ties
+    ("row_select_every_group", 1, 65536, 65536, 64, 300, 1),
+    ("row_select_batch", 2, 9000, 4500, 128, 2048, 2),
 ]
 
 
@@ -61,7 +65,9 @@ def test_flat_topk_matches_oracle(name, batch, L, nq, dI, k, vr):
     qs = [(b, i) for b in range(batch) for i in range(nq)]
     if len(qs) > 120:  # every query near the keep-all edge and a spread of the rest
         rng = np.random.default_rng(5)
-        edge = [(b, i) for (b, i) in qs if abs((L - nq + i + 1) - k) <= 3]
+        # the keep-all edge and the row-length group edges (t + 1 = 512 R, 1024 R)
+        edges = {k} | {512 * r for r in (2, 4, 8, 16, 32, 64, 128)}
+        edge = [(b, i) for (b, i) in qs if min(abs((L - nq + i + 1) - e) for e in edges) <= 2]
         qs = sorted(set(edge + [qs[j] for j in rng.choice(len(qs), 100, replace=False)] + qs[-4:]))
     check(w, inp, tok, qs)
 
