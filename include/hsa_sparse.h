@@ -473,7 +473,7 @@ hsa_sparse_status_t hsa_sparse_set_stage_events(hsa_sparse_event_t const* events
  * hsa_sparse_last_kernels() then names the kernels of the thread's last
  * call, comma-separated, in launch order.  The events are the caller's
  * hipEvent_t handles and must stay valid while such calls are made.
- * n_events in [1, 32] with non-NULL arrays, or 0 with both NULL to stop.
+ * n_events in [1, 64] with non-NULL arrays, or 0 with both NULL to stop.
  */
 hsa_sparse_status_t hsa_sparse_set_kernel_events(hsa_sparse_event_t const* start,
                                                  hsa_sparse_event_t const* stop,

@@ -272,9 +272,9 @@ def test_per_head_validation(lib):
 
 
 def test_kernel_event_validation(lib):
-    Ev = ctypes.c_void_p * 40
+    Ev = ctypes.c_void_p * 80
     a, b = Ev(), Ev()
-    assert lib.hsa_sparse_set_kernel_events(a, b, 33) == 1      # at most 32 kernels
+    assert lib.hsa_sparse_set_kernel_events(a, b, 65) == 1      # at most 64 kernels
     assert lib.hsa_sparse_set_kernel_events(a, None, 4) == 1
     assert lib.hsa_sparse_set_kernel_events(None, None, 0) == 0  # off
     assert lib.hsa_sparse_last_kernels() == b""
