@@ -575,11 +575,13 @@ def measured_peaks(hip) -> dict:
     return out
 
 
-def roofline_entry(w: Workload, kernel: str, kernel_ms: float, lens, peaks: dict | None) -> dict:
+def roofline_entry(w: Workload, kernel: str, kernel_ms: float, n_launch: int, lens, peaks: dict | None) -> dict:
     """The roofline of one kernel: algorithmic work per launch over its
     average duration, against the roof its regime is bound by (bf16 MFMA
     for the contractions over shared, cache-resident operands; HBM for
-    kernels that stream their bytes once)."""
+    kernels that stream their bytes once).  kernel_ms is the kernel's time
+    in one step, summed over its n_launch launches (a long prefill runs the
+    attention once per query chunk); the rate is the same either way."""
     kw = kernel_work(w, kernel, lens)
     sec = kernel_ms / 1000.0
     if kw["bound"] == "mfma":
@@ -592,21 +594,24 @@ def roofline_entry(w: Workload, kernel: str, kernel_ms: float, lens, peaks: dict
             roof["gather_rate_GBs"] = kw["bytes"] / sec / 1e9
             roof["gather_note"] = ("algorithmic bytes gathered per second; rows shared by many queries are served "
                                    "from LDS, L2 and the MALL, so this is a rate, not a fraction of HBM")
-        roof["algorithmic_per_launch"] = kw["flops"]
+        roof["algorithmic_per_launch"] = kw["flops"] / n_launch
     else:
         achieved = kw["bytes"] / sec / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
         if peaks:
             roof["frac_of_measured_copy"] = achieved / peaks["copy_GBs"]
-        roof["algorithmic_per_launch"] = kw["bytes"]
+        roof["algorithmic_per_launch"] = kw["bytes"] / n_launch
     roof["traffic"] = recorded_traffic(w.name, kernel)
     roof["traffic_note"] = ("FETCH_SIZE and WRITE_SIZE per launch, scaled by a copy of known size: bytes between "
                             "L2 and the memory fabric, MALL hits included (an upper bound on DRAM bytes)")
     roof["kernel"] = kernel
     roof["stage"] = KERNEL_STAGE.get(kernel)
+    roof["launches_per_step"] = n_launch
+    roof["avg_launch_us"] = kernel_ms * 1000.0 / n_launch
     roof["kernel_ms_timed"] = kernel_ms
-    roof["kernel_ms_note"] = "the kernel's launches in one step, summed (a long prefill runs it once per query chunk)"
+    roof["kernel_ms_note"] = ("the kernel's launches in one step, summed (a long prefill runs it once per query chunk); "
+                              "algorithmic_per_launch is the step's work over its launches")
     return roof
 
 
@@ -864,7 +869,7 @@ def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=Tr
         "gpu_step_ms_all_stage_events": gpu_step_ms,
         "stage_rates": stage_rates(w, work, stage_ms),
         "step_roofline": step,
-        "roofline": roofline_entry(w, dom, dom_ms, lens, peaks),
+        "roofline": roofline_entry(w, dom, dom_ms, len(dom_idx), lens, peaks),
         "parity": parity,
         **extras,
     }

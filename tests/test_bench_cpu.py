@@ -135,10 +135,13 @@ def test_rooflines_are_fractions():
         assert r["hbm_frac"] is None or r["hbm_frac"] <= 1.0, name
         assert r.get("mfma_frac", 0.0) <= 1.0, name
     assert rates["sparse_attn"]["hbm_frac"] is None
-    roof = bench.roofline_entry(w, "k_sparse_attn", 5.5, None, None)
+    roof = bench.roofline_entry(w, "k_sparse_attn", 5.5, 32, None, None)
     assert roof["bound"] == "mfma" and 0 < roof["frac"] < 1
     assert roof["achieved"] == pytest.approx(4.0 * 128 * 16 * 132_121_600 / 5.5e-3 / 1e12)
+    # 32 launches of 2048 queries: the same rate, the work and time split over them
+    assert roof["algorithmic_per_launch"] == pytest.approx(4.0 * 128 * 16 * 132_121_600 / 32)
+    assert roof["avg_launch_us"] == pytest.approx(5500.0 / 32)
     # decode streams its rows once: HBM roof
     wd = WORKLOADS["decode_128k"]
-    assert bench.roofline_entry(wd, "k_sparse_attn", 0.0097, None, None)["bound"] == "hbm"
+    assert bench.roofline_entry(wd, "k_sparse_attn", 0.0097, 1, None, None)["bound"] == "hbm"
     assert bench.kernel_work(w, "k_block_scores_max")["bytes"] == 4.0 * w.n_q
