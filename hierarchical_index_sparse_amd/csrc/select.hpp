@@ -122,7 +122,8 @@ __device__ __forceinline__ uint32_t full_threshold(const uint32_t (&key)[R], int
 }
 
 // Exact search over the n compacted keys of the target bin (one wave).
-template <int R2>
+// FROM_SCORES: cand holds the fp32 scores' bits, turned into keys here.
+template <int R2, bool FROM_SCORES = false>
 __device__ __forceinline__ uint32_t bin_threshold(const uint32_t* cand, int n, int need) {
   const int lane = lane_id();
   uint32_t ck[R2];
@@ -130,7 +131,7 @@ __device__ __forceinline__ uint32_t bin_threshold(const uint32_t* cand, int n, i
 #pragma unroll
   for (int r = 0; r < R2; ++r) {
     const int idx = r * kWave + lane;
-    ck[r] = idx < n ? cand[idx] : 0u;
+    ck[r] = idx < n ? (FROM_SCORES ? score_key(__uint_as_float(cand[idx])) : cand[idx]) : 0u;
     if (idx < n) {
       all_and &= ck[r];
       all_or |= ck[r];
@@ -321,6 +322,187 @@ __device__ __forceinline__ void select_top(const uint32_t (&key)[R], int want, S
     pos += tk;
   }
   if constexpr (END_SYNC) sel_sync<NW>();  // LDS may be reused by the caller
+}
+
+
+// ---- the same select over fp32 scores held directly
+//
+// For callers that hold the scores: the order of score_key() on finite
+// scores is the order of the scores themselves (-0 and +0 equal), so the
+// scores are compared as floats and no key is formed per element.  Empty
+// slots hold a quiet NaN: fminf / fmaxf pass over it and every comparison
+// with it is false; it falls into histogram bin 0, whose count starts at
+// minus the number of empty slots.  Same result as select_top on the keys.
+
+// Bitwise search over all scores of the group (keys formed on the fly).
+template <int NW, int R>
+__device__ __forceinline__ uint32_t full_threshold_f(const float (&v)[R], int want, int* red) {
+  uint32_t T = 0;
+  int parity = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cnt += __popcll(ballot(v[r] == v[r] && score_key(v[r]) >= cand));
+    cnt = group_sum<NW>(cnt, red, parity);
+    parity ^= 1;
+    if (cnt >= want) T = cand;
+  }
+  return T;
+}
+
+// The want-th largest key over the group's scores (1 <= want <= number of
+// non-empty slots; n_empty = number of empty slots in the whole group).
+template <int NW, int R>
+__device__ __forceinline__ uint32_t find_threshold_f(const float (&v)[R], int want, int n_empty, SelectSmem<NW>& sm) {
+  const int wave = sel_wave<NW>();
+  const int lane = lane_id();
+  const int tid = wave * kWave + lane;
+  constexpr int NT = NW * kWave;
+
+  float flo = INFINITY, fhi = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    flo = fminf(flo, v[r]);
+    fhi = fmaxf(fhi, v[r]);
+  }
+  uint32_t lo = wave_min_u32(score_key(flo)), hi = wave_max_u32(score_key(fhi));
+  for (int b = tid; b < kBins; b += NT) sm.hist[b] = b == 0 ? -n_empty : 0;
+  if (lane == 0) {
+    sm.kmin[wave] = lo;
+    sm.kmax[wave] = hi;
+  }
+  if (tid == 0) sm.info[2] = 0;
+  sel_sync<NW>();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, sm.kmin[w]);
+    hi = max(hi, sm.kmax[w]);
+  }
+  if (lo == hi) return hi;  // every non-empty score is equal
+  const float smin = key_to_score(lo);
+  const float range = key_to_score(hi) - smin;
+  if (!(range < INFINITY)) {
+    sel_sync<NW>();
+    return full_threshold_f<NW, R>(v, want, sm.red);
+  }
+  const float scale = (float)(kBins - 1) / range;
+  constexpr int RP = (R + 3) / 4;
+  uint32_t binp[RP];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) binp[p] = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    // fmaxf sends an empty slot (NaN) to 0, i.e. to bin 0
+    const int bn = min((int)fmaxf((v[r] - smin) * scale, 0.f), kBins - 2);
+    binp[r / 4] |= (uint32_t)bn << (8 * (r % 4));
+    atomicAdd(&sm.hist[bn], 1);
+  }
+  auto bin_at = [&](int r) { return (int)((binp[r / 4] >> (8 * (r % 4))) & 0xFFu); };
+  sel_sync<NW>();
+  if (wave == 0) {
+    const int c0 = sm.hist[4 * lane], c1 = sm.hist[4 * lane + 1], c2 = sm.hist[4 * lane + 2],
+              c3 = lane == kWave - 1 ? 0 : sm.hist[4 * lane + 3];
+    const int mine = c0 + c1 + c2 + c3;
+    const int pre = wave_incl_scan(mine);
+    int above = __builtin_amdgcn_readlane(pre, kWave - 1) - pre;
+    const int cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      if (above < want && want <= above + cs[e]) {
+        sm.info[0] = 4 * lane + e;
+        sm.info[1] = above;
+      }
+      above += cs[e];
+    }
+  }
+  sel_sync<NW>();
+  const int tb = sm.info[0];
+  const int need = want - sm.info[1];
+  if (sm.hist[tb] > kBinCap) {
+    sel_sync<NW>();
+    return full_threshold_f<NW, R>(v, want, sm.red);
+  }
+  // compact the target bin's scores (any order); in bin 0 the empty slots
+  // are passed over
+  auto compact = [&](auto in_bin) {
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cnt += in_bin(r);
+    int wtot;
+    int pos = wave_excl_scan(cnt, wtot);
+    int base = 0;
+    if (lane == 0 && wtot) base = atomicAdd(&sm.info[2], wtot);
+    pos += __builtin_amdgcn_readlane(base, 0);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (in_bin(r)) sm.cand[pos++] = __float_as_uint(v[r]);
+  };
+  if (tb != 0) compact([&](int r) { return bin_at(r) == tb; });
+  else compact([&](int r) { return bin_at(r) == 0 && v[r] == v[r]; });
+  sel_sync<NW>();
+  if (wave == 0) {
+    const int n = sm.hist[tb];
+    uint32_t T;
+    if (n <= 64) T = bin_threshold<1, true>(sm.cand, n, need);
+    else if (n <= 256) T = bin_threshold<4, true>(sm.cand, n, need);
+    else T = bin_threshold<kBinCap / kWave, true>(sm.cand, n, need);
+    if (lane == 0) sm.info[3] = (int)T;
+  }
+  sel_sync<NW>();
+  return (uint32_t)sm.info[3];
+}
+
+// select_top over fp32 scores (empty slots: quiet NaN, n_empty of them in
+// the group).  emit(pos, idx, take) as in select_top.
+template <int NW, int R, bool END_SYNC = true, typename Emit>
+__device__ __forceinline__ void select_top_f(const float (&v)[R], int want, int n_empty, SelectSmem<NW>& sm,
+                                             Emit&& emit) {
+  const int wave = sel_wave<NW>();
+  const int lane = lane_id();
+  const float Tf = key_to_score(find_threshold_f<NW, R>(v, want, n_empty, sm));
+
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    gt += v[r] > Tf;
+    eq += v[r] == Tf;
+  }
+  int gt_w, eq_w;
+  (void)wave_excl_scan(gt, gt_w);
+  const int eq_ex = wave_excl_scan(eq, eq_w);
+  int gt_total = gt_w, eq_before = 0, sel_before = 0;
+  if constexpr (NW > 1) {
+    int* g = sm.red + 2 * NW;
+    int* e = sm.red + 3 * NW;
+    if (lane == 0) {
+      g[wave] = gt_w;
+      e[wave] = eq_w;
+    }
+    __syncthreads();
+    gt_total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) gt_total += g[w];
+    const int need_all = want - gt_total;
+    for (int w = 0; w < wave; ++w) {
+      sel_before += g[w] + min(max(need_all - eq_before, 0), e[w]);
+      eq_before += e[w];
+    }
+  }
+  const int need_eq = want - gt_total;
+  int ties = min(max(need_eq - (eq_before + eq_ex), 0), eq);
+  int sel_w;
+  int pos = sel_before + wave_excl_scan(gt + ties, sel_w);
+  const int idx0 = (wave * kWave + lane) * R;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int is_eq = v[r] == Tf;
+    const int tk = (int)(v[r] > Tf) | (is_eq & (int)(ties > 0));
+    ties -= is_eq & tk;
+    emit(pos, idx0 + r, tk != 0);
+    pos += tk;
+  }
+  if constexpr (END_SYNC) sel_sync<NW>();
 }
 
 }  // namespace hsa

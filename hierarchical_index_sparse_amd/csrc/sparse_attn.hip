@@ -9,18 +9,19 @@
 // v_mfma_f32_16x16x32_bf16 (zero-padded when G < 16), so every gathered K/V
 // row (256 bytes) is read once for all G heads.  Per tile of 32 list
 // entries:
-//   * S^T = K_tile Q^T (2 x 4 MFMAs): A = 16 gathered K rows (16-byte loads
-//     of 8 head dims each), B = the query heads, held in registers.  The
-//     accumulator layout gives each lane one head and 8 tokens, which is the
-//     A-operand layout P needs for P V, so no shuffle of P is required.
+//   * S^T = K_tile Q^T (2 x 4 MFMAs): A = 16 K rows (gathered with whole-row
+//     coalesced loads and staged in LDS), B = the query heads, held in
+//     registers.  The accumulator layout gives each lane one head and 8
+//     tokens, which is the A-operand layout P needs for P V, so no shuffle
+//     of P is required.
 //   * online softmax in the exp2 domain (running max and sum per head).
-//   * O += P V (8 output tiles of 16 dims): each lane gathers, for its 8
-//     tokens, 16 contiguous bytes (dims 8j .. 8j+7) of each V row; output
-//     tile c takes dims 8j + c, so its B operand is element c of those 8
-//     chunks (16-bit packing only; no LDS transpose, and V costs the same 8
-//     16-byte loads per tile as K).  P is split into bf16 hi + lo parts
-//     (two MFMAs), which keeps P's rounding error near 2^-17 instead of
-//     bf16's 2^-9.
+//   * O += P V (8 output tiles of 16 dims): each lane loads, for its 8
+//     tokens, 16 contiguous bytes (dims 8j .. 8j+7) of each V row straight
+//     from memory into registers (each load instruction still covers 4
+//     whole rows); output tile c takes dims 8j + c, so its B operand is
+//     element c of those 8 chunks (16-bit packing only; V needs no LDS).  P
+//     is split into bf16 hi + lo parts (two MFMAs), which keeps P's rounding
+//     error near 2^-17 instead of bf16's 2^-9.
 // Splits (decode) write unnormalised partial results with their running max
 // and sum; k_attn_merge combines them (log-sum-exp merge).  When the split
 // count is a multiple of 4, the 4 waves of a workgroup hold 4 consecutive
@@ -67,7 +68,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                                      float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
                                                      int chunk, int nsplit, float scale_log2, int n_items,
                                                      const int32_t* __restrict__ lens, bool premerge) {
-  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * 2 * kStageBytes];
+  // per wave: the staged K rows of one tile (V goes from memory straight
+  // into the P V operand registers)
+  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * kStageBytes];
   const int wave = threadIdx.x / kWave;
   const int item = blockIdx.x * 4 + wave;
   if (item >= n_items) return;
@@ -116,27 +119,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   };
   // Coalesced gather of one tile's 32 K rows and 32 V rows: instruction i
   // reads rows 4i .. 4i+3, 16 lanes (16 bytes each) per 256-byte row.
-  auto gload = [&](int my, u32x4 (&kr)[8], u32x4 (&vr)[8]) {
+  auto kload = [&](int my, u32x4 (&kr)[8]) {
     const int mine = max(my, 0);  // an invalid entry loads row 0 (masked later)
     const unsigned col = 16u * (unsigned)(lane & 15);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const unsigned off = (unsigned)__shfl(mine, 4 * i + (lane >> 4), kWave) + col;
       kr[i] = *reinterpret_cast<const u32x4*>(Kb + off);
-      vr[i] = *reinterpret_cast<const u32x4*>(Vb + off);
+    }
+  };
+  // One tile's V rows straight into the P V operand layout: w[e] holds dims
+  // 8 jl .. 8 jl + 7 of the lane's P token e (tokens 4 gq + e, then
+  // 16 + 4 gq + e - 4); instruction e still reads 4 whole rows.
+  auto vload = [&](int my, u32x4 (&w)[8]) {
+    const int mine = max(my, 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int tr = (e < 4) ? 4 * gq + e : 16 + 4 * gq + (e - 4);
+      const unsigned off = (unsigned)__shfl(mine, tr, kWave) + 16u * (unsigned)jl;
+      w[e] = *reinterpret_cast<const u32x4*>(Vb + off);
     }
   };
   // this wave's staging buffers: 32 rows of 272 bytes (256 + 16 pad, which
   // makes the 16-row MFMA operand reads bank-conflict free)
-  unsigned char* kst = stage_lds + (size_t)wave * 2 * kStageBytes;
-  unsigned char* vst = kst + kStageBytes;
-  auto stage = [&](const u32x4 (&kr)[8], const u32x4 (&vr)[8]) {
+  unsigned char* kst = stage_lds + (size_t)wave * kStageBytes;
+  auto stage = [&](const u32x4 (&kr)[8]) {
     const int off = (lane >> 4) * kRowBytes + 16 * (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(kst + off + 4 * i * kRowBytes) = kr[i];
-      *reinterpret_cast<u32x4*>(vst + off + 4 * i * kRowBytes) = vr[i];
-    }
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(kst + off + 4 * i * kRowBytes) = kr[i];
   };
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -146,12 +156,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 
   // pipeline: tile i in LDS, tile i+1 in flight to registers, list entries
   // of tile i+2 in flight
-  u32x4 kr[8], vr[8];
+  // (tile i's V in registers, loaded when tile i-1's P V is done)
+  u32x4 kr[8], w[8];
   int my = entry(start + (lane & 31));
   int my_next = entry(start + 32 + (lane & 31));
-  gload(my, kr, vr);
-  stage(kr, vr);
-  if (start + 32 < end) gload(my_next, kr, vr);
+  kload(my, kr);
+  stage(kr);
+  vload(my, w);
+  if (start + 32 < end) kload(my_next, kr);
   wave_sync();
   for (int p0 = start; p0 < end; p0 += 32) {
     const uint32_t vmask = (uint32_t)ballot(my >= 0);
@@ -167,14 +179,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), qf[ks], s1, 0, 0, 0);
       }
-      // V chunks (dims 8jl .. 8jl+7) of this lane's 8 P tokens
-      u32x4 w[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tr = (e < 4) ? 4 * gq + e : 16 + 4 * gq + (e - 4);
-        w[e] = *reinterpret_cast<const u32x4*>(vst + tr * kRowBytes + 16 * jl);
-      }
-
       // ---- online softmax (lane: head jl, tokens 4gq+e and 16+4gq+e)
       float sv[8];
 #pragma unroll
@@ -243,10 +247,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
       }
     }
+    if (p0 + 32 < end) vload(my_next, w);  // tile i's P V is done with w
     wave_sync();  // tile i's LDS reads are done
-    if (p0 + 32 < end) stage(kr, vr);
+    if (p0 + 32 < end) stage(kr);
     wave_sync();
-    if (p0 + 64 < end) gload(my_next2, kr, vr);
+    if (p0 + 64 < end) kload(my_next2, kr);
     my = my_next;
     my_next = my_next2;
   }
@@ -273,19 +278,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         const float* src[4];
         float mw[4], M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          src[w] = reinterpret_cast<const float*>(stage_lds + (size_t)w * 2 * kStageBytes) + h * kPartStride;
-          mw[w] = src[w][128];
-          M = fmaxf(M, mw[w]);
+        for (int wi = 0; wi < 4; ++wi) {
+          src[wi] = reinterpret_cast<const float*>(stage_lds + (size_t)wi * kStageBytes) + h * kPartStride;
+          mw[wi] = src[wi][128];
+          M = fmaxf(M, mw[wi]);
         }
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, Ls = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float a = __builtin_amdgcn_exp2f(mw[w] - M);  // 0 for a split without tokens
-            Ls += a * src[w][129];
+          for (int wi = 0; wi < 4; ++wi) {
+            const float a = __builtin_amdgcn_exp2f(mw[wi] - M);  // 0 for a split without tokens
+            Ls += a * src[wi][129];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += a * src[w][d0 + e];
+            for (int e = 0; e < 8; ++e) acc[e] += a * src[wi][d0 + e];
           }
         }
         float* dst = part + ((size_t)blockIdx.x * 16 + h) * kPartStride;

@@ -581,6 +581,7 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   // real length are read but masked below)
   const float* sc = scores + (size_t)q * m * B;  // 32-byte aligned: m * B is a multiple of 8
   const int idx0 = threadIdx.x * R;
+  const float empty = __uint_as_float(0x7FC00000u);  // quiet NaN: an empty slot of select_top_f
   float v[R];
   if constexpr (R >= 4) {
 #pragma unroll
@@ -593,7 +594,7 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int idx = idx0 + r + e;
-          v[r + e] = idx < n_valid ? sc[idx] : 0.f;
+          v[r + e] = idx < n_valid ? sc[idx] : empty;
         }
       }
     }
@@ -601,7 +602,7 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int idx = idx0 + r;
-      v[r] = sc[idx < n_valid ? idx : 0];
+      v[r] = idx < n_valid ? sc[idx] : empty;
     }
   }
   for (int p = threadIdx.x; p < n_sel; p += NT) bl[p] = blq[p];
@@ -616,6 +617,9 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
     }
     n_sel = lo + 1;
     n_valid = (n_sel - 1) * B + (t - c * B + 1);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (idx0 + r >= n_valid) v[r] = empty;
     if (n_valid <= k) {
       for (int slot = threadIdx.x; slot < k; slot += NT) {
         const int j = slot < n_valid ? bl[slot >> log2B] : -1;
@@ -624,13 +628,10 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
       return;
     }
   }
-  uint32_t key[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) key[r] = idx0 + r < n_valid ? score_key(v[r]) : 0u;
   const int bmask = B - 1;
   const int tbase = ONEBLK ? (bl[min(idx0 >> log2B, n_sel - 1)] << log2B) | (idx0 & bmask) : 0;
   const int dummy = k + lane_id();
-  select_top<NW, R, STAGED>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) {
+  select_top_f<NW, R, STAGED>(v, k, NT * R - n_valid, lds, [&](int pos, int idx, bool take) {
     const int v = ONEBLK ? tbase + (idx - idx0) : (bl[idx >> log2B] << log2B) | (idx & bmask);
     if constexpr (STAGED) stage[take ? pos : dummy] = v;
     else if (take) out[pos] = v;
