@@ -223,13 +223,28 @@ CSRC = os.path.join(ROOT, "hierarchical_index_sparse_amd", "csrc")
 
 
 def kernel_source_hash(kernel: str) -> str:
-    """sha256 of the .hip file that defines `kernel` and of every header."""
+    """sha256 of the .hip file that defines `kernel` and of the local headers
+    it includes (directly or through other headers), in a fixed order."""
     import glob
     import hashlib
-    h = hashlib.sha256()
+    import re
+    inc_dirs = [CSRC, os.path.join(os.path.dirname(CSRC), os.pardir, "include")]
     defining = [f for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")))
                 if f"void {kernel}(" in open(f).read()]
-    for f in defining + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))):
+    seen, todo = [], list(defining)
+    while todo:
+        f = todo.pop(0)
+        if f in seen:
+            continue
+        seen.append(f)
+        for name in re.findall(r'^#include "([^"]+)"', open(f).read(), flags=re.M):
+            for d in inc_dirs:
+                path = os.path.join(d, name)
+                if os.path.exists(path):
+                    todo.append(path)
+                    break
+    h = hashlib.sha256()
+    for f in defining + sorted(set(seen) - set(defining)):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

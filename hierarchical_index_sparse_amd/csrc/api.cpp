@@ -247,9 +247,11 @@ hsa::Dims chunk_dims(const hsa::Dims& d, int i0, int i1) {
 }
 
 // chunks per sequence (0: one launch for the whole batch).  The last chunk
-// of a sequence may be shorter (and then split if it has few rows).
+// of a sequence may be shorter (and then split if it has few rows).  Below
+// four chunks the extra launches cost more than they gain (4096-query
+// prefills measured the same or slower in 2048-query launches).
 int attn_chunks(const hsa::Dims& d) {
-  if (d.lens || d.nq < 2 * kAttnChunkQ) return 0;
+  if (d.lens || d.nq < 4 * kAttnChunkQ) return 0;
   return (d.nq + kAttnChunkQ - 1) / kAttnChunkQ;
 }
 

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void k_flat_scores(const uint16_t* __restrict_
 
 // Rows of at most kFlatRowMax candidates (contexts up to 64K tokens): one
 // 16-wave workgroup per query holds the whole score row in registers
-// (R keys per thread) and runs the exact select of select.hpp once, with
+// (R scores per thread) and runs the exact select of select.hpp once, with
 // the kept tokens staged in LDS and written in coalesced stores.  The row
 // is read from memory once and nothing is merged.  Queries are launched in
 // groups of similar row length (R = the smallest power of two with
@@ -132,25 +132,35 @@ __global__ __launch_bounds__(1024) void k_flat_row_select(const float* __restric
   }
   const float* sc = scores + q * Lp;
   const int idx0 = threadIdx.x * R;
-  uint32_t key[R];
+  const float empty = __uint_as_float(0x7FC00000u);  // quiet NaN: an empty slot of select_top_f
+  float v[R];
   if constexpr (R >= 4) {
 #pragma unroll
     for (int r = 0; r < R; r += 4) {
       if (idx0 + r + 3 < n) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[r + e] = score_key(v[e]);
+        for (int e = 0; e < 4; ++e) v[r + e] = x[e];
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[r + e] = idx0 + r + e < n ? score_key(sc[idx0 + r + e]) : 0u;
+        for (int e = 0; e < 4; ++e) v[r + e] = idx0 + r + e < n ? sc[idx0 + r + e] : empty;
       }
     }
   } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) key[r] = idx0 + r < n ? score_key(sc[idx0 + r]) : 0u;
+    for (int r = 0; r < R; ++r) v[r] = idx0 + r < n ? sc[idx0 + r] : empty;
   }
   const int dummy = k + lane_id();
-  select_top<16, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) { stage[take ? pos : dummy] = idx; });
+  if constexpr (R <= 32) {
+    select_top_f<16, R>(v, k, NT * R - n, lds, [&](int pos, int idx, bool take) { stage[take ? pos : dummy] = idx; });
+  } else {
+    // (64 per thread: the key form, which spills fewer of the 128 registers
+    // a 1024-thread workgroup allows)
+    uint32_t key[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) key[r] = v[r] == v[r] ? score_key(v[r]) : 0u;
+    select_top<16, R>(key, k, lds, [&](int pos, int idx, bool take, uint32_t) { stage[take ? pos : dummy] = idx; });
+  }
   if ((k & 3) == 0) {
     for (int p = threadIdx.x * 4; p < k; p += NT * 4)
       *reinterpret_cast<i32x4*>(out + p) = *reinterpret_cast<const i32x4*>(stage + p);

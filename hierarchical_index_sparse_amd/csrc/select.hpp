@@ -354,7 +354,8 @@ __device__ __forceinline__ uint32_t full_threshold_f(const float (&v)[R], int wa
 // The want-th largest key over the group's scores (1 <= want <= number of
 // non-empty slots; n_empty = number of empty slots in the whole group).
 template <int NW, int R>
-__device__ __forceinline__ uint32_t find_threshold_f(const float (&v)[R], int want, int n_empty, SelectSmem<NW>& sm) {
+__device__ __forceinline__ bool hist_threshold_f(const float (&v)[R], int want, int n_empty, SelectSmem<NW>& sm,
+                                                 uint32_t& T_out) {
   const int wave = sel_wave<NW>();
   const int lane = lane_id();
   const int tid = wave * kWave + lane;
@@ -379,13 +380,13 @@ __device__ __forceinline__ uint32_t find_threshold_f(const float (&v)[R], int wa
     lo = min(lo, sm.kmin[w]);
     hi = max(hi, sm.kmax[w]);
   }
-  if (lo == hi) return hi;  // every non-empty score is equal
+  if (lo == hi) {  // every non-empty score is equal
+    T_out = hi;
+    return true;
+  }
   const float smin = key_to_score(lo);
   const float range = key_to_score(hi) - smin;
-  if (!(range < INFINITY)) {
-    sel_sync<NW>();
-    return full_threshold_f<NW, R>(v, want, sm.red);
-  }
+  if (!(range < INFINITY)) return false;
   const float scale = (float)(kBins - 1) / range;
   constexpr int RP = (R + 3) / 4;
   uint32_t binp[RP];
@@ -419,27 +420,22 @@ __device__ __forceinline__ uint32_t find_threshold_f(const float (&v)[R], int wa
   sel_sync<NW>();
   const int tb = sm.info[0];
   const int need = want - sm.info[1];
-  if (sm.hist[tb] > kBinCap) {
-    sel_sync<NW>();
-    return full_threshold_f<NW, R>(v, want, sm.red);
-  }
+  if (sm.hist[tb] > kBinCap) return false;
   // compact the target bin's scores (any order); in bin 0 the empty slots
   // are passed over
-  auto compact = [&](auto in_bin) {
-    int cnt = 0;
+  const bool bin0 = tb == 0;
+  auto in_bin = [&](int r) { return bin_at(r) == tb && (!bin0 || v[r] == v[r]); };
+  int cnt = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) cnt += in_bin(r);
-    int wtot;
-    int pos = wave_excl_scan(cnt, wtot);
-    int base = 0;
-    if (lane == 0 && wtot) base = atomicAdd(&sm.info[2], wtot);
-    pos += __builtin_amdgcn_readlane(base, 0);
+  for (int r = 0; r < R; ++r) cnt += in_bin(r);
+  int wtot;
+  int pos = wave_excl_scan(cnt, wtot);
+  int base = 0;
+  if (lane == 0 && wtot) base = atomicAdd(&sm.info[2], wtot);
+  pos += __builtin_amdgcn_readlane(base, 0);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (in_bin(r)) sm.cand[pos++] = __float_as_uint(v[r]);
-  };
-  if (tb != 0) compact([&](int r) { return bin_at(r) == tb; });
-  else compact([&](int r) { return bin_at(r) == 0 && v[r] == v[r]; });
+  for (int r = 0; r < R; ++r)
+    if (in_bin(r)) sm.cand[pos++] = __float_as_uint(v[r]);
   sel_sync<NW>();
   if (wave == 0) {
     const int n = sm.hist[tb];
@@ -450,7 +446,16 @@ __device__ __forceinline__ uint32_t find_threshold_f(const float (&v)[R], int wa
     if (lane == 0) sm.info[3] = (int)T;
   }
   sel_sync<NW>();
-  return (uint32_t)sm.info[3];
+  T_out = (uint32_t)sm.info[3];
+  return true;
+}
+
+template <int NW, int R>
+__device__ __forceinline__ uint32_t find_threshold_f(const float (&v)[R], int want, int n_empty, SelectSmem<NW>& sm) {
+  uint32_t T;
+  if (hist_threshold_f<NW, R>(v, want, n_empty, sm, T)) return T;
+  sel_sync<NW>();  // (uniform) the histogram's LDS is read no more
+  return full_threshold_f<NW, R>(v, want, sm.red);
 }
 
 // select_top over fp32 scores (empty slots: quiet NaN, n_empty of them in
