@@ -228,7 +228,7 @@ def kernel_source_hash(kernel: str) -> str:
     import glob
     import hashlib
     import re
-    inc_dirs = [CSRC, os.path.join(os.path.dirname(CSRC), os.pardir, "include")]
+    inc_dirs = [CSRC, os.path.normpath(os.path.join(CSRC, os.pardir, os.pardir, "include"))]
     defining = [f for f in sorted(glob.glob(os.path.join(CSRC, "*.hip")))
                 if f"void {kernel}(" in open(f).read()]
     seen, todo = [], list(defining)
@@ -244,7 +244,7 @@ def kernel_source_hash(kernel: str) -> str:
                     todo.append(path)
                     break
     h = hashlib.sha256()
-    for f in defining + sorted(set(seen) - set(defining)):
+    for f in defining + sorted(set(seen) - set(defining), key=os.path.basename):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
