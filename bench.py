@@ -151,7 +151,7 @@ def algorithmic_work(w: Workload, lens=None) -> dict:
 KERNEL_STAGE = {
     "k_block_summary": "block_summary", "k_super_summary": "block_summary", "k_head_landmarks": "block_summary",
     "k_block_scores": "block_topm", "k_block_scores_mfma": "block_topm", "k_block_select": "block_topm",
-    "k_block_scores_max": "block_topm",
+    "k_block_scores_max": "block_topm", "k_block_topm_tile": "block_topm",
     "k_block_topm_decode": "block_topm", "k_block_topm_l2": "block_topm", "k_block_topm_3level_decode": "block_topm",
     "k_head_scores_mfma": "block_topm", "k_head_select": "block_topm",
     "k_token_scores": "token_topk", "k_token_scores_tiled": "token_topk", "k_bm_scores": "token_topk",

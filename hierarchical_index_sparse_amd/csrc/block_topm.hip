@@ -175,6 +175,110 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
   }
 }
 
+// Prefill block top-m in one launch (contexts of at most kTileMaxBlocks
+// blocks): one workgroup takes 16 consecutive queries of one sequence and
+// computes their block scores on the matrix cores straight into LDS (A =
+// the 16 queries' indexer vectors, held in registers; wave w takes summary
+// rows 32w .. 32w+31 of every 128-row tile up to the last query's causal
+// block, two MFMA chains at a time; the landmark maximum is an xor shuffle
+// across adjacent lanes).  Each wave then runs the one-wave select for 4 of
+// the queries on their LDS rows, so the scores never leave the chip.  Row
+// slot j of a query holds block j; only blocks 1 .. c-1 are candidates.
+constexpr int kTileMaxBlocks = 2048;
+constexpr int kTileQ = 16;
+
+template <int DI, int NL, int R>
+__global__ __launch_bounds__(256) void k_block_topm_tile(const uint16_t* __restrict__ qI,
+                                                         const uint16_t* __restrict__ S, int32_t* __restrict__ blk,
+                                                         int L, int nq, int B, int nb, int m, int qtiles_per_seq,
+                                                         int ldsw) {
+  constexpr int KS = DI / 32;
+  extern __shared__ __attribute__((aligned(16))) float sc[];  // [kTileQ][ldsw]
+  __shared__ SelectSmem<1> sms[4];
+  const int b = blockIdx.x / qtiles_per_seq;
+  const int i0 = (blockIdx.x % qtiles_per_seq) * kTileQ;
+  const int nqt = min(kTileQ, nq - i0);
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int jl = lane & 15, gq = lane >> 4;
+  const int c_last = query_pos(L, nq, i0 + nqt - 1) / B;
+  const int nrows = nb * NL;
+  if (c_last + 1 > m) {  // (uniform) some query of the tile scores blocks
+    u32x4 a[KS];
+    {
+      const uint16_t* qsrc = qI + ((size_t)b * nq + i0 + min(jl, nqt - 1)) * DI + 8 * gq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[ks] = *reinterpret_cast<const u32x4*>(qsrc + 32 * ks);
+    }
+    const int row_end = c_last * NL;  // rows of blocks 0 .. c_last - 1
+    for (int r0 = 32 * wave; r0 < row_end; r0 += 128) {
+      u32x4 bs[2][KS];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int row = min(r0 + 16 * nt + jl, nrows - 1);
+        const uint16_t* src = S + ((size_t)b * nrows + row) * DI + 8 * gq;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bs[nt][ks] = *reinterpret_cast<const u32x4*>(src + 32 * ks);
+      }
+      f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[ks]),
+                                                            __builtin_bit_cast(bf16x8, bs[nt][ks]), acc[nt], 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        // lane: queries 4gq + e, summary row r0 + 16nt + jl
+        if constexpr (NL > 1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[nt][e] = group_max_f<NL>(acc[nt][e]);
+        }
+        const int row = r0 + 16 * nt + jl;
+        if (row % NL == 0 && row < row_end) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[(4 * gq + e) * ldsw + row / NL] = acc[nt][e];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int qq = wave; qq < nqt; qq += 4) {
+    const int i = i0 + qq;
+    const int c = query_pos(L, nq, i) / B;
+    int32_t* out = blk + ((size_t)b * nq + i) * m;
+    if (c + 1 <= m) {
+      for (int j = lane; j < m; j += kWave) out[j] = j <= c ? j : -1;
+      continue;
+    }
+    const int want = m - 2;
+    const int n = c - 1;  // candidates: blocks 1 .. c-1, in slots 1 .. c-1
+    if (lane == 0) {
+      out[0] = 0;
+      out[m - 1] = c;
+    }
+    if (want == 0) continue;
+    const float empty = __uint_as_float(0x7FC00000u);
+    const float* row = sc + qq * ldsw;
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; r += (R >= 4 ? 4 : 1)) {
+      const int j0 = lane * R + r;
+      if constexpr (R >= 4) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (j0 < ldsw) x = *reinterpret_cast<const f32x4*>(row + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[r + e] = (j0 + e >= 1 && j0 + e <= n) ? x[e] : empty;
+      } else {
+        v[r] = (j0 >= 1 && j0 <= n) ? row[j0] : empty;
+      }
+    }
+    select_top_f<1, R, false>(v, want, kWave * R - n, sms[wave], [&](int pos, int idx, bool take) {
+      if (take) out[1 + pos] = idx;
+    });
+  }
+}
+
 // Score-only build of the block-score contraction (a measurement aid: the
 // scores of k_block_scores_mfma without the selection), tiled for the
 // matrix cores.  One workgroup takes 256 consecutive queries (wave w holds
@@ -579,6 +683,38 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
   // the last query has the most causal blocks
   const int c_max = (s.L - 1) / s.B;
   const int n_max = c_max - 1;
+  if (c_max + 1 > s.m && s.nq >= 64 && s.nb <= kTileMaxBlocks && !s.lens) {
+    // scores and select in one launch, the scores in LDS
+    const int qtiles = (s.nq + kTileQ - 1) / kTileQ;
+    const int ldsw = (s.nb + 3) & ~3;
+    const size_t lds = (size_t)kTileQ * ldsw * sizeof(float);
+    const int r = pick_r(n_max, 1);
+#define HSA_TT(DI, NL, RR)                                                                                     \
+  do {                                                                                                         \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_topm_tile<DI, NL, RR>),          \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                  \
+    if (e != hipSuccess) return e;                                                                             \
+    HSA_LAUNCH((k_block_topm_tile<DI, NL, RR>), dim3(qtiles * s.b), dim3(256), lds, st, qI, S, blk, s.L, s.nq, \
+               s.B, s.nb, s.m, qtiles, ldsw);                                                                  \
+  } while (0)
+#define HSA_TR(DI, NL)                                 \
+  switch (r) {                                         \
+    case 1: HSA_TT(DI, NL, 1); break;                  \
+    case 2: HSA_TT(DI, NL, 2); break;                  \
+    case 4: HSA_TT(DI, NL, 4); break;                  \
+    case 8: HSA_TT(DI, NL, 8); break;                  \
+    case 16: HSA_TT(DI, NL, 16); break;                \
+    default: HSA_TT(DI, NL, 32); break;                \
+  }
+    if (s.dI == 64) {
+      if (s.nL == 1) { HSA_TR(64, 1) } else if (s.nL == 2) { HSA_TR(64, 2) } else { HSA_TR(64, 4) }
+    } else {
+      if (s.nL == 1) { HSA_TR(128, 1) } else if (s.nL == 2) { HSA_TR(128, 2) } else { HSA_TR(128, 4) }
+    }
+#undef HSA_TR
+#undef HSA_TT
+    return hipGetLastError();
+  }
   if (c_max + 1 > s.m && s.nq >= 64) {
     const int qtiles = (s.nq + 63) / 64;
     dim3 grid((s.nb * s.nL + 127) / 128, qtiles * s.b);
