@@ -225,17 +225,23 @@ ForwardLayout heads_layout(const hsa::Dims& d) {
 }
 
 // ---- prefill attention in query chunks
-// Long prefills run the attention on chunks of kAttnChunkQ consecutive
-// queries, one launch each, in order on the caller's stream: a chunk of
-// queries [i0, i1) of a sequence is itself a prefill call (n_q = i1 - i0
-// over the context's first L - (n_q - i1) tokens).  Each query's attention
-// is independent, and a chunk of at least 2048 (query, kv head) rows is
-// never split, so the outputs are the bits of one launch.  Measured on the
-// 64K prefill (attention of all 65536 queries): one launch 5.50 ms, chunks
-// of 32768 queries 4.94, 16384 4.64, 8192 4.54, 4096 4.42, 2048 4.35 ms;
-// 1024-query chunks are split (fewer than 2048 rows) and take 6.29 ms.  The
-// 512K chunked prefill (all queries at the end of the context) is unchanged.
-constexpr int kAttnChunkQ = 2048;
+// Long prefills run the attention on chunks of consecutive queries holding
+// at least kAttnChunkRows (query, kv head) rows, one launch each, in order
+// on the caller's stream: a chunk of queries [i0, i1) of a sequence is
+// itself a prefill call (n_q = i1 - i0 over the context's first
+// L - (n_q - i1) tokens).  Each query's attention is independent, and a
+// chunk of at least 2048 rows is never split, so the outputs are the bits
+// of one launch.  2048 rows are 512 workgroups, one round of the chip at two
+// per CU: every wave of a launch starts together and walks its ascending
+// list at about the same pace as the others, so the rows they gather at
+// any moment are close together and stay in the L2s and the MALL.
+// Measured on the 64K prefill (attention of all 65536 queries, one kv
+// head): one launch 5.50 ms, chunks of 32768 queries 4.94, 16384 4.64, 8192
+// 4.54, 4096 4.42, 2048 4.35 ms; 1024-query chunks are split (fewer than
+// 2048 rows) and take 6.29 ms.
+constexpr int kAttnChunkRows = 2048;
+
+int attn_chunk_q(const hsa::Dims& d) { return (kAttnChunkRows + d.Hkv - 1) / d.Hkv; }
 
 hsa::Dims chunk_dims(const hsa::Dims& d, int i0, int i1) {
   hsa::Dims c = d;
@@ -248,18 +254,20 @@ hsa::Dims chunk_dims(const hsa::Dims& d, int i0, int i1) {
 
 // chunks per sequence (0: one launch for the whole batch).  The last chunk
 // of a sequence may be shorter (and then split if it has few rows).  Below
-// four chunks the extra launches cost more than they gain (4096-query
-// prefills measured the same or slower in 2048-query launches).
+// four chunks the extra launches cost more than they gain (4096-row
+// prefills measured the same or slower in 2048-row launches).
 int attn_chunks(const hsa::Dims& d) {
-  if (d.lens || d.nq < 4 * kAttnChunkQ) return 0;
-  return (d.nq + kAttnChunkQ - 1) / kAttnChunkQ;
+  const int cq = attn_chunk_q(d);
+  if (d.lens || d.nq < 4 * cq) return 0;
+  return (d.nq + cq - 1) / cq;
 }
 
 size_t chunked_attn_ws_bytes(const hsa::Dims& d) {
   size_t ws = 0;
   const int n = attn_chunks(d);
   for (int c = 0; c < n; ++c)  // every sequence has the same chunk shapes
-    ws = std::max(ws, hsa::sparse_attn_ws_bytes(chunk_dims(d, c * kAttnChunkQ, std::min(d.nq, (c + 1) * kAttnChunkQ))));
+    ws = std::max(ws, hsa::sparse_attn_ws_bytes(
+                          chunk_dims(d, c * attn_chunk_q(d), std::min(d.nq, (c + 1) * attn_chunk_q(d)))));
   return ws;
 }
 
@@ -535,7 +543,7 @@ static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, con
   if (const int nc = attn_chunks(d)) {
     for (int b = 0; b < d.b; ++b)
       for (int c = 0; c < nc; ++c) {
-        const int i0 = c * kAttnChunkQ, i1 = std::min(d.nq, (c + 1) * kAttnChunkQ);
+        const int i0 = c * attn_chunk_q(d), i1 = std::min(d.nq, (c + 1) * attn_chunk_q(d));
         const size_t q0 = (size_t)b * d.nq + i0;
         const size_t kv0 = (size_t)b * d.L * d.Hkv * d.d;
         e = hsa::launch_sparse_attn(chunk_dims(d, i0, i1), Q + q0 * d.Hq * d.d, K + kv0, V + kv0, tok + q0 * d.k,

@@ -307,31 +307,34 @@ def test_one_query_with_a_long_list(name, L, m, k):
 
 
 @pytest.mark.parametrize("name,batch,L,nq,dI,B,m,k,Hq,Hkv", [
-    # attention chunks of 2048 queries, the last of 1232 (2464 rows with 2
-    # kv heads: not split)
-    ("chunked_attention_two_seqs", 2, 12000, 9424, 64, 64, 16, 256, 4, 2),
-    # a last chunk of one query: its attention runs split and merged
+    # 2 kv heads: chunks of 1024 queries (2048 rows), 9 of them, none split
+    ("chunked_attention_two_seqs", 2, 12000, 9216, 64, 64, 16, 256, 4, 2),
+    # the same with a last chunk of 208 queries (416 rows: split and merged)
+    ("chunked_attention_ragged_tail", 1, 12000, 9424, 64, 64, 16, 256, 4, 2),
+    # one kv head: chunks of 2048 queries, the last of one query
     ("chunked_attention_one_query_tail", 1, 9000, 8193, 128, 32, 12, 300, 16, 1),
 ])
 def test_prefill_chunked_attention(name, batch, L, nq, dI, B, m, k, Hq, Hkv):
-    # long prefills run the attention in launches of 2048 queries: the
-    # outputs are the unchunked entry points' (bit for bit where no chunk is
-    # split), and every query at a chunk edge (plus a sample) matches the
-    # oracle
+    # long prefills run the attention in launches of ceil(2048 / Hkv)
+    # queries: the outputs are the unchunked entry points' (bit for bit
+    # where no chunk is split), and every query at a chunk edge (plus a
+    # sample) matches the oracle
     w = small(name, batch=batch, seq_len=L, n_q=nq, d_index=dI, block=B, top_m=m, top_k=k, n_heads_q=Hq,
               n_heads_kv=Hkv)
     inp = make_small(w, 4)
     dev = pipeline.to_device(inp)
     ref = pipeline.to_host(pipeline.run_stages(w, dev))
     got = pipeline.to_host(pipeline.run_forward(w, dev))
-    split_tail = nq % 2048 != 0 and (nq % 2048) * Hkv < 2048
+    cq = -(-2048 // Hkv)  # queries per chunk
+    split_tail = nq % cq != 0 and (nq % cq) * Hkv < 2048
     for key in ("S", "blk", "tok") + (() if split_tail else ("O", "lse")):
         assert np.array_equal(got[key], ref[key]), key
     assert np.abs(got["O"] - ref["O"]).max() <= ATOL and np.abs(got["lse"] - ref["lse"]).max() <= ATOL
     del dev
     torch.cuda.empty_cache()
     S = oracle_summaries(inp, w)
-    edges = {0, 2047, 2048, 4095, 4096, 8191, 8192, nq - 1} & set(range(nq))
+    edges = {e for c in range(1, nq // cq + 1) for e in (c * cq - 1, c * cq)} | {0, nq - 1}
+    edges &= set(range(nq))
     rng = np.random.default_rng(2)
     qs = sorted(edges | set(int(x) for x in rng.integers(0, nq, 10)))
     check_queries(got, inp, w, S, [(b, i) for b in range(batch) for i in qs])
