@@ -169,6 +169,292 @@ __global__ __launch_bounds__(1024) void k_flat_row_select(const float* __restric
   }
 }
 
+// Rows of more than kFlatStreamMin candidates: one 4-wave workgroup per
+// query selects straight from the score row in memory, in passes (after the
+// first, the row, at most 256 KB, comes from L2).  Wave w owns a contiguous
+// segment of the row and reads it with coalesced 16-byte loads, so index
+// order is segment, then load, then lane, then element.
+//   1. the row's minimum and maximum;
+//   2. a 255-bin linear histogram between them and a suffix scan for the bin
+//      that holds the want-th largest score; a bin of more than kBinCap
+//      scores is narrowed to its own minimum and maximum and histogrammed
+//      again (a few levels at most; a bitwise search over all keys if that
+//      does not end it);
+//   3. the bin's scores compacted into LDS and the threshold found exactly
+//      among them (bitwise search over their keys, one wave);
+//   4. counts of scores above and equal to the threshold per wave: the
+//      ties kept are the first ones in index order;
+//   5. the kept indices written in ascending order, each at the slot wave
+//      scans give it.
+// Few registers and 5 KB of LDS per workgroup: many workgroups share a CU,
+// where the register-resident select of one 1024-thread workgroup per
+// query left each CU one select at a time.
+constexpr int kFlatStreamMin = 16384;
+
+__global__ __launch_bounds__(256) void k_flat_stream_select(const float* __restrict__ scores,
+                                                            int32_t* __restrict__ tok, int L, int nq, int Lp, int k,
+                                                            int i_lo) {
+  constexpr int NW = 4;
+  constexpr int NT = NW * kWave;
+  __shared__ int hist[kBins];
+  __shared__ uint32_t cand[kBinCap];
+  __shared__ uint32_t wlo[NW], whi[NW];
+  __shared__ int wcnt[2][NW];
+  __shared__ int info[4];  // target bin, count above it, compaction slot, threshold key
+  const int i = i_lo + (int)blockIdx.x;
+  const size_t q = (size_t)blockIdx.y * nq + i;
+  const int n = query_pos(L, nq, i) + 1;  // candidates: tokens 0 .. t
+  int32_t* out = tok + q * k;
+  const int tid = threadIdx.x;
+  if (n <= k) {  // every causal token is kept
+    for (int x = tid; x < k; x += NT) out[x] = x < n ? x : -1;
+    return;
+  }
+  const float* row = scores + q * Lp;
+  const int wave = tid / kWave, lane = lane_id();
+  const int segw = (n + NW * 256 - 1) / (NW * 256) * 256;  // 64 lanes x 4 per load
+  const int s0 = min(n, wave * segw), s1 = min(n, s0 + segw);
+  const int want = k;
+  auto load4 = [&](int b, float (&v)[4], bool (&ok)[4]) {
+    const int idx = b + 4 * lane;
+    if (idx + 3 < s1) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(row + idx);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = x[e];
+        ok[e] = true;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ok[e] = idx + e < s1;
+        v[e] = ok[e] ? row[idx + e] : 0.f;
+      }
+    }
+  };
+  // minimum and maximum over the group, as keys (order-preserving)
+  auto group_minmax = [&](uint32_t lo, uint32_t hi, uint32_t& glo, uint32_t& ghi) {
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    if (lane == 0) {
+      wlo[wave] = lo;
+      whi[wave] = hi;
+    }
+    __syncthreads();
+    glo = wlo[0];
+    ghi = whi[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      glo = min(glo, wlo[w]);
+      ghi = max(ghi, whi[w]);
+    }
+  };
+  auto group_count = [&](int c, int slot) {
+    c = wave_incl_scan(c);
+    c = __builtin_amdgcn_readlane(c, kWave - 1);
+    if (lane == 0) wcnt[slot][wave] = c;
+    __syncthreads();
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) total += wcnt[slot][w];
+    return total;
+  };
+
+  // 1. extremes of the row
+  uint32_t klo = 0xFFFFFFFFu, khi = 0u;
+  for (int b = s0; b < s1; b += 256) {
+    float v[4];
+    bool ok[4];
+    load4(b, v, ok);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (ok[e]) {
+        const uint32_t kk = score_key(v[e]);
+        klo = min(klo, kk);
+        khi = max(khi, kk);
+      }
+  }
+  for (int x = tid; x < kBins; x += NT) hist[x] = 0;
+  if (tid == 0) info[2] = 0;
+  uint32_t glo, ghi;
+  group_minmax(klo, khi, glo, ghi);
+
+  // 2.-3. the threshold key T
+  uint32_t T = 0;
+  bool found = false;
+  int above = 0;  // scores above the interval [glo, ghi] (all kept)
+  for (int level = 0; level < 6; ++level) {
+    if (glo == ghi) {  // every score left in the interval is equal
+      T = ghi;
+      found = true;
+      break;
+    }
+    const float flo = key_to_score(glo), fhi = key_to_score(ghi);
+    const float range = fhi - flo;
+    if (!(range < INFINITY)) break;
+    const float scale = (float)(kBins - 1) / range;
+    auto bin_of = [&](float x) { return min((int)((x - flo) * scale), kBins - 2); };
+    for (int b = s0; b < s1; b += 256) {
+      float v[4];
+      bool ok[4];
+      load4(b, v, ok);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok[e] && v[e] >= flo && v[e] <= fhi) atomicAdd(&hist[bin_of(v[e])], 1);
+    }
+    __syncthreads();
+    const int need = want - above;
+    if (wave == 0) {
+      const int c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2],
+                c3 = lane == kWave - 1 ? 0 : hist[4 * lane + 3];
+      const int pre = wave_incl_scan(c0 + c1 + c2 + c3);
+      int abv = __builtin_amdgcn_readlane(pre, kWave - 1) - pre;
+      const int cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        if (abv < need && need <= abv + cs[e]) {
+          info[0] = 4 * lane + e;
+          info[1] = abv;
+        }
+        abv += cs[e];
+      }
+    }
+    __syncthreads();
+    const int tb = info[0];
+    const int cnt = hist[tb];
+    above += info[1];
+    if (cnt <= kBinCap) {
+      // compact the bin's scores (any order) and search among them
+      for (int b = s0; b < s1; b += 256) {
+        float v[4];
+        bool ok[4];
+        load4(b, v, ok);
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += ok[e] && v[e] >= flo && v[e] <= fhi && bin_of(v[e]) == tb;
+        int wtot;
+        int pos = wave_excl_scan(c, wtot);
+        int base = 0;
+        if (lane == 0 && wtot) base = atomicAdd(&info[2], wtot);
+        pos += __builtin_amdgcn_readlane(base, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (ok[e] && v[e] >= flo && v[e] <= fhi && bin_of(v[e]) == tb) cand[pos++] = __float_as_uint(v[e]);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int nc = info[2];
+        const int need_bin = want - above;
+        uint32_t Tb;
+        if (nc <= 64) Tb = bin_threshold<1, true>(cand, nc, need_bin);
+        else if (nc <= 256) Tb = bin_threshold<4, true>(cand, nc, need_bin);
+        else Tb = bin_threshold<kBinCap / kWave, true>(cand, nc, need_bin);
+        if (lane == 0) info[3] = (int)Tb;
+      }
+      __syncthreads();
+      T = (uint32_t)info[3];
+      found = true;
+      break;
+    }
+    // narrow the interval to the bin's own extremes and histogram again
+    uint32_t blo = 0xFFFFFFFFu, bhi = 0u;
+    for (int b = s0; b < s1; b += 256) {
+      float v[4];
+      bool ok[4];
+      load4(b, v, ok);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ok[e] && v[e] >= flo && v[e] <= fhi && bin_of(v[e]) == tb) {
+          const uint32_t kk = score_key(v[e]);
+          blo = min(blo, kk);
+          bhi = max(bhi, kk);
+        }
+    }
+    __syncthreads();  // every thread has read hist[tb] and info
+    for (int x = tid; x < kBins; x += NT) hist[x] = 0;
+    group_minmax(blo, bhi, glo, ghi);
+  }
+  if (!found) {
+    // bitwise search over the keys of the whole row: the largest T with
+    // at least `want` keys >= T
+    T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c_t = T | (1u << bit);
+      int c = 0;
+      for (int b = s0; b < s1; b += 256) {
+        float v[4];
+        bool ok[4];
+        load4(b, v, ok);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c += ok[e] && score_key(v[e]) >= c_t;
+      }
+      if (group_count(c, bit & 1) >= want) T = c_t;
+      __syncthreads();  // wcnt[bit & 1] is rewritten two bits later
+    }
+  }
+  const float Tf = key_to_score(T);
+
+  // 4. scores above / equal to T per wave; ties to the lowest indices
+  int gt = 0, eq = 0;
+  for (int b = s0; b < s1; b += 256) {
+    float v[4];
+    bool ok[4];
+    load4(b, v, ok);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gt += ok[e] && v[e] > Tf;
+      eq += ok[e] && v[e] == Tf;
+    }
+  }
+  __syncthreads();  // wcnt may still be read by the bitwise search
+  gt = __builtin_amdgcn_readlane(wave_incl_scan(gt), kWave - 1);
+  eq = __builtin_amdgcn_readlane(wave_incl_scan(eq), kWave - 1);
+  if (lane == 0) {
+    wcnt[0][wave] = gt;
+    wcnt[1][wave] = eq;
+  }
+  __syncthreads();
+  int gt_total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) gt_total += wcnt[0][w];
+  const int need_eq = want - gt_total;
+  int pos = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    pos += wcnt[0][w] + min(max(need_eq - eq_before, 0), wcnt[1][w]);
+    eq_before += wcnt[1][w];
+  }
+  const int ties = min(max(need_eq - eq_before, 0), wcnt[1][wave]);  // this wave's kept ties
+
+  // 5. write the kept indices in order
+  int ties_used = 0;
+  for (int b = s0; b < s1; b += 256) {
+    float v[4];
+    bool ok[4];
+    load4(b, v, ok);
+    int te = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) te += ok[e] && v[e] == Tf;
+    int tw;
+    int tr = ties_used + wave_excl_scan(te, tw);  // ties before this lane's first, in index order
+    bool keep[4];
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool is_eq = ok[e] && v[e] == Tf;
+      keep[e] = (ok[e] && v[e] > Tf) || (is_eq && tr < ties);
+      tr += is_eq;
+      c += keep[e];
+    }
+    ties_used += tw;
+    int cw;
+    int p = pos + wave_excl_scan(c, cw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (keep[e]) out[p++] = b + 4 * lane + e;
+    pos += cw;
+  }
+}
+
 // One (query, chunk).  Lists of chunk winners are (key, token) pairs in
 // ascending token order with their count.
 template <int NW, int R>
@@ -367,12 +653,18 @@ hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* k
       const int i_hi = std::min(s.nq, 1024 * R - base);
       if (i_lo >= i_hi) continue;
       const dim3 grid(i_hi - i_lo, s.b);
+      if (512 * R >= kFlatStreamMin) {  // rows of more than 16384 candidates
+        HSA_LAUNCH(k_flat_stream_select, grid, dim3(256), 0, st, scores, tok, s.L, s.nq, Lp, s.k, i_lo);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        continue;
+      }
 #define HSA_FR(RR)                                                                                         \
   case RR:                                                                                                 \
     HSA_LAUNCH((k_flat_row_select<RR>), grid, dim3(1024), dyn, st, scores, tok, s.L, s.nq, Lp, s.k, i_lo); \
     break;
       switch (R) {
-        HSA_FR(1) HSA_FR(2) HSA_FR(4) HSA_FR(8) HSA_FR(16) HSA_FR(32) HSA_FR(64)
+        HSA_FR(1) HSA_FR(2) HSA_FR(4) HSA_FR(8) HSA_FR(16)
       }
 #undef HSA_FR
       hipError_t e = hipGetLastError();
