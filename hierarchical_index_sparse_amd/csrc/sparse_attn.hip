@@ -35,6 +35,12 @@ namespace hsa {
 constexpr int kPartStride = 130;  // 128 dims + running max + running sum
 constexpr int kRowBytes = 272;    // staged kv row: 256 bytes + 16 bytes of padding
 constexpr int kStageBytes = 32 * kRowBytes;
+// K tiles loaded straight into LDS (global_load_lds_dwordx4), two buffers per
+// wave, swizzled instead of padded: 16-byte chunk c of tile row r sits at
+// unit 16 r + (c ^ (r & 15)).
+constexpr bool kAttnKDma = true;
+constexpr int kKTileBytes = 32 * 256;
+constexpr int kWaveLds = kAttnKDma ? 2 * kKTileBytes : kStageBytes;
 // The running max per head is only moved when a tile's max exceeds it by more
 // than this (log2 units), so O is rescaled on few tiles; P = exp2(s - max)
 // then stays below 2^kLazyMax.
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                                      const int32_t* __restrict__ lens, bool premerge) {
   // per wave: the staged K rows of one tile (V goes from memory straight
   // into the P V operand registers)
-  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * kWaveLds];
   const int wave = threadIdx.x / kWave;
   const int item = blockIdx.x * 4 + wave;
   if (item >= n_items) return;
@@ -113,10 +119,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   // byte offset of list entry `pos`'s row if it is a valid token of this
   // sequence, else -1
   const int Lb = seq_len_of(lens, L, b);  // entries at or past the sequence's length are skipped
-  auto entry = [&](int pos) {
-    const int v = pos < end ? tl[pos] : -1;
-    return (v >= 0 && v < Lb) ? (int)__umul24((unsigned)v, (unsigned)row_bytes) : -1;
-  };
+  auto entry_raw = [&](int pos) { return pos < end ? tl[pos] : -1; };
+  auto row_off = [&](int v) { return (v >= 0 && v < Lb) ? (int)__umul24((unsigned)v, (unsigned)row_bytes) : -1; };
+  auto entry = [&](int pos) { return row_off(entry_raw(pos)); };
   // Coalesced gather of one tile's 32 K rows and 32 V rows: instruction i
   // reads rows 4i .. 4i+3, 16 lanes (16 bytes each) per 256-byte row.
   auto kload = [&](int my, u32x4 (&kr)[8]) {
@@ -142,7 +147,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   };
   // this wave's staging buffers: 32 rows of 272 bytes (256 + 16 pad, which
   // makes the 16-row MFMA operand reads bank-conflict free)
-  unsigned char* kst = stage_lds + (size_t)wave * kStageBytes;
+  unsigned char* kst = stage_lds + (size_t)wave * kWaveLds;
+  // K tile straight into LDS buffer kb: instruction i takes rows 4i .. 4i+3
+  // (whole 256-byte rows, coalesced as before); lane 16 rr + cc lands in unit
+  // 64 i + 16 rr + cc, so it loads chunk cc ^ (r & 15) of row r = 4i + rr
+  auto kdma = [&](int my, unsigned char* kb) {
+    const int mine = max(my, 0);
+    const int rr = lane >> 4, cc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + rr;
+      const unsigned off = (unsigned)__shfl(mine, r, kWave) + 16u * (unsigned)(cc ^ (r & 15));
+      __builtin_amdgcn_global_load_lds((const void*)(Kb + off),
+                                       (__attribute__((address_space(3))) void*)(kb + 1024 * i), 16, 0, 0);
+    }
+  };
   auto stage = [&](const u32x4 (&kr)[8]) {
     const int off = (lane >> 4) * kRowBytes + 16 * (lane & 15);
 #pragma unroll
@@ -160,22 +179,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   u32x4 kr[8], w[8];
   int my = entry(start + (lane & 31));
   int my_next = entry(start + 32 + (lane & 31));
-  kload(my, kr);
-  stage(kr);
-  vload(my, w);
-  if (start + 32 < end) kload(my_next, kr);
-  wave_sync();
+  if constexpr (kAttnKDma) {
+    // K_0 into buffer 0, V_0, K_1 into buffer 1.  Before tile t's K is read,
+    // the wave waits until at most 8 of its vector-memory operations are in
+    // flight: tile t's V loads (8) always follow tile t's K in issue order
+    // (scheduling barriers keep them there), so K_t is then complete while
+    // K_{t+1}, issued after V_t, may still be in flight.
+    kdma(my, kst);
+    __builtin_amdgcn_sched_barrier(0);
+    vload(my, w);
+    __builtin_amdgcn_sched_barrier(0);
+    if (start + 32 < end) kdma(my_next, kst + kKTileBytes);
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    kload(my, kr);
+    stage(kr);
+    vload(my, w);
+    if (start + 32 < end) kload(my_next, kr);
+    wave_sync();
+  }
   for (int p0 = start; p0 < end; p0 += 32) {
     const uint32_t vmask = (uint32_t)ballot(my >= 0);
-    const int my_next2 = entry(p0 + 64 + (lane & 31));
+    // (the list entries of tile t+2: loaded here, turned into row offsets
+    // where they are used, so nothing waits for them early)
+    const int raw_next2 = entry_raw(p0 + 64 + (lane & 31));
+    const unsigned char* kt = kAttnKDma ? kst + (((p0 - start) >> 5) & 1) * kKTileBytes : kst;
+    if constexpr (kAttnKDma) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt((8 & 0xF) | (7 << 4) | (0xF << 8));  // vmcnt(8): K_t is in LDS
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     if (vmask != 0u) {
       // ---- S^T = K Q^T over two 16-token tiles (A = staged K rows)
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kst + jl * kRowBytes + 16 * (gq + 4 * ks));
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kst + (16 + jl) * kRowBytes + 16 * (gq + 4 * ks));
+        const int c = gq + 4 * ks;
+        const u32x4 a0 = kAttnKDma ? *reinterpret_cast<const u32x4*>(kt + 16 * (16 * jl + (c ^ jl)))
+                                   : *reinterpret_cast<const u32x4*>(kst + jl * kRowBytes + 16 * c);
+        const u32x4 a1 = kAttnKDma ? *reinterpret_cast<const u32x4*>(kt + 16 * (16 * (16 + jl) + (c ^ jl)))
+                                   : *reinterpret_cast<const u32x4*>(kst + (16 + jl) * kRowBytes + 16 * c);
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), qf[ks], s1, 0, 0, 0);
       }
@@ -247,11 +291,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
       }
     }
-    if (p0 + 32 < end) vload(my_next, w);  // tile i's P V is done with w
-    wave_sync();  // tile i's LDS reads are done
-    if (p0 + 32 < end) stage(kr);
-    wave_sync();
-    if (p0 + 64 < end) kload(my_next2, kr);
+    int my_next2;
+    if constexpr (kAttnKDma) {
+      // V_{t+1}, then K_{t+2} into the buffer tile t was read from
+      __builtin_amdgcn_sched_barrier(0);
+      if (p0 + 32 < end) vload(my_next, w);  // tile t's P V is done with w
+      __builtin_amdgcn_sched_barrier(0);
+      wave_sync();  // tile t's LDS reads are done
+      my_next2 = row_off(raw_next2);
+      if (p0 + 64 < end) kdma(my_next2, const_cast<unsigned char*>(kt));
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (p0 + 32 < end) vload(my_next, w);  // tile i's P V is done with w
+      wave_sync();  // tile i's LDS reads are done
+      if (p0 + 32 < end) stage(kr);
+      wave_sync();
+      my_next2 = row_off(raw_next2);
+      if (p0 + 64 < end) kload(my_next2, kr);
+    }
     my = my_next;
     my_next = my_next2;
   }
@@ -279,7 +336,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         float mw[4], M = -INFINITY;
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
-          src[wi] = reinterpret_cast<const float*>(stage_lds + (size_t)wi * kStageBytes) + h * kPartStride;
+          src[wi] = reinterpret_cast<const float*>(stage_lds + (size_t)wi * kWaveLds) + h * kPartStride;
           mw[wi] = src[wi][128];
           M = fmaxf(M, mw[wi]);
         }
