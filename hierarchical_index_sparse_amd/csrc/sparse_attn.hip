@@ -180,16 +180,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   int my = entry(start + (lane & 31));
   int my_next = entry(start + 32 + (lane & 31));
   if constexpr (kAttnKDma) {
-    // K_0 into buffer 0, V_0, K_1 into buffer 1.  Before tile t's K is read,
-    // the wave waits until at most 8 of its vector-memory operations are in
-    // flight: tile t's V loads (8) always follow tile t's K in issue order
-    // (scheduling barriers keep them there), so K_t is then complete while
-    // K_{t+1}, issued after V_t, may still be in flight.
+    // Issue order, kept by scheduling barriers: K_0 (into buffer 0), K_1
+    // (buffer 1), V_0; then per tile t: the list entries of tile t+2 (one
+    // load, always issued), [reads of K_t, softmax, P V], K_{t+2} (into the
+    // buffer K_t was read from), V_{t+1}.  Before K_t is read the wave waits
+    // until at most N of its vector-memory operations are in flight, N being
+    // the count issued after K_t's last one that is certain in every case
+    // (t = 0: K_1 if any, V_0, one list load; t >= 1: one list load, K_{t+1}
+    // if any, V_t, one list load), so K_t is complete and what follows it
+    // may still be in flight.
     kdma(my, kst);
     __builtin_amdgcn_sched_barrier(0);
-    vload(my, w);
-    __builtin_amdgcn_sched_barrier(0);
     if (start + 32 < end) kdma(my_next, kst + kKTileBytes);
+    __builtin_amdgcn_sched_barrier(0);
+    vload(my, w);
     __builtin_amdgcn_sched_barrier(0);
   } else {
     kload(my, kr);
@@ -202,11 +206,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     const uint32_t vmask = (uint32_t)ballot(my >= 0);
     // (the list entries of tile t+2: loaded here, turned into row offsets
     // where they are used, so nothing waits for them early)
-    const int raw_next2 = entry_raw(p0 + 64 + (lane & 31));
+    const int pos2 = p0 + 64 + (lane & 31);
+    const int raw_next2 = kAttnKDma ? tl[min(pos2, k - 1)] : entry_raw(pos2);  // (KDma: always one load)
     const unsigned char* kt = kAttnKDma ? kst + (((p0 - start) >> 5) & 1) * kKTileBytes : kst;
     if constexpr (kAttnKDma) {
+      // s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt (7) and
+      // lgkmcnt (15) left alone
+#define HSA_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (7 << 4) | (0xF << 8))
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt((8 & 0xF) | (7 << 4) | (0xF << 8));  // vmcnt(8): K_t is in LDS
+      if (p0 == start) {
+        if (start + 32 < end) HSA_VMCNT(17);
+        else HSA_VMCNT(9);
+      } else {
+        if (p0 + 32 < end) HSA_VMCNT(18);
+        else HSA_VMCNT(10);
+      }
+#undef HSA_VMCNT
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -293,13 +308,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     }
     int my_next2;
     if constexpr (kAttnKDma) {
-      // V_{t+1}, then K_{t+2} into the buffer tile t was read from
+      // K_{t+2} into the buffer tile t was read from, then V_{t+1}
+      __builtin_amdgcn_sched_barrier(0);
+      my_next2 = row_off(pos2 < end ? raw_next2 : -1);
+      wave_sync();  // tile t's LDS reads are done
+      if (p0 + 64 < end) kdma(my_next2, const_cast<unsigned char*>(kt));
       __builtin_amdgcn_sched_barrier(0);
       if (p0 + 32 < end) vload(my_next, w);  // tile t's P V is done with w
-      __builtin_amdgcn_sched_barrier(0);
-      wave_sync();  // tile t's LDS reads are done
-      my_next2 = row_off(raw_next2);
-      if (p0 + 64 < end) kdma(my_next2, const_cast<unsigned char*>(kt));
       __builtin_amdgcn_sched_barrier(0);
     } else {
       if (p0 + 32 < end) vload(my_next, w);  // tile i's P V is done with w
