@@ -10,7 +10,7 @@
 // row (256 bytes) is read once for all G heads.  Per tile of 32 list
 // entries:
 //   * S^T = K_tile Q^T (2 x 4 MFMAs): A = 16 K rows (gathered with whole-row
-//     coalesced loads and staged in LDS), B = the query heads, held in
+//     coalesced loads straight into LDS), B = the query heads, held in
 //     registers.  The accumulator layout gives each lane one head and 8
 //     tokens, which is the A-operand layout P needs for P V, so no shuffle
 //     of P is required.
@@ -33,14 +33,11 @@
 namespace hsa {
 
 constexpr int kPartStride = 130;  // 128 dims + running max + running sum
-constexpr int kRowBytes = 272;    // staged kv row: 256 bytes + 16 bytes of padding
-constexpr int kStageBytes = 32 * kRowBytes;
-// K tiles loaded straight into LDS (global_load_lds_dwordx4), two buffers per
+// K tiles go straight into LDS (global_load_lds_dwordx4), two buffers per
 // wave, swizzled instead of padded: 16-byte chunk c of tile row r sits at
 // unit 16 r + (c ^ (r & 15)).
-constexpr bool kAttnKDma = true;
 constexpr int kKTileBytes = 32 * 256;
-constexpr int kWaveLds = kAttnKDma ? 2 * kKTileBytes : kStageBytes;
+constexpr int kWaveLds = 2 * kKTileBytes;
 // The running max per head is only moved when a tile's max exceeds it by more
 // than this (log2 units), so O is rescaled on few tiles; P = exp2(s - max)
 // then stays below 2^kLazyMax.
@@ -119,20 +116,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   // byte offset of list entry `pos`'s row if it is a valid token of this
   // sequence, else -1
   const int Lb = seq_len_of(lens, L, b);  // entries at or past the sequence's length are skipped
-  auto entry_raw = [&](int pos) { return pos < end ? tl[pos] : -1; };
   auto row_off = [&](int v) { return (v >= 0 && v < Lb) ? (int)__umul24((unsigned)v, (unsigned)row_bytes) : -1; };
-  auto entry = [&](int pos) { return row_off(entry_raw(pos)); };
-  // Coalesced gather of one tile's 32 K rows and 32 V rows: instruction i
-  // reads rows 4i .. 4i+3, 16 lanes (16 bytes each) per 256-byte row.
-  auto kload = [&](int my, u32x4 (&kr)[8]) {
-    const int mine = max(my, 0);  // an invalid entry loads row 0 (masked later)
-    const unsigned col = 16u * (unsigned)(lane & 15);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const unsigned off = (unsigned)__shfl(mine, 4 * i + (lane >> 4), kWave) + col;
-      kr[i] = *reinterpret_cast<const u32x4*>(Kb + off);
-    }
-  };
+  auto entry = [&](int pos) { return row_off(pos < end ? tl[pos] : -1); };
   // One tile's V rows straight into the P V operand layout: w[e] holds dims
   // 8 jl .. 8 jl + 7 of the lane's P token e (tokens 4 gq + e, then
   // 16 + 4 gq + e - 4); instruction e still reads 4 whole rows.
@@ -145,8 +130,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       w[e] = *reinterpret_cast<const u32x4*>(Vb + off);
     }
   };
-  // this wave's staging buffers: 32 rows of 272 bytes (256 + 16 pad, which
-  // makes the 16-row MFMA operand reads bank-conflict free)
   unsigned char* kst = stage_lds + (size_t)wave * kWaveLds;
   // K tile straight into LDS buffer kb: instruction i takes rows 4i .. 4i+3
   // (whole 256-byte rows, coalesced as before); lane 16 rr + cc lands in unit
@@ -162,24 +145,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                        (__attribute__((address_space(3))) void*)(kb + 1024 * i), 16, 0, 0);
     }
   };
-  auto stage = [&](const u32x4 (&kr)[8]) {
-    const int off = (lane >> 4) * kRowBytes + 16 * (lane & 15);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(kst + off + 4 * i * kRowBytes) = kr[i];
-  };
   auto wave_sync = [] {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // pipeline: tile i in LDS, tile i+1 in flight to registers, list entries
-  // of tile i+2 in flight
-  // (tile i's V in registers, loaded when tile i-1's P V is done)
-  u32x4 kr[8], w[8];
+  u32x4 w[8];
   int my = entry(start + (lane & 31));
   int my_next = entry(start + 32 + (lane & 31));
-  if constexpr (kAttnKDma) {
+  {
     // Issue order, kept by scheduling barriers: K_0 (into buffer 0), K_1
     // (buffer 1), V_0; then per tile t: the list entries of tile t+2 (one
     // load, always issued), [reads of K_t, softmax, P V], K_{t+2} (into the
@@ -195,21 +170,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     __builtin_amdgcn_sched_barrier(0);
     vload(my, w);
     __builtin_amdgcn_sched_barrier(0);
-  } else {
-    kload(my, kr);
-    stage(kr);
-    vload(my, w);
-    if (start + 32 < end) kload(my_next, kr);
-    wave_sync();
   }
   for (int p0 = start; p0 < end; p0 += 32) {
     const uint32_t vmask = (uint32_t)ballot(my >= 0);
     // (the list entries of tile t+2: loaded here, turned into row offsets
     // where they are used, so nothing waits for them early)
     const int pos2 = p0 + 64 + (lane & 31);
-    const int raw_next2 = kAttnKDma ? tl[min(pos2, k - 1)] : entry_raw(pos2);  // (KDma: always one load)
-    const unsigned char* kt = kAttnKDma ? kst + (((p0 - start) >> 5) & 1) * kKTileBytes : kst;
-    if constexpr (kAttnKDma) {
+    const int raw_next2 = tl[min(pos2, k - 1)];  // always one load (the wait counts rely on it)
+    const unsigned char* kt = kst + (((p0 - start) >> 5) & 1) * kKTileBytes;
+    {
       // s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt (7) and
       // lgkmcnt (15) left alone
 #define HSA_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (7 << 4) | (0xF << 8))
@@ -231,10 +200,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int c = gq + 4 * ks;
-        const u32x4 a0 = kAttnKDma ? *reinterpret_cast<const u32x4*>(kt + 16 * (16 * jl + (c ^ jl)))
-                                   : *reinterpret_cast<const u32x4*>(kst + jl * kRowBytes + 16 * c);
-        const u32x4 a1 = kAttnKDma ? *reinterpret_cast<const u32x4*>(kt + 16 * (16 * (16 + jl) + (c ^ jl)))
-                                   : *reinterpret_cast<const u32x4*>(kst + (16 + jl) * kRowBytes + 16 * c);
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + 16 * (16 * jl + (c ^ jl)));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + 16 * (16 * (16 + jl) + (c ^ jl)));
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), qf[ks], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), qf[ks], s1, 0, 0, 0);
       }
@@ -307,7 +274,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       }
     }
     int my_next2;
-    if constexpr (kAttnKDma) {
+    {
       // K_{t+2} into the buffer tile t was read from, then V_{t+1}
       __builtin_amdgcn_sched_barrier(0);
       my_next2 = row_off(pos2 < end ? raw_next2 : -1);
@@ -316,13 +283,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       __builtin_amdgcn_sched_barrier(0);
       if (p0 + 32 < end) vload(my_next, w);  // tile t's P V is done with w
       __builtin_amdgcn_sched_barrier(0);
-    } else {
-      if (p0 + 32 < end) vload(my_next, w);  // tile i's P V is done with w
-      wave_sync();  // tile i's LDS reads are done
-      if (p0 + 32 < end) stage(kr);
-      wave_sync();
-      my_next2 = row_off(raw_next2);
-      if (p0 + 64 < end) kload(my_next2, kr);
     }
     my = my_next;
     my_next = my_next2;
