@@ -176,18 +176,20 @@ __global__ __launch_bounds__(256) void k_block_scores_mfma(const uint16_t* __res
 }
 
 // Prefill block top-m in one launch (contexts of at most kTileMaxBlocks
-// blocks): one workgroup takes 16 consecutive queries of one sequence and
+// blocks): one workgroup takes kTileQ (16, or 8 when that leaves too few
+// workgroups to fill the chip) consecutive queries of one sequence and
 // computes their block scores on the matrix cores straight into LDS (A =
-// the 16 queries' indexer vectors, held in registers; wave w takes summary
+// the queries' indexer vectors, held in registers (16 rows, the last query
+// repeated past kTileQ); wave w takes summary
 // rows 32w .. 32w+31 of every 128-row tile up to the last query's causal
 // block, two MFMA chains at a time; the landmark maximum is an xor shuffle
-// across adjacent lanes).  Each wave then runs the one-wave select for 4 of
-// the queries on their LDS rows, so the scores never leave the chip.  Row
+// across adjacent lanes).  Each wave then runs the one-wave select for a
+// quarter of the queries on their LDS rows, so the scores never leave the
+// chip.  Row
 // slot j of a query holds block j; only blocks 1 .. c-1 are candidates.
 constexpr int kTileMaxBlocks = 2048;
-constexpr int kTileQ = 16;
 
-template <int DI, int NL, int R>
+template <int DI, int NL, int R, int kTileQ>
 __global__ __launch_bounds__(256) void k_block_topm_tile(const uint16_t* __restrict__ qI,
                                                          const uint16_t* __restrict__ S, int32_t* __restrict__ blk,
                                                          int L, int nq, int B, int nb, int m, int qtiles_per_seq,
@@ -237,7 +239,8 @@ __global__ __launch_bounds__(256) void k_block_topm_tile(const uint16_t* __restr
         const int row = r0 + 16 * nt + jl;
         if (row % NL == 0 && row < row_end) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sc[(4 * gq + e) * ldsw + row / NL] = acc[nt][e];
+          for (int e = 0; e < 4; ++e)
+            if (4 * gq + e < kTileQ) sc[(4 * gq + e) * ldsw + row / NL] = acc[nt][e];
         }
       }
     }
@@ -684,33 +687,39 @@ hipError_t launch_block_topm(const Dims& s, const uint16_t* qI, const uint16_t* 
   const int c_max = (s.L - 1) / s.B;
   const int n_max = c_max - 1;
   if (c_max + 1 > s.m && s.nq >= 64 && s.nb <= kTileMaxBlocks && !s.lens) {
-    // scores and select in one launch, the scores in LDS
-    const int qtiles = (s.nq + kTileQ - 1) / kTileQ;
+    // scores and select in one launch, the scores in LDS; 8 queries per
+    // workgroup when 16 would leave fewer than 1024 workgroups
+    const int tq = (long long)s.b * ((s.nq + 15) / 16) >= 1024 ? 16 : 8;
+    const int qtiles = (s.nq + tq - 1) / tq;
     const int ldsw = (s.nb + 3) & ~3;
-    const size_t lds = (size_t)kTileQ * ldsw * sizeof(float);
+    const size_t lds = (size_t)tq * ldsw * sizeof(float);
     const int r = pick_r(n_max, 1);
-#define HSA_TT(DI, NL, RR)                                                                                     \
-  do {                                                                                                         \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_topm_tile<DI, NL, RR>),          \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                  \
-    if (e != hipSuccess) return e;                                                                             \
-    HSA_LAUNCH((k_block_topm_tile<DI, NL, RR>), dim3(qtiles * s.b), dim3(256), lds, st, qI, S, blk, s.L, s.nq, \
-               s.B, s.nb, s.m, qtiles, ldsw);                                                                  \
+#define HSA_TT(DI, NL, RR, TQ)                                                                                     \
+  do {                                                                                                             \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_block_topm_tile<DI, NL, RR, TQ>),          \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
+    if (e != hipSuccess) return e;                                                                                 \
+    HSA_LAUNCH((k_block_topm_tile<DI, NL, RR, TQ>), dim3(qtiles * s.b), dim3(256), lds, st, qI, S, blk, s.L, s.nq, \
+               s.B, s.nb, s.m, qtiles, ldsw);                                                                      \
   } while (0)
-#define HSA_TR(DI, NL)                                 \
-  switch (r) {                                         \
-    case 1: HSA_TT(DI, NL, 1); break;                  \
-    case 2: HSA_TT(DI, NL, 2); break;                  \
-    case 4: HSA_TT(DI, NL, 4); break;                  \
-    case 8: HSA_TT(DI, NL, 8); break;                  \
-    case 16: HSA_TT(DI, NL, 16); break;                \
-    default: HSA_TT(DI, NL, 32); break;                \
+#define HSA_TQ(DI, NL, RR)             \
+  if (tq == 16) HSA_TT(DI, NL, RR, 16); \
+  else HSA_TT(DI, NL, RR, 8);
+#define HSA_TR(DI, NL)                    \
+  switch (r) {                            \
+    case 1: HSA_TQ(DI, NL, 1) break;      \
+    case 2: HSA_TQ(DI, NL, 2) break;      \
+    case 4: HSA_TQ(DI, NL, 4) break;      \
+    case 8: HSA_TQ(DI, NL, 8) break;      \
+    case 16: HSA_TQ(DI, NL, 16) break;    \
+    default: HSA_TQ(DI, NL, 32) break;    \
   }
     if (s.dI == 64) {
       if (s.nL == 1) { HSA_TR(64, 1) } else if (s.nL == 2) { HSA_TR(64, 2) } else { HSA_TR(64, 4) }
     } else {
       if (s.nL == 1) { HSA_TR(128, 1) } else if (s.nL == 2) { HSA_TR(128, 2) } else { HSA_TR(128, 4) }
     }
+#undef HSA_TQ
 #undef HSA_TR
 #undef HSA_TT
     return hipGetLastError();
