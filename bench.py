@@ -156,7 +156,7 @@ KERNEL_STAGE = {
     "k_head_scores_mfma": "block_topm", "k_head_select": "block_topm",
     "k_token_scores": "token_topk", "k_token_scores_tiled": "token_topk", "k_bm_scores": "token_topk",
     "k_token_select": "token_topk", "k_token_enum": "token_topk",
-    "k_sparse_attn": "sparse_attn", "k_attn_merge": "sparse_attn",
+    "k_sparse_attn": "sparse_attn", "k_attn_merge": "sparse_attn", "k_select_attn": "sparse_attn",
 }
 
 
@@ -200,6 +200,12 @@ def kernel_work(w: Workload, kernel: str, lens=None) -> dict:
             return {"bytes": nqt * dI * 2 + st * dI * 2 + st * 4, "flops": 2.0 * dI * st, "bound": bound}
         if kernel == "k_token_select":
             return {"bytes": st * 4 + nqt * w.top_k * 4, "flops": 0.0, "bound": "hbm"}
+        if kernel == "k_select_attn":
+            # the token select (scores and block lists in) and the attention
+            # (the list it selects stays on chip; the list written out is
+            # counted where the attention would read it)
+            a = work["sparse_attn"]
+            return {"bytes": a["bytes"] + st * 4 + nqt * w.top_m * 4, "flops": a["flops"], "bound": "hbm"}
     if stage is None:
         return {"bytes": 0.0, "flops": 0.0, "bound": "hbm"}
     # prefill attention gathers K/V rows that many queries share (a working
@@ -418,10 +424,12 @@ class HipEvents:
 # ------------------------------------------------------- flat indexer
 
 
-def flat_comparison(w: Workload, dev: dict, shape, stage_ms: dict, steps: int, hip) -> dict | None:
+def flat_comparison(w: Workload, dev: dict, shape, S, stage_ms: dict, steps: int, hip) -> dict | None:
     """Time hsa_flat_topk (score every causal token, keep top-k) on the same
-    indexer inputs, against the hierarchical indexer's stages of hsa_forward
-    (summary + block top-m + token top-k) - the comparison the HISA page
+    indexer inputs, against the hierarchical indexer: the summary and block
+    top-m stages of hsa_forward plus hsa_token_topk on its block lists (the
+    whole token stage, scorer and select, also where hsa_forward runs the
+    select inside its attention launch) - the comparison the HISA page
     reports.  None when the flat indexer does not support the shape."""
     import torch
 
@@ -429,28 +437,39 @@ def flat_comparison(w: Workload, dev: dict, shape, stage_ms: dict, steps: int, h
     need = _lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_FLAT_TOPK)
     if need == 0 and w.top_k < w.seq_len:
         return None  # unsupported shape
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     tok = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device="cuda")
-    _lib.hsa_flat_topk(shape, dev["qI"], dev["kI"], tok, ws)
-    torch.cuda.synchronize()
+    blk = torch.empty((w.batch, w.n_q, w.top_m), dtype=torch.int32, device="cuda")
+    _lib.hsa_block_topm(shape, dev["qI"], S, blk)
     n = max(3, min(steps, 10))
-    ev = [(hip.create(), hip.create()) for _ in range(n)]
     stream = torch.cuda.current_stream().cuda_stream
-    for a, b in ev:
-        hip.record(a, stream)
-        _lib.hsa_flat_topk(shape, dev["qI"], dev["kI"], tok, ws)
-        hip.record(b, stream)
-    torch.cuda.synchronize()
-    flat_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev]))
-    for a, b in ev:
-        hip.destroy(a)
-        hip.destroy(b)
-    del ws, tok
+
+    def timed(call):
+        call()
+        torch.cuda.synchronize()
+        ev = [(hip.create(), hip.create()) for _ in range(n)]
+        for a, b in ev:
+            hip.record(a, stream)
+            call()
+            hip.record(b, stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev]))
+        for a, b in ev:
+            hip.destroy(a)
+            hip.destroy(b)
+        return ms
+
+    ws = torch.empty(max(_lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_TOKEN_TOPK), 1), dtype=torch.uint8,
+                     device="cuda")
+    token_ms = timed(lambda: _lib.hsa_token_topk(shape, dev["qI"], dev["kI"], blk, tok, ws))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    flat_ms = timed(lambda: _lib.hsa_flat_topk(shape, dev["qI"], dev["kI"], tok, ws))
+    del ws, tok, blk
     torch.cuda.empty_cache()
-    hier_ms = stage_ms["block_summary"] + stage_ms["block_topm"] + stage_ms["token_topk"]
+    hier_ms = stage_ms["block_summary"] + stage_ms["block_topm"] + token_ms
     return {"flat_indexer_ms": flat_ms, "hierarchical_indexer_ms": hier_ms, "speedup": flat_ms / hier_ms,
-            "note": "same inputs and output form; hierarchical = summary + block top-m + token top-k stages "
-                    "of hsa_forward"}
+            "token_topk_ms": token_ms,
+            "note": "same inputs and output form; hierarchical = summary + block top-m stages of hsa_forward "
+                    "+ hsa_token_topk (scorer and select) on its block lists"}
 
 
 def two_level_comparison(w: Workload, dev: dict, shape, stage_ms: dict, blk3, steps: int, hip) -> dict:
@@ -543,6 +562,9 @@ def dense_comparison(w: Workload, dev: dict, steps: int, hip, step_ms: float) ->
 
 
 # the SURVEY configurations reported beside the headline workload
+# the timed region's steps whose dominant-kernel dispatches carry events
+EVENT_EVERY = 8
+
 CONFIG_WORKLOADS = ("decode_128k", "chunked_prefill_512k", "decode_512k", "landmark_decode_1m")
 
 
@@ -625,7 +647,8 @@ def roofline_entry(w: Workload, kernel: str, kernel_ms: float, n_launch: int, le
     roof["launches_per_step"] = n_launch
     roof["avg_launch_us"] = kernel_ms * 1000.0 / n_launch
     roof["kernel_ms_timed"] = kernel_ms
-    roof["kernel_ms_note"] = ("the kernel's launches in one step, summed (a long prefill runs it once per query chunk); "
+    roof["kernel_ms_note"] = ("the kernel's launches in one step, summed (a long prefill runs it once per query chunk), "
+                              f"by HIP events on every {EVENT_EVERY}th step of the timed region; "
                               "algorithmic_per_launch is the step's work over its launches")
     return roof
 
@@ -788,26 +811,33 @@ def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=Tr
     dom = max(kernel_us, key=lambda x: x[1])[0]
     dom_idx = [i for i in range(nk) if names[i] == dom]
 
-    # Timed region: K whole steps; only the dominant kernel's dispatches
-    # carry events, giving its duration in each step (event arrays built
-    # before the loop).
-    timed = [[(hip.create(), hip.create()) for _ in dom_idx] for _ in range(args.steps)]
+    # Timed region: K whole steps.  The dominant kernel's dispatches carry
+    # start/stop events on every EVENT_EVERY-th step (steps 0, 8, 16, ...),
+    # giving its duration in those steps; an event-carrying dispatch costs
+    # the stream several microseconds (about 6 us per decode step), so events
+    # on every step would slow the very steps being timed.  Event arrays are
+    # built before the loop.
+    sampled = list(range(0, args.steps, EVENT_EVERY))
+    timed = [[(hip.create(), hip.create()) for _ in dom_idx] for _ in sampled]
     Ev = ctypes.c_void_p * (dom_idx[-1] + 1)
-    ev_arrays = []
-    for evs in timed:
+    ev_arrays = [None] * args.steps
+    for s_i, evs in zip(sampled, timed):
         st_ev, sp_ev = Ev(), Ev()
         for i, (a, b) in zip(dom_idx, evs):
             st_ev[i], sp_ev[i] = a, b
-        ev_arrays.append((st_ev, sp_ev))
+        ev_arrays[s_i] = (st_ev, sp_ev)
     set_kev = lib.hsa_sparse_set_kernel_events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for st_ev, sp_ev in ev_arrays:
-        set_kev(st_ev, sp_ev, dom_idx[-1] + 1)
-        step()
+    for evs in ev_arrays:
+        if evs is not None:
+            set_kev(evs[0], evs[1], dom_idx[-1] + 1)
+            step()
+            set_kev(None, None, 0)
+        else:
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    _lib.hsa_sparse_set_kernel_events(None, None)
     dom_ms = float(np.mean([sum(hip.elapsed_ms(a, b) for a, b in evs) for evs in timed]))
     for evs in timed:
         for a, b in evs:
@@ -852,7 +882,7 @@ def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=Tr
     if headline:
         # the flat indexer takes one length for the batch
         if not (args.no_flat or lens is not None or w.group or w.per_head):
-            extras["indexer_vs_flat"] = flat_comparison(w, dev, shape, stage_ms, args.steps, hip)
+            extras["indexer_vs_flat"] = flat_comparison(w, dev, shape, out["S"], stage_ms, args.steps, hip)
         if w.group:
             blk3 = pipeline.alloc_outputs(w)["blk"]
             _lib.hsa_block_topm_3level(shape, w.group, w.top_m2, dev["qI"], out["S"], out["S2"], out["sup"], blk3)

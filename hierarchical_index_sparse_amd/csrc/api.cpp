@@ -271,6 +271,10 @@ size_t chunked_attn_ws_bytes(const hsa::Dims& d) {
   return ws;
 }
 
+// Decode-shaped calls run the token select inside the attention launch
+// (hsa::launch_select_attn); prefill keeps the two steps apart.
+bool fuse_select_attn(const hsa::Dims& d) { return !attn_chunks(d) && hsa::select_attn_fusable(d); }
+
 ForwardLayout forward_layout(const hsa::Dims& d) {
   using hsa::align_up;
   ForwardLayout f;
@@ -279,8 +283,12 @@ ForwardLayout forward_layout(const hsa::Dims& d) {
   f.tok_off = align_up(nqt * d.m * sizeof(int32_t));
   f.stage_off = f.tok_off + align_up(nqt * d.k * sizeof(int32_t));
   size_t stage = hsa::block_topm_ws_bytes(d);
-  stage = std::max(stage, hsa::token_topk_ws_bytes(d));
-  stage = std::max(stage, attn_chunks(d) ? chunked_attn_ws_bytes(d) : hsa::sparse_attn_ws_bytes(d));
+  if (fuse_select_attn(d)) {  // the scores and the attention partials are live together
+    stage = std::max(stage, hsa::select_attn_ws_bytes(d));
+  } else {
+    stage = std::max(stage, hsa::token_topk_ws_bytes(d));
+    stage = std::max(stage, attn_chunks(d) ? chunked_attn_ws_bytes(d) : hsa::sparse_attn_ws_bytes(d));
+  }
   f.total = f.stage_off + stage;
   return f;
 }
@@ -537,10 +545,18 @@ static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, con
   }
   if (e != hipSuccess) return hf(e, "block top-m");
   HSA_MARK(2)
-  e = hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
+  // (with the select inside the attention launch, stage 3 is the scorer
+  // alone and stage 4 the select, the attention and the merge)
+  const bool fuse = fuse_select_attn(d);
+  e = fuse ? hsa::launch_token_scores(d, qI, kI, blk, stage, stream)
+           : hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
   if (e != hipSuccess) return hf(e, "token top-k");
   HSA_MARK(3)
-  if (const int nc = attn_chunks(d)) {
+  if (fuse) {
+    e = hsa::launch_select_attn(d, static_cast<const float*>(stage), blk, tok, Q, K, V, O, lse,
+                                static_cast<char*>(stage) + hsa::token_topk_ws_bytes(d), stream);
+    if (e != hipSuccess) return hf(e, "token select + sparse attention");
+  } else if (const int nc = attn_chunks(d)) {
     for (int b = 0; b < d.b; ++b)
       for (int c = 0; c < nc; ++c) {
         const int i0 = c * attn_chunk_q(d), i1 = std::min(d.nq, (c + 1) * attn_chunk_q(d));

@@ -90,6 +90,20 @@ size_t sparse_attn_ws_bytes(const Dims& s);
 hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                               const int32_t* tok, float* O, float* lse, void* ws, hipStream_t st);
 
+// steps 3 and 4 for few queries (decode): the scorer alone
+// (launch_token_scores, into the first token_topk_ws_bytes of ws; nothing
+// when no query scores), then the select and the attention in one launch
+// plus the merge (launch_select_attn: scores as written by the scorer, the
+// attention partials in the next sparse_attn_ws_bytes).  Only for shapes
+// where select_attn_fusable holds; same lists and outputs, bit for bit, as
+// launch_token_topk + launch_sparse_attn.
+hipError_t launch_token_scores(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk, void* ws,
+                               hipStream_t st);
+bool select_attn_fusable(const Dims& s);
+size_t select_attn_ws_bytes(const Dims& s);
+hipError_t launch_select_attn(const Dims& s, const float* scores, const int32_t* blk, int32_t* tok, const uint16_t* Q,
+                              const uint16_t* K, const uint16_t* V, float* O, float* lse, void* ws, hipStream_t st);
+
 // the flat indexer (every causal token scored), the baseline of step 3
 bool flat_topk_supported(const Dims& s);
 size_t flat_topk_ws_bytes(const Dims& s);

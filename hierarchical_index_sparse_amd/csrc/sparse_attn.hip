@@ -29,6 +29,7 @@
 // partial per workgroup reaches memory and the merge reads a quarter.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "token_select.hpp"
 
 namespace hsa {
 
@@ -64,23 +65,21 @@ __device__ __forceinline__ float sum_x32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                     const uint16_t* __restrict__ V, const int32_t* __restrict__ tok,
-                                                     float* __restrict__ O, float* __restrict__ lse,
-                                                     float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
-                                                     int chunk, int nsplit, float scale_log2, int n_items,
-                                                     const int32_t* __restrict__ lens, bool premerge) {
-  // per wave: the staged K rows of one tile (V goes from memory straight
-  // into the P V operand registers)
-  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * kWaveLds];
+// One wave's share of the attention: list positions [start, end) of query q
+// for kv head g (item = this wave's (query, kv head, split) index).  The
+// list entries are tl[pos - base] for pos <= last: with LIST_LDS, tl is an
+// LDS copy of positions base .. last, else the query's row of the list in
+// memory (base 0, last k - 1).  Splits write their partial result
+// (combined across the workgroup's 4 waves first when `premerge`, which all
+// 4 waves then reach); else O and lse.
+template <bool SPLIT, bool LIST_LDS>
+__device__ __forceinline__ void attend_list(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                            const uint16_t* __restrict__ V, const int32_t* __restrict__ tl,
+                                            int base, int last, float* __restrict__ O, float* __restrict__ lse,
+                                            float* __restrict__ part, unsigned char* stage_lds, int item, int q,
+                                            int g, int L, int nq, int Hq, int Hkv, int start, int end,
+                                            float scale_log2, const int32_t* __restrict__ lens, bool premerge) {
   const int wave = threadIdx.x / kWave;
-  const int item = blockIdx.x * 4 + wave;
-  if (item >= n_items) return;
-  const int split = item % nsplit;
-  const int qg = item / nsplit;
-  const int g = qg % Hkv;
-  const int q = qg / Hkv;
   const int b = q / nq;
   const int G = Hq / Hkv;
   const int lane = lane_id();
@@ -99,9 +98,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     }
   }
 
-  const int start = split * chunk;
-  const int end = min(k, start + chunk);
-  const int32_t* tl = tok + (size_t)q * k;
   // this (sequence, kv head)'s rows; a row's byte offset fits 31 bits
   // (seq_len * n_heads_kv * 256 < 2^31, checked at the API)
   const unsigned char* Kb = reinterpret_cast<const unsigned char*>(K + ((size_t)b * L * Hkv + g) * 128);
@@ -117,7 +113,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   // sequence, else -1
   const int Lb = seq_len_of(lens, L, b);  // entries at or past the sequence's length are skipped
   auto row_off = [&](int v) { return (v >= 0 && v < Lb) ? (int)__umul24((unsigned)v, (unsigned)row_bytes) : -1; };
-  auto entry = [&](int pos) { return row_off(pos < end ? tl[pos] : -1); };
+  auto entry = [&](int pos) { return row_off(pos < end ? tl[pos - base] : -1); };
   // One tile's V rows straight into the P V operand layout: w[e] holds dims
   // 8 jl .. 8 jl + 7 of the lane's P token e (tokens 4 gq + e, then
   // 16 + 4 gq + e - 4); instruction e still reads 4 whole rows.
@@ -176,19 +172,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // (the list entries of tile t+2: loaded here, turned into row offsets
     // where they are used, so nothing waits for them early)
     const int pos2 = p0 + 64 + (lane & 31);
-    const int raw_next2 = tl[min(pos2, k - 1)];  // always one load (the wait counts rely on it)
+    const int raw_next2 = tl[min(pos2, last) - base];  // always one load (the wait counts rely on it)
     const unsigned char* kt = kst + (((p0 - start) >> 5) & 1) * kKTileBytes;
     {
       // s_waitcnt immediates: vmcnt in bits 3:0 and 15:14, expcnt (7) and
       // lgkmcnt (15) left alone
 #define HSA_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (7 << 4) | (0xF << 8))
       __builtin_amdgcn_sched_barrier(0);
+      constexpr int nl = LIST_LDS ? 0 : 1;  // vector-memory loads per list read
       if (p0 == start) {
-        if (start + 32 < end) HSA_VMCNT(17);
-        else HSA_VMCNT(9);
+        if (start + 32 < end) HSA_VMCNT(16 + nl);
+        else HSA_VMCNT(8 + nl);
       } else {
-        if (p0 + 32 < end) HSA_VMCNT(18);
-        else HSA_VMCNT(10);
+        if (p0 + 32 < end) HSA_VMCNT(16 + 2 * nl);
+        else HSA_VMCNT(8 + 2 * nl);
       }
 #undef HSA_VMCNT
       __builtin_amdgcn_sched_barrier(0);
@@ -361,6 +358,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   }
 }
 
+template <bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_sparse_attn(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                     const uint16_t* __restrict__ V, const int32_t* __restrict__ tok,
+                                                     float* __restrict__ O, float* __restrict__ lse,
+                                                     float* __restrict__ part, int L, int nq, int Hq, int Hkv, int k,
+                                                     int chunk, int nsplit, float scale_log2, int n_items,
+                                                     const int32_t* __restrict__ lens, bool premerge) {
+  // per wave: the staged K rows of one tile (V goes from memory straight
+  // into the P V operand registers)
+  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * kWaveLds];
+  const int item = blockIdx.x * 4 + (int)threadIdx.x / kWave;
+  if (item >= n_items) return;
+  const int split = item % nsplit;
+  const int qg = item / nsplit;
+  const int q = qg / Hkv;
+  const int start = split * chunk;
+  attend_list<SPLIT, false>(Q, K, V, tok + (size_t)q * k, 0, k - 1, O, lse, part, stage_lds, item, q, qg % Hkv, L, nq,
+                            Hq, Hkv, start, min(k, start + chunk), scale_log2, lens, premerge);
+}
+
+// Decode: the token select (step 3's top-k) and the attention in one
+// launch.  A workgroup holds 4 consecutive splits of one (query, kv head),
+// as k_sparse_attn's do when it pre-merges.  Its 8 waves first run the
+// query's exact select, the same as k_token_select's, and keep in LDS the
+// positions of the list its 4 splits attend to.  Waves 0-3 then attend as
+// k_sparse_attn's waves do, with the same code, splits and pre-merge, so
+// the partial results carry the same bits.  Waves 4-7 write the
+// workgroup's part of the list to `tok` (kv head 0 only) and end.  Every
+// workgroup of a query repeats the select.  That costs 4 bytes per
+// candidate (the scores) and no time where the launch has one workgroup per
+// CU or fewer, and it removes a launch, the list's round trip through memory
+// and a launch gap from the step.
+template <int R, bool ONEBLK>
+__global__ __launch_bounds__(512) void k_select_attn(const float* __restrict__ scores, const int32_t* __restrict__ blk,
+                                                     int32_t* __restrict__ tok, const uint16_t* __restrict__ Q,
+                                                     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                                     float* __restrict__ part, int L, int nq, int B, int log2B, int m,
+                                                     int k, int Hq, int Hkv, int chunk, int nsplit, float scale_log2,
+                                                     const int32_t* __restrict__ lens) {
+  constexpr int NW = 8;
+  __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * kWaveLds];
+  __shared__ SelectSmem<NW> sel;
+  // the block list (m entries, padded to 4), then list positions
+  // [p_lo, p_hi) and one dummy slot per lane
+  extern __shared__ __attribute__((aligned(16))) int dyn_lds[];
+  int* bl = dyn_lds;
+  int* plist = dyn_lds + ((m + 3) & ~3);
+  const int item0 = blockIdx.x * 4;
+  const int qg = item0 / nsplit;
+  const int s0 = item0 % nsplit;
+  const int q = qg / Hkv, g = qg % Hkv;
+  const int p_lo = s0 * chunk, p_hi = min(k, p_lo + 4 * chunk);
+  const int dummy = 4 * chunk + lane_id();
+  const bool selected = select_query_tokens<NW, R, ONEBLK, true>(
+      scores, blk, q, L, nq, B, log2B, m, k, lens, p_lo, p_hi, sel, bl, [&](int slot, int v) { plist[slot - p_lo] = v; },
+      [&](int pos, int v, bool take) { plist[(take && pos >= p_lo && pos < p_hi) ? pos - p_lo : dummy] = v; });
+  if (!selected) __syncthreads();  // (the select ends with a barrier, keeping all does not)
+  const int wave = (int)threadIdx.x / kWave;
+  if (wave >= 4) {
+    if (g == 0) {
+      int32_t* out = tok + (size_t)q * k + p_lo;
+      const int n = p_hi - p_lo, x = (int)threadIdx.x - 256;
+      if ((k & 3) == 0) {  // 16-byte aligned, n a multiple of 4
+        for (int p = 4 * x; p < n; p += 4 * 256)
+          *reinterpret_cast<u32x4*>(out + p) = *reinterpret_cast<const u32x4*>(plist + p);
+      } else {
+        for (int p = x; p < n; p += 256) out[p] = plist[p];
+      }
+    }
+    return;
+  }
+  const int start = (s0 + wave) * chunk;
+  attend_list<true, true>(Q, K, V, plist, p_lo, p_hi - 1, nullptr, nullptr, part, stage_lds, item0 + wave, q, g, L, nq,
+                          Hq, Hkv, start, min(k, start + chunk), scale_log2, lens, true);
+}
+
 // Log-sum-exp merge of the splits of one (query, head), spread over CC
 // workgroups of 128 / CC output columns each: the partials come from other
 // XCDs' caches, so the merge is paced by how many loads the CUs keep in
@@ -474,6 +547,23 @@ size_t sparse_attn_ws_bytes(const Dims& s) {
   return align_up((size_t)s.b * s.nq * s.Hkv * nsplit * 16 * kPartStride * sizeof(float));
 }
 
+// Log-sum-exp merge of `nsplit` partials per (query, kv head) into O and
+// lse: about 1024 merge workgroups, few (query, head) rows get more column
+// chunks.
+static hipError_t launch_merge(const Dims& s, const float* part, float* O, float* lse, int nsplit, hipStream_t st) {
+  const long long rows = (long long)s.b * s.nq * s.Hq;
+  const dim3 mb(256);
+  if (rows >= 512)
+    HSA_LAUNCH(k_attn_merge<1>, dim3((unsigned)rows), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  else if (rows >= 256)
+    HSA_LAUNCH(k_attn_merge<2>, dim3((unsigned)(rows * 2)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  else if (rows >= 128)
+    HSA_LAUNCH(k_attn_merge<4>, dim3((unsigned)(rows * 4)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  else
+    HSA_LAUNCH(k_attn_merge<8>, dim3((unsigned)(rows * 8)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  return hipGetLastError();
+}
+
 hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                               const int32_t* tok, float* O, float* lse, void* ws, hipStream_t st) {
   const long long nq_total = (long long)s.b * s.nq;
@@ -496,19 +586,80 @@ hipError_t launch_sparse_attn(const Dims& s, const uint16_t* Q, const uint16_t* 
                      s.k, chunk, nsplit, scale_log2, n_items, s.lens, premerge);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (premerge) nsplit /= 4;
-  // about 1024 merge workgroups: few (query, head) rows get more column chunks
-  const long long rows = nq_total * s.Hq;
-  const dim3 mb(256);
-  if (rows >= 512)
-    HSA_LAUNCH(k_attn_merge<1>, dim3((unsigned)rows), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
-  else if (rows >= 256)
-    HSA_LAUNCH(k_attn_merge<2>, dim3((unsigned)(rows * 2)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
-  else if (rows >= 128)
-    HSA_LAUNCH(k_attn_merge<4>, dim3((unsigned)(rows * 4)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
-  else
-    HSA_LAUNCH(k_attn_merge<8>, dim3((unsigned)(rows * 8)), mb, 0, st, part, O, lse, s.Hq, s.Hkv, nsplit);
+  return launch_merge(s, part, O, lse, premerge ? nsplit / 4 : nsplit, st);
+}
+
+// ---- decode: select and attention in one launch
+
+constexpr size_t kMaxLdsBytes = 160 * 1024;
+
+// Whether any query of the call scores its candidates (else every query
+// keeps all of them), and the select's slots per thread over 8 waves.
+static bool sa_scoring(const Dims& s) { return (long long)s.k < (long long)s.m * s.B && s.L > s.k; }
+static int sa_slots(const Dims& s) {
+  if (!sa_scoring(s)) return 1;
+  int r = 1;
+  while ((long long)r * 512 < (long long)s.m * s.B) r <<= 1;
+  return r;
+}
+static size_t sa_dyn_lds(const Dims& s, int chunk) {
+  return sizeof(int) * ((size_t)((s.m + 3) & ~3) + 4 * (size_t)chunk + kWave);
+}
+
+bool select_attn_fusable(const Dims& s) {
+  const long long nq_total = (long long)s.b * s.nq;
+  if (nq_total == 0) return false;
+  int nsplit, chunk;
+  split_plan(s, nsplit, chunk);
+  if (nsplit < 4 || nsplit % 4 != 0) return false;  // 4 splits of one (query, kv head) per workgroup
+  if (sa_slots(s) > 32) return false;
+  return sa_dyn_lds(s, chunk) + 4 * kWaveLds + sizeof(SelectSmem<8>) <= kMaxLdsBytes;
+}
+
+size_t select_attn_ws_bytes(const Dims& s) { return token_topk_ws_bytes(s) + sparse_attn_ws_bytes(s); }
+
+template <int R, bool ONEBLK>
+static hipError_t launch_sa_k(const Dims& s, const float* scores, const int32_t* blk, int32_t* tok,
+                              const uint16_t* Q, const uint16_t* K, const uint16_t* V, float* part, int chunk,
+                              int nsplit, hipStream_t st) {
+  const void* fn = reinterpret_cast<const void*>(&k_select_attn<R, ONEBLK>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sa_dyn_lds(s, chunk));
+  if (e != hipSuccess) return e;
+  const int n_wg = (int)((long long)s.b * s.nq * s.Hkv * nsplit / 4);
+  HSA_LAUNCH((k_select_attn<R, ONEBLK>), dim3(n_wg), dim3(512), sa_dyn_lds(s, chunk), st, scores, blk, tok, Q, K, V,
+             part, s.L, s.nq, s.B, __builtin_ctz((unsigned)s.B), s.m, s.k, s.Hq, s.Hkv, chunk, nsplit,
+             s.scale * 1.4426950408889634f, s.lens);
   return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_sa_r(const Dims& s, const float* scores, const int32_t* blk, int32_t* tok,
+                              const uint16_t* Q, const uint16_t* K, const uint16_t* V, float* part, int chunk,
+                              int nsplit, hipStream_t st) {
+  if (R <= s.B) return launch_sa_k<R, true>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st);
+  if constexpr (R > 8) return launch_sa_k<R, false>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st);
+  return hipErrorInvalidValue;  // B >= 8
+}
+
+hipError_t launch_select_attn(const Dims& s, const float* scores, const int32_t* blk, int32_t* tok, const uint16_t* Q,
+                              const uint16_t* K, const uint16_t* V, float* O, float* lse, void* ws, hipStream_t st) {
+  if ((long long)s.b * s.nq == 0) return hipSuccess;
+  if (!select_attn_fusable(s)) return hipErrorInvalidValue;
+  int nsplit, chunk;
+  split_plan(s, nsplit, chunk);
+  float* part = static_cast<float*>(ws);
+  hipError_t e;
+  switch (sa_slots(s)) {
+    case 1: e = launch_sa_r<1>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st); break;
+    case 2: e = launch_sa_r<2>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st); break;
+    case 4: e = launch_sa_r<4>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st); break;
+    case 8: e = launch_sa_r<8>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st); break;
+    case 16: e = launch_sa_r<16>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st); break;
+    case 32: e = launch_sa_r<32>(s, scores, blk, tok, Q, K, V, part, chunk, nsplit, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  return launch_merge(s, part, O, lse, nsplit / 4, st);
 }
 
 }  // namespace hsa

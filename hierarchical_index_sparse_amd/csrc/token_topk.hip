@@ -30,16 +30,11 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
+#include "token_select.hpp"
 
 namespace hsa {
 
 // Largest m with m * B <= 32768 candidates at the smallest block size.
-
-__device__ __forceinline__ void candidate_count(int t, int B, int m, int& c, int& n_sel, int& n_valid) {
-  c = t / B;
-  n_sel = (c + 1 <= m) ? c + 1 : m;
-  n_valid = (n_sel - 1) * B + (t - c * B + 1);
-}
 
 // Workgroup (q, y) writes the 1024-slot chunks y, y + gridDim.y, ... of
 // query q's list.  B >= 8, so 4 consecutive slots from a multiple of 4 lie
@@ -560,83 +555,16 @@ __global__ __launch_bounds__(NW * 64) void k_token_select(const float* __restric
   int* bl = dyn_lds;
   int* stage = dyn_lds + ((m + 3) & ~3);
   const int q = blockIdx.x;
-  const int i = q % nq;
-  const int t = query_pos(seq_len_of(lens, L, q / nq), nq, i);
-  int c, n_sel, n_valid;
-  candidate_count(t, B, m, c, n_sel, n_valid);  // upper bounds: the list may be shorter
   int32_t* out = tok + (size_t)q * k;
-  const int32_t* blq = blk + (size_t)q * m;
-  if (n_valid <= k) {
-    // keep all: a slot is a token iff its entry is a block and the token is
-    // causal; the invalid slots all follow the valid ones
-    for (int slot = threadIdx.x; slot < k; slot += NT) {
-      const int j = slot < n_valid ? blq[slot >> log2B] : -1;
-      const int tk = (j << log2B) + (slot & (B - 1));
-      out[slot] = (j >= 0 && slot < n_valid && tk <= t) ? tk : -1;
-    }
-    return;
-  }
-  // the slot scores do not depend on the block list: both loads in flight
-  // together, one round trip before the barrier (slots past the list's
-  // real length are read but masked below)
-  const float* sc = scores + (size_t)q * m * B;  // 32-byte aligned: m * B is a multiple of 8
-  const int idx0 = threadIdx.x * R;
-  const float empty = __uint_as_float(0x7FC00000u);  // quiet NaN: an empty slot of select_top_f
-  float v[R];
-  if constexpr (R >= 4) {
-#pragma unroll
-    for (int r = 0; r < R; r += 4) {
-      if (idx0 + r + 3 < n_valid) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(sc + idx0 + r);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[r + e] = x[e];
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int idx = idx0 + r + e;
-          v[r + e] = idx < n_valid ? sc[idx] : empty;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int idx = idx0 + r;
-      v[r] = idx < n_valid ? sc[idx] : empty;
-    }
-  }
-  for (int p = threadIdx.x; p < n_sel; p += NT) bl[p] = blq[p];
-  __syncthreads();
-  // the list's length: its entries are a valid prefix, then -1
-  if (bl[n_sel - 1] < 0) {  // (uniform) shorter than min(c + 1, m)
-    int lo = 0, hi = n_sel - 1;  // bl[lo] is valid, bl[hi] is not
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (bl[mid] >= 0) lo = mid;
-      else hi = mid;
-    }
-    n_sel = lo + 1;
-    n_valid = (n_sel - 1) * B + (t - c * B + 1);
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (idx0 + r >= n_valid) v[r] = empty;
-    if (n_valid <= k) {
-      for (int slot = threadIdx.x; slot < k; slot += NT) {
-        const int j = slot < n_valid ? bl[slot >> log2B] : -1;
-        out[slot] = slot < n_valid ? (j << log2B) + (slot & (B - 1)) : -1;
-      }
-      return;
-    }
-  }
-  const int bmask = B - 1;
-  const int tbase = ONEBLK ? (bl[min(idx0 >> log2B, n_sel - 1)] << log2B) | (idx0 & bmask) : 0;
   const int dummy = k + lane_id();
-  select_top_f<NW, R, STAGED>(v, k, NT * R - n_valid, lds, [&](int pos, int idx, bool take) {
-    const int v = ONEBLK ? tbase + (idx - idx0) : (bl[idx >> log2B] << log2B) | (idx & bmask);
-    if constexpr (STAGED) stage[take ? pos : dummy] = v;
-    else if (take) out[pos] = v;
-  });
+  const bool selected = select_query_tokens<NW, R, ONEBLK, STAGED>(
+      scores, blk, q, L, nq, B, log2B, m, k, lens, 0, k, lds, bl, [&](int slot, int v) { out[slot] = v; },
+      [&](int pos, int v, bool take) {
+        if constexpr (STAGED) stage[take ? pos : dummy] = v;
+        else if (take) out[pos] = v;
+      });
   if constexpr (STAGED) {
+    if (!selected) return;
     // select_top ends with a barrier: the staged list is complete
     if ((k & 3) == 0) {
       for (int p = threadIdx.x * 4; p < k; p += NT * 4)
@@ -795,6 +723,48 @@ static hipError_t launch_tiled(const Dims& s, int qw, const uint16_t* qI, const 
   return launch_tiled_t<128, 1>(s, qI, kI, blk, scores, st);
 }
 
+hipError_t launch_token_scores(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
+                               void* ws, hipStream_t st) {
+  const int nq_total = s.b * s.nq;
+  if (nq_total == 0 || !((long long)s.k < (long long)s.m * s.B && s.L > s.k)) return hipSuccess;
+  float* scores = static_cast<float*>(ws);
+  const int qw = tiled_qw(s);
+  if (use_block_major(s)) {
+    unsigned char* base = static_cast<unsigned char*>(ws);
+    const BmLayout lay = bm_layout(s, align_up((size_t)nq_total * s.m * s.B * sizeof(float)));
+    int* counts = reinterpret_cast<int*>(base + lay.counts);
+    int* offsets = reinterpret_cast<int*>(base + lay.offsets);
+    int* chunk_off = reinterpret_cast<int*>(base + lay.chunk_off);
+    int* cursor = reinterpret_cast<int*>(base + lay.cursor);
+    int2* entries = reinterpret_cast<int2*>(base + lay.entries);
+    const int nl = s.b * s.nb;
+    const long long total = (long long)nq_total * s.m;
+    const int g1 = (int)std::min<long long>((total + 255) / 256, 8192);
+    HSA_LAUNCH(k_bm_zero, dim3(std::min((nl + 255) / 256, 1024)), dim3(256), 0, st, counts, nl);
+    HSA_LAUNCH(k_bm_count, dim3(g1), dim3(256), 0, st, blk, counts, s.L, s.nq, s.B, s.m, s.k, s.nb, total);
+    HSA_LAUNCH(k_bm_scan, dim3(1), dim3(1024), 0, st, counts, offsets, chunk_off, cursor, nl);
+    HSA_LAUNCH(k_bm_fill, dim3(g1), dim3(256), 0, st, blk, cursor, entries, s.L, s.nq, s.B, s.m, s.k, s.nb,
+                       total);
+    const int gs = (int)((total + kBmChunk - 1) / kBmChunk + nl);
+    if (s.dI == 64)
+      HSA_LAUNCH((k_bm_scores<64>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off, scores,
+                         s.L, s.nq, s.B, s.m, s.nb, nl);
+    else
+      HSA_LAUNCH((k_bm_scores<128>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off,
+                         scores, s.L, s.nq, s.B, s.m, s.nb, nl);
+    return hipGetLastError();
+  }
+  if (qw > 0) return launch_tiled(s, qw, qI, kI, blk, scores, st);
+  dim3 grid(s.m, nq_total);
+  if (s.dI == 64)
+    HSA_LAUNCH((k_token_scores<64>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m, s.k,
+                       s.lens);
+  else
+    HSA_LAUNCH((k_token_scores<128>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m, s.k,
+                       s.lens);
+  return hipGetLastError();
+}
+
 hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk, int32_t* tok,
                              void* ws, hipStream_t st) {
   const int nq_total = s.b * s.nq;
@@ -803,44 +773,7 @@ hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* 
   const bool any_scoring = (long long)s.k < (long long)s.m * s.B && s.L > s.k;
   int n_max = s.m * s.B;
   if (any_scoring) {
-    const int qw = tiled_qw(s);
-    hipError_t e;
-    if (use_block_major(s)) {
-      unsigned char* base = static_cast<unsigned char*>(ws);
-      const BmLayout lay = bm_layout(s, align_up((size_t)nq_total * s.m * s.B * sizeof(float)));
-      int* counts = reinterpret_cast<int*>(base + lay.counts);
-      int* offsets = reinterpret_cast<int*>(base + lay.offsets);
-      int* chunk_off = reinterpret_cast<int*>(base + lay.chunk_off);
-      int* cursor = reinterpret_cast<int*>(base + lay.cursor);
-      int2* entries = reinterpret_cast<int2*>(base + lay.entries);
-      const int nl = s.b * s.nb;
-      const long long total = (long long)nq_total * s.m;
-      const int g1 = (int)std::min<long long>((total + 255) / 256, 8192);
-      HSA_LAUNCH(k_bm_zero, dim3(std::min((nl + 255) / 256, 1024)), dim3(256), 0, st, counts, nl);
-      HSA_LAUNCH(k_bm_count, dim3(g1), dim3(256), 0, st, blk, counts, s.L, s.nq, s.B, s.m, s.k, s.nb, total);
-      HSA_LAUNCH(k_bm_scan, dim3(1), dim3(1024), 0, st, counts, offsets, chunk_off, cursor, nl);
-      HSA_LAUNCH(k_bm_fill, dim3(g1), dim3(256), 0, st, blk, cursor, entries, s.L, s.nq, s.B, s.m, s.k, s.nb,
-                         total);
-      const int gs = (int)((total + kBmChunk - 1) / kBmChunk + nl);
-      if (s.dI == 64)
-        HSA_LAUNCH((k_bm_scores<64>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off, scores,
-                           s.L, s.nq, s.B, s.m, s.nb, nl);
-      else
-        HSA_LAUNCH((k_bm_scores<128>), dim3(gs), dim3(256), 0, st, qI, kI, entries, offsets, chunk_off,
-                           scores, s.L, s.nq, s.B, s.m, s.nb, nl);
-      e = hipGetLastError();
-    } else if (qw > 0) {
-      e = launch_tiled(s, qw, qI, kI, blk, scores, st);
-    } else {
-      dim3 grid(s.m, nq_total);
-      if (s.dI == 64)
-        HSA_LAUNCH((k_token_scores<64>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
-                           s.k, s.lens);
-      else
-        HSA_LAUNCH((k_token_scores<128>), grid, dim3(256), 0, st, qI, kI, blk, scores, s.L, s.nq, s.B, s.m,
-                           s.k, s.lens);
-      e = hipGetLastError();
-    }
+    const hipError_t e = launch_token_scores(s, qI, kI, blk, ws, st);
     if (e != hipSuccess) return e;
   } else {  // every query keeps all of its candidates
     const dim3 grid((unsigned)nq_total, (unsigned)std::min<long long>((s.k + 1023ll) / 1024, 4096));

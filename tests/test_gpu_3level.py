@@ -48,6 +48,10 @@ CASES = [
     (case("fewer_candidates_than_m", 2, 10100, 118, 128, 32, 1, 31, 209, 8, 2), 2),
     (case("fewer_candidates_decode", 3, 20000, 1, 64, 16, 1, 40, 100, 4, 3), 2),
     (case("fewer_candidates_keep_all", 1, 9000, 50, 64, 16, 1, 60, 960, 8, 2), 2),
+    # the same in decode with the token select inside the attention launch:
+    # at most 20 (select) or 12 (keep all) blocks for m = 40
+    (case("fewer_candidates_select_attn", 2, 20000, 1, 64, 16, 1, 40, 256, 4, 5), 2),
+    (case("fewer_candidates_select_attn_keep_all", 2, 20000, 1, 64, 16, 1, 40, 256, 4, 3), 2),
 ]
 
 

@@ -51,6 +51,13 @@ SMALL_CASES = [
     # decode with 2048 scored blocks: the one-launch block top-m at its limit (R = 2)
     (small("decode_fused_r2", batch=3, seq_len=32790, n_q=2, d_index=128, block=16, top_m=40, top_k=300,
            n_heads_q=4, n_heads_kv=1), 2),
+    # decode with the token select inside the attention launch: a thread's
+    # 32 slots span two blocks (R > B), and two kv heads (each workgroup of
+    # a query repeats its select; kv head 0 writes the list)
+    (small("decode_select_attn_multiblock", batch=2, seq_len=40000, n_q=1, d_index=64, block=16, top_m=600,
+           top_k=1000, n_heads_q=8, n_heads_kv=1), 2),
+    (small("decode_select_attn_gqa2", batch=3, seq_len=30000, n_q=1, d_index=64, block=32, top_m=100,
+           top_k=512, n_heads_q=8, n_heads_kv=2), 2),
 ]
 
 
