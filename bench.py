@@ -157,6 +157,7 @@ KERNEL_STAGE = {
     "k_token_scores": "token_topk", "k_token_scores_tiled": "token_topk", "k_bm_scores": "token_topk",
     "k_token_select": "token_topk", "k_token_enum": "token_topk",
     "k_sparse_attn": "sparse_attn", "k_attn_merge": "sparse_attn", "k_select_attn": "sparse_attn",
+    "k_block_token_decode": "block_topm",
 }
 
 
@@ -200,6 +201,12 @@ def kernel_work(w: Workload, kernel: str, lens=None) -> dict:
             return {"bytes": nqt * dI * 2 + st * dI * 2 + st * 4, "flops": 2.0 * dI * st, "bound": bound}
         if kernel == "k_token_select":
             return {"bytes": st * 4 + nqt * w.top_k * 4, "flops": 0.0, "bound": "hbm"}
+        if kernel == "k_block_token_decode":
+            # the block top-m and the token scorer: both stages' bytes, less
+            # the block lists the scorer would read back
+            tb = work["block_topm"]
+            return {"bytes": tb["bytes"] + st * dI * 2 + st * 4, "flops": tb["flops"] + 2.0 * dI * st,
+                    "bound": "hbm"}
         if kernel == "k_select_attn":
             # the token select (scores and block lists in) and the attention
             # (the list it selects stays on chip; the list written out is
@@ -424,13 +431,14 @@ class HipEvents:
 # ------------------------------------------------------- flat indexer
 
 
-def flat_comparison(w: Workload, dev: dict, shape, S, stage_ms: dict, steps: int, hip) -> dict | None:
+def flat_comparison(w: Workload, dev: dict, shape, S, start_block: int, steps: int, hip) -> dict | None:
     """Time hsa_flat_topk (score every causal token, keep top-k) on the same
-    indexer inputs, against the hierarchical indexer: the summary and block
-    top-m stages of hsa_forward plus hsa_token_topk on its block lists (the
-    whole token stage, scorer and select, also where hsa_forward runs the
-    select inside its attention launch) - the comparison the HISA page
-    reports.  None when the flat indexer does not support the shape."""
+    indexer inputs, against the hierarchical indexer called step by step:
+    hsa_block_summary (the blocks a step re-summarises), hsa_block_topm and
+    hsa_token_topk (scorer and select), so that no part of the indexer is
+    hidden in a launch that hsa_forward shares with another step - the
+    comparison the HISA page reports.  None when the flat indexer does not
+    support the shape."""
     import torch
 
     from hierarchical_index_sparse_amd import _lib
@@ -439,7 +447,6 @@ def flat_comparison(w: Workload, dev: dict, shape, S, stage_ms: dict, steps: int
         return None  # unsupported shape
     tok = torch.empty((w.batch, w.n_q, w.top_k), dtype=torch.int32, device="cuda")
     blk = torch.empty((w.batch, w.n_q, w.top_m), dtype=torch.int32, device="cuda")
-    _lib.hsa_block_topm(shape, dev["qI"], S, blk)
     n = max(3, min(steps, 10))
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -458,18 +465,25 @@ def flat_comparison(w: Workload, dev: dict, shape, S, stage_ms: dict, steps: int
             hip.destroy(b)
         return ms
 
-    ws = torch.empty(max(_lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_TOKEN_TOPK), 1), dtype=torch.uint8,
-                     device="cuda")
-    token_ms = timed(lambda: _lib.hsa_token_topk(shape, dev["qI"], dev["kI"], blk, tok, ws))
+    ws_b = torch.empty(max(_lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_BLOCK_TOPM), 1),
+                       dtype=torch.uint8, device="cuda")
+    ws_t = torch.empty(max(_lib.hsa_sparse_workspace_size(shape, _lib.HSA_SPARSE_OP_TOKEN_TOPK), 1),
+                       dtype=torch.uint8, device="cuda")
+
+    def hierarchical():
+        _lib.hsa_block_summary(shape, dev["kI"], dev.get("W"), start_block, S)
+        _lib.hsa_block_topm(shape, dev["qI"], S, blk, ws_b)
+        _lib.hsa_token_topk(shape, dev["qI"], dev["kI"], blk, tok, ws_t)
+
+    hier_ms = timed(hierarchical)
+    del ws_b, ws_t
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     flat_ms = timed(lambda: _lib.hsa_flat_topk(shape, dev["qI"], dev["kI"], tok, ws))
     del ws, tok, blk
     torch.cuda.empty_cache()
-    hier_ms = stage_ms["block_summary"] + stage_ms["block_topm"] + token_ms
     return {"flat_indexer_ms": flat_ms, "hierarchical_indexer_ms": hier_ms, "speedup": flat_ms / hier_ms,
-            "token_topk_ms": token_ms,
-            "note": "same inputs and output form; hierarchical = summary + block top-m stages of hsa_forward "
-                    "+ hsa_token_topk (scorer and select) on its block lists"}
+            "note": "same inputs and output form; hierarchical = hsa_block_summary (re-summarised blocks) + "
+                    "hsa_block_topm + hsa_token_topk, called one after the other"}
 
 
 def two_level_comparison(w: Workload, dev: dict, shape, stage_ms: dict, blk3, steps: int, hip) -> dict:
@@ -882,7 +896,7 @@ def measure(w: Workload, inp: dict, args, hip, peaks=None, ora=None, headline=Tr
     if headline:
         # the flat indexer takes one length for the batch
         if not (args.no_flat or lens is not None or w.group or w.per_head):
-            extras["indexer_vs_flat"] = flat_comparison(w, dev, shape, out["S"], stage_ms, args.steps, hip)
+            extras["indexer_vs_flat"] = flat_comparison(w, dev, shape, out["S"], start_block, args.steps, hip)
         if w.group:
             blk3 = pipeline.alloc_outputs(w)["blk"]
             _lib.hsa_block_topm_3level(shape, w.group, w.top_m2, dev["qI"], out["S"], out["S2"], out["sup"], blk3)

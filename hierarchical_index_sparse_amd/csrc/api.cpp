@@ -537,7 +537,15 @@ static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, con
   if (e != hipSuccess) return hf(e, "super-block summary");
   HSA_MARK(1)
   const hsa::SummaryFold sf{kI, landmark_W, S, summary_start_block};
-  if (l3) {
+  // Decode: the select runs inside the attention launch (stage 3 is then
+  // the scorer alone and stage 4 the select, the attention and the merge);
+  // with one summary vector per block, the token scores are also computed
+  // in the block top-m launch (stage 3 is then empty).
+  const bool fuse = fuse_select_attn(d);
+  const bool fuse_bt = fuse && !l3 && hsa::block_token_fusable(d, fold ? &sf : nullptr);
+  if (fuse_bt) {
+    e = hsa::launch_block_token_decode(d, qI, S, kI, blk, static_cast<float*>(stage), stream, fold ? &sf : nullptr);
+  } else if (l3) {
     e = hsa::launch_block_topm_3level(d, l3->lgG, l3->m2, qI, S, l3->S2, l3->sup, blk, stage, stream,
                                       fold ? &sf : nullptr, l3->S2);
   } else {
@@ -545,11 +553,9 @@ static hsa_sparse_status_t forward_impl(const hsa::Dims& d, const char* who, con
   }
   if (e != hipSuccess) return hf(e, "block top-m");
   HSA_MARK(2)
-  // (with the select inside the attention launch, stage 3 is the scorer
-  // alone and stage 4 the select, the attention and the merge)
-  const bool fuse = fuse_select_attn(d);
-  e = fuse ? hsa::launch_token_scores(d, qI, kI, blk, stage, stream)
-           : hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
+  if (fuse_bt) e = hipSuccess;
+  else if (fuse) e = hsa::launch_token_scores(d, qI, kI, blk, stage, stream);
+  else e = hsa::launch_token_topk(d, qI, kI, blk, tok, stage, stream);
   if (e != hipSuccess) return hf(e, "token top-k");
   HSA_MARK(3)
   if (fuse) {

@@ -20,6 +20,7 @@
 #include "kernels.hpp"
 #include "select.hpp"
 #include "summary.hpp"
+#include "token_select.hpp"
 
 namespace hsa {
 
@@ -590,6 +591,196 @@ __global__ __launch_bounds__(1024) void k_block_topm_decode(const uint16_t* __re
   select_top<NWS, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
     if (take) out[1 + pos] = 1 + idx;
   });
+}
+
+// Decode, the block top-m and step 3's token scores in one launch (few
+// queries, one summary vector per block, at most kFusedMaxBlocks scored
+// blocks).  P workgroups per query each repeat the query's block selection
+// (as k_block_topm_decode: the causal blocks' scores into LDS, the one-wave
+// select), keep the list in LDS, and then score the tokens of every P-th
+// kept block (list positions p, p + P, ...) into the slot-ordered scores,
+// as k_token_scores does; workgroup p = 0 writes the list.  The repeats
+// read the query's block summaries again (from L2: the P workgroups of a
+// query get workgroup ids congruent mod 8, which the hardware deals to one
+// XCD), and the launch saves a launch gap and the list's trip through
+// memory.  Workgroups past the queries summarise the newest blocks when the
+// host folds that in.
+constexpr int kBtMaxM = 1024;
+
+template <int DI, int R>
+__global__ __launch_bounds__(1024) void k_block_token_decode(
+    const uint16_t* __restrict__ qI, const uint16_t* __restrict__ S, const uint16_t* __restrict__ kI,
+    int32_t* __restrict__ blk, float* __restrict__ scores, int L, int nq, int B, int log2B, int nb, int m, int k,
+    int nq_total, int P, int n_query_wg, uint16_t* __restrict__ S_out, int sum_start, int nsum,
+    const int32_t* __restrict__ lens) {
+  constexpr int LPR = DI / 8;      // lanes per row
+  constexpr int RPI = 1024 / LPR;  // rows per round of the workgroup
+  constexpr int U = 8;             // rounds of loads in flight
+  __shared__ __attribute__((aligned(16))) float sc[kFusedMaxBlocks];
+  __shared__ SelectSmem<1> sm;
+  __shared__ float red[1][1024 / LPR][DI];
+  __shared__ int lst[kBtMaxM];
+  if ((int)blockIdx.x >= n_query_wg) {  // folded summary of a newest block (uniform)
+    const int w = (int)blockIdx.x - n_query_wg;
+    const int bs = w / nsum;
+    const int Lb = seq_len_of(lens, L, bs);
+    const int jb = (lens ? (Lb - 1) / B : sum_start) + w % nsum;
+    if (jb >= nb || jb * B >= Lb) return;
+    summarise_block<DI, 1, 1024>(kI, nullptr, S_out, L, Lb, B, nb, jb, bs, red);
+    return;
+  }
+  // workgroup x: XCD x % 8; queries 8 g + x % 8 of group g = x / (8 P)
+  const int x = blockIdx.x;
+  const int slot = x >> 3;
+  const int q = (slot / P) * 8 + (x & 7);
+  const int p = slot % P;
+  if (q >= nq_total) return;
+  const int tid = threadIdx.x;
+  const int b = q / nq;
+  const int t = query_pos(seq_len_of(lens, L, b), nq, q % nq);
+  const int c = t / B;
+  const int col8 = tid % LPR, r0 = tid / LPR;
+  float qv[8];
+  {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(qI + (size_t)q * DI + col8 * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[2 * e] = bf16_lo(v[e]);
+      qv[2 * e + 1] = bf16_hi(v[e]);
+    }
+  }
+  // ---- the block list, in LDS
+  if (c + 1 <= m) {
+    for (int j = tid; j < m; j += 1024) lst[j] = j <= c ? j : -1;
+  } else {
+    const int want = m - 2;
+    const int n = c - 1;  // candidates: blocks 1 .. c-1 (index = block - 1)
+    if (tid == 0) {
+      lst[0] = 0;
+      lst[m - 1] = c;
+    }
+    if (want > 0) {
+      const uint16_t* Sb = S + ((size_t)b * nb + 1) * DI;  // row j-1 = block j
+      for (int base = 0; base < n; base += U * RPI) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int row = min(base + u * RPI + r0, n - 1);
+          v[u] = *reinterpret_cast<const u32x4*>(Sb + (size_t)row * DI + col8 * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float dot = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dot += qv[2 * e] * bf16_lo(v[u][e]);
+            dot += qv[2 * e + 1] * bf16_hi(v[u][e]);
+          }
+          dot = group_sum_f<LPR>(dot);
+          const int row = base + u * RPI + r0;
+          if (col8 == 0 && row < n) sc[row] = dot;
+        }
+      }
+      __syncthreads();
+      if (tid < kWave) {  // one-wave select, R keys per lane
+        uint32_t key[R];
+#pragma unroll
+        for (int r = 0; r < R; r += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sc + tid * R + r);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) key[r + e] = tid * R + r + e < n ? score_key(v[e]) : 0u;
+        }
+        select_top<1, R, false>(key, want, sm, [&](int pos, int idx, bool take, uint32_t) {
+          if (take) lst[1 + pos] = 1 + idx;
+        });
+      }
+    }
+  }
+  __syncthreads();
+  if (p == 0)
+    for (int j = tid; j < m; j += 1024) blk[(size_t)q * m + j] = lst[j];
+
+  // ---- token scores of list positions p, p + P, ... (slot i * B + r)
+  int cq, n_sel, n_valid;
+  candidate_count(t, B, m, cq, n_sel, n_valid);
+  if (n_valid <= k) return;  // the query keeps all of its candidates
+  const int mine = (n_sel - p + P - 1) / P;
+  if (mine <= 0) return;
+  const int total = mine * B;  // rows of this workgroup's blocks
+  const uint16_t* kseq = kI + (size_t)b * L * DI;
+  float* outq = scores + (size_t)q * m * B;
+  for (int base = 0; base < total; base += U * RPI) {
+    u32x4 v[U];
+    int slot_of[U], rows_of[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int g = min(base + u * RPI + r0, total - 1);
+      const int i = p + (g >> log2B) * P;
+      const int j = max(lst[i], 0);
+      const int r = g & (B - 1);
+      const int rows = min(B, t - j * B + 1);
+      slot_of[u] = i * B + r;
+      rows_of[u] = lst[i] >= 0 ? rows - r : 0;  // > 0: a causal row of a kept block
+      v[u] = *reinterpret_cast<const u32x4*>(kseq + ((size_t)j * B + min(r, rows - 1)) * DI + col8 * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot += qv[2 * e] * bf16_lo(v[u][e]);
+        dot += qv[2 * e + 1] * bf16_hi(v[u][e]);
+      }
+      dot = group_sum_f<LPR>(dot);
+      if (col8 == 0 && base + u * RPI + r0 < total && rows_of[u] > 0) outq[slot_of[u]] = dot;
+    }
+  }
+}
+
+// Workgroups per query of k_block_token_decode (0: not used): the launch
+// should fill the chip in one round (one 1024-thread workgroup per CU),
+// with at least 4 workgroups per query to share out its token rows.
+static int block_token_parts(const Dims& s, int n_fold) {
+  const int groups = (s.b * s.nq + 7) / 8;
+  return std::min(8, (256 - n_fold) / (8 * groups));
+}
+
+static int block_token_fold_wgs(const Dims& s, const SummaryFold* fold) {
+  if (!fold) return 0;
+  return s.b * (s.lens ? 1 : s.nb - fold->start_block);
+}
+
+bool block_token_fusable(const Dims& s, const SummaryFold* fold) {
+  const int nq_total = s.b * s.nq;
+  const int c_max = (s.L - 1) / s.B;
+  if (nq_total == 0 || s.nq >= 64 || s.nL != 1 || c_max + 1 <= s.m || c_max - 1 > kFusedMaxBlocks) return false;
+  if (!((long long)s.k < (long long)s.m * s.B && s.L > s.k) || s.m > kBtMaxM) return false;
+  return block_token_parts(s, block_token_fold_wgs(s, fold)) >= 4;
+}
+
+hipError_t launch_block_token_decode(const Dims& s, const uint16_t* qI, const uint16_t* S, const uint16_t* kI,
+                                     int32_t* blk, float* scores, hipStream_t st, const SummaryFold* fold) {
+  if (!block_token_fusable(s, fold)) return hipErrorInvalidValue;
+  const int nq_total = s.b * s.nq;
+  const int n_fold = block_token_fold_wgs(s, fold);
+  const int P = block_token_parts(s, n_fold);
+  const int n_query_wg = ((nq_total + 7) / 8) * 8 * P;
+  const int nsum = fold ? (s.lens ? 1 : s.nb - fold->start_block) : 1;
+  uint16_t* S_out = fold ? fold->S : nullptr;
+  const int start = fold ? fold->start_block : s.nb;
+  const int n_max = (s.L - 1) / s.B - 1;
+  const dim3 grid(n_query_wg + n_fold);
+  const int log2B = __builtin_ctz((unsigned)s.B);
+#define HSA_BT(DI, RR)                                                                                              \
+  HSA_LAUNCH((k_block_token_decode<DI, RR>), grid, dim3(1024), 0, st, qI, S, kI, blk, scores, s.L, s.nq, s.B, log2B, \
+             s.nb, s.m, s.k, nq_total, P, n_query_wg, S_out, start, nsum, s.lens)
+  if (s.dI == 64) {
+    if (n_max <= 1024) HSA_BT(64, 16); else HSA_BT(64, 32);
+  } else {
+    if (n_max <= 1024) HSA_BT(128, 16); else HSA_BT(128, 32);
+  }
+#undef HSA_BT
+  return hipGetLastError();
 }
 
 template <int NW, int R>

@@ -80,6 +80,13 @@ hipError_t launch_block_topm_3level(const Dims& s, int lgG, int m2, const uint16
                                     const uint16_t* S2, int32_t* sup, int32_t* blk, void* ws, hipStream_t st,
                                     const SummaryFold* fold = nullptr, uint16_t* S2_out = nullptr);
 
+// steps 2 and 3's scores for few queries (decode): the block lists and the
+// token scores of launch_token_scores in one launch (with the summary fold
+// as in launch_block_topm), only where block_token_fusable holds
+bool block_token_fusable(const Dims& s, const SummaryFold* fold);
+hipError_t launch_block_token_decode(const Dims& s, const uint16_t* qI, const uint16_t* S, const uint16_t* kI,
+                                     int32_t* blk, float* scores, hipStream_t st, const SummaryFold* fold);
+
 // step 3: scores into [b*nq, m*B] fp32, then the top-k select
 size_t token_topk_ws_bytes(const Dims& s);
 hipError_t launch_token_topk(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,

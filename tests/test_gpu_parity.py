@@ -58,6 +58,13 @@ SMALL_CASES = [
            top_k=1000, n_heads_q=8, n_heads_kv=1), 2),
     (small("decode_select_attn_gqa2", batch=3, seq_len=30000, n_q=1, d_index=64, block=32, top_m=100,
            top_k=512, n_heads_q=8, n_heads_kv=2), 2),
+    # decode with the token scores inside the block top-m launch too (8
+    # workgroups per query): 1873 and 998 scored blocks (32 and 16 keys per
+    # lane of the block select), one and two queries per sequence
+    (small("decode_block_token_r32", batch=4, seq_len=30000, n_q=1, d_index=64, block=16, top_m=100,
+           top_k=512, n_heads_q=8, n_heads_kv=1), 2),
+    (small("decode_block_token_r16_nq2", batch=3, seq_len=16000, n_q=2, d_index=128, block=16, top_m=64,
+           top_k=512, n_heads_q=4, n_heads_kv=1), 2),
 ]
 
 

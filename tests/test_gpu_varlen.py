@@ -62,6 +62,11 @@ CASES = [
     (4, 40000, 64, 16, 20, 300, 1),
     # a capacity with no scoring at all: the summary update runs on its own
     (3, 100, 64, 16, 8, 40, 1),
+    # the block top-m with the token scores in one launch, then the select
+    # inside the attention launch (lengths with c + 1 < m, = m and > m,
+    # keeping all candidates or scoring them)
+    (8, 20000, 128, 16, 64, 512, 1),
+    (6, 12000, 64, 16, 40, 256, 1),
 ]
 
 
