@@ -390,14 +390,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 // candidate (the scores) and no time where the launch has one workgroup per
 // CU or fewer, and it removes a launch, the list's round trip through memory
 // and a launch gap from the step.
+// Waves of a k_select_attn workgroup: all select, 4 attend.
+constexpr int kSaWaves = 8;
+
 template <int R, bool ONEBLK>
-__global__ __launch_bounds__(512) void k_select_attn(const float* __restrict__ scores, const int32_t* __restrict__ blk,
+__global__ __launch_bounds__(kSaWaves * 64) void k_select_attn(const float* __restrict__ scores, const int32_t* __restrict__ blk,
                                                      int32_t* __restrict__ tok, const uint16_t* __restrict__ Q,
                                                      const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                                      float* __restrict__ part, int L, int nq, int B, int log2B, int m,
                                                      int k, int Hq, int Hkv, int chunk, int nsplit, float scale_log2,
                                                      const int32_t* __restrict__ lens) {
-  constexpr int NW = 8;
+  constexpr int NW = kSaWaves;
+  constexpr int NT = NW * kWave;
   __shared__ __attribute__((aligned(16))) unsigned char stage_lds[4 * kWaveLds];
   __shared__ SelectSmem<NW> sel;
   // the block list (m entries, padded to 4), then list positions
@@ -419,12 +423,12 @@ __global__ __launch_bounds__(512) void k_select_attn(const float* __restrict__ s
   if (wave >= 4) {
     if (g == 0) {
       int32_t* out = tok + (size_t)q * k + p_lo;
-      const int n = p_hi - p_lo, x = (int)threadIdx.x - 256;
+      const int n = p_hi - p_lo, x = (int)threadIdx.x - 256, nx = NT - 256;
       if ((k & 3) == 0) {  // 16-byte aligned, n a multiple of 4
-        for (int p = 4 * x; p < n; p += 4 * 256)
+        for (int p = 4 * x; p < n; p += 4 * nx)
           *reinterpret_cast<u32x4*>(out + p) = *reinterpret_cast<const u32x4*>(plist + p);
       } else {
-        for (int p = x; p < n; p += 256) out[p] = plist[p];
+        for (int p = x; p < n; p += nx) out[p] = plist[p];
       }
     }
     return;
@@ -599,7 +603,7 @@ static bool sa_scoring(const Dims& s) { return (long long)s.k < (long long)s.m *
 static int sa_slots(const Dims& s) {
   if (!sa_scoring(s)) return 1;
   int r = 1;
-  while ((long long)r * 512 < (long long)s.m * s.B) r <<= 1;
+  while ((long long)r * kSaWaves * 64 < (long long)s.m * s.B) r <<= 1;
   return r;
 }
 static size_t sa_dyn_lds(const Dims& s, int chunk) {
@@ -613,7 +617,7 @@ bool select_attn_fusable(const Dims& s) {
   split_plan(s, nsplit, chunk);
   if (nsplit < 4 || nsplit % 4 != 0) return false;  // 4 splits of one (query, kv head) per workgroup
   if (sa_slots(s) > 32) return false;
-  return sa_dyn_lds(s, chunk) + 4 * kWaveLds + sizeof(SelectSmem<8>) <= kMaxLdsBytes;
+  return sa_dyn_lds(s, chunk) + 4 * kWaveLds + sizeof(SelectSmem<kSaWaves>) <= kMaxLdsBytes;
 }
 
 size_t select_attn_ws_bytes(const Dims& s) { return token_topk_ws_bytes(s) + sparse_attn_ws_bytes(s); }
@@ -626,7 +630,7 @@ static hipError_t launch_sa_k(const Dims& s, const float* scores, const int32_t*
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sa_dyn_lds(s, chunk));
   if (e != hipSuccess) return e;
   const int n_wg = (int)((long long)s.b * s.nq * s.Hkv * nsplit / 4);
-  HSA_LAUNCH((k_select_attn<R, ONEBLK>), dim3(n_wg), dim3(512), sa_dyn_lds(s, chunk), st, scores, blk, tok, Q, K, V,
+  HSA_LAUNCH((k_select_attn<R, ONEBLK>), dim3(n_wg), dim3(kSaWaves * 64), sa_dyn_lds(s, chunk), st, scores, blk, tok, Q, K, V,
              part, s.L, s.nq, s.B, __builtin_ctz((unsigned)s.B), s.m, s.k, s.Hq, s.Hkv, chunk, nsplit,
              s.scale * 1.4426950408889634f, s.lens);
   return hipGetLastError();
