@@ -11,12 +11,13 @@ line.
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 Kernel times come from start/stop events that each kernel's dispatch
-carries (hsa_sparse_set_kernel_events, hipExtLaunchKernelGGL), which add no
-work to the stream: an untimed pass times every kernel of a step and names
-the dominant (longest) one; in the timed region only that kernel carries
-events.  The roofline entry divides that kernel's algorithmic bytes (or
-flops) per launch, computed in closed form below, by its average duration
-over the timed steps.  Stage times (an untimed pass with the stage events of
+carries (hsa_sparse_set_kernel_events, hipExtLaunchKernelGGL): an untimed
+pass times every kernel of a step and names the dominant (longest) one; in
+the timed region that kernel's dispatches carry events on every 8th step
+(an event-carrying dispatch costs the stream a few microseconds).  The
+roofline entry divides that kernel's algorithmic bytes (or flops) per
+launch, computed in closed form below, by its average duration over those
+steps.  Stage times (an untimed pass with the stage events of
 hsa_sparse_set_stage_events, a few microseconds of stream time each) are
 reported alongside.
 The CPU baseline times the plain CPU oracle on a stratified sample of the
@@ -1005,8 +1006,8 @@ def oracle_state(w: Workload, inp: dict):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill_64k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-sample", type=int, default=1024, help="queries the CPU oracle is timed on")
     ap.add_argument("--batch", type=int, default=0,
