@@ -43,7 +43,7 @@ constexpr int kFlatMergeLarge = 16 * 64 * 32;
 constexpr int kFlatStageMax = 8192;
 constexpr int kFlatKeysPerWG = 512;  // score tile: 64 queries x 512 tokens (128 per wave)
 
-template <int DI>
+template <int DI, bool STREAM>
 __global__ __launch_bounds__(256) void k_flat_scores(const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI,
                                                      float* __restrict__ scores, int L, int nq, int Lp,
                                                      int qtiles_per_seq) {
@@ -101,7 +101,10 @@ __global__ __launch_bounds__(256) void k_flat_scores(const uint16_t* __restrict_
       for (int kt = 0; kt < 2; ++kt) {
         // lane: tokens s0 .. s0+3 of query i0 + 16mt + jl
         const int s0 = key0 + 16 * kt + 4 * gq;
-        if (s0 <= tq[mt]) *reinterpret_cast<f32x4*>(dst + s0) = acc[mt][kt];
+        if (s0 <= tq[mt]) {
+          if constexpr (STREAM) __builtin_nontemporal_store(acc[mt][kt], reinterpret_cast<f32x4*>(dst + s0));
+          else *reinterpret_cast<f32x4*>(dst + s0) = acc[mt][kt];
+        }
       }
     }
   }
@@ -624,10 +627,15 @@ hipError_t launch_flat_topk(const Dims& s, const uint16_t* qI, const uint16_t* k
   if (s.k < s.L) {
     const int qtiles = (s.nq + 63) / 64;
     dim3 grid((s.L + kFlatKeysPerWG - 1) / kFlatKeysPerWG, qtiles * s.b);
-    if (s.dI == 64)
-      HSA_LAUNCH((k_flat_scores<64>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+    const bool nt = (size_t)nq_total * Lp * sizeof(float) > kStreamStoreBytes;
+    if (s.dI == 64 && nt)
+      HSA_LAUNCH((k_flat_scores<64, true>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+    else if (s.dI == 64)
+      HSA_LAUNCH((k_flat_scores<64, false>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+    else if (nt)
+      HSA_LAUNCH((k_flat_scores<128, true>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
     else
-      HSA_LAUNCH((k_flat_scores<128>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
+      HSA_LAUNCH((k_flat_scores<128, false>), grid, dim3(256), 0, st, qI, kI, scores, s.L, s.nq, Lp, qtiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     p += align_up((size_t)nq_total * Lp * sizeof(float));

@@ -17,6 +17,13 @@ namespace hsa {
 // kernel list.
 void kernel_slot(const char* name, hipEvent_t* start, hipEvent_t* stop);
 
+// Score buffers larger than the 256 MB last-level cache (MALL) are written
+// with non-temporal stores: they are read back only once the whole buffer
+// is written, so caching them on the way only evicts the rows the scorer
+// itself re-reads.  (Smaller buffers stay cached for the select that
+// follows.)
+constexpr size_t kStreamStoreBytes = size_t(256) << 20;
+
 // Every kernel of the library is launched through this: with recording on,
 // the dispatch itself carries the kernel's start and stop events
 // (hipExtLaunchKernelGGL), so timing a kernel adds no work to the stream.

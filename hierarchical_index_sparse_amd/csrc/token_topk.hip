@@ -204,7 +204,7 @@ __host__ __device__ inline TiledLayout tiled_layout(int nJ, int QW, int m, int D
   return t;
 }
 
-template <int DI, int QW>
+template <int DI, int QW, bool STREAM>
 __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_token_scores_tiled(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI, const int32_t* __restrict__ blk,
     float* __restrict__ scores, int L, int nq, int B, int m, int k, int tiles_per_seq, int n_tiles, int nJ_max,
@@ -369,7 +369,8 @@ __global__ __launch_bounds__(kTiledWaves * 64) __attribute__((amdgpu_waves_per_e
           if (valid) {
             const int s0 = j * B + 16 * mt + 4 * kgrp;
             if (s0 + 3 <= t) {
-              *reinterpret_cast<f32x4*>(dst + 16 * mt) = acc;
+              if constexpr (STREAM) __builtin_nontemporal_store(acc, reinterpret_cast<f32x4*>(dst + 16 * mt));
+              else *reinterpret_cast<f32x4*>(dst + 16 * mt) = acc;
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
@@ -694,21 +695,29 @@ static int tiled_qw(const Dims& s) {
   return 0;
 }
 
-template <int DI, int QW>
-static hipError_t launch_tiled_t(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
-                                 float* scores, hipStream_t st) {
+template <int DI, int QW, bool NT>
+static hipError_t launch_tiled_nt(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
+                                  float* scores, hipStream_t st) {
   const int QT = 64 * QW;
   const int tiles_per_seq = (s.nq + QT - 1) / QT;
   const int n_tiles = tiles_per_seq * s.b;
   const size_t lds = tiled_layout(s.nb, QW, s.m, DI).total;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_token_scores_tiled<DI, QW>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_token_scores_tiled<DI, QW, NT>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
   if (e != hipSuccess) return e;
   // about two workgroups per CU in total, at most 4 per tile
   const int parts = std::max(1, std::min(4, (512 + n_tiles - 1) / n_tiles));
-  HSA_LAUNCH((k_token_scores_tiled<DI, QW>), dim3(n_tiles * parts), dim3(kTiledWaves * 64), lds, st, qI, kI,
+  HSA_LAUNCH((k_token_scores_tiled<DI, QW, NT>), dim3(n_tiles * parts), dim3(kTiledWaves * 64), lds, st, qI, kI,
                      blk, scores, s.L, s.nq, s.B, s.m, s.k, tiles_per_seq, n_tiles, s.nb, parts);
   return hipGetLastError();
+}
+
+template <int DI, int QW>
+static hipError_t launch_tiled_t(const Dims& s, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
+                                 float* scores, hipStream_t st) {
+  if ((size_t)s.b * s.nq * s.m * s.B * sizeof(float) > kStreamStoreBytes)
+    return launch_tiled_nt<DI, QW, true>(s, qI, kI, blk, scores, st);
+  return launch_tiled_nt<DI, QW, false>(s, qI, kI, blk, scores, st);
 }
 
 static hipError_t launch_tiled(const Dims& s, int qw, const uint16_t* qI, const uint16_t* kI, const int32_t* blk,
