@@ -457,6 +457,11 @@ hsa_sparse_status_t hsa_forward_heads(const hsa_sparse_shape_t* shape,
  * made by the calling thread records events[0] on its stream before step 1 and events[s] after
  * step s (s = 1..4); a NULL entry is not recorded.  Each recorded event costs the stream a few microseconds, which
  * matters for short (decode) steps, so record only the boundaries needed.
+ * Where a decode-shaped call runs two steps in one launch, the events
+ * follow the launches: with the token select inside the attention launch,
+ * event 3 follows the token scorer and step 4 holds the select; with the
+ * token scores inside the block top-m launch as well, event 3 follows
+ * event 2 directly.
  * The events are the caller's hipEvent_t handles and must stay valid while
  * such calls are made.  n_events must be 5 with at least one non-NULL
  * entry, or 0 with events == NULL to stop recording.
@@ -468,8 +473,9 @@ hsa_sparse_status_t hsa_sparse_set_stage_events(hsa_sparse_event_t const* events
  * Per-kernel timing (profiling aid).  After this call, kernel i (0-based,
  * in launch order) of every entry-point call made by the calling thread
  * carries start[i] and stop[i] in its dispatch, recorded when that kernel
- * starts and ends (hipExtLaunchKernelGGL), so the stream runs no extra
- * work for them; NULL entries and kernels past n_events - 1 record nothing.
+ * starts and ends (hipExtLaunchKernelGGL); NULL entries and kernels past
+ * n_events - 1 record nothing.  An event-carrying dispatch costs the stream
+ * a few microseconds, so time a sample of calls where steps are short.
  * hsa_sparse_last_kernels() then names the kernels of the thread's last
  * call, comma-separated, in launch order.  The events are the caller's
  * hipEvent_t handles and must stay valid while such calls are made.
