@@ -951,23 +951,27 @@ def block_score_mfma(w: Workload, dev: dict, S, hip, steps: int, peaks: dict | N
     _lib.hsa_block_score_max(shape, dev["qI"], S, out, ws)
     torch.cuda.synchronize()
     n = max(5, min(steps, 20))
-    ev = [(hip.create(), hip.create()) for _ in range(n)]
+    # events around each kernel of the call (a second kernel reduces per-chunk
+    # maxima when the rows are split over workgroups); the time runs from the
+    # first kernel's start to the last kernel's end
+    ev = [[hip.create() for _ in range(4)] for _ in range(n)]
     names = None
-    for a, b in ev:
-        _lib.hsa_sparse_set_kernel_events([a], [b])
+    for a0, a1, b0, b1 in ev:
+        _lib.hsa_sparse_set_kernel_events([a0, a1], [b0, b1])
         _lib.hsa_block_score_max(shape, dev["qI"], S, out, ws)
         names = _lib.hsa_sparse_last_kernels()
     torch.cuda.synchronize()
     _lib.hsa_sparse_set_kernel_events(None, None)
-    us = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev])) * 1000.0
-    for a, b in ev:
-        hip.destroy(a)
-        hip.destroy(b)
+    last = len(names) - 1
+    us = float(np.mean([hip.elapsed_ms(e[0], e[2 + last]) for e in ev])) * 1000.0
+    for e in ev:
+        for x in e:
+            hip.destroy(x)
     del out, ws
     sb, _, _ = per_query_counts(w)
     flops = 2.0 * w.d_index * w.n_landmarks * float(sb.sum()) * w.batch
     tfs = flops / (us / 1e6) / 1e12
-    res = {"kernel": names[0], "kernel_us": us, "algorithmic_GFLOP": flops / 1e9, "achieved_TFLOPs": tfs,
+    res = {"kernel": names[0], "kernels": names, "kernel_us": us, "algorithmic_GFLOP": flops / 1e9, "achieved_TFLOPs": tfs,
            "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tfs / MFMA_BF16_PEAK_TFLOPS,
            "block_topm_stage_ms": stage_ms,
            "note": "score-only build of the block-score MFMA tiling (per-query maximum on chip, 4 B per query "

@@ -285,56 +285,63 @@ __global__ __launch_bounds__(256) void k_block_topm_tile(const uint16_t* __restr
 
 // Score-only build of the block-score contraction (a measurement aid: the
 // scores of k_block_scores_mfma without the selection), tiled for the
-// matrix cores.  One workgroup takes 256 consecutive queries (wave w holds
-// queries 64w .. 64w+63 as MFMA A operands in registers) and walks its
-// chunk of 128-row summary tiles; each tile is loaded once per workgroup
-// into LDS (padded rows, double-buffered: the next tile's rows are in
-// flight in registers while the current one is multiplied) and read by all
-// four waves as B operands, so every summary row fetched from L2 feeds 256
-// queries.  Instead of writing every score it keeps, per query, the maximum
-// over the scored blocks 1 .. c-1 (all landmark rows of a block count, so
-// the landmark maximum is part of it), reduced over lanes on chip: one
-// float per (query, chunk) leaves the chip.  -inf marks a query with no
-// scored block in the chunk.
+// matrix cores.  One workgroup of 8 waves takes 256 consecutive queries:
+// waves w and w + 4 hold queries 64 (w % 4) .. 64 (w % 4) + 63 as MFMA A
+// operands in registers and share the 16-row groups of every 128-row
+// summary tile between them (even groups to w, odd groups to w + 4), so
+// two waves per SIMD keep the matrix cores fed.  Each tile is loaded once
+// per workgroup into LDS (padded rows, double-buffered: the next tile's
+// rows are in flight in registers while the current one is multiplied) and
+// read by all eight waves as B operands, so every summary row fetched from
+// L2 feeds 256 queries.  Instead of writing every score it keeps, per
+// query, the maximum over the scored blocks 1 .. c-1 (all landmark rows of
+// a block count, so the landmark maximum is part of it), reduced over lanes
+// and over the wave pair on chip: one float per (query, chunk) leaves the
+// chip.  -inf marks a query with no scored block in the chunk.  A row group
+// that every query of the wave scores in full takes the maximum without
+// per-element bounds; groups past every query's causal rows are skipped.
 constexpr int kMaxQT = 256;   // queries per workgroup
 constexpr int kMaxRT = 128;   // summary rows per tile
+constexpr int kMaxWaves = 8;  // waves per workgroup
 
 template <int DI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_block_scores_max(
-    const uint16_t* __restrict__ qI, const uint16_t* __restrict__ S, float* __restrict__ out, int L, int nq, int B,
-    int nb, int NL, int m, int qtiles_per_seq, int tiles_per_chunk, int nchunks) {
+__global__ __launch_bounds__(kMaxWaves * 64) void k_block_scores_max(
+    const uint16_t* __restrict__ qI, const uint16_t* __restrict__ S, float* __restrict__ out, int L, int nq,
+    int log2B, int nb, int NL, int m, int qtiles_per_seq, int tiles_per_chunk, int nchunks) {
   constexpr int KS = DI / 32;
+  constexpr int NT = kMaxWaves * 64;
   constexpr int LPR = DI / 8;              // 16-byte lanes per summary row
-  constexpr int RPP = 256 / LPR;           // rows per load pass of the workgroup
+  constexpr int RPP = NT / LPR;            // rows per load pass of the workgroup
   constexpr int NP = kMaxRT / RPP;         // load passes per tile
   constexpr int PITCH = DI + 8;            // LDS row pitch (bf16): 16-byte reads conflict-free
   __shared__ __attribute__((aligned(16))) uint16_t bt[2][kMaxRT * PITCH];
+  __shared__ float pair_mx[4][64];
   const int b = blockIdx.y / qtiles_per_seq;
   // the latest query tiles (the most causal tiles) are dispatched first
   const int i0 = (qtiles_per_seq - 1 - (int)(blockIdx.y % qtiles_per_seq)) * kMaxQT;
   const int chunk = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
+  const int qgrp = wave & 3, half = wave >> 2;  // query group, row-group parity
   const int lane = lane_id();
   const int jl = lane & 15, gq = lane >> 4;
   const int nrows = nb * NL;
   const int i_last = min(nq, i0 + kMaxQT) - 1;
-  const int c_last = query_pos(L, nq, i_last) / B;
+  const int c_last = query_pos(L, nq, i_last) >> log2B;
   // rows any query of the tile scores: blocks 1 .. c_last - 1
   const int tile_lo = chunk * tiles_per_chunk;
   const int tile_hi = min((c_last * NL + kMaxRT - 1) / kMaxRT, (chunk + 1) * tiles_per_chunk);  // exclusive
-
+  // scored rows of query i: NL <= row < hi(i) (none when c + 1 <= m)
+  auto rows_hi = [&](int i) {
+    const int c = query_pos(L, nq, i) >> log2B;
+    return c + 1 > m ? c * NL : 0;
+  };
   // the lane's accumulator entries hold queries qw + 16 mt + 4 gq + e
-  const int qw = i0 + 64 * wave;
-  int row_hi[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = qw + 16 * mt + 4 * gq + e;
-      const int c = i < nq ? query_pos(L, nq, i) / B : 0;
-      row_hi[mt][e] = c + 1 > m ? c * NL : 0;  // scored rows: NL <= row < c * NL
-    }
+  const int qw = i0 + 64 * qgrp;
+  const bool wave_live = qw < nq;  // uniform over the wave
+  const int hi_first = wave_live ? rows_hi(qw) : 0;                 // every live query scores rows below this
+  const int hi_last = wave_live ? rows_hi(min(nq, qw + 64) - 1) : 0;  // no query scores rows from here on
+
   float mx[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -373,9 +380,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const bool more = tile + 1 < tile_hi;  // uniform
       if (more) load_tile(tile + 1);
       const uint16_t* bb = bt[buf];
-#pragma unroll 2
-      for (int nt = 0; nt < kMaxRT / 16; ++nt) {
-        const int row = tile * kMaxRT + 16 * nt + jl;
+#pragma unroll
+      for (int g = 0; g < kMaxRT / 32; ++g) {
+        const int nt = 2 * g + half;
+        const int row0 = tile * kMaxRT + 16 * nt;  // the group's first row (uniform)
+        if (row0 >= hi_last) break;                 // no query of the wave scores these rows or later ones
         u32x4 bs[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -391,11 +400,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int mt = 0; mt < 4; ++mt)
             acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt][ks]),
                                                               __builtin_bit_cast(bf16x8, bs[ks]), acc[mt], 0, 0, 0);
+        if (row0 >= NL && row0 + 16 <= hi_first) {  // every query of the wave scores all 16 rows
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (row >= NL && row < row_hi[mt][e]) mx[mt][e] = fmaxf(mx[mt][e], acc[mt][e]);
+            for (int e = 0; e < 4; ++e) mx[mt][e] = fmaxf(mx[mt][e], acc[mt][e]);
+        } else {
+          const int row = row0 + jl;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = qw + 16 * mt + 4 * gq + e;
+              if (row >= NL && row < rows_hi(i)) mx[mt][e] = fmaxf(mx[mt][e], acc[mt][e]);
+            }
+        }
       }
       if (more) {
         stage_tile(buf ^ 1);  // the other buffer: last read two tiles ago, before the barrier below
@@ -404,15 +423,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   }
-  // max over the 16 rows (lanes jl) of each accumulator entry
+  // max over the 16 rows (lanes jl) of each accumulator entry, then over
+  // the wave pair: the odd-group wave hands its maxima to the even one
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = group_max_f<16>(mx[mt][e]);
-      const int i = qw + 16 * mt + 4 * gq + e;
-      if (jl == 0 && i < nq) out[((size_t)b * nq + i) * nchunks + chunk] = v;
-    }
+    for (int e = 0; e < 4; ++e) mx[mt][e] = group_max_f<16>(mx[mt][e]);
+  if (half == 1 && jl == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pair_mx[qgrp][16 * mt + 4 * gq + e] = mx[mt][e];
+  }
+  __syncthreads();
+  if (half == 0 && jl == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * mt + 4 * gq + e;
+        const int i = qw + r;
+        if (i < nq) out[((size_t)b * nq + i) * nchunks + chunk] = fmaxf(mx[mt][e], pair_mx[qgrp][r]);
+      }
+  }
 }
 
 // The per-chunk maxima of k_block_scores_max reduced to one per query.
@@ -818,10 +851,14 @@ size_t block_topm_ws_bytes(const Dims& s) { return align_up((size_t)s.b * s.nq *
 // tiles of its chunk, so the tiles are split into chunks only as far as
 // needed to give about two workgroups per CU (512), the most the LDS holds,
 // so that causal tiles of very different lengths still spread over the chip.
+constexpr int kScoreMaxWgs = 256;
+
 static void score_max_plan(const Dims& s, int& tiles_per_chunk, int& nchunks) {
   const int qtiles = std::max(1, s.b * ((s.nq + kMaxQT - 1) / kMaxQT));
   const int ntiles = std::max(1, (s.nb * s.nL + kMaxRT - 1) / kMaxRT);
-  const int want = std::max(1, std::min(ntiles, (512 + qtiles - 1) / qtiles));
+  // about one 8-wave workgroup per CU; row chunks only when the query
+  // tiles alone would leave CUs idle
+  const int want = std::max(1, std::min(ntiles, (kScoreMaxWgs + qtiles - 1) / qtiles));
   tiles_per_chunk = (ntiles + want - 1) / want;
   nchunks = (ntiles + tiles_per_chunk - 1) / tiles_per_chunk;
 }
@@ -841,11 +878,13 @@ hipError_t launch_block_score_max(const Dims& s, const uint16_t* qI, const uint1
   const int qtiles = (s.nq + kMaxQT - 1) / kMaxQT;
   float* dst = nchunks > 1 ? static_cast<float*>(ws) : out;
   const dim3 grid(nchunks, qtiles * s.b);
+  const int log2B = __builtin_ctz((unsigned)s.B);
+  const dim3 block(kMaxWaves * 64);
   if (s.dI == 64)
-    HSA_LAUNCH((k_block_scores_max<64>), grid, dim3(256), 0, st, qI, S, dst, s.L, s.nq, s.B, s.nb, s.nL, s.m, qtiles,
+    HSA_LAUNCH((k_block_scores_max<64>), grid, block, 0, st, qI, S, dst, s.L, s.nq, log2B, s.nb, s.nL, s.m, qtiles,
                tpc, nchunks);
   else
-    HSA_LAUNCH((k_block_scores_max<128>), grid, dim3(256), 0, st, qI, S, dst, s.L, s.nq, s.B, s.nb, s.nL, s.m,
+    HSA_LAUNCH((k_block_scores_max<128>), grid, block, 0, st, qI, S, dst, s.L, s.nq, log2B, s.nb, s.nL, s.m,
                qtiles, tpc, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 1) return e;
