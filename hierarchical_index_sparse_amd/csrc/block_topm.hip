@@ -770,12 +770,15 @@ __global__ __launch_bounds__(1024) void k_block_token_decode(
   }
 }
 
-// Workgroups per query of k_block_token_decode (0: not used): the launch
-// should fill the chip in one round (one 1024-thread workgroup per CU),
-// with at least 4 workgroups per query to share out its token rows.
-static int block_token_parts(const Dims& s, int n_fold) {
+// Workgroups per query of k_block_token_decode (0: not used): the query
+// workgroups should fill the chip in one round (one 1024-thread workgroup
+// per CU), with at least 4 per query to share out its token rows.  The few
+// summary workgroups of a fold run on the CUs the first query workgroups
+// free (decode_128k: 8 per query and 32 summaries, 41.0 µs per step,
+// against 7 per query sharing the first round with them, 41.5 µs).
+static int block_token_parts(const Dims& s) {
   const int groups = (s.b * s.nq + 7) / 8;
-  return std::min(8, (256 - n_fold) / (8 * groups));
+  return std::min(8, 256 / (8 * groups));
 }
 
 static int block_token_fold_wgs(const Dims& s, const SummaryFold* fold) {
@@ -783,12 +786,12 @@ static int block_token_fold_wgs(const Dims& s, const SummaryFold* fold) {
   return s.b * (s.lens ? 1 : s.nb - fold->start_block);
 }
 
-bool block_token_fusable(const Dims& s, const SummaryFold* fold) {
+bool block_token_fusable(const Dims& s, const SummaryFold* /*fold*/) {
   const int nq_total = s.b * s.nq;
   const int c_max = (s.L - 1) / s.B;
   if (nq_total == 0 || s.nq >= 64 || s.nL != 1 || c_max + 1 <= s.m || c_max - 1 > kFusedMaxBlocks) return false;
   if (!((long long)s.k < (long long)s.m * s.B && s.L > s.k) || s.m > kBtMaxM) return false;
-  return block_token_parts(s, block_token_fold_wgs(s, fold)) >= 4;
+  return block_token_parts(s) >= 4;
 }
 
 hipError_t launch_block_token_decode(const Dims& s, const uint16_t* qI, const uint16_t* S, const uint16_t* kI,
@@ -796,7 +799,7 @@ hipError_t launch_block_token_decode(const Dims& s, const uint16_t* qI, const ui
   if (!block_token_fusable(s, fold)) return hipErrorInvalidValue;
   const int nq_total = s.b * s.nq;
   const int n_fold = block_token_fold_wgs(s, fold);
-  const int P = block_token_parts(s, n_fold);
+  const int P = block_token_parts(s);
   const int n_query_wg = ((nq_total + 7) / 8) * 8 * P;
   const int nsum = fold ? (s.lens ? 1 : s.nb - fold->start_block) : 1;
   uint16_t* S_out = fold ? fold->S : nullptr;
