@@ -657,6 +657,12 @@ def roofline_entry(w: Workload, kernel: str, kernel_ms: float, n_launch: int, le
     roof["traffic"] = recorded_traffic(w.name, kernel)
     roof["traffic_note"] = ("FETCH_SIZE and WRITE_SIZE per launch, scaled by a copy of known size: bytes between "
                             "L2 and the memory fabric, MALL hits included (an upper bound on DRAM bytes)")
+    if roof["traffic"] is not None:
+        # the counted bytes over the launch time: the second reading of the
+        # HBM fraction, an upper bound on the DRAM rate (MALL hits included)
+        rate = roof["traffic"] / (kernel_ms / 1000.0 / n_launch) / 1e9
+        roof["traffic_GBs"] = rate
+        roof["traffic_frac_of_hbm_peak"] = rate / HBM_PEAK_GBS
     roof["kernel"] = kernel
     roof["stage"] = KERNEL_STAGE.get(kernel)
     roof["launches_per_step"] = n_launch
