@@ -977,8 +977,8 @@ def block_score_mfma(w: Workload, dev: dict, S, hip, steps: int, peaks: dict | N
     sb, _, _ = per_query_counts(w)
     flops = 2.0 * w.d_index * w.n_landmarks * float(sb.sum()) * w.batch
     tfs = flops / (us / 1e6) / 1e12
-    res = {"kernel": names[0], "kernels": names, "kernel_us": us, "algorithmic_GFLOP": flops / 1e9, "achieved_TFLOPs": tfs,
-           "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tfs / MFMA_BF16_PEAK_TFLOPS,
+    res = {"kernel": names[0], "kernels": names, "kernel_us": us, "algorithmic_GFLOP": flops / 1e9,
+           "achieved_TFLOPs": tfs, "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS, "frac": tfs / MFMA_BF16_PEAK_TFLOPS,
            "block_topm_stage_ms": stage_ms,
            "note": "score-only build of the block-score MFMA tiling (per-query maximum on chip, 4 B per query "
                    "written); the block_topm stage (scores written, then the exact top-m select) for comparison"}
