@@ -65,6 +65,12 @@ SMALL_CASES = [
            top_k=512, n_heads_q=8, n_heads_kv=1), 2),
     (small("decode_block_token_r16_nq2", batch=3, seq_len=16000, n_q=2, d_index=128, block=16, top_m=64,
            top_k=512, n_heads_q=4, n_heads_kv=1), 2),
+    # the same launch with fewer workgroups per query: 40 queries (6 per
+    # query) and 64 queries (4 per query, the fewest it takes)
+    (small("decode_block_token_p6", batch=40, seq_len=6000, n_q=1, d_index=64, block=16, top_m=30,
+           top_k=200, n_heads_q=4, n_heads_kv=1), 2),
+    (small("decode_block_token_p4", batch=64, seq_len=6000, n_q=1, d_index=128, block=16, top_m=30,
+           top_k=200, n_heads_q=4, n_heads_kv=1), 2),
 ]
 
 
@@ -141,11 +147,16 @@ DECODE_FOLD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("L,nq,B,dI,nL", DECODE_FOLD_CASES)
-def test_incremental_decode_summaries(L, nq, B, dI, nL):
+# batches whose block top-m launch has fewer workgroups per query (6 and 4)
+# and the summary-fold workgroups past the first round of the chip
+DECODE_FOLD_CASES_WIDE = [(5000, 1, 32, 64, 1, 40), (5000, 1, 32, 128, 1, 64)]
+
+
+@pytest.mark.parametrize("L,nq,B,dI,nL,batch", [c + (3,) for c in DECODE_FOLD_CASES] + DECODE_FOLD_CASES_WIDE)
+def test_incremental_decode_summaries(L, nq, B, dI, nL, batch):
     # decode-shaped calls with only the newest blocks re-summarised: the same
     # bits as a full forward, and every query equal to the oracle
-    w = small("decode_inc", batch=3, seq_len=L, n_q=nq, d_index=dI, block=B, top_m=6, top_k=150,
+    w = small("decode_inc", batch=batch, seq_len=L, n_q=nq, d_index=dI, block=B, top_m=6, top_k=150,
               n_heads_q=8, n_heads_kv=2, n_landmarks=nL)
     inp = datagen.make_inputs(w, q_range=3, centre_range=2, noise_range=2)
     dev = pipeline.to_device(inp)
