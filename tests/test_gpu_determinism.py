@@ -8,7 +8,8 @@ must be bit-identical.  This catches races in the selects and merges (the
 block-major token scorer fills its per-block lists through atomic cursors,
 the decode attention merges split partials) and any read of a scratch
 location the call did not write first.  The cases take the decode, chunked
-prefill, keep-all, three-level, per-head, variable-length and flat paths.
+prefill, keep-all, three-level, per-head, variable-length and flat paths,
+and the score-only block-score contraction.
 """
 import numpy as np
 import pytest
@@ -137,3 +138,21 @@ def test_flat_topk_repeatable():
     _lib.hsa_flat_topk(shape, dev["qI"], dev["kI"], b, dirty_workspace(shape, _lib.HSA_SPARSE_OP_FLAT_TOPK))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n_q,seq_len,block", [(130, 200000, 16), (65536, 65536, 128)])
+def test_block_score_max_repeatable(n_q, seq_len, block):
+    # the score-only block-score contraction: per-chunk maxima through the
+    # workspace and a reduce (a few queries against many summary rows), and
+    # one launch straight into the output (many queries)
+    w = W(name="det_score_max", seq_len=seq_len, n_q=n_q, d_index=64, block=block, top_m=5, top_k=50, n_heads_q=1)
+    dev = pipeline.to_device(datagen.make_inputs(w, attention=False))
+    shape = _lib.shape_of(w)
+    S = torch.zeros((w.batch, w.n_blocks, 1, w.d_index), dtype=torch.bfloat16, device="cuda")
+    _lib.hsa_block_summary(shape, dev["kI"], None, 0, S)
+    a = torch.full((w.batch, w.n_q), float("nan"), dtype=torch.float32, device="cuda")
+    b = torch.full((w.batch, w.n_q), 1.0e30, dtype=torch.float32, device="cuda")
+    _lib.hsa_block_score_max(shape, dev["qI"], S, a)
+    _lib.hsa_block_score_max(shape, dev["qI"], S, b, dirty_workspace(shape, _lib.HSA_SPARSE_OP_BLOCK_SCORE_MAX))
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
